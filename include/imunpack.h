@@ -1,0 +1,225 @@
+/*
+ * imunpack.h -- C ABI of the IM-Unpack exact low bit-width integer GEMM path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method source: the summary page "IM-Unpack: Training and Inference with
+ * Arbitrarily Low Precision Integers".  A float GEMM C = A.B is quantized with
+ * round-to-nearest (RTN) so that the p-percentile magnitude of each matrix maps
+ * to the integer beta ("Measured effects" table: p = 95%, beta = 15 / 31);
+ * heavy hitters stay as out-of-range integers instead of being clipped
+ * (summary paragraph, "Problem").  Out-of-range integers are unpacked into
+ * several in-range b-bit integers placed in extra rows or columns, chosen per
+ * matrix from outlier counts (row, column or Mix unpacking; "Approach" and the
+ * unpack-ratio rows of the table), and low bit-width GEMMs on the unpacked
+ * matrices followed by bit-shift scaling and accumulation give the original
+ * integer product exactly ("Approach").
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ * - Every data pointer is a DEVICE pointer unless marked "host".  The caller
+ *   owns every buffer; no entry point allocates or frees memory.
+ * - All work is enqueued on `stream` (HIP stream; 0 = the null stream).  Only
+ *   imu_plan_unpack and imu_imunpack_matmul wait for the device, once each, to
+ *   read the plan header (the unpacked sizes are data dependent).
+ * - Argument errors are returned synchronously and nothing is enqueued.
+ *   Conditions found on the device (non-finite input, |x.r| >= 2^31) are
+ *   latched in the operand's statistics and returned at the next wait.
+ * - The integer result C is defined modulo 2^32 (two's complement int32),
+ *   which equals the exact product whenever it fits in int32.
+ * - Batched operands (batch > 1) are independent problems: each batch entry
+ *   has its own percentile scale, plan and unpacked sizes.
+ * - Calls on one stream are ordered; calls that share a workspace must not
+ *   overlap in time.
+ */
+#ifndef IMUNPACK_H
+#define IMUNPACK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IMU_OK = 0,
+  IMU_ERR_INVALID_ARG = 1, /* bad shape, stride, dtype, parameter or null pointer */
+  IMU_ERR_NONFINITE = 2,   /* an input element is NaN or +-Inf */
+  IMU_ERR_RANGE = 3,       /* |fl32(x * r)| >= 2^31: the code does not fit int32 */
+  IMU_ERR_WORKSPACE = 4,   /* workspace too small; *ws_needed holds the size */
+  IMU_ERR_HIP = 5,         /* a HIP runtime call failed (detail: imu_last_error) */
+  IMU_ERR_UNSUPPORTED = 6  /* valid request beyond this build's limits (see imu_last_error) */
+} imu_status;
+
+typedef enum { IMU_F32 = 0, IMU_BF16 = 1 } imu_dtype;
+
+/* IMU_NORMAL: element (r, c) of the logical matrix is stored at r*ld + c.
+ * IMU_TRANSPOSED: the stored array is the transpose: element (r, c) is at c*ld + r
+ * (a weight W of shape N x K used as B = W^T with layout TRANSPOSED). */
+typedef enum { IMU_NORMAL = 0, IMU_TRANSPOSED = 1 } imu_layout;
+
+/* Unpacking strategy of one operand ("Approach"; Mix in the unpack-ratio rows). */
+typedef enum { IMU_ROW = 0, IMU_COL = 1, IMU_MIX = 2 } imu_strategy;
+
+/* Candidate depth maps the planner chooses from (Mix allows all four):
+ * ROW: each row gets its largest digit count; COL: each column does;
+ * CR: heavy columns first, then rows; RC: heavy rows first, then columns. */
+typedef enum { IMU_CAND_ROW = 0, IMU_CAND_COL = 1, IMU_CAND_CR = 2, IMU_CAND_RC = 3 } imu_candidate;
+
+/* One operand as it enters C = A.B.  `rows` x `cols` is the LOGICAL shape
+ * (A: M x K, B: K x N).  `ld` >= stored row length; `batch` >= 1 entries spaced
+ * `batch_stride` elements apart.  `data` must be 16-byte aligned. */
+typedef struct {
+  const void* data;
+  int32_t dtype;  /* imu_dtype */
+  int32_t layout; /* imu_layout */
+  int64_t rows, cols, ld;
+  int64_t batch, batch_stride;
+} imu_matrix;
+
+/* beta >= 1: the integer the p-percentile magnitude maps to.
+ * p = p_num / p_den in (0, 1], held as a ratio of integers.
+ * bits in [2, 8]: an in-range code satisfies |q| <= 2^(bits-1) - 1; unpacked
+ * digits are signed base-2^(bits-1) digits and fit in int8.
+ * gamma >= 0: a line is heavy when its out-of-range count exceeds gamma times
+ * the mean count of its dimension (2 by default).
+ * strat_a / strat_b: imu_strategy of A and B. */
+typedef struct {
+  int32_t beta, p_num, p_den, bits, gamma;
+  int32_t strat_a, strat_b;
+} imu_params;
+
+/* Host-side summary of one batch entry's plan, filled by imu_plan_unpack. */
+typedef struct {
+  int64_t m, k, n;           /* original sizes M, K, N of this problem */
+  int64_t m_u, k_u, n_u;     /* unpacked sizes M', K', N' (no padding) */
+  int64_t m_alloc, n_alloc;  /* rows of A' and of B'^T as laid out (padded) */
+  int64_t k_pad;             /* row length in bytes of A' and B'^T (padded K') */
+  int64_t m_base, n_base;    /* first extra row of A' / first extra row of B'^T */
+  int64_t a_offset, b_offset;/* byte offsets of this entry in the unpacked buffers */
+  int32_t n_seg;             /* number of exponent segments of K' */
+  int32_t choice_a, choice_b;/* imu_candidate chosen for A and B */
+  int32_t pad_;
+  double unpack_ratio;       /* M'K'N' / (MKN) */
+  int64_t pair_sizes[16][3]; /* (M',K',N') of every candidate pair, A-major; -1 if not allowed */
+} imu_plan_info;
+
+/* Byte offsets inside one batch entry of a statistics buffer (see imu_stats_layout).
+ * Header words at offset 0: float alpha, r, s, kth; uint32 maxkey; int32 status;
+ * uint32 sel_prefix, sel_rank; uint64 total (T, out-of-range codes). */
+typedef struct {
+  int64_t stride;                    /* bytes per batch entry */
+  int64_t row_oob, col_oob;          /* int32[rows], int32[cols] */
+  int64_t row_maxdig, col_maxdig;    /* int32[rows], int32[cols] */
+  int64_t cr_rowdig, rc_coldig;      /* int32[rows], int32[cols]: residual maxima (Mix) */
+  int64_t hist;                      /* uint32[32768] percentile histogram */
+} imu_stats_view;
+
+/* Byte offsets inside a plan buffer.  Headers of all batch entries come first
+ * (`header_stride` bytes each); each entry's arrays follow at
+ * headers_bytes + b * entry_stride. */
+typedef struct {
+  int64_t header_stride, headers_bytes, entry_stride;
+  int64_t da_r, da_c, db_r, db_c;    /* int32 depth maps: [M], [K], [K], [N] */
+  int64_t lvl_a, lvl_b;              /* int32 [levels][M] / [levels][N]: unpacked row of (line, level) */
+  int64_t kpre;                      /* int32 [segments][K+1]: per-segment prefix over k */
+  int64_t amap, bmap;                /* int32 [m_alloc_max] / [n_alloc_max]: line | level << 24, -1 = padding */
+  int64_t levels, segments;          /* array extents used above */
+  int64_t m_alloc_max, n_alloc_max;
+} imu_plan_view;
+
+/* ---- sizes and layouts (host only, no device work) ------------------------ */
+
+/* Bytes of one operand's statistics buffer (all batch entries). 0 on bad input. */
+size_t imu_stats_bytes(const imu_matrix* x);
+imu_status imu_stats_layout(const imu_matrix* x, imu_stats_view* view /* host */);
+
+/* Bytes of the device plan buffer for A, B and p (all batch entries). 0 on bad input. */
+size_t imu_plan_bytes(const imu_matrix* a, const imu_matrix* b, const imu_params* p);
+imu_status imu_plan_layout(const imu_matrix* a, const imu_matrix* b, const imu_params* p,
+                           imu_plan_view* view /* host */);
+
+/* ---- the five entry points ------------------------------------------------ */
+
+/* RTN quantization of one operand: the percentile scale and the outlier counts.
+ * (Page: "Measured effects" table, p and beta rows; summary: heavy hitters
+ * kept as out-of-range integers; "Approach": outlier counts per line.)
+ * For each batch entry: alpha = the ceil(p*N)-th smallest |x| (if 0, the
+ * largest |x|; if that is 0 too, r = s = 0 and every code is 0);
+ * r = fl32(beta/alpha), s = fl32(alpha/beta); q = round_half_even(fl32(x*r)),
+ * never clipped.  A code is out of range when |q| >= 2^(bits-1).  Writes per
+ * row and per column out-of-range counts and largest digit counts and the total
+ * T into `stats` (imu_stats_bytes(x) bytes, contents replaced).
+ * q_out: optional int32 codes, logical rows x cols row-major per batch entry,
+ * entries rows*cols apart; NULL to skip.  Asynchronous: device-detected errors
+ * are reported by the next imu_plan_unpack. */
+imu_status imu_quantize_rtn(const imu_matrix* x, const imu_params* p, void* stats,
+                            int32_t* q_out, hipStream_t stream);
+
+/* Plan of the unpacking ("Approach": row/column unpacking chosen per matrix
+ * from outlier counts; Mix rows of the table).  Needs the statistics of A and
+ * B from imu_quantize_rtn; with a Mix strategy the operand is read once more to
+ * find the residual digit counts outside heavy lines.  Chooses for each batch
+ * entry the allowed candidate pair with the smallest M'.K'.N' (ties: A-major
+ * order ROW < COL < CR < RC) and writes depth maps, index maps and exponent
+ * segments into `plan` (imu_plan_bytes bytes).  Waits once for the device and
+ * fills info[0..batch-1] (host).  Returns IMU_ERR_NONFINITE / IMU_ERR_RANGE if
+ * quantization found such input (then the plan is not valid). */
+imu_status imu_plan_unpack(const imu_matrix* a, const imu_matrix* b, const imu_params* p,
+                           void* stats_a, void* stats_b, void* plan,
+                           imu_plan_info* info /* host, batch entries */, hipStream_t stream);
+
+/* Unpack one operand into int8 digits ("Approach": out-of-range integers
+ * decomposed into several in-range low bit-width integers in extra rows or
+ * columns; summary: "larger matrices").  operand 0 = A -> A' (m_alloc x k_pad per
+ * entry), operand 1 = B -> B'^T (n_alloc x k_pad per entry), each entry at
+ * info.a_offset / info.b_offset of x_u.  Rows are level-major (original lines
+ * first, then level 1 lines, ...); columns are the exponent segments of K'
+ * (e = v + v' ascending, then k, then v), each padded with zero bytes to a
+ * multiple of 64.  Every byte of the valid rows is written. */
+imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p,
+                      const void* stats, const void* plan, const imu_plan_info* info,
+                      int8_t* x_u, hipStream_t stream);
+
+/* Low bit-width GEMMs on the unpacked operands with the shift-and-accumulate
+ * fold and dequantization ("Approach": bit-shift scaling and accumulation
+ * reproduce the integer GEMM exactly).  For each exponent segment e the int8
+ * MFMA product P_e = A'[:,K'_e] . B'[K'_e,:] is accumulated as
+ * acc = acc * 2^(bits-1) + P_e (from the highest e down); each unpacked
+ * element (i,u),(n,w) then adds acc << ((bits-1)(u+w)) into C[i,n] (mod 2^32).
+ * c: int32 M x N row-major per entry (ldc elements per row, entries
+ * c_batch_stride apart).  out (optional): fl32(fl32(C) * fl32(s_A * s_B)),
+ * same layout as c.  The caller's info must come from the same plan. */
+imu_status imu_unpacked_gemm(const int8_t* a_u, const int8_t* b_u, const imu_params* p,
+                             const void* stats_a, const void* stats_b, const void* plan,
+                             const imu_plan_info* info, int64_t batch, int32_t* c, int64_t ldc,
+                             int64_t c_batch_stride, float* out, hipStream_t stream);
+
+/* The whole path: quantize A and B, plan, unpack, GEMM, fold, dequantize.
+ * c / out: M x N row-major per batch entry, entries M*N apart (out optional).
+ * ws: device workspace of ws_bytes.  If it is too small the call returns
+ * IMU_ERR_WORKSPACE with *ws_needed set (the plan is deterministic, so a retry
+ * with a larger workspace is exact); ws_needed may be NULL.  info: optional
+ * host array of batch entries. */
+imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const imu_params* p,
+                               int32_t* c, float* out, void* ws, size_t ws_bytes,
+                               size_t* ws_needed, imu_plan_info* info, hipStream_t stream);
+
+/* Fixed part of the imu_imunpack_matmul workspace (statistics and plan); the
+ * unpacked operands need sum over entries of (m_alloc + n_alloc) * k_pad more. */
+size_t imu_workspace_fixed_bytes(const imu_matrix* a, const imu_matrix* b, const imu_params* p);
+
+/* ---- diagnostics ----------------------------------------------------------- */
+
+const char* imu_status_string(imu_status s);
+/* Detail of the last error on the calling thread (empty string if none). */
+const char* imu_last_error(void);
+/* Library version string. */
+const char* imu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IMUNPACK_H */

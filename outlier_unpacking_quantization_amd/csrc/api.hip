@@ -1,0 +1,463 @@
+// C ABI of the IM-Unpack integer GEMM library: argument validation, buffer
+// carving, kernel launches and the one plan-header readback.  Contains no
+// kernels; the device work lives in quantize.hip, plan.hip, unpack.hip and
+// gemm.hip.
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace imu;
+
+namespace {
+
+thread_local std::string g_err;
+
+imu_status fail(imu_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define IMU_HIP(call)                                                                              \
+  do {                                                                                             \
+    hipError_t e_ = (call);                                                                        \
+    if (e_ != hipSuccess) return fail(IMU_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+#define IMU_TRY(call)                                                                              \
+  do {                                                                                             \
+    imu_status s_ = (call);                                                                        \
+    if (s_ != IMU_OK) return s_;                                                                   \
+  } while (0)
+
+constexpr int64_t kMaxLine = (1ll << 24) - 1;  // line index packed in 24 bits of a map word
+
+struct Operand {
+  const imu_matrix* m;
+  int64_t R, C;          // logical
+  int64_t srows, scols;  // stored
+  bool tr;
+  int dtype;
+  int elem;
+};
+
+imu_status check_matrix(const imu_matrix* x, const char* name, Operand* op) {
+  if (!x) return fail(IMU_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!x->data) return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".data is NULL");
+  if (x->dtype != IMU_F32 && x->dtype != IMU_BF16)
+    return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".dtype must be IMU_F32 or IMU_BF16");
+  if (x->layout != IMU_NORMAL && x->layout != IMU_TRANSPOSED)
+    return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".layout must be IMU_NORMAL or IMU_TRANSPOSED");
+  if (x->rows < 1 || x->cols < 1)
+    return fail(IMU_ERR_INVALID_ARG, std::string(name) + " must have rows >= 1 and cols >= 1");
+  if (x->rows > kMaxLine || x->cols > kMaxLine)
+    return fail(IMU_ERR_UNSUPPORTED, std::string(name) + ": rows and cols must be below 2^24");
+  if ((unsigned long long)x->rows * (unsigned long long)x->cols >= (1ull << 32))
+    return fail(IMU_ERR_UNSUPPORTED, std::string(name) + ": rows*cols must be below 2^32");
+  if (x->batch < 1 || x->batch > 65535)
+    return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".batch must be in [1, 65535]");
+  op->m = x;
+  op->R = x->rows;
+  op->C = x->cols;
+  op->tr = x->layout == IMU_TRANSPOSED;
+  op->srows = op->tr ? x->cols : x->rows;
+  op->scols = op->tr ? x->rows : x->cols;
+  op->dtype = x->dtype;
+  op->elem = x->dtype == IMU_F32 ? 4 : 2;
+  if (x->ld < op->scols) return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".ld is below the stored row length");
+  if (x->batch > 1 && x->batch_stride < (op->srows - 1) * x->ld + op->scols)
+    return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".batch_stride overlaps batch entries");
+  return IMU_OK;
+}
+
+imu_status check_params(const imu_params* p) {
+  if (!p) return fail(IMU_ERR_INVALID_ARG, "params is NULL");
+  if (p->bits < 2 || p->bits > 8) return fail(IMU_ERR_INVALID_ARG, "bits must be in [2, 8]");
+  if (p->beta < 1) return fail(IMU_ERR_INVALID_ARG, "beta must be >= 1");
+  if (p->p_den < 1 || p->p_den > 1000000) return fail(IMU_ERR_INVALID_ARG, "p_den must be in [1, 1e6]");
+  if (p->p_num < 1 || p->p_num > p->p_den) return fail(IMU_ERR_INVALID_ARG, "p = p_num/p_den must be in (0, 1]");
+  if (p->gamma < 0 || p->gamma > 1000000) return fail(IMU_ERR_INVALID_ARG, "gamma must be in [0, 1e6]");
+  for (int s : {p->strat_a, p->strat_b})
+    if (s != IMU_ROW && s != IMU_COL && s != IMU_MIX)
+      return fail(IMU_ERR_INVALID_ARG, "strategy must be IMU_ROW, IMU_COL or IMU_MIX");
+  return IMU_OK;
+}
+
+imu_status check_pair(const imu_matrix* a, const imu_matrix* b, const imu_params* p, Operand* oa,
+                      Operand* ob) {
+  IMU_TRY(check_matrix(a, "a", oa));
+  IMU_TRY(check_matrix(b, "b", ob));
+  IMU_TRY(check_params(p));
+  if (a->cols != b->rows) return fail(IMU_ERR_INVALID_ARG, "a.cols must equal b.rows (K)");
+  if (a->batch != b->batch) return fail(IMU_ERR_INVALID_ARG, "a.batch must equal b.batch");
+  return IMU_OK;
+}
+
+StreamArgs stream_args(const Operand& op, uint8_t* stats, const StatsLayout& L, const imu_params* p) {
+  StreamArgs s{};
+  const imu_matrix* x = op.m;
+  s.x = x->data;
+  s.srows = op.srows;
+  s.scols = op.scols;
+  s.ld = x->ld;
+  s.bstride = x->batch_stride;
+  const bool aligned = (reinterpret_cast<uintptr_t>(x->data) % 16) == 0;
+  s.vec_ok = aligned && op.scols % 8 == 0 && x->ld % 8 == 0 && (x->batch == 1 || x->batch_stride % 8 == 0);
+  s.stats = stats;
+  s.stats_stride = L.stride;
+  s.srow_oob = op.tr ? L.col_oob : L.row_oob;
+  s.scol_oob = op.tr ? L.row_oob : L.col_oob;
+  s.srow_maxdig = op.tr ? L.col_maxdig : L.row_maxdig;
+  s.scol_maxdig = op.tr ? L.row_maxdig : L.col_maxdig;
+  s.srow_res = op.tr ? L.rc_coldig : L.cr_rowdig;
+  s.scol_res = op.tr ? L.cr_rowdig : L.rc_coldig;
+  s.hist = L.hist;
+  s.transposed = op.tr ? 1 : 0;
+  s.beta = p->beta;
+  s.p_num = p->p_num;
+  s.p_den = p->p_den;
+  s.gamma = p->gamma;
+  return s;
+}
+
+imu_status quantize_impl(const Operand& op, const imu_params* p, uint8_t* stats, int32_t* q_out,
+                         hipStream_t s) {
+  const StatsLayout L = stats_layout(op.R, op.C);
+  const int batch = (int)op.m->batch;
+  IMU_HIP(launch_fill_u32(stats, 0u, L.stride * batch / 4, s));
+  StreamArgs sa = stream_args(op, stats, L, p);
+  const int64_t n = op.R * op.C;
+  const bool bf16 = op.dtype == IMU_BF16;
+  IMU_HIP(launch_hist(op.dtype, sa, batch, 0, s));
+  IMU_HIP(launch_select(stats, L.stride, L.hist, batch, n, 0, bf16 ? 1 : 0, p->beta, p->p_num, p->p_den, s));
+  if (!bf16) {
+    for (int pass = 1; pass <= 2; ++pass) {
+      IMU_HIP(launch_hist(op.dtype, sa, batch, pass, s));
+      IMU_HIP(launch_select(stats, L.stride, L.hist, batch, n, pass, pass == 2, p->beta, p->p_num,
+                            p->p_den, s));
+    }
+  }
+  IMU_HIP(launch_round_count(op.dtype, p->bits, sa, batch, q_out, s));
+  return IMU_OK;
+}
+
+imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
+                     uint8_t* stats_b, uint8_t* plan, imu_plan_info* info, hipStream_t s) {
+  const StatsLayout la = stats_layout(oa.R, oa.C), lb = stats_layout(ob.R, ob.C);
+  const int batch = (int)oa.m->batch;
+  if (p->strat_a == IMU_MIX) {
+    StreamArgs sa = stream_args(oa, stats_a, la, p);
+    IMU_HIP(launch_residual(oa.dtype, p->bits, sa, batch, s));
+  }
+  if (p->strat_b == IMU_MIX) {
+    StreamArgs sb = stream_args(ob, stats_b, lb, p);
+    IMU_HIP(launch_residual(ob.dtype, p->bits, sb, batch, s));
+  }
+  PlanArgs pa{};
+  pa.stats_a = stats_a;
+  pa.stats_b = stats_b;
+  pa.stats_stride_a = la.stride;
+  pa.stats_stride_b = lb.stride;
+  pa.sla = la;
+  pa.slb = lb;
+  pa.plan = plan;
+  pa.pl = plan_layout(oa.R, oa.C, ob.C, batch, p->bits);
+  pa.gamma = p->gamma;
+  pa.strat_a = p->strat_a;
+  pa.strat_b = p->strat_b;
+  pa.bits = p->bits;
+  IMU_HIP(launch_plan(pa, s));
+  std::vector<uint8_t> hdrs((size_t)batch * kPlanHeaderStride);
+  IMU_HIP(hipMemcpyAsync(hdrs.data(), plan, hdrs.size(), hipMemcpyDeviceToHost, s));
+  IMU_HIP(hipStreamSynchronize(s));
+  int status = 0;
+  int64_t aoff = 0, boff = 0;
+  for (int b = 0; b < batch; ++b) {
+    const PlanHeader* h = reinterpret_cast<const PlanHeader*>(hdrs.data() + (size_t)b * kPlanHeaderStride);
+    status |= h->status;
+    if (info) {
+      imu_plan_info& f = info[b];
+      std::memset(&f, 0, sizeof(f));
+      f.m = oa.R;
+      f.k = oa.C;
+      f.n = ob.C;
+      f.m_u = h->m_u;
+      f.k_u = h->k_u;
+      f.n_u = h->n_u;
+      f.m_alloc = h->m_alloc;
+      f.n_alloc = h->n_alloc;
+      f.k_pad = h->k_pad;
+      f.m_base = h->m_base;
+      f.n_base = h->n_base;
+      f.a_offset = aoff;
+      f.b_offset = boff;
+      f.n_seg = h->n_seg;
+      f.choice_a = h->choice_a;
+      f.choice_b = h->choice_b;
+      f.unpack_ratio = (double)h->m_u * (double)h->k_u * (double)h->n_u /
+                       ((double)oa.R * (double)oa.C * (double)ob.C);
+      std::memcpy(f.pair_sizes, h->pair, sizeof(f.pair_sizes));
+    }
+    aoff += unpacked_entry_bytes(h, 0);
+    boff += unpacked_entry_bytes(h, 1);
+  }
+  if (status & kStatusNonfinite) return fail(IMU_ERR_NONFINITE, "an input element is NaN or Inf");
+  if (status & kStatusRange) return fail(IMU_ERR_RANGE, "|x * r| >= 2^31 for some element");
+  return IMU_OK;
+}
+
+imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, const uint8_t* stats,
+                       const uint8_t* plan, const imu_plan_info* info, int8_t* x_u, hipStream_t s) {
+  const StatsLayout L = stats_layout(op.R, op.C);
+  const imu_matrix* x = op.m;
+  UnpackArgs u{};
+  u.x = x->data;
+  u.bstride = x->batch_stride;
+  // element (outer o, inner k) of the logical operand in memory
+  const int64_t ld = x->ld;
+  if (operand == 0) {  // A: outer = row i, inner = col k
+    u.so = op.tr ? 1 : ld;
+    u.sk = op.tr ? ld : 1;
+    u.n_outer = op.R;
+    u.K = op.C;
+  } else {  // B: outer = col n, inner = row k
+    u.so = op.tr ? ld : 1;
+    u.sk = op.tr ? 1 : ld;
+    u.n_outer = op.C;
+    u.K = op.R;
+  }
+  u.operand = operand;
+  u.stats = stats;
+  u.stats_stride = L.stride;
+  u.plan = plan;
+  u.pl = plan_layout(info[0].m, info[0].k, info[0].n, x->batch, p->bits);
+  u.out = x_u;
+  IMU_HIP(launch_unpack(op.dtype, p->bits, u, (int)x->batch, s));
+  return IMU_OK;
+}
+
+imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, const uint8_t* stats_a,
+                     const uint8_t* stats_b, const uint8_t* plan, const imu_plan_info* info,
+                     int64_t batch, int32_t* c, int64_t ldc, int64_t cbs, float* out, hipStream_t s) {
+  const int64_t M = info[0].m, K = info[0].k, N = info[0].n;
+  const StatsLayout la = stats_layout(M, K), lb = stats_layout(K, N);
+  const PlanLayout pl = plan_layout(M, K, N, batch, p->bits);
+  for (int64_t b = 0; b < batch; ++b) {
+    const imu_plan_info& f = info[b];
+    const uint8_t* pe = plan + pl.headers_bytes + b * pl.entry_stride;
+    GemmArgs g{};
+    g.a_u = a_u + f.a_offset;
+    g.b_u = b_u + f.b_offset;
+    g.hdr = plan + b * kPlanHeaderStride;
+    g.amap = reinterpret_cast<const int32_t*>(pe + pl.amap);
+    g.bmap = reinterpret_cast<const int32_t*>(pe + pl.bmap);
+    g.sa = reinterpret_cast<const StatsHeader*>(stats_a + b * la.stride);
+    g.sb = reinterpret_cast<const StatsHeader*>(stats_b + b * lb.stride);
+    g.c = c + b * cbs;
+    g.out = out ? out + b * cbs : nullptr;
+    g.ldc = ldc;
+    g.M = M;
+    g.N = N;
+    g.m_alloc = f.m_alloc;
+    g.n_alloc = f.n_alloc;
+    g.m_base = f.m_base;
+    g.n_base = f.n_base;
+    g.k_pad = f.k_pad;
+    g.bits = p->bits;
+    const bool extras = f.m_alloc > f.m_base || f.n_alloc > f.n_base;
+    if (extras) {
+      IMU_HIP(launch_fill_2d(g.c, M, N, ldc, s));
+      g.mode = 2;
+      IMU_HIP(launch_gemm(g, s));
+      g.mode = 1;
+    } else {
+      g.mode = 0;
+    }
+    IMU_HIP(launch_gemm(g, s));
+  }
+  return IMU_OK;
+}
+
+imu_status check_info(const imu_plan_info* info, int64_t batch, int64_t M, int64_t K, int64_t N) {
+  if (!info) return fail(IMU_ERR_INVALID_ARG, "info is NULL");
+  for (int64_t b = 0; b < batch; ++b)
+    if (info[b].m != M || info[b].k != K || info[b].n != N || info[b].k_pad <= 0)
+      return fail(IMU_ERR_INVALID_ARG, "info does not describe this problem");
+  return IMU_OK;
+}
+
+int64_t fixed_bytes(const Operand& oa, const Operand& ob, const imu_params* p) {
+  const int64_t batch = oa.m->batch;
+  return round_up(stats_layout(oa.R, oa.C).stride * batch, 256) +
+         round_up(stats_layout(ob.R, ob.C).stride * batch, 256) +
+         round_up(plan_layout(oa.R, oa.C, ob.C, batch, p->bits).total, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t imu_stats_bytes(const imu_matrix* x) {
+  Operand op;
+  if (check_matrix(x, "x", &op) != IMU_OK) return 0;
+  return (size_t)(stats_layout(op.R, op.C).stride * x->batch);
+}
+
+imu_status imu_stats_layout(const imu_matrix* x, imu_stats_view* v) {
+  Operand op;
+  IMU_TRY(check_matrix(x, "x", &op));
+  if (!v) return fail(IMU_ERR_INVALID_ARG, "view is NULL");
+  const StatsLayout L = stats_layout(op.R, op.C);
+  v->stride = L.stride;
+  v->row_oob = L.row_oob;
+  v->col_oob = L.col_oob;
+  v->row_maxdig = L.row_maxdig;
+  v->col_maxdig = L.col_maxdig;
+  v->cr_rowdig = L.cr_rowdig;
+  v->rc_coldig = L.rc_coldig;
+  v->hist = L.hist;
+  return IMU_OK;
+}
+
+size_t imu_plan_bytes(const imu_matrix* a, const imu_matrix* b, const imu_params* p) {
+  Operand oa, ob;
+  if (check_pair(a, b, p, &oa, &ob) != IMU_OK) return 0;
+  return (size_t)plan_layout(oa.R, oa.C, ob.C, a->batch, p->bits).total;
+}
+
+imu_status imu_plan_layout(const imu_matrix* a, const imu_matrix* b, const imu_params* p,
+                           imu_plan_view* v) {
+  Operand oa, ob;
+  IMU_TRY(check_pair(a, b, p, &oa, &ob));
+  if (!v) return fail(IMU_ERR_INVALID_ARG, "view is NULL");
+  const PlanLayout L = plan_layout(oa.R, oa.C, ob.C, a->batch, p->bits);
+  v->header_stride = kPlanHeaderStride;
+  v->headers_bytes = L.headers_bytes;
+  v->entry_stride = L.entry_stride;
+  v->da_r = L.da_r;
+  v->da_c = L.da_c;
+  v->db_r = L.db_r;
+  v->db_c = L.db_c;
+  v->lvl_a = L.lvl_a;
+  v->lvl_b = L.lvl_b;
+  v->kpre = L.kpre;
+  v->amap = L.amap;
+  v->bmap = L.bmap;
+  v->levels = L.levels;
+  v->segments = L.segments;
+  v->m_alloc_max = L.m_alloc_max;
+  v->n_alloc_max = L.n_alloc_max;
+  return IMU_OK;
+}
+
+size_t imu_workspace_fixed_bytes(const imu_matrix* a, const imu_matrix* b, const imu_params* p) {
+  Operand oa, ob;
+  if (check_pair(a, b, p, &oa, &ob) != IMU_OK) return 0;
+  return (size_t)fixed_bytes(oa, ob, p);
+}
+
+imu_status imu_quantize_rtn(const imu_matrix* x, const imu_params* p, void* stats, int32_t* q_out,
+                            hipStream_t stream) {
+  Operand op;
+  IMU_TRY(check_matrix(x, "x", &op));
+  IMU_TRY(check_params(p));
+  if (!stats) return fail(IMU_ERR_INVALID_ARG, "stats is NULL");
+  return quantize_impl(op, p, static_cast<uint8_t*>(stats), q_out, stream);
+}
+
+imu_status imu_plan_unpack(const imu_matrix* a, const imu_matrix* b, const imu_params* p, void* stats_a,
+                           void* stats_b, void* plan, imu_plan_info* info, hipStream_t stream) {
+  Operand oa, ob;
+  IMU_TRY(check_pair(a, b, p, &oa, &ob));
+  if (!stats_a || !stats_b || !plan) return fail(IMU_ERR_INVALID_ARG, "stats or plan is NULL");
+  return plan_impl(oa, ob, p, static_cast<uint8_t*>(stats_a), static_cast<uint8_t*>(stats_b),
+                   static_cast<uint8_t*>(plan), info, stream);
+}
+
+imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p, const void* stats,
+                      const void* plan, const imu_plan_info* info, int8_t* x_u, hipStream_t stream) {
+  Operand op;
+  IMU_TRY(check_matrix(x, "x", &op));
+  IMU_TRY(check_params(p));
+  if (operand != 0 && operand != 1) return fail(IMU_ERR_INVALID_ARG, "operand must be 0 (A) or 1 (B)");
+  if (!stats || !plan || !x_u) return fail(IMU_ERR_INVALID_ARG, "stats, plan or x_u is NULL");
+  if (!info) return fail(IMU_ERR_INVALID_ARG, "info is NULL");
+  const int64_t M = operand == 0 ? op.R : info[0].m, K = operand == 0 ? op.C : op.R,
+                N = operand == 0 ? info[0].n : op.C;
+  IMU_TRY(check_info(info, x->batch, M, K, N));
+  return unpack_impl(op, operand, p, static_cast<const uint8_t*>(stats), static_cast<const uint8_t*>(plan),
+                     info, x_u, stream);
+}
+
+imu_status imu_unpacked_gemm(const int8_t* a_u, const int8_t* b_u, const imu_params* p, const void* stats_a,
+                             const void* stats_b, const void* plan, const imu_plan_info* info,
+                             int64_t batch, int32_t* c, int64_t ldc, int64_t c_batch_stride, float* out,
+                             hipStream_t stream) {
+  IMU_TRY(check_params(p));
+  if (!a_u || !b_u || !stats_a || !stats_b || !plan || !c)
+    return fail(IMU_ERR_INVALID_ARG, "a NULL pointer was passed");
+  if (!info || batch < 1) return fail(IMU_ERR_INVALID_ARG, "info is NULL or batch < 1");
+  IMU_TRY(check_info(info, batch, info[0].m, info[0].k, info[0].n));
+  if (ldc < info[0].n) return fail(IMU_ERR_INVALID_ARG, "ldc is below N");
+  if (batch > 1 && c_batch_stride < (info[0].m - 1) * ldc + info[0].n)
+    return fail(IMU_ERR_INVALID_ARG, "c_batch_stride overlaps batch entries");
+  return gemm_impl(a_u, b_u, p, static_cast<const uint8_t*>(stats_a), static_cast<const uint8_t*>(stats_b),
+                   static_cast<const uint8_t*>(plan), info, batch, c, ldc, c_batch_stride, out, stream);
+}
+
+imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const imu_params* p, int32_t* c,
+                               float* out, void* ws, size_t ws_bytes, size_t* ws_needed,
+                               imu_plan_info* info, hipStream_t stream) {
+  Operand oa, ob;
+  IMU_TRY(check_pair(a, b, p, &oa, &ob));
+  if (!c) return fail(IMU_ERR_INVALID_ARG, "c is NULL");
+  const int64_t batch = a->batch;
+  const int64_t fixed = fixed_bytes(oa, ob, p);
+  if (ws_needed) *ws_needed = (size_t)fixed;
+  if (!ws || (int64_t)ws_bytes < fixed)
+    return fail(IMU_ERR_WORKSPACE, "workspace below the fixed part (statistics and plan)");
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  uint8_t* stats_a = w;
+  uint8_t* stats_b = stats_a + round_up(stats_layout(oa.R, oa.C).stride * batch, 256);
+  uint8_t* plan = stats_b + round_up(stats_layout(ob.R, ob.C).stride * batch, 256);
+  IMU_TRY(quantize_impl(oa, p, stats_a, nullptr, stream));
+  IMU_TRY(quantize_impl(ob, p, stats_b, nullptr, stream));
+  std::vector<imu_plan_info> local;
+  if (!info) {
+    local.resize((size_t)batch);
+    info = local.data();
+  }
+  IMU_TRY(plan_impl(oa, ob, p, stats_a, stats_b, plan, info, stream));
+  const imu_plan_info& last = info[batch - 1];
+  const int64_t a_bytes = last.a_offset + round_up(last.m_alloc * last.k_pad, 256);
+  const int64_t b_bytes = last.b_offset + round_up(last.n_alloc * last.k_pad, 256);
+  const int64_t needed = fixed + a_bytes + b_bytes;
+  if (ws_needed) *ws_needed = (size_t)needed;
+  if ((int64_t)ws_bytes < needed) return fail(IMU_ERR_WORKSPACE, "workspace below the unpacked operands' size");
+  int8_t* a_u = reinterpret_cast<int8_t*>(w + fixed);
+  int8_t* b_u = a_u + a_bytes;
+  IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, info, a_u, stream));
+  IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, info, b_u, stream));
+  return gemm_impl(a_u, b_u, p, stats_a, stats_b, plan, info, batch, c, ob.C, oa.R * ob.C, out, stream);
+}
+
+const char* imu_status_string(imu_status s) {
+  switch (s) {
+    case IMU_OK: return "ok";
+    case IMU_ERR_INVALID_ARG: return "invalid argument";
+    case IMU_ERR_NONFINITE: return "non-finite input";
+    case IMU_ERR_RANGE: return "code out of int32 range";
+    case IMU_ERR_WORKSPACE: return "workspace too small";
+    case IMU_ERR_HIP: return "HIP runtime error";
+    case IMU_ERR_UNSUPPORTED: return "unsupported request";
+  }
+  return "unknown status";
+}
+
+const char* imu_last_error(void) { return g_err.c_str(); }
+
+const char* imu_version(void) { return "imunpack 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,226 @@
+// Internal definitions shared by the HIP kernels and the C-ABI host code of
+// the IM-Unpack integer GEMM library (gfx950).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "imunpack.h"
+
+namespace imu {
+
+// ---------------------------------------------------------------------------
+// constants
+// ---------------------------------------------------------------------------
+constexpr int kHistBins = 32768;    // 15-bit magnitude key of bf16 (and the top of fp32)
+constexpr int kKPad = 64;           // every exponent segment of K' is padded to this many bytes
+constexpr int kMaxSeg = 64;         // room for 2*max_digits(2)-1 = 61 segments
+constexpr int kStatusNonfinite = 1; // device status bits
+constexpr int kStatusRange = 2;
+
+__host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+__host__ __device__ inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
+__host__ __device__ inline int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+__host__ __device__ inline int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// Largest number of base-2^(bits-1) digits of a code with |q| < 2^31.
+__host__ __device__ inline int max_digits(int bits) { return (31 + bits - 2) / (bits - 1); }
+
+// ---------------------------------------------------------------------------
+// statistics buffer of one operand (one slot per batch entry)
+// ---------------------------------------------------------------------------
+struct StatsHeader {
+  float alpha, r, s, kth;
+  uint32_t maxkey;      // largest |x| as an fp32 bit pattern without sign
+  int32_t status;       // kStatus* bits
+  uint32_t sel_prefix;  // radix-select state: key prefix found so far
+  uint32_t sel_rank;    // rank still to find inside that prefix (1-based)
+  unsigned long long total;  // T: out-of-range codes
+  int32_t pad0, pad1;
+  int64_t rows, cols;
+};
+static_assert(sizeof(StatsHeader) == 64, "stats header");
+
+struct StatsLayout {
+  int64_t R = 0, C = 0;
+  int64_t row_oob = 0, col_oob = 0, row_maxdig = 0, col_maxdig = 0, cr_rowdig = 0, rc_coldig = 0;
+  int64_t hist = 0, stride = 0;
+};
+
+inline StatsLayout stats_layout(int64_t R, int64_t C) {
+  StatsLayout L;
+  L.R = R;
+  L.C = C;
+  int64_t o = 256;
+  auto take = [&](int64_t bytes) {
+    int64_t at = o;
+    o += round_up(bytes, 256);
+    return at;
+  };
+  L.row_oob = take(4 * R);
+  L.col_oob = take(4 * C);
+  L.row_maxdig = take(4 * R);
+  L.col_maxdig = take(4 * C);
+  L.cr_rowdig = take(4 * R);
+  L.rc_coldig = take(4 * C);
+  L.hist = take(4 * (int64_t)kHistBins);
+  L.stride = o;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// plan buffer
+// ---------------------------------------------------------------------------
+struct PlanHeader {
+  int32_t choice_a, choice_b, status, n_seg;
+  int64_t m_u, k_u, n_u;
+  int64_t m_base, n_base, m_alloc, n_alloc;
+  int64_t k_pad;
+  int32_t lev_a, lev_b, emax, pad0;
+  int64_t pair[16][3];
+  int64_t seg_off[kMaxSeg + 1];
+  int32_t seg_len[kMaxSeg];
+};
+constexpr int64_t kPlanHeaderStride = 2048;
+static_assert(sizeof(PlanHeader) <= kPlanHeaderStride, "plan header");
+// byte offsets read by the Python binding
+static_assert(offsetof(PlanHeader, n_seg) == 12, "plan header layout");
+static_assert(offsetof(PlanHeader, pair) == 96, "plan header layout");
+static_assert(offsetof(PlanHeader, seg_off) == 480, "plan header layout");
+static_assert(offsetof(PlanHeader, seg_len) == 1000, "plan header layout");
+
+struct PlanLayout {
+  int64_t M = 0, K = 0, N = 0, batch = 0;
+  int64_t pad_m = 0, pad_n = 0;  // base/extra boundary and allocation granularity
+  int64_t levels = 0, segments = 0, m_alloc_max = 0, n_alloc_max = 0;
+  int64_t headers_bytes = 0, entry_stride = 0;
+  int64_t da_r = 0, da_c = 0, db_r = 0, db_c = 0, lvl_a = 0, lvl_b = 0, kpre = 0, amap = 0, bmap = 0;
+  int64_t total = 0;
+};
+
+// GEMM macro tile (rows of A' x rows of B'^T) used for a problem of this shape;
+// the plan pads the base region and the allocation to these multiples.
+struct GemmTile {
+  int bm, bn;
+};
+inline GemmTile gemm_tile_for(int64_t M, int64_t N) {
+  (void)M;
+  (void)N;
+  return GemmTile{128, 128};
+}
+
+inline PlanLayout plan_layout(int64_t M, int64_t K, int64_t N, int64_t batch, int bits) {
+  PlanLayout L;
+  L.M = M;
+  L.K = K;
+  L.N = N;
+  L.batch = batch;
+  GemmTile t = gemm_tile_for(M, N);
+  L.pad_m = t.bm;
+  L.pad_n = t.bn;
+  int D = max_digits(bits);
+  L.levels = D;
+  L.segments = 2 * D - 1;
+  L.m_alloc_max = round_up(M, L.pad_m) + (int64_t)(D - 1) * M + L.pad_m;
+  L.n_alloc_max = round_up(N, L.pad_n) + (int64_t)(D - 1) * N + L.pad_n;
+  L.headers_bytes = round_up(batch * kPlanHeaderStride, 256);
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    int64_t at = o;
+    o += round_up(bytes, 256);
+    return at;
+  };
+  L.da_r = take(4 * M);
+  L.da_c = take(4 * K);
+  L.db_r = take(4 * K);
+  L.db_c = take(4 * N);
+  L.lvl_a = take(4 * M * L.levels);
+  L.lvl_b = take(4 * N * L.levels);
+  L.kpre = take(4 * (K + 1) * L.segments);
+  L.amap = take(4 * L.m_alloc_max);
+  L.bmap = take(4 * L.n_alloc_max);
+  L.entry_stride = o;
+  L.total = L.headers_bytes + batch * L.entry_stride;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+template <int DT>
+struct Elem;
+template <>
+struct Elem<IMU_F32> {
+  using T = float;
+  static constexpr int bytes = 4;
+};
+template <>
+struct Elem<IMU_BF16> {
+  using T = uint16_t;
+  static constexpr int bytes = 2;
+};
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Magnitude key of |x| as an fp32 bit pattern (sign dropped).
+__device__ inline uint32_t mag_key(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// Number of base-2^(BITS-1) digits of |q| (1 for |q| < 2^(BITS-1)).
+template <int BITS>
+__device__ inline int digit_count(uint32_t m) {
+  int bl = 32 - __clz((int)m);  // bit length; 0 for m == 0
+  return bl == 0 ? 1 : 1 + (bl - 1) / (BITS - 1);
+}
+
+// RTN code of x: one binary32 product, round half to even.  Sets *bad when the
+// code does not fit int32 (|x r| >= 2^31, including Inf/NaN products).
+__device__ inline int32_t rtn_code(float x, float r, bool* bad) {
+  float y = x * r;
+  if (!(__builtin_fabsf(y) < 2147483648.0f)) {
+    *bad = true;
+    return 0;
+  }
+  return (int32_t)__builtin_rintf(y);
+}
+
+// Signed digit t of q: sign(q) * ((|q| >> ((BITS-1) t)) mod 2^(BITS-1)).
+template <int BITS>
+__device__ inline int32_t digit_of(int32_t q, int t) {
+  uint32_t m = q < 0 ? (uint32_t)(-(int64_t)q) : (uint32_t)q;
+  int sh = (BITS - 1) * t;
+  uint32_t d = sh >= 32 ? 0u : ((m >> sh) & ((1u << (BITS - 1)) - 1u));
+  return q < 0 ? -(int32_t)d : (int32_t)d;
+}
+
+__device__ inline int wave_sum_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline int wave_max_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// launch argument blocks
+// ---------------------------------------------------------------------------
+struct StreamArgs {       // one operand traversed in stored orientation
+  const void* x;
+  int64_t srows, scols, ld, bstride;  // stored shape and strides (elements)
+  int vec_ok;                          // 8-element vector loads are safe
+  uint8_t* stats;
+  int64_t stats_stride;
+  // stored-row / stored-column arrays (logical rows or cols depending on layout)
+  int64_t srow_oob, scol_oob, srow_maxdig, scol_maxdig, srow_res, scol_res, hist;
+  int transposed;  // logical = stored^T
+  int beta, p_num, p_den, gamma;
+};
+
+}  // namespace imu

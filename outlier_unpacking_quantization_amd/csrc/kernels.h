@@ -1,0 +1,71 @@
+// Host-side launchers of the HIP kernels (internal).
+#pragma once
+
+#include "common.h"
+
+namespace imu {
+
+// Byte offset of batch entry b inside the unpacked buffer of an operand: the
+// entries before it, each (rows x k_pad) rounded up to 256 bytes.
+__host__ __device__ inline int64_t unpacked_entry_bytes(const PlanHeader* h, int operand) {
+  return round_up((operand == 0 ? h->m_alloc : h->n_alloc) * h->k_pad, 256);
+}
+
+// quantize.hip
+hipError_t launch_fill_u32(void* p, uint32_t v, int64_t nwords, hipStream_t s);
+hipError_t launch_fill_2d(int32_t* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
+hipError_t launch_hist(int dtype, const StreamArgs& a, int batch, int pass, hipStream_t s);
+hipError_t launch_select(uint8_t* stats, int64_t stats_stride, int64_t hist_off, int batch,
+                         int64_t nelem, int pass, int final_pass, int beta, int p_num, int p_den,
+                         hipStream_t s);
+hipError_t launch_round_count(int dtype, int bits, const StreamArgs& a, int batch, int32_t* q_out,
+                              hipStream_t s);
+hipError_t launch_residual(int dtype, int bits, const StreamArgs& a, int batch, hipStream_t s);
+
+// plan.hip
+struct PlanArgs {
+  const uint8_t* stats_a;
+  const uint8_t* stats_b;
+  int64_t stats_stride_a, stats_stride_b;
+  StatsLayout sla, slb;
+  uint8_t* plan;
+  PlanLayout pl;
+  int gamma, strat_a, strat_b, bits;
+};
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+
+// unpack.hip
+struct UnpackArgs {
+  const void* x;
+  int64_t bstride;
+  int64_t so, sk;          // element strides of the outer line index and of k
+  int64_t n_outer, K;      // outer lines (A: M rows, B: N cols) and inner length K
+  int operand;             // 0 = A, 1 = B
+  const uint8_t* stats;
+  int64_t stats_stride;
+  const uint8_t* plan;
+  PlanLayout pl;
+  int8_t* out;                  // start of the unpacked buffer (all batch entries)
+};
+hipError_t launch_unpack(int dtype, int bits, const UnpackArgs& a, int batch, hipStream_t s);
+
+// gemm.hip
+struct GemmArgs {
+  const int8_t* a_u;
+  const int8_t* b_u;
+  const uint8_t* hdr;      // this entry's plan header
+  const int32_t* amap;
+  const int32_t* bmap;
+  const StatsHeader* sa;
+  const StatsHeader* sb;
+  int32_t* c;
+  float* out;
+  int64_t ldc;
+  int64_t M, N;
+  int64_t m_alloc, n_alloc, m_base, n_base, k_pad;
+  int bits;
+  int mode;                // 0: base tiles, store C; 1: base tiles, add to C; 2: extra tiles, atomics
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace imu
