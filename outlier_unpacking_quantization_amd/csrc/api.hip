@@ -91,6 +91,7 @@ imu_status check_pair(const imu_matrix* a, const imu_matrix* b, const imu_params
   IMU_TRY(check_matrix(b, "b", ob));
   IMU_TRY(check_params(p));
   if (a->cols != b->rows) return fail(IMU_ERR_INVALID_ARG, "a.cols must equal b.rows (K)");
+  if (a->cols > kMaxK) return fail(IMU_ERR_UNSUPPORTED, "K must be below 2^22 - 1");
   if (a->batch != b->batch) return fail(IMU_ERR_INVALID_ARG, "a.batch must equal b.batch");
   return IMU_OK;
 }
@@ -122,24 +123,32 @@ StreamArgs stream_args(const Operand& op, uint8_t* stats, const StatsLayout& L, 
   return s;
 }
 
-imu_status quantize_impl(const Operand& op, const imu_params* p, uint8_t* stats, int32_t* q_out,
-                         hipStream_t s) {
-  const StatsLayout L = stats_layout(op.R, op.C);
-  const int batch = (int)op.m->batch;
-  IMU_HIP(launch_fill_u32(stats, 0u, L.stride * batch / 4, s));
-  StreamArgs sa = stream_args(op, stats, L, p);
-  const int64_t n = op.R * op.C;
-  const bool bf16 = op.dtype == IMU_BF16;
-  IMU_HIP(launch_hist(op.dtype, sa, batch, 0, s));
-  IMU_HIP(launch_select(stats, L.stride, L.hist, batch, n, 0, bf16 ? 1 : 0, p->beta, p->p_num, p->p_den, s));
-  if (!bf16) {
-    for (int pass = 1; pass <= 2; ++pass) {
-      IMU_HIP(launch_hist(op.dtype, sa, batch, pass, s));
-      IMU_HIP(launch_select(stats, L.stride, L.hist, batch, n, pass, pass == 2, p->beta, p->p_num,
-                            p->p_den, s));
+// Quantize up to two operands; operands of one dtype share every launch.
+// `zeroed`: the caller already cleared the statistics buffers.
+imu_status quantize_ops(const Operand* const* ops, uint8_t* const* stats, int32_t* const* q, int nops,
+                        const imu_params* p, hipStream_t s, bool zeroed) {
+  if (!zeroed)
+    for (int i = 0; i < nops; ++i)
+      IMU_HIP(launch_fill_u32(stats[i], 0u, stats_layout(ops[i]->R, ops[i]->C).stride * ops[i]->m->batch / 4, s));
+  for (int dt : {(int)IMU_BF16, (int)IMU_F32}) {
+    QuantJobs J{};
+    int32_t* qq[2] = {nullptr, nullptr};
+    for (int i = 0; i < nops; ++i) {
+      if (ops[i]->dtype != dt) continue;
+      QuantOp& o = J.op[J.nops];
+      o.s = stream_args(*ops[i], stats[i], stats_layout(ops[i]->R, ops[i]->C), p);
+      o.batch = (int)ops[i]->m->batch;
+      qq[J.nops] = q[i];
+      ++J.nops;
     }
+    if (!J.nops) continue;
+    IMU_HIP(launch_hist(dt, J, 0, dt == IMU_BF16, s));
+    if (dt == IMU_F32) {
+      IMU_HIP(launch_hist(dt, J, 1, 0, s));
+      IMU_HIP(launch_hist(dt, J, 2, 1, s));
+    }
+    IMU_HIP(launch_round_count(dt, p->bits, J, qq[0], qq[1], s));
   }
-  IMU_HIP(launch_round_count(op.dtype, p->bits, sa, batch, q_out, s));
   return IMU_OK;
 }
 
@@ -147,13 +156,17 @@ imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, 
                      uint8_t* stats_b, uint8_t* plan, imu_plan_info* info, hipStream_t s) {
   const StatsLayout la = stats_layout(oa.R, oa.C), lb = stats_layout(ob.R, ob.C);
   const int batch = (int)oa.m->batch;
-  if (p->strat_a == IMU_MIX) {
-    StreamArgs sa = stream_args(oa, stats_a, la, p);
-    IMU_HIP(launch_residual(oa.dtype, p->bits, sa, batch, s));
-  }
-  if (p->strat_b == IMU_MIX) {
-    StreamArgs sb = stream_args(ob, stats_b, lb, p);
-    IMU_HIP(launch_residual(ob.dtype, p->bits, sb, batch, s));
+  for (int dt : {(int)IMU_BF16, (int)IMU_F32}) {
+    QuantJobs J{};
+    if (p->strat_a == IMU_MIX && oa.dtype == dt) {
+      J.op[J.nops].s = stream_args(oa, stats_a, la, p);
+      J.op[J.nops++].batch = batch;
+    }
+    if (p->strat_b == IMU_MIX && ob.dtype == dt) {
+      J.op[J.nops].s = stream_args(ob, stats_b, lb, p);
+      J.op[J.nops++].batch = batch;
+    }
+    if (J.nops) IMU_HIP(launch_residual(dt, p->bits, J, s));
   }
   PlanArgs pa{};
   pa.stats_a = stats_a;
@@ -364,7 +377,10 @@ imu_status imu_quantize_rtn(const imu_matrix* x, const imu_params* p, void* stat
   IMU_TRY(check_matrix(x, "x", &op));
   IMU_TRY(check_params(p));
   if (!stats) return fail(IMU_ERR_INVALID_ARG, "stats is NULL");
-  return quantize_impl(op, p, static_cast<uint8_t*>(stats), q_out, stream);
+  const Operand* ops[1] = {&op};
+  uint8_t* st[1] = {static_cast<uint8_t*>(stats)};
+  int32_t* q[1] = {q_out};
+  return quantize_ops(ops, st, q, 1, p, stream, false);
 }
 
 imu_status imu_plan_unpack(const imu_matrix* a, const imu_matrix* b, const imu_params* p, void* stats_a,
@@ -422,8 +438,12 @@ imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const i
   uint8_t* stats_a = w;
   uint8_t* stats_b = stats_a + round_up(stats_layout(oa.R, oa.C).stride * batch, 256);
   uint8_t* plan = stats_b + round_up(stats_layout(ob.R, ob.C).stride * batch, 256);
-  IMU_TRY(quantize_impl(oa, p, stats_a, nullptr, stream));
-  IMU_TRY(quantize_impl(ob, p, stats_b, nullptr, stream));
+  // statistics of A and B are adjacent: clear both with one launch
+  IMU_HIP(launch_fill_u32(stats_a, 0u, (int64_t)(plan - stats_a) / 4, stream));
+  const Operand* ops[2] = {&oa, &ob};
+  uint8_t* st[2] = {stats_a, stats_b};
+  int32_t* q[2] = {nullptr, nullptr};
+  IMU_TRY(quantize_ops(ops, st, q, 2, p, stream, true));
   std::vector<imu_plan_info> local;
   if (!info) {
     local.resize((size_t)batch);

@@ -36,7 +36,8 @@ struct StatsHeader {
   uint32_t sel_prefix;  // radix-select state: key prefix found so far
   uint32_t sel_rank;    // rank still to find inside that prefix (1-based)
   unsigned long long total;  // T: out-of-range codes
-  int32_t pad0, pad1;
+  uint32_t arrive;           // workgroups that finished the current histogram pass
+  int32_t pad1;
   int64_t rows, cols;
 };
 static_assert(sizeof(StatsHeader) == 64, "stats header");
@@ -80,6 +81,7 @@ struct PlanHeader {
   int64_t pair[16][3];
   int64_t seg_off[kMaxSeg + 1];
   int32_t seg_len[kMaxSeg];
+  int64_t tstamp[8];  // planner phase timestamps (wall clock ticks), diagnostics only
 };
 constexpr int64_t kPlanHeaderStride = 2048;
 static_assert(sizeof(PlanHeader) <= kPlanHeaderStride, "plan header");
@@ -95,8 +97,17 @@ struct PlanLayout {
   int64_t levels = 0, segments = 0, m_alloc_max = 0, n_alloc_max = 0;
   int64_t headers_bytes = 0, entry_stride = 0;
   int64_t da_r = 0, da_c = 0, db_r = 0, db_c = 0, lvl_a = 0, lvl_b = 0, kpre = 0, amap = 0, bmap = 0;
+  int64_t kmap = 0, kmap_max = 0;
   int64_t total = 0;
 };
+
+// One entry of the K' position table: k | v << 22 | v' << 27 (A's and B's inner
+// index); kKmapPad marks zero padding at the end of an exponent segment.
+constexpr uint32_t kKmapPad = 0xFFFFFFFFu;
+constexpr int64_t kMaxK = (1ll << 22) - 2;
+__host__ __device__ inline uint32_t kmap_pack(int64_t k, int v, int vp) {
+  return (uint32_t)k | ((uint32_t)v << 22) | ((uint32_t)vp << 27);
+}
 
 // GEMM macro tile (rows of A' x rows of B'^T) used for a problem of this shape;
 // the plan pads the base region and the allocation to these multiples.
@@ -139,6 +150,8 @@ inline PlanLayout plan_layout(int64_t M, int64_t K, int64_t N, int64_t batch, in
   L.kpre = take(4 * (K + 1) * L.segments);
   L.amap = take(4 * L.m_alloc_max);
   L.bmap = take(4 * L.n_alloc_max);
+  L.kmap_max = K * (int64_t)D * D + kKPad * L.segments;
+  L.kmap = take(4 * L.kmap_max);
   L.entry_stride = o;
   L.total = L.headers_bytes + batch * L.entry_stride;
   return L;
@@ -221,6 +234,18 @@ struct StreamArgs {       // one operand traversed in stored orientation
   int64_t srow_oob, scol_oob, srow_maxdig, scol_maxdig, srow_res, scol_res, hist;
   int transposed;  // logical = stored^T
   int beta, p_num, p_den, gamma;
+};
+
+// Work split of the streaming kernels: operand o owns workgroups
+// [wg_begin, wg_begin + wgs_per_entry * batch).
+struct QuantOp {
+  StreamArgs s;
+  int batch;
+  int wg_begin, wgs_per_entry, rows_per_wg;
+};
+struct QuantJobs {
+  QuantOp op[2];
+  int nops;
 };
 
 }  // namespace imu

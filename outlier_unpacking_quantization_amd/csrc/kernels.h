@@ -14,13 +14,9 @@ __host__ __device__ inline int64_t unpacked_entry_bytes(const PlanHeader* h, int
 // quantize.hip
 hipError_t launch_fill_u32(void* p, uint32_t v, int64_t nwords, hipStream_t s);
 hipError_t launch_fill_2d(int32_t* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
-hipError_t launch_hist(int dtype, const StreamArgs& a, int batch, int pass, hipStream_t s);
-hipError_t launch_select(uint8_t* stats, int64_t stats_stride, int64_t hist_off, int batch,
-                         int64_t nelem, int pass, int final_pass, int beta, int p_num, int p_den,
-                         hipStream_t s);
-hipError_t launch_round_count(int dtype, int bits, const StreamArgs& a, int batch, int32_t* q_out,
-                              hipStream_t s);
-hipError_t launch_residual(int dtype, int bits, const StreamArgs& a, int batch, hipStream_t s);
+hipError_t launch_hist(int dtype, QuantJobs J, int pass, int final_pass, hipStream_t s);
+hipError_t launch_round_count(int dtype, int bits, QuantJobs J, int32_t* q0, int32_t* q1, hipStream_t s);
+hipError_t launch_residual(int dtype, int bits, QuantJobs J, hipStream_t s);
 
 // plan.hip
 struct PlanArgs {
