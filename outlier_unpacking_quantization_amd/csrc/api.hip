@@ -91,7 +91,7 @@ imu_status check_pair(const imu_matrix* a, const imu_matrix* b, const imu_params
   IMU_TRY(check_matrix(b, "b", ob));
   IMU_TRY(check_params(p));
   if (a->cols != b->rows) return fail(IMU_ERR_INVALID_ARG, "a.cols must equal b.rows (K)");
-  if (a->cols > kMaxK) return fail(IMU_ERR_UNSUPPORTED, "K must be below 2^22 - 1");
+  if (a->cols > kMaxK) return fail(IMU_ERR_UNSUPPORTED, "K must be below 2^20 - 1");
   if (a->batch != b->batch) return fail(IMU_ERR_INVALID_ARG, "a.batch must equal b.batch");
   return IMU_OK;
 }
@@ -242,6 +242,8 @@ imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, cons
     u.K = op.R;
   }
   u.operand = operand;
+  u.vec_ok = (reinterpret_cast<uintptr_t>(x->data) % 16) == 0 && ld % 8 == 0 &&
+             (x->batch == 1 || x->batch_stride % 8 == 0);
   u.stats = stats;
   u.stats_stride = L.stride;
   u.plan = plan;

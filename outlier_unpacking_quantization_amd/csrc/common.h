@@ -101,12 +101,16 @@ struct PlanLayout {
   int64_t total = 0;
 };
 
-// One entry of the K' position table: k | v << 22 | v' << 27 (A's and B's inner
-// index); kKmapPad marks zero padding at the end of an exponent segment.
+// One entry of the K' position table: k | v << 20 | v' << 25 | lastA << 30 |
+// lastB << 31, where v / v' are A's / B's inner index and lastA / lastB mark the
+// last inner index of k (dA-1 / dB-1), the only one that carries digits at the
+// unpacked levels u > 0.  kKmapPad marks zero padding at the end of an exponent
+// segment.
 constexpr uint32_t kKmapPad = 0xFFFFFFFFu;
-constexpr int64_t kMaxK = (1ll << 22) - 2;
-__host__ __device__ inline uint32_t kmap_pack(int64_t k, int v, int vp) {
-  return (uint32_t)k | ((uint32_t)v << 22) | ((uint32_t)vp << 27);
+constexpr int64_t kMaxK = (1ll << 20) - 2;
+__host__ __device__ inline uint32_t kmap_pack(int64_t k, int v, int vp, int dA, int dB) {
+  return (uint32_t)k | ((uint32_t)v << 20) | ((uint32_t)vp << 25) | ((uint32_t)(v == dA - 1) << 30) |
+         ((uint32_t)(vp == dB - 1) << 31);
 }
 
 // GEMM macro tile (rows of A' x rows of B'^T) used for a problem of this shape;

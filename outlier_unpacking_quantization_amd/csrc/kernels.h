@@ -37,6 +37,7 @@ struct UnpackArgs {
   int64_t so, sk;          // element strides of the outer line index and of k
   int64_t n_outer, K;      // outer lines (A: M rows, B: N cols) and inner length K
   int operand;             // 0 = A, 1 = B
+  int vec_ok;              // 16-byte loads of 8 consecutive k are aligned (inner-contiguous only)
   const uint8_t* stats;
   int64_t stats_stride;
   const uint8_t* plan;

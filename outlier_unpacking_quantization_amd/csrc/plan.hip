@@ -498,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
               kpre[(int64_t)s * (K + 1) + i] = ex[j];
               uint32_t* km = kmap + seg_off[s] + ex[j];
               const int lo = max(0, s - (dB - 1));
-              for (int v = 0; v < c; ++v) km[v] = kmap_pack(i, lo + v, s - lo - v);
+              for (int v = 0; v < c; ++v) km[v] = kmap_pack(i, lo + v, s - lo - v, dA, dB);
               ex[j] += c;
             }
           }

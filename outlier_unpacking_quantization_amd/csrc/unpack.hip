@@ -7,20 +7,26 @@
 //
 // Layout written (per batch entry): A' is m_alloc x k_pad, B'^T is n_alloc x
 // k_pad, int8, K' contiguous.  Row (line o, level u) sits at lvl[u][o]
-// (level-major).  Column j of a row holds the triple kmap[j] = (k, v, v') of the
+// (level-major).  Column j of a row holds the entry kmap[j] = (k, v, v') of the
 // exponent segment it lies in (or zero padding).  Digit t of a code whose inner
 // line has depth dK goes to inner index min(t, dK-1) and level t - min(t, dK-1),
 // so at level 0 every position holds digit (own inner index) and at level u > 0
 // only the last inner index dK-1 holds digit dK-1+u.
 //
-// Two mappings, both writing every byte of every valid row exactly once:
-// * inner-contiguous operands (A row-major, B = W^T): each thread owns 16
-//   consecutive k, computes their codes once per row and scatters their digit
-//   bytes into an LDS copy of each exponent segment (positions from kpre), which
-//   the workgroup then streams out with 16-byte stores;
-// * outer-contiguous operands (A = X^T, B row-major): lanes walk 64 adjacent
-//   lines so every gather is one 128-byte line; bytes are assembled in an LDS
-//   tile and written back row by row.
+// Work split: a workgroup owns L lines and a run of k windows of W.  Per window
+// it stages the lines' codes in LDS as sign-magnitude words (|q| << 1 | sign),
+// with one pad word every 32 words, so that lanes reading nearby k hit distinct
+// banks, and one zero word per line.  Then, for each level u and exponent
+// segment s, it walks the K' positions whose k lies in the window, which are
+// the contiguous range [seg_off + kpre[s][kw0], seg_off + kpre[s][kw1]), plus
+// the segment's zero padding in the last window.  A thread decodes 4
+// consecutive table entries once (LDS slot of k, bit offset of digit t) and
+// then, for every line, reads 4 codes, extracts the digits and writes one dword
+// (byte stores only where a window boundary cuts the dword), so every byte of
+// every valid row is written exactly once.  Inner-contiguous operands (A
+// row-major, B = W^T) stage 16 lines x 512 k with 16-byte loads;
+// outer-contiguous operands (A = X^T, B row-major) stage 64 lines x 128 k, a
+// wave reading 64 adjacent lines of one k.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,15 +34,58 @@ namespace imu {
 
 namespace {
 
-constexpr int kIcWindow = 65536;  // bytes of an unpacked row assembled in LDS at a time
-constexpr int kSegReg = 16;       // segment starts of a k-group kept in registers
-constexpr int kOcChunk = 256;   // K' positions per tile (outer-contiguous path)
-constexpr int kOcStride = kOcChunk / 4 + 1;  // tile row stride in words (bank spread)
+constexpr int kThreads = 256;
+constexpr int kTargetWgs = 2048;  // workgroups aimed for per launch (8 per CU)
+
+template <bool OC>
+struct Shape {
+  static constexpr int L = OC ? 64 : 16;     // lines per workgroup
+  static constexpr int W = OC ? 128 : 512;   // k per window
+  static constexpr int LS = W + W / 32 + 1;  // LDS words per line (odd)
+};
 
 template <int DT>
 __device__ inline float load_elem(const typename Elem<DT>::T* p) {
   if constexpr (DT == IMU_BF16) return bf16_to_f32(*p);
   else return *p;
+}
+
+// 8 consecutive elements from a 16-byte aligned address.
+template <int DT>
+__device__ inline void load8_vec(const typename Elem<DT>::T* p, float v[8]) {
+  if constexpr (DT == IMU_BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 x0 = *reinterpret_cast<const float4*>(p);
+    const float4 x1 = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = x0.x, v[1] = x0.y, v[2] = x0.z, v[3] = x0.w;
+    v[4] = x1.x, v[5] = x1.y, v[6] = x1.z, v[7] = x1.w;
+  }
+}
+
+__device__ inline int slot(int kk) { return kk + (kk >> 5); }
+
+// Sign-magnitude word of the RTN code of x (|q| < 2^31, so |q| << 1 fits).
+__device__ inline uint32_t code_word(float x, float r) {
+  bool bad = false;
+  const int32_t q = rtn_code(x, r, &bad);
+  const uint32_t m = q < 0 ? 0u - (uint32_t)q : (uint32_t)q;
+  return (m << 1) | (uint32_t)(q < 0);
+}
+
+// Two's-complement byte of the signed digit whose magnitude starts at bit sh1
+// of the sign-magnitude word w (sh1 = 1 + t (BITS-1) <= 31).
+template <int BITS>
+__device__ inline uint32_t digit_byte(uint32_t w, uint32_t sh1) {
+  const uint32_t d = (w >> sh1) & ((1u << (BITS - 1)) - 1u);
+  const uint32_t sm = 0u - (w & 1u);
+  return ((d ^ sm) - sm) & 0xFFu;
 }
 
 __device__ inline int64_t entry_offset(const uint8_t* plan, int b, int operand) {
@@ -46,213 +95,171 @@ __device__ inline int64_t entry_offset(const uint8_t* plan, int b, int operand) 
   return off;
 }
 
-// Byte of unpacked row (line, level u) at the position whose table entry is `ent`.
-template <int DT, int BITS>
-__device__ inline uint32_t unpack_byte(uint32_t ent, const typename Elem<DT>::T* line, int64_t sk, float r, int u,
-                                       bool is_a, const int32_t* own_depth) {
-  if (ent == kKmapPad) return 0u;
-  const int64_t k = ent & 0x3FFFFFu;
-  const int v = (ent >> 22) & 31, vp = (ent >> 27) & 31;
-  const int kap = is_a ? v : vp;  // this operand's inner index
-  int t = kap;
-  if (u > 0) t = (kap == own_depth[k] - 1) ? kap + u : -1;
-  if (t < 0) return 0u;
-  bool bad = false;
-  const int32_t q = rtn_code(load_elem<DT>(line + k * sk), r, &bad);
-  return (uint32_t)(uint8_t)(int8_t)digit_of<BITS>(q, t);
-}
-
-// Digit bytes of one group of 16 k in exponent segment s of unpacked row level u,
-// written into the LDS row window [w0, w1) starting at position `pos`.
-template <int BITS>
-__device__ inline void emit_group(uint8_t* row_buf, int64_t w0, int64_t w1, int64_t pos, int s, int u, bool is_a,
-                                  int nk, const float* xs, const int* dA, const int* dB, float r) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j < nk) {
-      const int lo = max(0, s - (dB[j] - 1)), hi = min(dA[j] - 1, s);
-      if (hi >= lo) {
-        const int dK = is_a ? dA[j] : dB[j];
-        bool bad = false;
-        const int32_t q = rtn_code(xs[j], r, &bad);
-        for (int v = lo; v <= hi; ++v, ++pos) {
-          if (pos < w0 || pos >= w1) continue;
-          const int kap = is_a ? v : s - v;  // this operand's inner index
-          const int tt = u == 0 ? kap : (kap == dK - 1 ? kap + u : -1);
-          row_buf[pos - w0] = tt < 0 ? (uint8_t)0 : (uint8_t)(int8_t)digit_of<BITS>(q, tt);
-        }
-      }
-    }
-  }
-}
-
-// Inner-contiguous operands.  Each thread owns groups of 16 consecutive k.  For
-// every unpacked row it issues the loads of a group together (16 elements,
-// both inner depths, the group's start in each exponent segment), writes the
-// group's digit bytes into an LDS copy of the row, and the workgroup streams
-// the row out with 16-byte stores.  Rows longer than the LDS buffer are done
-// in windows (each window recomputes the bytes that fall into it).
-template <int DT, int BITS>
-__global__ __launch_bounds__(256) void unpack_ic_kernel(UnpackArgs a, int lines_per_wg) {
+template <int DT, int BITS, bool OC>
+__global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins_per_wg) {
   using T = typename Elem<DT>::T;
-  __shared__ __attribute__((aligned(16))) uint8_t row_buf[kIcWindow];
+  constexpr int L = Shape<OC>::L, W = Shape<OC>::W, LS = Shape<OC>::LS;
+  constexpr int D = (31 + BITS - 2) / (BITS - 1);
+  constexpr uint32_t kZero = LS - 1;  // zero word of each line
+  __shared__ uint32_t codes[L * LS];
+  __shared__ int64_t rowoff[L];  // byte offset of row (line, level u), -1 if the line has no level u
+  __shared__ int s_dout[L];
   __shared__ int64_t s_off[kMaxSeg + 1];
-  __shared__ int32_t s_len[kMaxSeg];
-  const int b = blockIdx.y;
-  const int64_t o0 = (int64_t)blockIdx.x * lines_per_wg;
-  const int64_t o1 = min64(o0 + lines_per_wg, a.n_outer);
-  const T* xb = static_cast<const T*>(a.x) + b * a.bstride;
-  const float r = reinterpret_cast<const StatsHeader*>(a.stats + b * a.stats_stride)->r;
-  const PlanLayout& L = a.pl;
-  const uint8_t* pe = a.plan + L.headers_bytes + b * L.entry_stride;
-  const PlanHeader* ph = reinterpret_cast<const PlanHeader*>(a.plan + b * kPlanHeaderStride);
-  const bool is_a = a.operand == 0;
-  const int32_t* da_c = reinterpret_cast<const int32_t*>(pe + L.da_c);
-  const int32_t* db_r = reinterpret_cast<const int32_t*>(pe + L.db_r);
-  const int32_t* dout = reinterpret_cast<const int32_t*>(pe + (is_a ? L.da_r : L.db_c));
-  const int32_t* lvl = reinterpret_cast<const int32_t*>(pe + (is_a ? L.lvl_a : L.lvl_b));
-  const int32_t* kpre = reinterpret_cast<const int32_t*>(pe + L.kpre);
-  int8_t* out = a.out + entry_offset(a.plan, b, a.operand);
-  const int64_t kp = ph->k_pad, K = a.K;
-  const int nseg = ph->n_seg;
-  const int t = threadIdx.x;
-  const int64_t ngroups = ceil_div(K, 16);
-  for (int s = t; s <= nseg; s += blockDim.x) {
-    s_off[s] = ph->seg_off[s];
-    if (s < nseg) s_len[s] = ph->seg_len[s];
-  }
-  for (int64_t o = o0; o < o1; ++o) {
-    const T* line = xb + o * a.so;
-    const int d = dout[o];
-    for (int u = 0; u < d; ++u) {
-      int8_t* row = out + (int64_t)lvl[(int64_t)u * a.n_outer + o] * kp;
-      for (int64_t w0 = 0; w0 < kp; w0 += kIcWindow) {
-        const int64_t w1 = min64(w0 + kIcWindow, kp);
-        __syncthreads();  // the previous window has been copied out (and s_off is staged)
-        for (int s = 0; s < nseg; ++s)  // zero padding at the end of each segment
-          for (int64_t p = max64(s_off[s] + s_len[s], w0) + t; p < min64(s_off[s + 1], w1); p += blockDim.x)
-            row_buf[p - w0] = 0;
-        for (int64_t g = t; g < ngroups; g += blockDim.x) {
-          const int64_t k0 = g * 16;
-          const int nk = (int)min64(16, K - k0);
-          // every load of the group first (indices clamped into range)
-          float xs[16];
-          int dA[16], dB[16], sp[kSegReg];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int64_t k = min64(k0 + j, K - 1);
-            xs[j] = load_elem<DT>(line + k);
-            dA[j] = da_c[k];
-            dB[j] = db_r[k];
-          }
-#pragma unroll
-          for (int s = 0; s < kSegReg; ++s) sp[s] = kpre[(int64_t)min(s, nseg - 1) * (K + 1) + k0];
-#pragma unroll
-          for (int sr = 0; sr < kSegReg; ++sr) {  // segments whose start is in registers
-            if (sr < nseg)
-              emit_group<BITS>(row_buf, w0, w1, s_off[sr] + sp[sr], sr, u, is_a, nk, xs, dA, dB, r);
-          }
-          for (int s = kSegReg; s < nseg; ++s)
-            emit_group<BITS>(row_buf, w0, w1, s_off[s] + kpre[(int64_t)s * (K + 1) + k0], s, u, is_a, nk, xs, dA,
-                             dB, r);
-        }
-        __syncthreads();
-        for (int64_t p = w0 + 16 * t; p < w1; p += 16 * blockDim.x)
-          *reinterpret_cast<uint4*>(row + p) = *reinterpret_cast<const uint4*>(&row_buf[p - w0]);
-      }
-    }
-  }
-}
 
-template <int DT, int BITS>
-__global__ __launch_bounds__(256) void unpack_oc_kernel(UnpackArgs a) {
-  using T = typename Elem<DT>::T;
-  __shared__ uint32_t tab[kOcChunk];
-  __shared__ uint32_t tile[64 * kOcStride];
-  __shared__ int32_t rowpos[64];
-  __shared__ int dmax_s;
-  const int b = blockIdx.y;
-  const int64_t o0 = (int64_t)blockIdx.x * 64;
+  const int b = blockIdx.z;
+  const int64_t o0 = (int64_t)blockIdx.x * L;
+  const int64_t K = a.K, nwin = ceil_div(K, W);
+  const int64_t w_begin = (int64_t)blockIdx.y * wins_per_wg;
+  const int64_t w_end = min64(w_begin + wins_per_wg, nwin);
+  if (w_begin >= w_end) return;
   const T* xb = static_cast<const T*>(a.x) + b * a.bstride;
   const float r = reinterpret_cast<const StatsHeader*>(a.stats + b * a.stats_stride)->r;
-  const PlanLayout& L = a.pl;
-  const uint8_t* pe = a.plan + L.headers_bytes + b * L.entry_stride;
+  const PlanLayout& P = a.pl;
+  const uint8_t* pe = a.plan + P.headers_bytes + b * P.entry_stride;
   const PlanHeader* ph = reinterpret_cast<const PlanHeader*>(a.plan + b * kPlanHeaderStride);
   const bool is_a = a.operand == 0;
-  const int32_t* own_depth = reinterpret_cast<const int32_t*>(pe + (is_a ? L.da_c : L.db_r));
-  const int32_t* dout = reinterpret_cast<const int32_t*>(pe + (is_a ? L.da_r : L.db_c));
-  const int32_t* lvl = reinterpret_cast<const int32_t*>(pe + (is_a ? L.lvl_a : L.lvl_b));
-  const uint32_t* kmap = reinterpret_cast<const uint32_t*>(pe + L.kmap);
+  const int32_t* dout = reinterpret_cast<const int32_t*>(pe + (is_a ? P.da_r : P.db_c));
+  const int32_t* lvl = reinterpret_cast<const int32_t*>(pe + (is_a ? P.lvl_a : P.lvl_b));
+  const int32_t* kpre = reinterpret_cast<const int32_t*>(pe + P.kpre);
+  const uint32_t* kmap = reinterpret_cast<const uint32_t*>(pe + P.kmap);
   int8_t* out = a.out + entry_offset(a.plan, b, a.operand);
   const int64_t kp = ph->k_pad;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t o = o0 + lane;
-  const bool line_ok = o < a.n_outer;
-  const int my_d = line_ok ? dout[o] : 0;
-  if (wave == 0) {
-    const int m = wave_max_i32(my_d);
-    if (lane == 0) dmax_s = m;
+  const int nseg = ph->n_seg;
+  const int tid = threadIdx.x;
+  const int kap_sh = is_a ? 20 : 25, last_sh = is_a ? 30 : 31;
+
+  for (int s = tid; s <= nseg; s += kThreads) s_off[s] = ph->seg_off[s];
+  if (tid < L) {
+    s_dout[tid] = o0 + tid < a.n_outer ? dout[o0 + tid] : 0;
+    codes[tid * LS + kZero] = 0u;
   }
   __syncthreads();
-  const int dmax = dmax_s;
-  const T* line = xb + (line_ok ? o : 0) * a.so;
-  for (int64_t j0 = 0; j0 < kp; j0 += kOcChunk) {
-    __syncthreads();
-    tab[t] = j0 + t < kp ? kmap[j0 + t] : kKmapPad;
-    for (int u = 0; u < dmax; ++u) {
-      if (t < 64) rowpos[t] = (o0 + t < a.n_outer && dout[o0 + t] > u) ? lvl[(int64_t)u * a.n_outer + o0 + t] : -1;
-      __syncthreads();
-      if (my_d > u) {
-        for (int q = wave; q < kOcChunk / 4; q += 4) {
-          uint32_t w = 0;
+  int umax = 0;
+  for (int i = 0; i < L; ++i) umax = max(umax, s_dout[i]);
+
+  for (int64_t w = w_begin; w < w_end; ++w) {
+    const int64_t kw0 = w * W, kw1 = min64(kw0 + W, K);
+    __syncthreads();  // readers of the previous window are done
+    if constexpr (!OC) {
+      constexpr int G = W / 8;  // groups of 8 k per line
+      constexpr int kIter = L * G / kThreads;
+      static_assert(L * G % kThreads == 0, "staging split");
+      if (a.vec_ok && kw1 == kw0 + W) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            w |= unpack_byte<DT, BITS>(tab[4 * q + i], line, a.sk, r, u, is_a, own_depth) << (8 * i);
-          tile[lane * kOcStride + q] = w;
+        for (int it = 0; it < kIter; ++it) {
+          const int item = tid + it * kThreads;
+          const int i = item / G, kk = (item % G) * 8;
+          const int64_t o = min64(o0 + i, a.n_outer - 1);
+          float v[8];
+          load8_vec<DT>(xb + o * a.so + kw0 + kk, v);
+          uint32_t* dst = &codes[i * LS + slot(kk)];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dst[j] = code_word(v[j], r);
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < kIter; ++it) {
+          const int item = tid + it * kThreads;
+          const int i = item / G, kk = (item % G) * 8;
+          const int64_t o = min64(o0 + i, a.n_outer - 1);
+          const T* line = xb + o * a.so;
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = load_elem<DT>(line + min64(kw0 + kk + j, K - 1) * a.sk);
+          uint32_t* dst = &codes[i * LS + slot(kk)];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dst[j] = code_word(v[j], r);
         }
       }
-      __syncthreads();
-      for (int item = t; item < 64 * (kOcChunk / 4); item += blockDim.x) {
-        const int rr = item / (kOcChunk / 4), wq = item % (kOcChunk / 4);
-        const int64_t j = j0 + 4 * wq;
-        const int32_t row = rowpos[rr];
-        if (row >= 0 && j < kp) *reinterpret_cast<uint32_t*>(out + (int64_t)row * kp + j) = tile[rr * kOcStride + wq];
+    } else {
+      constexpr int kIter = L * W / kThreads;
+      static_assert(L * W % kThreads == 0, "staging split");
+#pragma unroll 8
+      for (int it = 0; it < kIter; ++it) {
+        const int item = tid + it * kThreads;
+        const int i = item % L, kk = item / L;
+        const int64_t o = min64(o0 + i, a.n_outer - 1);
+        const int64_t k = min64(kw0 + kk, K - 1);
+        codes[i * LS + slot(kk)] = code_word(load_elem<DT>(xb + o * a.so + k * a.sk), r);
       }
+    }
+    __syncthreads();
+    const bool last_win = kw1 == K;
+    for (int u = 0; u < umax; ++u) {
+      if (tid < L)
+        rowoff[tid] = s_dout[tid] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + o0 + tid] * kp : (int64_t)-1;
       __syncthreads();
+      for (int s = 0; s < nseg; ++s) {
+        const int32_t* kps = kpre + (int64_t)s * (K + 1);
+        const int64_t P0 = s_off[s] + kps[kw0];
+        const int64_t P1 = last_win ? s_off[s + 1] : s_off[s] + kps[kw1];
+        const int64_t g_end = (P1 + 3) >> 2;
+        for (int64_t g = (P0 >> 2) + tid; g < g_end; g += kThreads) {
+          const uint4 e4 = *reinterpret_cast<const uint4*>(kmap + 4 * g);
+          const uint32_t ent[4] = {e4.x, e4.y, e4.z, e4.w};
+          uint32_t adr[4], sh[4];
+          bool inr[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int64_t p = 4 * g + c;
+            inr[c] = p >= P0 && p < P1;
+            const uint32_t e = ent[c];
+            const int kap = (int)((e >> kap_sh) & 31u);
+            const bool last = (e >> last_sh) & 1u;
+            const int t = u == 0 ? kap : (last ? kap + u : D);
+            const int kk = (int)((int64_t)(e & 0xFFFFFu) - kw0);
+            const bool ok = inr[c] && e != kKmapPad && t < D && kk >= 0 && kk < W;
+            adr[c] = ok ? (uint32_t)slot(kk) : kZero;
+            sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
+          }
+          const bool full = inr[0] && inr[3];
+#pragma unroll 8
+          for (int i = 0; i < L; ++i) {
+            const int64_t ro = rowoff[i];
+            if (ro < 0) continue;
+            const uint32_t* cl = codes + i * LS;
+            uint32_t dw = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dw |= digit_byte<BITS>(cl[adr[c]], sh[c]) << (8 * c);
+            int8_t* dst = out + ro + 4 * g;
+            if (full) {
+              *reinterpret_cast<uint32_t*>(dst) = dw;
+            } else {
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                if (inr[c]) dst[c] = (int8_t)(uint8_t)(dw >> (8 * c));
+            }
+          }
+        }
+      }
+      __syncthreads();  // before rowoff is rewritten
     }
   }
+}
+
+template <int DT, bool OC>
+hipError_t unpack_launch(int bits, const UnpackArgs& a, int batch, hipStream_t s) {
+  constexpr int L = Shape<OC>::L, W = Shape<OC>::W;
+  const int64_t nblk = ceil_div(a.n_outer, L), nwin = ceil_div(a.K, W);
+  const int64_t want_y = min64(nwin, max64(1, ceil_div(kTargetWgs, nblk * batch)));
+  const int64_t wpg = ceil_div(nwin, want_y);
+  dim3 grid((unsigned)nblk, (unsigned)ceil_div(nwin, wpg), (unsigned)batch);
+  switch (bits) {
+#define IMU_UP(B)                                                                                     \
+  case B:                                                                                             \
+    hipLaunchKernelGGL((unpack_kernel<DT, B, OC>), grid, dim3(kThreads), 0, s, a, (int)wpg);          \
+    break;
+    IMU_UP(2) IMU_UP(3) IMU_UP(4) IMU_UP(5) IMU_UP(6) IMU_UP(7) IMU_UP(8)
+#undef IMU_UP
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int DT>
 hipError_t unpack_dt(int bits, const UnpackArgs& a, int batch, hipStream_t s) {
-  const bool inner_contiguous = a.sk == 1;
-  if (inner_contiguous) {
-    const int lines = (int)min64(max64(a.n_outer * batch / 512, 1), 16);
-    dim3 grid((unsigned)ceil_div(a.n_outer, lines), (unsigned)batch);
-    switch (bits) {
-#define IMU_UP(B)                                                                                  \
-  case B:                                                                                          \
-    hipLaunchKernelGGL((unpack_ic_kernel<DT, B>), grid, dim3(256), 0, s, a, lines);               \
-    break;
-      IMU_UP(2) IMU_UP(3) IMU_UP(4) IMU_UP(5) IMU_UP(6) IMU_UP(7) IMU_UP(8)
-#undef IMU_UP
-      default:
-        return hipErrorInvalidValue;
-    }
-  } else {
-    dim3 grid((unsigned)ceil_div(a.n_outer, 64), (unsigned)batch);
-    switch (bits) {
-#define IMU_UP(B)                                                                                  \
-  case B:                                                                                          \
-    hipLaunchKernelGGL((unpack_oc_kernel<DT, B>), grid, dim3(256), 0, s, a);                       \
-    break;
-      IMU_UP(2) IMU_UP(3) IMU_UP(4) IMU_UP(5) IMU_UP(6) IMU_UP(7) IMU_UP(8)
-#undef IMU_UP
-      default:
-        return hipErrorInvalidValue;
-    }
-  }
-  return hipGetLastError();
+  return a.sk == 1 ? unpack_launch<DT, false>(bits, a, batch, s) : unpack_launch<DT, true>(bits, a, batch, s);
 }
 
 }  // namespace
