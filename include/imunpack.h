@@ -175,10 +175,14 @@ imu_status imu_plan_unpack(const imu_matrix* a, const imu_matrix* b, const imu_p
  * decomposed into several in-range low bit-width integers in extra rows or
  * columns; summary: "larger matrices").  operand 0 = A -> A' (m_alloc x k_pad per
  * entry), operand 1 = B -> B'^T (n_alloc x k_pad per entry), each entry at
- * info.a_offset / info.b_offset of x_u.  Rows are level-major (original lines
+ * info.a_offset / info.b_offset of x_u.  B'^T is row-major.  A' is stored in
+ * MFMA fragment order: 1 KB blocks of 32 rows x 32 K' bytes, ordered by row
+ * block then K' block, block (rb, c) at byte (rb * k_pad/32 + c) * 1024; inside
+ * a block, bytes [16h, 16h + 16) of the block's row r are at 16 * (r + 32h)
+ * (h = 0, 1).  Rows are level-major (original lines
  * first, then level 1 lines, ...); columns are the exponent segments of K'
  * (e = v + v' ascending, then k, then v), each padded with zero bytes to a
- * multiple of 64.  Every byte of the valid rows is written. */
+ * multiple of 128.  Every byte of the valid rows is written. */
 imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p,
                       const void* stats, const void* plan, const imu_plan_info* info,
                       int8_t* x_u, hipStream_t stream);

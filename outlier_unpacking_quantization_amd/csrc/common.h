@@ -13,7 +13,7 @@ namespace imu {
 // constants
 // ---------------------------------------------------------------------------
 constexpr int kHistBins = 32768;    // 15-bit magnitude key of bf16 (and the top of fp32)
-constexpr int kKPad = 64;           // every exponent segment of K' is padded to this many bytes
+constexpr int kKPad = 128;          // every exponent segment of K' is padded to this many bytes
 constexpr int kMaxSeg = 64;         // room for 2*max_digits(2)-1 = 61 segments
 constexpr int kStatusNonfinite = 1; // device status bits
 constexpr int kStatusRange = 2;
@@ -113,6 +113,17 @@ __host__ __device__ inline uint32_t kmap_pack(int64_t k, int v, int vp, int dA, 
          ((uint32_t)(vp == dB - 1) << 31);
 }
 
+// Byte offset of element (row, p) of A' in MFMA fragment order: 1 KB blocks of
+// 32 rows x 32 K' bytes, ordered by row block then K' block; inside a block,
+// 16-byte half h of row r is lane r + 32 h.  Split into a row part and a K'
+// part that add up.
+__host__ __device__ inline int64_t frag_row_offset(int64_t row, int64_t k_pad) {
+  return (row >> 5) * (k_pad >> 5) * 1024 + (row & 31) * 16;
+}
+__host__ __device__ inline int64_t frag_pos_offset(int64_t p) {
+  return (p >> 5) * 1024 + ((p >> 4) & 1) * 512 + (p & 15);
+}
+
 // GEMM macro tile (rows of A' x rows of B'^T) used for a problem of this shape;
 // the plan pads the base region and the allocation to these multiples.
 struct GemmTile {
@@ -121,7 +132,7 @@ struct GemmTile {
 inline GemmTile gemm_tile_for(int64_t M, int64_t N) {
   (void)M;
   (void)N;
-  return GemmTile{128, 128};
+  return GemmTile{256, 128};
 }
 
 inline PlanLayout plan_layout(int64_t M, int64_t K, int64_t N, int64_t batch, int bits) {

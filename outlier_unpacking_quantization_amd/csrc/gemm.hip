@@ -11,8 +11,21 @@
 // unpacked row (i, u) and column (n, w) into C[i, n] with a further shift of
 // (bits-1)(u+w); all int32 arithmetic wraps modulo 2^32.
 //
-// Operands: A' (m_alloc x k_pad) and B'^T (n_alloc x k_pad), both K-contiguous,
-// so both MFMA operands load 16 contiguous bytes per lane.
+// Operands: A' (m_alloc x k_pad) and B'^T (n_alloc x k_pad), both K-contiguous.
+// Workgroup tile 256 x 128, four waves stacked along M, each owning 64 rows x
+// 128 columns (2 x 4 blocks of 32 x 32, 128 accumulator registers).  A wave's A
+// rows belong to it alone, and A' is stored in MFMA fragment order, so its A
+// fragments are contiguous 1 KB loads straight into registers; the B tile (128
+// x 128 bytes per K step, read 8 lanes per 128-byte row) is shared by the four
+// waves and goes through LDS, double-buffered, rows 144 bytes apart (16-byte
+// reads of 8 consecutive rows then touch disjoint banks).  Both operands are
+// prefetched two K steps ahead in a register ring (one wave per SIMD, so
+// latency is hidden by depth rather than by occupancy).  This keeps LDS
+// traffic at about 70% of its read bandwidth when the matrix cores run at peak,
+// where staging both operands through LDS would exceed it.  Segments are padded
+// to the K step, so a step never straddles two exponents.  Tiles are ordered in
+// groups of 8 tile rows and dealt to the 8 XCDs in contiguous runs, so the
+// workgroups sharing an XCD's L2 share A and B panels.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,85 +36,166 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDS_STRIDE = BK + 16;  // bytes per staged row (padding spreads LDS banks)
+constexpr int BM = 256, BN = 128, BK = 128;
+constexpr int kThreads = 256;
+constexpr int BSTR = BK + 16;  // LDS bytes per staged B row
+constexpr int kGroupM = 8;     // tile rows per ordering group
+constexpr int kXcds = 8;
+constexpr int kDepth = 2;     // K steps of A and B in flight per thread
+static_assert(BK == kKPad, "a K step must not straddle exponent segments");
 
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) int8_t sB[BN * LDS_STRIDE];
-  const PlanHeader* ph = reinterpret_cast<const PlanHeader*>(g.hdr);
-  const int tn = blockIdx.x, tm = blockIdx.y;
-  const bool base_tile = (int64_t)tm * BM < g.m_base && (int64_t)tn * BN < g.n_base;
-  if (g.mode == 2 && base_tile) return;
-  const int64_t row0 = (int64_t)tm * BM, col0 = (int64_t)tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int nseg = ph->n_seg;
-  const int shift = g.bits - 1;
+struct TileCoord {
+  int tm, tn;
+};
 
-  v16i acc[2][2];
+// Workgroup w of a launch over tiles_m x tiles_n tiles -> its tile.  Hardware
+// deals workgroups to XCDs round-robin (w % 8); XCD x gets the contiguous run of
+// tile ids [start(x), start(x) + count(x)) in grouped order.
+__device__ inline TileCoord tile_of(int w, int tiles_m, int tiles_n) {
+  const int T = tiles_m * tiles_n;
+  const int x = w % kXcds, slot = w / kXcds;
+  const int per = T / kXcds, rem = T % kXcds;
+  const int id = x * per + min(x, rem) + slot;
+  const int group = id / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(kGroupM, tiles_m - first_m);
+  const int in = id - group * kGroupM * tiles_n;
+  return TileCoord{first_m + in % gm, in / gm};
+}
+
+__device__ inline void shift_acc(v16i (&acc)[2][4], int sh) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16i{0};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = sh >= 32 ? 0 : (int)((uint32_t)acc[i][j][r] << sh);
+}
 
-  // global -> LDS: each thread copies 2 x 16 bytes of A and of B per K step
-  const int ld_row = tid >> 1, ld_col = (tid & 1) * 32;
-  const int8_t* ga = g.a_u + (row0 + ld_row) * g.k_pad + ld_col;
-  const int8_t* gb = g.b_u + (col0 + ld_row) * g.k_pad + ld_col;
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BSTR];
+  const PlanHeader* ph = reinterpret_cast<const PlanHeader*>(g.hdr);
+  const int64_t rows = g.mode == 2 ? g.m_alloc : g.m_base;
+  const int64_t cols = g.mode == 2 ? g.n_alloc : g.n_base;
+  const int tiles_m = (int)(rows / BM), tiles_n = (int)(cols / BN);
+  if ((int)blockIdx.x >= tiles_m * tiles_n) return;
+  const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n);
+  const bool base_tile = (int64_t)tc.tm * BM < g.m_base && (int64_t)tc.tn * BN < g.n_base;
+  if (g.mode == 2 && base_tile) return;
 
-  for (int s = nseg - 1; s >= 0; --s) {
-    if (s < nseg - 1) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t kp = g.k_pad;
+  const int64_t row0 = (int64_t)tc.tm * BM + wave * 64, col0 = (int64_t)tc.tn * BN;
+  const int shift = g.bits - 1;
+
+  // A' is in fragment order: fragment f (rows row0 + 32f ..) of K substep q at
+  // step k is the contiguous 1 KB at block (row0/32 + f, k/32 + q); lane l holds
+  // bytes [16l, 16l + 16) of it.
+  const int8_t* ga = g.a_u + frag_row_offset(row0, kp) + lane * 16;
+  const int64_t ga_f1 = (kp >> 5) * 1024;
+  // B staging: thread copies rows br + 32j (j < 4), bytes [bc, bc + 16) of the step
+  const int br = tid >> 3, bc = (tid & 7) * 16;
+  const int8_t* gb = g.b_u + (col0 + br) * kp + bc;
+  const int64_t gb_j = 32 * kp;
+  const int sb_w = br * BSTR + bc;
+  // B fragment j (columns col0 + 32j + lane%32), substep q
+  const int sb_r = (lane & 31) * BSTR + 16 * (lane >> 5);
+
+  v16i acc[2][4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = (int)((uint32_t)acc[i][j][r] << shift);
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{0};
+
+  // Segment cursors (wave-uniform): segments run from the highest exponent
+  // down; empty segments are skipped but still count in the shifts.
+  const int nseg = ph->n_seg;
+  const int64_t* off = ph->seg_off;
+  const int64_t steps = kp / BK;
+  int ls = nseg - 1;  // load cursor
+  while (ls > 0 && off[ls] == off[ls + 1]) --ls;
+  int64_t lk = off[ls], lend = off[ls + 1];
+  int cs = ls;  // compute cursor
+  int64_t ck = lk, cend = lend;
+  auto advance = [&](int& s, int64_t& k, int64_t& end) {
+    k += BK;
+    if (k >= end && s > 0) {
+      --s;
+      while (s > 0 && off[s] == off[s + 1]) --s;
+      k = off[s];
+      end = off[s + 1];
     }
-    const int64_t k0 = ph->seg_off[s], k1 = ph->seg_off[s + 1];
-    for (int64_t kk = k0; kk < k1; kk += BK) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(ga + kk);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(ga + kk + 16);
-      const uint4 b0 = *reinterpret_cast<const uint4*>(gb + kk);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(gb + kk + 16);
-      __syncthreads();
-      *reinterpret_cast<uint4*>(&sA[ld_row * LDS_STRIDE + ld_col]) = a0;
-      *reinterpret_cast<uint4*>(&sA[ld_row * LDS_STRIDE + ld_col + 16]) = a1;
-      *reinterpret_cast<uint4*>(&sB[ld_row * LDS_STRIDE + ld_col]) = b0;
-      *reinterpret_cast<uint4*>(&sB[ld_row * LDS_STRIDE + ld_col + 16]) = b1;
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) {
-        const int koff = ks * 32 + (lane >> 5) * 16;
-        v4i af[2], bf[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = *reinterpret_cast<const v4i*>(&sA[(wm * 64 + i * 32 + (lane & 31)) * LDS_STRIDE + koff]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bf[j] = *reinterpret_cast<const v4i*>(&sB[(wn * 64 + j * 32 + (lane & 31)) * LDS_STRIDE + koff]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-      }
-    }
+  };
+
+  // Register ring over kDepth K steps: slot t holds the A fragments and the B
+  // staging registers of the steps j with j % kDepth == t, loaded kDepth steps
+  // before their use.  Loads past the last step re-read the last step (they
+  // stay unconditional so the ring stays in registers); that data is never used.
+  const int64_t k_last = kp - BK;
+  v4i ar[kDepth][4][2];
+  v4i bs[kDepth][4];
+#define IMU_LOAD(t)                                                                          \
+  {                                                                                          \
+    const int64_t k_ = min64(lk, k_last);                                                    \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                          \
+      ar[t][q][0] = *reinterpret_cast<const v4i*>(ga + k_ * 32 + 1024 * q);                  \
+      ar[t][q][1] = *reinterpret_cast<const v4i*>(ga + ga_f1 + k_ * 32 + 1024 * q);          \
+    }                                                                                        \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[t][j] =                                 \
+        *reinterpret_cast<const v4i*>(gb + j * gb_j + k_);                                   \
+    advance(ls, lk, lend);                                                                   \
+  }
+#define IMU_STORE_B(t, buf) \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(&sB[buf][sb_w + j * 32 * BSTR]) = bs[t][j];
+#define IMU_STEP(t)                                                                              \
+  if (i0 + t < steps) {                                                                          \
+    const int64_t j_ = i0 + t;                                                                   \
+    if (cs != prev_s) {                                                                          \
+      shift_acc(acc, shift * (prev_s - cs));                                                     \
+      prev_s = cs;                                                                               \
+    }                                                                                            \
+    const int8_t* sbuf = sB[j_ & 1];                                                             \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                              \
+      v4i bf[4];                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) bf[j] =                                      \
+          *reinterpret_cast<const v4i*>(sbuf + sb_r + j * 32 * BSTR + 32 * q);                   \
+      _Pragma("unroll") for (int f = 0; f < 2; ++f)                                              \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
+        acc[f][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[t][q][f], bf[j], acc[f][j], 0, 0, 0); \
+    }                                                                                            \
+    IMU_STORE_B((t + 1) % kDepth, (j_ + 1) & 1);                                                 \
+    IMU_LOAD(t);                                                                                 \
+    __syncthreads();                                                                             \
+    advance(cs, ck, cend);                                                                       \
   }
 
-  // epilogue: accumulator register r of lane l holds tile element
+  static_assert(kDepth == 2, "the ring below is written out for two slots");
+  IMU_LOAD(0);
+  IMU_LOAD(1);
+  IMU_STORE_B(0, 0);
+  __syncthreads();
+  int prev_s = cs;
+  for (int64_t i0 = 0; i0 < steps; i0 += kDepth) {
+    IMU_STEP(0);
+    IMU_STEP(1);
+  }
+#undef IMU_LOAD
+#undef IMU_STORE_B
+#undef IMU_STEP
+  if (prev_s > 0) shift_acc(acc, shift * prev_s);  // exponents below the last non-empty segment
+
+  // epilogue: accumulator register r of lane l holds element
   // (8*(r/4) + 4*(l/32) + r%4, l%32) of each 32x32 block
   const float sab = g.sa->s * g.sb->s;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t gr = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t gc = col0 + wn * 64 + j * 32 + (lane & 31);
-        const int32_t v = acc[i][j][r];
+        const int64_t gr = row0 + f * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t gc = col0 + j * 32 + (lane & 31);
+        const int32_t v = acc[f][j][r];
         if (g.mode == 2) {
           const int32_t am = g.amap[gr], bm = g.bmap[gc];
           if (am < 0 || bm < 0) continue;
@@ -123,9 +217,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int64_t rows = g.mode == 2 ? g.m_alloc : g.m_base;
   const int64_t cols = g.mode == 2 ? g.n_alloc : g.n_base;
-  dim3 grid((unsigned)(cols / BN), (unsigned)(rows / BM));
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, s, g);
+  if (rows % BM || cols % BN) return hipErrorInvalidValue;
+  const int64_t tiles = (rows / BM) * (cols / BN);
+  if (tiles == 0) return hipSuccess;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 

@@ -5,8 +5,12 @@
 // in-range low bit-width integers placed in extra rows / columns ("Approach"),
 // turning each matrix into a larger one (summary paragraph).
 //
-// Layout written (per batch entry): A' is m_alloc x k_pad, B'^T is n_alloc x
-// k_pad, int8, K' contiguous.  Row (line o, level u) sits at lvl[u][o]
+// Layout written (per batch entry): B'^T is n_alloc x k_pad, int8, row-major
+// (K' contiguous).  A' (m_alloc x k_pad) is stored in MFMA fragment order: each
+// block of 32 rows x 32 bytes of K' is 1 KB, lane l = (row % 32) + 32 * (16-byte
+// half) holding 16 consecutive bytes, blocks ordered by row block then K' block
+// (frag_row_offset / frag_pos_offset), so the GEMM reads A fragments as
+// contiguous 1 KB loads.  Row (line o, level u) sits at lvl[u][o]
 // (level-major).  Column j of a row holds the entry kmap[j] = (k, v, v') of the
 // exponent segment it lies in (or zero padding).  Digit t of a code whose inner
 // line has depth dK goes to inner index min(t, dK-1) and level t - min(t, dK-1),
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
   constexpr int D = (31 + BITS - 2) / (BITS - 1);
   constexpr uint32_t kZero = LS - 1;  // zero word of each line
   __shared__ uint32_t codes[L * LS];
-  __shared__ int64_t rowoff[L];  // byte offset of row (line, level u), -1 if the line has no level u
+  __shared__ int64_t rowoff[L];  // row part of the byte offset of row (line, level u), -1 if absent
   __shared__ int s_dout[L];
   __shared__ int64_t s_off[kMaxSeg + 1];
 
@@ -186,8 +190,10 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
     __syncthreads();
     const bool last_win = kw1 == K;
     for (int u = 0; u < umax; ++u) {
-      if (tid < L)
-        rowoff[tid] = s_dout[tid] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + o0 + tid] * kp : (int64_t)-1;
+      if (tid < L) {
+        const int64_t row = s_dout[tid] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + o0 + tid] : (int64_t)-1;
+        rowoff[tid] = row < 0 ? (int64_t)-1 : is_a ? frag_row_offset(row, kp) : row * kp;
+      }
       __syncthreads();
       for (int s = 0; s < nseg; ++s) {
         const int32_t* kps = kpre + (int64_t)s * (K + 1);
@@ -213,6 +219,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
             sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
           }
           const bool full = inr[0] && inr[3];
+          const int64_t pos = is_a ? frag_pos_offset(4 * g) : 4 * g;
 #pragma unroll 8
           for (int i = 0; i < L; ++i) {
             const int64_t ro = rowoff[i];
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
             uint32_t dw = 0;
 #pragma unroll
             for (int c = 0; c < 4; ++c) dw |= digit_byte<BITS>(cl[adr[c]], sh[c]) << (8 * c);
-            int8_t* dst = out + ro + 4 * g;
+            int8_t* dst = out + ro + pos;
             if (full) {
               *reinterpret_cast<uint32_t*>(dst) = dw;
             } else {

@@ -2,7 +2,7 @@
 oracle per batch entry, and map the HIP path's padded unpacked layout back to
 the canonical one.  The padded layout is the documented one (include/imunpack.h):
 extra lines start at m_base / n_base, and every exponent segment of K' starts
-at a multiple of 64 bytes; both are reconstructed here from the oracle's own
+at a multiple of 128 bytes; both are reconstructed here from the oracle's own
 index maps, not read from the GPU plan arrays."""
 from __future__ import annotations
 
@@ -13,7 +13,7 @@ from oracle import imunpack_oracle as O
 from outlier_unpacking_quantization_amd import binding as B
 from outlier_unpacking_quantization_amd import workloads as W
 
-KPAD = 64
+KPAD = 128
 
 
 def to_device(op: W.Operand) -> B.Matrix:
@@ -66,6 +66,15 @@ def padded_k_index(trip: np.ndarray) -> np.ndarray:
     start = np.concatenate([[0], np.cumsum(sizes)])
     e = trip[:, 3]
     return np.array(off)[e] + (np.arange(trip.shape[0]) - start[e])
+
+
+def untile_a(flat: np.ndarray, m_alloc: int, kp: int) -> np.ndarray:
+    """A' as stored (MFMA fragment order, include/imunpack.h) -> row-major m_alloc x kp.
+
+    Block (row block rb, K' block c) is 1 KB at (rb * kp/32 + c) * 1024; inside
+    it, 16-byte half h of row r of the block is lane r + 32 h."""
+    t = np.asarray(flat).reshape(m_alloc // 32, kp // 32, 2, 32, 16)  # rb, c, h, r, byte
+    return t.transpose(0, 3, 1, 2, 4).reshape(m_alloc, kp)
 
 
 def ulp_diff(a: np.ndarray, b: np.ndarray) -> int:

@@ -107,7 +107,8 @@ def test_staged_path_matches_oracle(cfg):
         assert info["k_pad"] == seg_off[-1]
         # unpacked operands, padding stripped through the documented layout
         kp = info["k_pad"]
-        A_g = a_u[info["a_offset"]:info["a_offset"] + info["m_alloc"] * kp].view(info["m_alloc"], kp).cpu().numpy()
+        A_g = G.untile_a(a_u[info["a_offset"]:info["a_offset"] + info["m_alloc"] * kp].cpu().numpy(),
+                         info["m_alloc"], kp)
         B_g = b_u[info["b_offset"]:info["b_offset"] + info["n_alloc"] * kp].view(info["n_alloc"], kp).cpu().numpy()
         rows = G.padded_line_index(pl.rows_a, M, info["m_base"])
         cols = G.padded_line_index(pl.cols_b, N, info["n_base"])
