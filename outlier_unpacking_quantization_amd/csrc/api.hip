@@ -2,6 +2,7 @@
 // carving, kernel launches and the one plan-header readback.  Contains no
 // kernels; the device work lives in quantize.hip, plan.hip, unpack.hip and
 // gemm.hip.
+#include <cstdint>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -152,8 +153,8 @@ imu_status quantize_ops(const Operand* const* ops, uint8_t* const* stats, int32_
   return IMU_OK;
 }
 
-imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
-                     uint8_t* stats_b, uint8_t* plan, imu_plan_info* info, hipStream_t s) {
+imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
+                       uint8_t* stats_b, uint8_t* plan, hipStream_t s) {
   const StatsLayout la = stats_layout(oa.R, oa.C), lb = stats_layout(ob.R, ob.C);
   const int batch = (int)oa.m->batch;
   for (int dt : {(int)IMU_BF16, (int)IMU_F32}) {
@@ -182,14 +183,56 @@ imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, 
   pa.strat_b = p->strat_b;
   pa.bits = p->bits;
   IMU_HIP(launch_plan(pa, s));
-  std::vector<uint8_t> hdrs((size_t)batch * kPlanHeaderStride);
-  IMU_HIP(hipMemcpyAsync(hdrs.data(), plan, hdrs.size(), hipMemcpyDeviceToHost, s));
-  IMU_HIP(hipStreamSynchronize(s));
+  return IMU_OK;
+}
+
+// Per-thread pinned staging buffer for the plan headers and an event marking
+// their arrival, so the host can wait for the headers alone while later
+// kernels keep the GPU busy.  Both live until the process ends.
+struct HeaderStage {
+  uint8_t* buf = nullptr;
+  size_t bytes = 0;
+  hipEvent_t ev = nullptr;
+  int dev = -1;
+};
+thread_local HeaderStage g_stage;
+
+imu_status stage_headers(const uint8_t* plan, size_t bytes, hipStream_t s, const uint8_t** out) {
+  int dev = 0;
+  IMU_HIP(hipGetDevice(&dev));
+  HeaderStage& st = g_stage;
+  if (st.ev && st.dev != dev) st.ev = nullptr;  // events belong to a device; the old one is kept alive
+  if (!st.ev) {
+    IMU_HIP(hipEventCreateWithFlags(&st.ev, hipEventDisableTiming));
+    st.dev = dev;
+  }
+  if (st.bytes < bytes) {
+    void* p = nullptr;
+    IMU_HIP(hipHostMalloc(&p, bytes, hipHostMallocDefault));
+    st.buf = static_cast<uint8_t*>(p);  // the previous buffer is not freed: a copy may still target it
+    st.bytes = bytes;
+  }
+  IMU_HIP(hipMemcpyAsync(st.buf, plan, bytes, hipMemcpyDeviceToHost, s));
+  IMU_HIP(hipEventRecord(st.ev, s));
+  *out = st.buf;
+  return IMU_OK;
+}
+
+// Fill info from the staged headers (B' entries follow all A' entries) and
+// report a failed plan.  *a_total / *b_total: bytes of all A' / B' entries.
+imu_status finish_plan(const Operand& oa, const Operand& ob, const uint8_t* hdrs, int batch, imu_plan_info* info,
+                       int64_t* a_total, int64_t* b_total) {
   int status = 0;
   int64_t aoff = 0, boff = 0;
   for (int b = 0; b < batch; ++b) {
-    const PlanHeader* h = reinterpret_cast<const PlanHeader*>(hdrs.data() + (size_t)b * kPlanHeaderStride);
+    const PlanHeader* h = reinterpret_cast<const PlanHeader*>(hdrs + (size_t)b * kPlanHeaderStride);
     status |= h->status;
+    aoff += unpacked_entry_bytes(h, 0);
+  }
+  const int64_t a_all = aoff;
+  aoff = 0;
+  for (int b = 0; b < batch; ++b) {
+    const PlanHeader* h = reinterpret_cast<const PlanHeader*>(hdrs + (size_t)b * kPlanHeaderStride);
     if (info) {
       imu_plan_info& f = info[b];
       std::memset(&f, 0, sizeof(f));
@@ -216,13 +259,28 @@ imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, 
     aoff += unpacked_entry_bytes(h, 0);
     boff += unpacked_entry_bytes(h, 1);
   }
+  if (a_total) *a_total = a_all;
+  if (b_total) *b_total = boff;
   if (status & kStatusNonfinite) return fail(IMU_ERR_NONFINITE, "an input element is NaN or Inf");
   if (status & kStatusRange) return fail(IMU_ERR_RANGE, "|x * r| >= 2^31 for some element");
   return IMU_OK;
 }
 
+imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
+                     uint8_t* stats_b, uint8_t* plan, imu_plan_info* info, hipStream_t s) {
+  IMU_TRY(plan_launch(oa, ob, p, stats_a, stats_b, plan, s));
+  const int batch = (int)oa.m->batch;
+  const uint8_t* hdrs = nullptr;
+  IMU_TRY(stage_headers(plan, (size_t)batch * kPlanHeaderStride, s, &hdrs));
+  IMU_HIP(hipEventSynchronize(g_stage.ev));
+  return finish_plan(oa, ob, hdrs, batch, info, nullptr, nullptr);
+}
+
+// Unpack one operand; M, K, N give the plan layout.  after_a: B' entries start
+// after all A' entries of x_u; cap: bytes available at x_u.
 imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, const uint8_t* stats,
-                       const uint8_t* plan, const imu_plan_info* info, int8_t* x_u, hipStream_t s) {
+                       const uint8_t* plan, int64_t M, int64_t K, int64_t N, int8_t* x_u, bool after_a,
+                       int64_t cap, hipStream_t s) {
   const StatsLayout L = stats_layout(op.R, op.C);
   const imu_matrix* x = op.m;
   UnpackArgs u{};
@@ -247,8 +305,10 @@ imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, cons
   u.stats = stats;
   u.stats_stride = L.stride;
   u.plan = plan;
-  u.pl = plan_layout(info[0].m, info[0].k, info[0].n, x->batch, p->bits);
+  u.pl = plan_layout(M, K, N, x->batch, p->bits);
   u.out = x_u;
+  u.after_a = after_a ? 1 : 0;
+  u.cap = cap;
   IMU_HIP(launch_unpack(op.dtype, p->bits, u, (int)x->batch, s));
   return IMU_OK;
 }
@@ -405,8 +465,8 @@ imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p,
   const int64_t M = operand == 0 ? op.R : info[0].m, K = operand == 0 ? op.C : op.R,
                 N = operand == 0 ? info[0].n : op.C;
   IMU_TRY(check_info(info, x->batch, M, K, N));
-  return unpack_impl(op, operand, p, static_cast<const uint8_t*>(stats), static_cast<const uint8_t*>(plan),
-                     info, x_u, stream);
+  return unpack_impl(op, operand, p, static_cast<const uint8_t*>(stats), static_cast<const uint8_t*>(plan), M, K,
+                     N, x_u, false, INT64_MAX, stream);
 }
 
 imu_status imu_unpacked_gemm(const int8_t* a_u, const int8_t* b_u, const imu_params* p, const void* stats_a,
@@ -451,17 +511,26 @@ imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const i
     local.resize((size_t)batch);
     info = local.data();
   }
-  IMU_TRY(plan_impl(oa, ob, p, stats_a, stats_b, plan, info, stream));
-  const imu_plan_info& last = info[batch - 1];
-  const int64_t a_bytes = last.a_offset + round_up(last.m_alloc * last.k_pad, 256);
-  const int64_t b_bytes = last.b_offset + round_up(last.n_alloc * last.k_pad, 256);
+  // The unpack kernels take their sizes and placement from the plan on the
+  // device, so they are queued right behind the plan; the host waits only for
+  // the plan headers (staged to pinned memory) while they run, then checks the
+  // workspace and sizes the GEMM launch.  If the plan failed or the workspace
+  // is too small the unpack kernels write nothing.
+  IMU_TRY(plan_launch(oa, ob, p, stats_a, stats_b, plan, stream));
+  const uint8_t* hdrs = nullptr;
+  IMU_TRY(stage_headers(plan, (size_t)batch * kPlanHeaderStride, stream, &hdrs));
+  int8_t* region = reinterpret_cast<int8_t*>(w + fixed);
+  const int64_t cap = (int64_t)ws_bytes - fixed;
+  IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap, stream));
+  IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap, stream));
+  IMU_HIP(hipEventSynchronize(g_stage.ev));
+  int64_t a_bytes = 0, b_bytes = 0;
+  IMU_TRY(finish_plan(oa, ob, hdrs, (int)batch, info, &a_bytes, &b_bytes));
   const int64_t needed = fixed + a_bytes + b_bytes;
   if (ws_needed) *ws_needed = (size_t)needed;
   if ((int64_t)ws_bytes < needed) return fail(IMU_ERR_WORKSPACE, "workspace below the unpacked operands' size");
-  int8_t* a_u = reinterpret_cast<int8_t*>(w + fixed);
-  int8_t* b_u = a_u + a_bytes;
-  IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, info, a_u, stream));
-  IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, info, b_u, stream));
+  int8_t* a_u = region;
+  int8_t* b_u = region + a_bytes;
   return gemm_impl(a_u, b_u, p, stats_a, stats_b, plan, info, batch, c, ob.C, oa.R * ob.C, out, stream);
 }
 

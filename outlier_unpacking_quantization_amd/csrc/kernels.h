@@ -43,6 +43,8 @@ struct UnpackArgs {
   const uint8_t* plan;
   PlanLayout pl;
   int8_t* out;                  // start of the unpacked buffer (all batch entries)
+  int after_a;                  // 1: B' entries follow all A' entries of the buffer
+  int64_t cap;                  // bytes available at out; entries that would not fit are skipped
 };
 hipError_t launch_unpack(int dtype, int bits, const UnpackArgs& a, int batch, hipStream_t s);
 

@@ -92,10 +92,19 @@ __device__ inline uint32_t digit_byte(uint32_t w, uint32_t sh1) {
   return ((d ^ sm) - sm) & 0xFFu;
 }
 
-__device__ inline int64_t entry_offset(const uint8_t* plan, int b, int operand) {
+// Byte offset of entry b's unpacked operand in the buffer (entries in batch
+// order; with after_a, B' entries follow all A' entries).  Returns -1 if any
+// entry's plan failed or holds a negative size, so nothing gets placed from
+// stale headers.
+__device__ inline int64_t entry_offset(const uint8_t* plan, int batch, int b, int operand, bool after_a) {
   int64_t off = 0;
-  for (int e = 0; e < b; ++e)
-    off += unpacked_entry_bytes(reinterpret_cast<const PlanHeader*>(plan + e * kPlanHeaderStride), operand);
+  for (int e = 0; e < batch; ++e) {
+    const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan + e * kPlanHeaderStride);
+    const int64_t ba = unpacked_entry_bytes(h, 0), bb = unpacked_entry_bytes(h, 1);
+    if (h->status != 0 || ba < 0 || bb < 0) return -1;
+    if (after_a) off += ba;
+    if (e < b) off += operand == 0 ? ba : bb;
+  }
   return off;
 }
 
@@ -126,7 +135,11 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
   const int32_t* lvl = reinterpret_cast<const int32_t*>(pe + (is_a ? P.lvl_a : P.lvl_b));
   const int32_t* kpre = reinterpret_cast<const int32_t*>(pe + P.kpre);
   const uint32_t* kmap = reinterpret_cast<const uint32_t*>(pe + P.kmap);
-  int8_t* out = a.out + entry_offset(a.plan, b, a.operand);
+  // entry placement and guards: nothing is written for an entry whose plan
+  // failed or which would not fit in the buffer (the host reports both)
+  const int64_t start = entry_offset(a.plan, (int)gridDim.z, b, a.operand, a.after_a != 0);
+  if (start < 0 || start + unpacked_entry_bytes(ph, a.operand) > a.cap) return;
+  int8_t* out = a.out + start;
   const int64_t kp = ph->k_pad;
   const int nseg = ph->n_seg;
   const int tid = threadIdx.x;
