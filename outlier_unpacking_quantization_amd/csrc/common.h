@@ -81,7 +81,7 @@ struct PlanHeader {
   int64_t pair[16][3];
   int64_t seg_off[kMaxSeg + 1];
   int32_t seg_len[kMaxSeg];
-  int64_t tstamp[8];  // planner phase timestamps (wall clock ticks), diagnostics only
+  int64_t reserved[8];
 };
 constexpr int64_t kPlanHeaderStride = 2048;
 static_assert(sizeof(PlanHeader) <= kPlanHeaderStride, "plan header");
@@ -91,6 +91,18 @@ static_assert(offsetof(PlanHeader, pair) == 96, "plan header layout");
 static_assert(offsetof(PlanHeader, seg_off) == 480, "plan header layout");
 static_assert(offsetof(PlanHeader, seg_len) == 1000, "plan header layout");
 
+// The planner splits the lines (rows of A, columns of B, then k) into chunks
+// of kPlanLines, one workgroup each; every workgroup keeps a record.
+constexpr int kPlanLines = 1024;
+constexpr int kPlanTasks = 64;  // >= max levels and >= max segments
+struct PlanWgRecord {
+  long long sum[24];       // candidate sizes: M'[4], N'[4], K'[4][4] of this chunk
+  int32_t cnt[kPlanTasks]; // per task (level or segment): entries of this chunk
+  int32_t off[kPlanTasks]; // per task: entries of earlier chunks of the same kind
+  int32_t mx[4];           // chunk maxima: depth (rows/cols) or dA, dB, dA + dB - 2 (k)
+};
+static_assert(sizeof(PlanWgRecord) % 16 == 0, "plan record");
+
 struct PlanLayout {
   int64_t M = 0, K = 0, N = 0, batch = 0;
   int64_t pad_m = 0, pad_n = 0;  // base/extra boundary and allocation granularity
@@ -98,6 +110,8 @@ struct PlanLayout {
   int64_t headers_bytes = 0, entry_stride = 0;
   int64_t da_r = 0, da_c = 0, db_r = 0, db_c = 0, lvl_a = 0, lvl_b = 0, kpre = 0, amap = 0, bmap = 0;
   int64_t kmap = 0, kmap_max = 0;
+  int64_t wg_a = 0, wg_b = 0, wg_k = 0;  // planner workgroups over A's rows, B's columns, k
+  int64_t cand = 0, rec = 0;             // packed candidate depths; workgroup records
   int64_t total = 0;
 };
 
@@ -167,6 +181,11 @@ inline PlanLayout plan_layout(int64_t M, int64_t K, int64_t N, int64_t batch, in
   L.bmap = take(4 * L.n_alloc_max);
   L.kmap_max = K * (int64_t)D * D + kKPad * L.segments;
   L.kmap = take(4 * L.kmap_max);
+  L.wg_a = ceil_div(M, kPlanLines);
+  L.wg_b = ceil_div(N, kPlanLines);
+  L.wg_k = ceil_div(K, kPlanLines);
+  L.cand = take(4 * (M + N + 2 * K));
+  L.rec = take((int64_t)sizeof(PlanWgRecord) * (L.wg_a + L.wg_b + L.wg_k));
   L.entry_stride = o;
   L.total = L.headers_bytes + batch * L.entry_stride;
   return L;

@@ -1,4 +1,4 @@
-// Unpacking planner (gfx950): one 1024-thread workgroup per batch entry.
+// Unpacking planner (gfx950): three short kernels over chunks of lines.
 //
 // Method: summary page "IM-Unpack: Training and Inference with Arbitrarily Low
 // Precision Integers", "Approach" (row/column unpacking chosen per matrix from
@@ -9,15 +9,23 @@
 // A-major order ROW < COL < CR < RC.  All work is integer; the plan is a pure
 // function of the per-line statistics, so it is deterministic.
 //
-// Phases: (1) the depth of every line under each of the 4 candidates, kept as
-// bytes in LDS, and the sums giving M'[4], N'[4] and K'[4][4]; choice of the
-// pair; (2) the chosen depth maps (global int32) and their histograms, which
-// give every level base and segment size up front; (3) one wave per scan task
-// (each level of A's rows, each level of B's columns, each exponent segment of
-// K'), each lane scanning a contiguous run, writes final positions: level-major
-// line maps, per-segment prefixes over k and the K' position table used by
-// the unpack kernels.  Problems whose candidate bytes exceed the LDS budget
-// take the same steps reading the statistics from global memory.
+// The lines (rows of A, columns of B, then k) are cut into chunks of
+// kPlanLines, one workgroup per chunk and batch entry:
+// (1) plan_sums: the depth of every line under each of the 4 candidates (packed
+//     bytes, kept for (2)) and the chunk's share of M'[4], N'[4], K'[4][4]; the
+//     last workgroup to finish adds the shares up and picks the pair.
+// (2) plan_counts: the chosen depth maps and, per chunk, the entries of every
+//     task (each level of A's rows or B's columns: lines deeper than the level;
+//     each exponent segment e of K': triples (k, v, v') with v + v' = e); the
+//     last workgroup turns them into level bases, padded segment offsets, the
+//     header sizes and each chunk's offset in every task.
+// (3) plan_write: each chunk scans its lines (a thread owns 4 consecutive
+//     lines, one block-wide scan per batch of tasks) and writes the level-major
+//     line maps, the per-segment prefixes over k and the K' position table used
+//     by the unpack kernels.
+// Records pass between the workgroups of one kernel as device-scope atomic
+// stores and loads (written through the XCD-local L2); the counter that elects
+// the last workgroup is the statistics header's, which is zero between passes.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,10 +33,39 @@ namespace imu {
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kCandBytes = 112 * 1024;  // LDS budget for candidate depth bytes
-constexpr int kMaxD = 32;               // >= max_digits(2) + 1
+constexpr int kPer = kPlanLines / kThreads;  // lines per thread
+constexpr int kMaxD = 32;                    // depths are clamped here (>= max_digits(2) + 1)
+constexpr int kTaskBatch = 8;                // scan tasks per block-wide scan
+static_assert(kPlanLines % kThreads == 0, "chunk split");
+static_assert(kMaxSeg <= kPlanTasks && kMaxD <= kPlanTasks, "task slots");
+
+__device__ inline void st_dev(long long* p, long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline long long ld_dev(const long long* p) {
+  return __hip_atomic_load(const_cast<long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline int32_t ld_dev(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Elects the workgroup that finishes last.  Every thread's earlier stores have
+// completed before the count is taken; the elected workgroup resets the
+// counter for the next kernel (stream ordered).
+__device__ inline bool last_to_arrive(uint32_t* counter, uint32_t total, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) *s_flag = atomicAdd(counter, 1u) == total - 1;
+  __syncthreads();
+  const bool last = *s_flag != 0;
+  if (last && threadIdx.x == 0) *counter = 0;
+  return last;
+}
 
 __device__ inline long long wave_sum_i64(long long v) {
 #pragma unroll
@@ -40,10 +77,7 @@ __device__ inline long long wave_sum_i64(long long v) {
   return v;
 }
 
-constexpr int kTaskBatch = 8;  // scan tasks handled per pass over the line runs
-
 // Block-wide exclusive scans of kTaskBatch counters per thread at once.
-// `tot` is LDS scratch of kWaves * kTaskBatch ints.
 __device__ inline void block_excl_scan_multi(const int* cnt, int* ex, int* tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl[kTaskBatch];
@@ -69,18 +103,6 @@ __device__ inline void block_excl_scan_multi(const int* cnt, int* ex, int* tot) 
   }
 }
 
-// add 1 to LDS counter `key` for every lane, one atomic per distinct key in the wave
-__device__ inline void wave_count(int* counters, int key, bool active) {
-  unsigned long long todo = __ballot(active);
-  while (todo) {
-    const int leader = __ffsll((long long)todo) - 1;
-    const int lk = __shfl(key, leader, 64);
-    const unsigned long long same = __ballot(active && key == lk) & todo;
-    if ((threadIdx.x & 63) == leader) atomicAdd(&counters[lk], __popcll(same));
-    todo &= ~same;
-  }
-}
-
 struct Src {
   const int32_t *row_oob, *col_oob, *row_max, *col_max, *cr_rowdig, *rc_coldig;
   long long T;
@@ -101,14 +123,17 @@ __device__ inline Src src_of(const uint8_t* st, const StatsLayout& L) {
   return s;
 }
 
-// Row depths of the 4 candidates (row, col, cr, rc) for row i, packed in bytes.
+// Row depths of the 4 candidates (row, col, cr, rc) for row i, packed in bytes:
+// ROW unpacks rows to their digit count, COL leaves rows whole, CR unpacks
+// rows to the digit count of their residual after the heavy columns, RC
+// unpacks only heavy rows (out-of-range count x C above gamma T).
 __device__ inline uint32_t row_depths(const Src& s, int64_t i, int gamma) {
   const int mx = min(max(1, s.row_max[i]), kMaxD);
   const int cr = min(max(1, s.cr_rowdig[i]), kMaxD);
   const int rc = (long long)s.row_oob[i] * s.R > gamma * s.T ? mx : 1;
   return (uint32_t)mx | 1u << 8 | (uint32_t)cr << 16 | (uint32_t)rc << 24;
 }
-// Column depths of the 4 candidates for column k, packed in bytes.
+// Column depths of the 4 candidates for column k, packed in bytes (mirror image).
 __device__ inline uint32_t col_depths(const Src& s, int64_t k, int gamma) {
   const int mx = min(max(1, s.col_max[k]), kMaxD);
   const int cr = (long long)s.col_oob[k] * s.C > gamma * s.T ? mx : 1;
@@ -116,45 +141,6 @@ __device__ inline uint32_t col_depths(const Src& s, int64_t k, int gamma) {
   return 1u | (uint32_t)mx << 8 | (uint32_t)cr << 16 | (uint32_t)rc << 24;
 }
 __device__ inline int pick(uint32_t packed, int c) { return (packed >> (8 * c)) & 0xFF; }
-
-constexpr int kRound = 4;  // lines per thread whose loads are issued together
-
-// Candidate depths of rows i0 + j*kThreads (j < kRound); all loads first.
-__device__ inline void rows_depths_round(const Src& s, int64_t i0, int64_t n, int gamma, uint32_t out[kRound]) {
-  int mx[kRound], cr[kRound], ob[kRound];
-#pragma unroll
-  for (int j = 0; j < kRound; ++j) {  // clamped indices: unconditional loads
-    const int64_t i = min64(i0 + (int64_t)j * kThreads, n - 1);
-    mx[j] = s.row_max[i];
-    cr[j] = s.cr_rowdig[i];
-    ob[j] = s.row_oob[i];
-  }
-#pragma unroll
-  for (int j = 0; j < kRound; ++j) {
-    const int m = min(max(1, mx[j]), kMaxD);
-    const int c = min(max(1, cr[j]), kMaxD);
-    const int h = (long long)ob[j] * s.R > gamma * s.T ? m : 1;
-    out[j] = (uint32_t)m | 1u << 8 | (uint32_t)c << 16 | (uint32_t)h << 24;
-  }
-}
-// Candidate depths of columns k0 + j*kThreads (j < kRound); all loads first.
-__device__ inline void cols_depths_round(const Src& s, int64_t k0, int64_t n, int gamma, uint32_t out[kRound]) {
-  int mx[kRound], rc[kRound], ob[kRound];
-#pragma unroll
-  for (int j = 0; j < kRound; ++j) {  // clamped indices: unconditional loads
-    const int64_t k = min64(k0 + (int64_t)j * kThreads, n - 1);
-    mx[j] = s.col_max[k];
-    rc[j] = s.rc_coldig[k];
-    ob[j] = s.col_oob[k];
-  }
-#pragma unroll
-  for (int j = 0; j < kRound; ++j) {
-    const int m = min(max(1, mx[j]), kMaxD);
-    const int h = (long long)ob[j] * s.C > gamma * s.T ? m : 1;
-    const int c = min(max(1, rc[j]), kMaxD);
-    out[j] = 1u | (uint32_t)m << 8 | (uint32_t)h << 16 | (uint32_t)c << 24;
-  }
-}
 
 __device__ inline bool allowed(int strat, int c) {
   return strat == IMU_MIX || (strat == IMU_ROW && c == 0) || (strat == IMU_COL && c == 1);
@@ -166,120 +152,144 @@ __device__ inline int seg_count(int dA, int dB, int e) {
   return max(0, hi - lo + 1);
 }
 
-// Chosen depth of one line: from the LDS candidate bytes, or recomputed.
-struct DepthView {
-  const uint32_t* lds;  // packed candidate bytes, or null
-  const int32_t* g;     // global chosen depth map (written in phase 2)
-  __device__ int operator()(int64_t i, int c) const { return lds ? pick(lds[i], c) : (int)g[i]; }
+// Chunk of workgroup w: kind 0 = rows of A, 1 = columns of B, 2 = k.
+struct Chunk {
+  int kind;
+  int64_t first, n;  // first line and number of lines of this kind
+  int64_t rank;      // chunk index within its kind
 };
+__device__ inline Chunk chunk_of(const PlanLayout& L, int64_t w) {
+  Chunk c;
+  if (w < L.wg_a) {
+    c.kind = 0;
+    c.rank = w;
+    c.n = L.M;
+  } else if (w < L.wg_a + L.wg_b) {
+    c.kind = 1;
+    c.rank = w - L.wg_a;
+    c.n = L.N;
+  } else {
+    c.kind = 2;
+    c.rank = w - L.wg_a - L.wg_b;
+    c.n = L.K;
+  }
+  c.first = c.rank * kPlanLines;
+  return c;
+}
 
-__global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
-  __shared__ uint32_t cand[kCandBytes / 4];
-  __shared__ long long red[kWaves][24];
-  __shared__ long long red_tot[24];
-  __shared__ long long gt_a[kMaxD + 1], gt_b[kMaxD + 1];  // lines with depth > u
-  __shared__ int smax[kWaves][5];
-  __shared__ long long seg_len_s[kMaxSeg];
-  __shared__ int choice[2];
-  __shared__ int hist_a[kMaxD + 1], hist_b[kMaxD + 1];
-  __shared__ int pair_hist[(kMaxD + 1) * (kMaxD + 1)];
-  __shared__ long long base_a[kMaxD + 1], base_b[kMaxD + 1];
-  __shared__ long long seg_off[kMaxSeg + 1];
-  __shared__ int scan_tot[kWaves * kTaskBatch];
-  const int b = blockIdx.x;
+struct Entry {  // one batch entry's plan buffers
+  PlanHeader* ph;
+  int32_t *da_r, *da_c, *db_r, *db_c, *lvl_a, *lvl_b, *amap, *bmap, *kpre;
+  uint32_t *kmap, *cand;
+  PlanWgRecord* rec;
+};
+__device__ inline Entry entry_of(const PlanArgs& a, int b) {
   const PlanLayout& L = a.pl;
+  uint8_t* e = a.plan + L.headers_bytes + b * L.entry_stride;
+  Entry x;
+  x.ph = reinterpret_cast<PlanHeader*>(a.plan + b * kPlanHeaderStride);
+  x.da_r = reinterpret_cast<int32_t*>(e + L.da_r);
+  x.da_c = reinterpret_cast<int32_t*>(e + L.da_c);
+  x.db_r = reinterpret_cast<int32_t*>(e + L.db_r);
+  x.db_c = reinterpret_cast<int32_t*>(e + L.db_c);
+  x.lvl_a = reinterpret_cast<int32_t*>(e + L.lvl_a);
+  x.lvl_b = reinterpret_cast<int32_t*>(e + L.lvl_b);
+  x.amap = reinterpret_cast<int32_t*>(e + L.amap);
+  x.bmap = reinterpret_cast<int32_t*>(e + L.bmap);
+  x.kpre = reinterpret_cast<int32_t*>(e + L.kpre);
+  x.kmap = reinterpret_cast<uint32_t*>(e + L.kmap);
+  x.cand = reinterpret_cast<uint32_t*>(e + L.cand);  // [M] A rows, [N] B cols, [K] A cols, [K] B rows
+  x.rec = reinterpret_cast<PlanWgRecord*>(e + L.rec);
+  return x;
+}
+
+__device__ inline uint32_t* arrive_counter(const PlanArgs& a, int b) {
+  return &reinterpret_cast<StatsHeader*>(const_cast<uint8_t*>(a.stats_a) + b * a.stats_stride_a)->arrive;
+}
+
+// --- (1) candidate depths and sizes; choice --------------------------------
+__global__ __launch_bounds__(kThreads) void plan_sums_kernel(PlanArgs a) {
+  __shared__ long long red[kWaves][24];
+  __shared__ long long tot[24];
+  __shared__ int s_flag;
+  const int b = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const PlanLayout& L = a.pl;
+  const Entry E = entry_of(a, b);
   const Src A = src_of(a.stats_a + b * a.stats_stride_a, a.sla);
   const Src B = src_of(a.stats_b + b * a.stats_stride_b, a.slb);
-  const int64_t M = L.M, K = L.K, N = L.N;
+  const Chunk c = chunk_of(L, blockIdx.x);
   const int gamma = a.gamma;
-  PlanHeader* ph = reinterpret_cast<PlanHeader*>(a.plan + b * kPlanHeaderStride);
-  uint8_t* e = a.plan + L.headers_bytes + b * L.entry_stride;
-  int32_t* da_r = reinterpret_cast<int32_t*>(e + L.da_r);
-  int32_t* da_c = reinterpret_cast<int32_t*>(e + L.da_c);
-  int32_t* db_r = reinterpret_cast<int32_t*>(e + L.db_r);
-  int32_t* db_c = reinterpret_cast<int32_t*>(e + L.db_c);
-  int32_t* lvl_a = reinterpret_cast<int32_t*>(e + L.lvl_a);
-  int32_t* lvl_b = reinterpret_cast<int32_t*>(e + L.lvl_b);
-  int32_t* amap = reinterpret_cast<int32_t*>(e + L.amap);
-  int32_t* bmap = reinterpret_cast<int32_t*>(e + L.bmap);
-  int32_t* kpre = reinterpret_cast<int32_t*>(e + L.kpre);
-  uint32_t* kmap = reinterpret_cast<uint32_t*>(e + L.kmap);
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const bool in_lds = 4 * (M + 2 * K + N) <= kCandBytes;
-  uint32_t* c_ar = cand;          // [M]  A's rows
-  uint32_t* c_ac = cand + M;      // [K]  A's columns
-  uint32_t* c_br = c_ac + K;      // [K]  B's rows
-  uint32_t* c_bc = c_br + K;      // [N]  B's columns
-  if (t == 0) ph->tstamp[0] = wall_clock64();
-
-  // --- 1. candidate depths and the sizes M'[4], N'[4], K'[4][4] ---------------
-  // Each round issues the loads of kRound lines per thread before using any.
   long long acc[24];
 #pragma unroll
   for (int j = 0; j < 24; ++j) acc[j] = 0;
-  for (int64_t i0 = t; i0 < M; i0 += kRound * kThreads) {
-    uint32_t d[kRound];
-    rows_depths_round(A, i0, M, gamma, d);
+  uint32_t dx[kPer], dy[kPer];
 #pragma unroll
-    for (int j = 0; j < kRound; ++j) {
-      const int64_t i = i0 + (int64_t)j * kThreads;
-      if (i >= M) continue;
-      if (in_lds) c_ar[i] = d[j];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] += pick(d[j], c);
+  for (int j = 0; j < kPer; ++j) {  // clamped indices: all loads issued before use
+    const int64_t i = min64(c.first + t + (int64_t)j * kThreads, c.n - 1);
+    if (c.kind == 0) dx[j] = row_depths(A, i, gamma);
+    else if (c.kind == 1) dx[j] = col_depths(B, i, gamma);
+    else {
+      dx[j] = col_depths(A, i, gamma);
+      dy[j] = row_depths(B, i, gamma);
     }
   }
-  for (int64_t n0 = t; n0 < N; n0 += kRound * kThreads) {
-    uint32_t d[kRound];
-    cols_depths_round(B, n0, N, gamma, d);
 #pragma unroll
-    for (int j = 0; j < kRound; ++j) {
-      const int64_t n = n0 + (int64_t)j * kThreads;
-      if (n >= N) continue;
-      if (in_lds) c_bc[n] = d[j];
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t i = c.first + t + (int64_t)j * kThreads;
+    if (i >= c.n) continue;
+    if (c.kind == 0) {
+      E.cand[i] = dx[j];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[4 + c] += pick(d[j], c);
-    }
-  }
-  for (int64_t k0 = t; k0 < K; k0 += kRound * kThreads) {
-    uint32_t x[kRound], y[kRound];
-    cols_depths_round(A, k0, K, gamma, x);
-    rows_depths_round(B, k0, K, gamma, y);
+      for (int q = 0; q < 4; ++q) acc[q] += pick(dx[j], q);
+    } else if (c.kind == 1) {
+      E.cand[L.M + i] = dx[j];
 #pragma unroll
-    for (int j = 0; j < kRound; ++j) {
-      const int64_t k = k0 + (int64_t)j * kThreads;
-      if (k >= K) continue;
-      if (in_lds) {
-        c_ac[k] = x[j];
-        c_br[k] = y[j];
-      }
+      for (int q = 0; q < 4; ++q) acc[4 + q] += pick(dx[j], q);
+    } else {
+      E.cand[L.M + L.N + i] = dx[j];
+      E.cand[L.M + L.N + L.K + i] = dy[j];
 #pragma unroll
       for (int ca = 0; ca < 4; ++ca)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[8 + ca * 4 + cb] += pick(x[j], ca) * pick(y[j], cb);
+        for (int cb = 0; cb < 4; ++cb) acc[8 + ca * 4 + cb] += pick(dx[j], ca) * pick(dy[j], cb);
     }
   }
-  if (t == 0) ph->tstamp[5] = wall_clock64();
 #pragma unroll
   for (int j = 0; j < 24; ++j) {
-    long long v = wave_sum_i64(acc[j]);
+    const long long v = wave_sum_i64(acc[j]);
     if (lane == 0) red[wave][j] = v;
   }
-  if (t == 0) ph->tstamp[6] = wall_clock64();
-  for (int i = t; i <= kMaxD; i += kThreads) {
-    hist_a[i] = 0;
-    hist_b[i] = 0;
+  __syncthreads();
+  PlanWgRecord* my = E.rec + blockIdx.x;
+  if (t < 24) {
+    long long v = 0;
+    for (int w = 0; w < kWaves; ++w) v += red[w][t];
+    st_dev(&my->sum[t], v);
   }
-  for (int i = t; i < (kMaxD + 1) * (kMaxD + 1); i += kThreads) pair_hist[i] = 0;
+  const uint32_t G = (uint32_t)(L.wg_a + L.wg_b + L.wg_k);
+  if (!last_to_arrive(arrive_counter(a, b), G, &s_flag)) return;
+
+  // the last workgroup: totals over all chunks, then the choice
+#pragma unroll
+  for (int j = 0; j < 24; ++j) acc[j] = 0;
+  for (uint32_t w = t; w < G; w += kThreads)
+#pragma unroll
+    for (int j = 0; j < 24; ++j) acc[j] += ld_dev(&E.rec[w].sum[j]);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 24; ++j) {
+    const long long v = wave_sum_i64(acc[j]);
+    if (lane == 0) red[wave][j] = v;
+  }
   __syncthreads();
   if (t < 24) {
     long long v = 0;
     for (int w = 0; w < kWaves; ++w) v += red[w][t];
-    red_tot[t] = v;
+    tot[t] = v;
   }
   __syncthreads();
   if (t == 0) {
-    const long long* tot = red_tot;
+    PlanHeader* ph = E.ph;
     int best_a = -1, best_b = -1;
     unsigned __int128 best = 0;
     for (int ca = 0; ca < 4; ++ca)
@@ -301,8 +311,6 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
           best_b = cb;
         }
       }
-    choice[0] = best_a;
-    choice[1] = best_b;
     ph->choice_a = best_a;
     ph->choice_b = best_b;
     ph->m_u = tot[best_a];
@@ -310,211 +318,258 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(PlanArgs a) {
     ph->n_u = tot[4 + best_b];
     ph->status = (int32_t)(reinterpret_cast<const StatsHeader*>(a.stats_a + b * a.stats_stride_a)->status |
                            reinterpret_cast<const StatsHeader*>(a.stats_b + b * a.stats_stride_b)->status);
-    ph->tstamp[1] = wall_clock64();
   }
-  __syncthreads();
-  const int ca = choice[0], cb = choice[1];
+}
 
-  // --- 2. chosen depth maps, their maxima and histograms -----------------------
-  int mxa = 1, mxb = 1, mxe = 0, mxx = 1, mxy = 1;
-  for (int64_t i0 = 0; i0 < M; i0 += kThreads) {
-    const int64_t i = i0 + t;
-    const bool ok = i < M;
-    const int d = ok ? pick(in_lds ? c_ar[i] : row_depths(A, i, gamma), ca) : 0;
-    if (ok) da_r[i] = d;
-    mxa = max(mxa, d);
-    wave_count(hist_a, d, ok);
-  }
-  for (int64_t n0 = 0; n0 < N; n0 += kThreads) {
-    const int64_t n = n0 + t;
-    const bool ok = n < N;
-    const int d = ok ? pick(in_lds ? c_bc[n] : col_depths(B, n, gamma), cb) : 0;
-    if (ok) db_c[n] = d;
-    mxb = max(mxb, d);
-    wave_count(hist_b, d, ok);
-  }
-  for (int64_t k0 = 0; k0 < K; k0 += kThreads) {
-    const int64_t k = k0 + t;
-    const bool ok = k < K;
-    int x = 1, y = 1;
-    if (ok) {
-      x = pick(in_lds ? c_ac[k] : col_depths(A, k, gamma), ca);
-      y = pick(in_lds ? c_br[k] : row_depths(B, k, gamma), cb);
-      da_c[k] = x;
-      db_r[k] = y;
+// --- (2) chosen depths, per-chunk task counts; bases, offsets, sizes --------
+__global__ __launch_bounds__(kThreads) void plan_counts_kernel(PlanArgs a) {
+  __shared__ int hist[(kMaxD + 1) * (kMaxD + 1)];  // depth histogram (rows/cols) or (dA, dB) pairs (k)
+  __shared__ int smax[kWaves][4];
+  __shared__ int s_flag;
+  __shared__ long long gt[2][kPlanTasks];  // lines deeper than u: A rows, B cols
+  __shared__ long long seg_len[kPlanTasks];
+  __shared__ int lev_s[2], nseg_s;
+  const int b = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const PlanLayout& L = a.pl;
+  const Entry E = entry_of(a, b);
+  const Chunk c = chunk_of(L, blockIdx.x);
+  const int ca = E.ph->choice_a, cb = E.ph->choice_b;
+  for (int i = t; i < (kMaxD + 1) * (kMaxD + 1); i += kThreads) hist[i] = 0;
+  __syncthreads();
+  uint32_t dx[kPer], dy[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t i = min64(c.first + t + (int64_t)j * kThreads, c.n - 1);
+    if (c.kind == 0) dx[j] = E.cand[i];
+    else if (c.kind == 1) dx[j] = E.cand[L.M + i];
+    else {
+      dx[j] = E.cand[L.M + L.N + i];
+      dy[j] = E.cand[L.M + L.N + L.K + i];
     }
-    mxe = max(mxe, x + y - 2);
-    mxx = max(mxx, x);
-    mxy = max(mxy, y);
-    wave_count(pair_hist, x * (kMaxD + 1) + y, ok);
   }
-  mxa = wave_max_i32(mxa);
-  mxb = wave_max_i32(mxb);
-  mxe = wave_max_i32(mxe);
-  mxx = wave_max_i32(mxx);
-  mxy = wave_max_i32(mxy);
+  int m0 = 1, m1 = 1, m2 = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t i = c.first + t + (int64_t)j * kThreads;
+    if (i >= c.n) continue;
+    if (c.kind < 2) {
+      const int d = pick(dx[j], c.kind == 0 ? ca : cb);
+      (c.kind == 0 ? E.da_r : E.db_c)[i] = d;
+      m0 = max(m0, d);
+      atomicAdd(&hist[d], 1);
+    } else {
+      const int x = pick(dx[j], ca), y = pick(dy[j], cb);
+      E.da_c[i] = x;
+      E.db_r[i] = y;
+      m0 = max(m0, x);
+      m1 = max(m1, y);
+      m2 = max(m2, x + y - 2);
+      atomicAdd(&hist[x * (kMaxD + 1) + y], 1);
+    }
+  }
+  m0 = wave_max_i32(m0);
+  m1 = wave_max_i32(m1);
+  m2 = wave_max_i32(m2);
   if (lane == 0) {
-    smax[wave][0] = mxa;
-    smax[wave][1] = mxb;
-    smax[wave][2] = mxe;
-    smax[wave][3] = mxx;
-    smax[wave][4] = mxy;
-  }
-  __syncthreads();  // (workgroup scope) global depth maps visible to the whole workgroup below
-  int lev_a = 1, lev_b = 1, emax = 0, xmax = 1, ymax = 1;
-  for (int w = 0; w < kWaves; ++w) {
-    lev_a = max(lev_a, smax[w][0]);
-    lev_b = max(lev_b, smax[w][1]);
-    emax = max(emax, smax[w][2]);
-    xmax = max(xmax, smax[w][3]);
-    ymax = max(ymax, smax[w][4]);
-  }
-  lev_a = min<int>(lev_a, (int)L.levels);
-  lev_b = min<int>(lev_b, (int)L.levels);
-  emax = min<int>(emax, (int)L.segments - 1);
-  const int nseg = emax + 1;
-  const int64_t m_base = round_up(M, L.pad_m), n_base = round_up(N, L.pad_n);
-  if (t == 0) ph->tstamp[2] = wall_clock64();
-
-  // segment sizes from the histogram of (A's, B's) inner depth pairs
-  if (t < nseg) {
-    long long len = 0;
-    for (int x = 1; x <= xmax; ++x)
-      for (int y = 1; y <= ymax; ++y) len += (long long)pair_hist[x * (kMaxD + 1) + y] * seg_count(x, y, t);
-    seg_len_s[t] = len;
-  }
-  if (t <= kMaxD) {  // lines with depth > t
-    long long ga = 0, gb = 0;
-    for (int d = t + 1; d <= kMaxD; ++d) {
-      ga += hist_a[d];
-      gb += hist_b[d];
-    }
-    gt_a[t] = ga;
-    gt_b[t] = gb;
+    smax[wave][0] = m0;
+    smax[wave][1] = m1;
+    smax[wave][2] = m2;
   }
   __syncthreads();
-  // level bases and padded segment offsets
+  int x_hi = 1, y_hi = 1;
+  for (int w = 0; w < kWaves; ++w) {
+    x_hi = max(x_hi, smax[w][0]);
+    y_hi = max(y_hi, smax[w][1]);
+  }
+  PlanWgRecord* my = E.rec + blockIdx.x;
+  if (t < kPlanTasks) {  // task counts of this chunk
+    int v = 0;
+    if (c.kind < 2) {
+      for (int d = t + 1; d <= x_hi; ++d) v += hist[d];  // lines with depth > t
+    } else {
+      for (int x = 1; x <= x_hi; ++x)
+        for (int y = 1; y <= y_hi; ++y) v += hist[x * (kMaxD + 1) + y] * seg_count(x, y, t);
+    }
+    st_dev(&my->cnt[t], v);
+  }
+  if (t < 3) {
+    int v = t == 2 ? 0 : 1;
+    for (int w = 0; w < kWaves; ++w) v = max(v, smax[w][t]);
+    st_dev(&my->mx[t], v);
+  }
+  const uint32_t G = (uint32_t)(L.wg_a + L.wg_b + L.wg_k);
+  if (!last_to_arrive(arrive_counter(a, b), G, &s_flag)) return;
+
+  // the last workgroup: per task, chunk offsets and totals (one thread per
+  // task and kind walks that kind's chunks in order)
+  const int64_t wk0[3] = {0, L.wg_a, L.wg_a + L.wg_b};
+  const int64_t wkn[3] = {L.wg_a, L.wg_b, L.wg_k};
+  for (int job = t; job < 3 * kPlanTasks; job += kThreads) {
+    const int kind = job / kPlanTasks, task = job % kPlanTasks;
+    long long run = 0;
+    for (int64_t r = 0; r < wkn[kind]; ++r) {
+      PlanWgRecord* rc = E.rec + wk0[kind] + r;
+      rc->off[task] = (int32_t)run;  // read by the next kernel
+      run += ld_dev(&rc->cnt[task]);
+    }
+    if (kind < 2) gt[kind][task] = run;
+    else seg_len[task] = run;
+  }
+  if (t < 3) {
+    int v = t == 2 ? 0 : 1;
+    for (int64_t w = 0; w < (int64_t)G; ++w) {
+      const Chunk cw = chunk_of(L, w);
+      const int mxv = t == 0 ? ld_dev(&E.rec[w].mx[0]) : ld_dev(&E.rec[w].mx[t == 1 ? 0 : 2]);
+      if ((t == 0 && cw.kind == 0) || (t == 1 && cw.kind == 1) || (t == 2 && cw.kind == 2)) v = max(v, mxv);
+    }
+    if (t < 2) lev_s[t] = min(v, (int)L.levels);
+    else nseg_s = min(v, (int)L.segments - 1) + 1;
+  }
+  __syncthreads();
   if (t == 0) {
-    long long pos = 0;
-    for (int u = 0; u < lev_a; ++u) {
-      base_a[u] = pos;
-      pos = (u == 0) ? m_base : pos + gt_a[u];
-    }
-    base_a[lev_a] = pos;
-    pos = 0;
-    for (int u = 0; u < lev_b; ++u) {
-      base_b[u] = pos;
-      pos = (u == 0) ? n_base : pos + gt_b[u];
-    }
-    base_b[lev_b] = pos;
+    PlanHeader* ph = E.ph;
+    const int lev_a = lev_s[0], lev_b = lev_s[1], nseg = nseg_s;
+    const int64_t m_base = round_up(L.M, L.pad_m), n_base = round_up(L.N, L.pad_n);
+    long long end_a = m_base, end_b = n_base;
+    for (int u = 1; u < lev_a; ++u) end_a += gt[0][u];
+    for (int u = 1; u < lev_b; ++u) end_b += gt[1][u];
     long long off = 0;
     for (int s = 0; s < nseg; ++s) {
-      const long long len = seg_len_s[s];
-      seg_off[s] = off;
       ph->seg_off[s] = off;
-      ph->seg_len[s] = (int32_t)len;
-      off += round_up(len, kKPad);
+      ph->seg_len[s] = (int32_t)seg_len[s];
+      off += round_up(seg_len[s], kKPad);
     }
-    seg_off[nseg] = off;
     ph->seg_off[nseg] = off;
     ph->n_seg = nseg;
     ph->k_pad = off;
     ph->m_base = m_base;
     ph->n_base = n_base;
-    ph->m_alloc = round_up(base_a[lev_a], L.pad_m);
-    ph->n_alloc = round_up(base_b[lev_b], L.pad_n);
+    ph->m_alloc = round_up(end_a, L.pad_m);
+    ph->n_alloc = round_up(end_b, L.pad_n);
     ph->lev_a = lev_a;
     ph->lev_b = lev_b;
-    ph->emax = emax;
-    ph->tstamp[3] = wall_clock64();
+    ph->emax = nseg - 1;
+  }
+}
+
+// --- (3) positions ----------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void plan_write_kernel(PlanArgs a) {
+  __shared__ int scan_tot[kWaves * kTaskBatch];
+  __shared__ long long base_s[kPlanTasks];  // level bases (rows/cols) or segment offsets (k)
+  __shared__ int off_s[kPlanTasks];
+  const int b = blockIdx.y, t = threadIdx.x;
+  const PlanLayout& L = a.pl;
+  const Entry E = entry_of(a, b);
+  const PlanHeader* ph = E.ph;
+  const Chunk c = chunk_of(L, blockIdx.x);
+  const int ntasks = c.kind == 0 ? ph->lev_a : c.kind == 1 ? ph->lev_b : ph->n_seg;
+  const PlanWgRecord* my = E.rec + blockIdx.x;
+  if (t < kPlanTasks) off_s[t] = my->off[t];
+  if (t == 0) {
+    if (c.kind < 2) {
+      // level u > 0 starts after the padded base and the levels 1..u-1, whose
+      // sizes are the totals of the previous chunks' last offsets + counts:
+      // recomputed here from the records of this kind's last chunk
+      const int64_t last = c.kind == 0 ? L.wg_a - 1 : L.wg_a + L.wg_b - 1;
+      const PlanWgRecord* lr = E.rec + last;
+      long long p = c.kind == 0 ? ph->m_base : ph->n_base;
+      base_s[0] = 0;
+      for (int u = 1; u < ntasks; ++u) {
+        base_s[u] = p;
+        p += (long long)lr->off[u] + lr->cnt[u];
+      }
+    } else {
+      for (int s = 0; s < ntasks; ++s) base_s[s] = ph->seg_off[s];
+    }
   }
   __syncthreads();
-  const DepthView VAR{in_lds ? c_ar : nullptr, da_r}, VAC{in_lds ? c_ac : nullptr, da_c};
-  const DepthView VBR{in_lds ? c_br : nullptr, db_r}, VBC{in_lds ? c_bc : nullptr, db_c};
-  const int64_t m_alloc = round_up(base_a[lev_a], L.pad_m), n_alloc = round_up(base_b[lev_b], L.pad_n);
-
-  // --- 3a. padding entries (disjoint from everything the scans write) ---------
-  for (int64_t r = M + t; r < m_base; r += kThreads) amap[r] = -1;
-  for (int64_t r = base_a[lev_a] + t; r < m_alloc; r += kThreads) amap[r] = -1;
-  for (int64_t r = N + t; r < n_base; r += kThreads) bmap[r] = -1;
-  for (int64_t r = base_b[lev_b] + t; r < n_alloc; r += kThreads) bmap[r] = -1;
-  for (int s = 0; s < nseg; ++s) {
-    const int64_t p0 = seg_off[s] + seg_len_s[s], p1 = seg_off[s + 1];
-    for (int64_t p = p0 + t; p < p1; p += kThreads) kmap[p] = kKmapPad;
+  const int64_t i0 = min64(c.first + (int64_t)t * kPer, c.n), i1 = min64(i0 + kPer, c.n);
+  int dA[kPer], dB[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t i = min64(i0 + j, c.n - 1);
+    if (c.kind == 0) dA[j] = E.da_r[i];
+    else if (c.kind == 1) dA[j] = E.db_c[i];
+    else {
+      dA[j] = E.da_c[i];
+      dB[j] = E.db_r[i];
+    }
   }
-  if (t == 0) ph->tstamp[7] = wall_clock64();
-
-  // --- 3b. scans: each thread owns a contiguous run of lines; a batch of tasks
-  // (levels of A's rows, levels of B's columns, or exponent segments of K') is
-  // counted over the run, one block-wide scan gives every run its offsets, and
-  // a second pass over the run writes the positions (adjacent threads write
-  // adjacent runs, so the stores stay close to coalesced).
-  for (int group = 0; group < 3; ++group) {
-    const int64_t n = group == 0 ? M : (group == 1 ? N : K);
-    const int ntasks = group == 0 ? lev_a : (group == 1 ? lev_b : nseg);
-    const int64_t len = ceil_div(n, kThreads);
-    const int64_t i0 = min64((int64_t)t * len, n), i1 = min64(i0 + len, n);
-    for (int tb = 0; tb < ntasks; tb += kTaskBatch) {
-      int cnt[kTaskBatch];
+  const int nl = (int)(i1 - i0);
+  for (int tb = 0; tb < ntasks; tb += kTaskBatch) {
+    int cnt[kTaskBatch], ex[kTaskBatch];
 #pragma unroll
-      for (int j = 0; j < kTaskBatch; ++j) cnt[j] = 0;
-      for (int64_t i = i0; i < i1; ++i) {
-        if (group < 2) {
-          const int d = group == 0 ? VAR(i, ca) : VBC(i, cb);
+    for (int j = 0; j < kTaskBatch; ++j) {
+      int v = 0;
 #pragma unroll
-          for (int j = 0; j < kTaskBatch; ++j) cnt[j] += d > tb + j;
+      for (int l = 0; l < kPer; ++l)
+        if (l < nl) v += c.kind < 2 ? (dA[l] > tb + j) : seg_count(dA[l], dB[l], tb + j);
+      cnt[j] = v;
+    }
+    block_excl_scan_multi(cnt, ex, scan_tot);
+#pragma unroll
+    for (int j = 0; j < kTaskBatch; ++j) {
+      const int task = tb + j;
+      if (task >= ntasks) continue;
+      long long pos = ex[j] + off_s[task];  // position inside the task
+#pragma unroll
+      for (int l = 0; l < kPer; ++l) {
+        if (l >= nl) continue;
+        const int64_t i = i0 + l;
+        if (c.kind < 2) {
+          const bool live = dA[l] > task;
+          const long long p = base_s[task] + pos;
+          (c.kind == 0 ? E.lvl_a : E.lvl_b)[(int64_t)task * c.n + i] = live ? (int32_t)p : -1;
+          if (live) (c.kind == 0 ? E.amap : E.bmap)[p] = (int32_t)(i | ((int64_t)task << 24));
+          pos += live;
         } else {
-          const int dA = VAC(i, ca), dB = VBR(i, cb);
-#pragma unroll
-          for (int j = 0; j < kTaskBatch; ++j) cnt[j] += seg_count(dA, dB, tb + j);
-        }
-      }
-      int ex[kTaskBatch];
-      block_excl_scan_multi(cnt, ex, scan_tot);
-      for (int64_t i = i0; i < i1; ++i) {
-        if (group < 2) {
-          const int d = group == 0 ? VAR(i, ca) : VBC(i, cb);
-          int32_t* lvl = group == 0 ? lvl_a : lvl_b;
-          int32_t* map = group == 0 ? amap : bmap;
-          const long long* base = group == 0 ? base_a : base_b;
-#pragma unroll
-          for (int j = 0; j < kTaskBatch; ++j) {
-            const int u = tb + j;
-            if (u < ntasks) {
-              const bool live = d > u;
-              const long long p = base[u] + ex[j];
-              lvl[(int64_t)u * n + i] = live ? (int32_t)p : -1;
-              if (live) map[p] = (int32_t)(i | ((int64_t)u << 24));
-              ex[j] += live;
-            }
-          }
-        } else {
-          const int dA = VAC(i, ca), dB = VBR(i, cb);
-#pragma unroll
-          for (int j = 0; j < kTaskBatch; ++j) {
-            const int s = tb + j;
-            if (s < ntasks) {
-              const int c = seg_count(dA, dB, s);
-              kpre[(int64_t)s * (K + 1) + i] = ex[j];
-              uint32_t* km = kmap + seg_off[s] + ex[j];
-              const int lo = max(0, s - (dB - 1));
-              for (int v = 0; v < c; ++v) km[v] = kmap_pack(i, lo + v, s - lo - v, dA, dB);
-              ex[j] += c;
-            }
-          }
+          const int cnt_l = seg_count(dA[l], dB[l], task);
+          E.kpre[(int64_t)task * (L.K + 1) + i] = (int32_t)pos;
+          uint32_t* km = E.kmap + base_s[task] + pos;
+          const int lo = max(0, task - (dB[l] - 1));
+          for (int v = 0; v < cnt_l; ++v) km[v] = kmap_pack(i, lo + v, task - lo - v, dA[l], dB[l]);
+          pos += cnt_l;
         }
       }
     }
   }
-  if (t < nseg) kpre[(int64_t)t * (K + 1) + K] = (int32_t)seg_len_s[t];
-  __syncthreads();
-  if (t == 0) ph->tstamp[4] = wall_clock64();
+  // padding (workgroup 0): rows between M and the padded base, after the last
+  // level up to the allocation, zero entries at the end of every segment, and
+  // the per-segment totals at kpre[s][K]
+  if (blockIdx.x == 0) {
+    __shared__ long long end_s[2];
+    if (t < 2) {
+      const int64_t last = t == 0 ? L.wg_a - 1 : L.wg_a + L.wg_b - 1;
+      const PlanWgRecord* lr = E.rec + last;
+      const int lev = t == 0 ? ph->lev_a : ph->lev_b;
+      long long p = t == 0 ? ph->m_base : ph->n_base;
+      for (int u = 1; u < lev; ++u) p += (long long)lr->off[u] + lr->cnt[u];
+      end_s[t] = p;
+    }
+    __syncthreads();
+    for (int64_t r = L.M + t; r < ph->m_base; r += kThreads) E.amap[r] = -1;
+    for (int64_t r = end_s[0] + t; r < ph->m_alloc; r += kThreads) E.amap[r] = -1;
+    for (int64_t r = L.N + t; r < ph->n_base; r += kThreads) E.bmap[r] = -1;
+    for (int64_t r = end_s[1] + t; r < ph->n_alloc; r += kThreads) E.bmap[r] = -1;
+    const int nseg = ph->n_seg;
+    for (int s = 0; s < nseg; ++s) {
+      const int64_t p0 = ph->seg_off[s] + ph->seg_len[s], p1 = ph->seg_off[s + 1];
+      for (int64_t p = p0 + t; p < p1; p += kThreads) E.kmap[p] = kKmapPad;
+    }
+    if (t < nseg) E.kpre[(int64_t)t * (L.K + 1) + L.K] = ph->seg_len[t];
+  }
 }
 
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)a.pl.batch), dim3(kThreads), 0, s, a);
+  const PlanLayout& L = a.pl;
+  const int64_t G = L.wg_a + L.wg_b + L.wg_k;
+  if (G <= 0 || G > 0x7FFFFFFF || L.batch < 1 || L.batch > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)G, (unsigned)L.batch);
+  hipLaunchKernelGGL(plan_sums_kernel, grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(plan_counts_kernel, grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(plan_write_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
