@@ -40,6 +40,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTargetWgs = 2048;  // workgroups aimed for per launch (8 per CU)
+constexpr int kInFlight = 4;      // table loads a thread issues before using them
 
 template <bool OC>
 struct Shape {
@@ -118,6 +119,8 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
   __shared__ int64_t rowoff[L];  // row part of the byte offset of row (line, level u), -1 if absent
   __shared__ int s_dout[L];
   __shared__ int64_t s_off[kMaxSeg + 1];
+  __shared__ int64_t s_p0[kMaxSeg + 1], s_p1[kMaxSeg + 1];
+  __shared__ int s_ng[kMaxSeg + 1], s_pre[kMaxSeg + 1];
 
   const int b = blockIdx.z;
   const int64_t o0 = (int64_t)blockIdx.x * L;
@@ -201,21 +204,60 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
       }
     }
     __syncthreads();
+    // this window's K' positions: per segment the range [P0, P1), as groups of
+    // 4 positions flattened over the segments (s_pre: first flat group of each
+    // segment), so that all segments' groups are spread over all threads
     const bool last_win = kw1 == K;
+    if (tid <= nseg) {
+      int64_t P0 = 0, P1 = 0;
+      if (tid < nseg) {
+        const int32_t* kps = kpre + (int64_t)tid * (K + 1);
+        P0 = s_off[tid] + kps[kw0];
+        P1 = last_win ? s_off[tid + 1] : s_off[tid] + kps[kw1];
+      }
+      s_p0[tid] = P0;
+      s_p1[tid] = P1;
+      s_ng[tid] = P1 > P0 ? (int)(((P1 + 3) >> 2) - (P0 >> 2)) : 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int q = 0; q < nseg; ++q) {
+        s_pre[q] = run;
+        run += s_ng[q];
+      }
+      s_pre[nseg] = run;
+    }
     for (int u = 0; u < umax; ++u) {
       if (tid < L) {
         const int64_t row = s_dout[tid] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + o0 + tid] : (int64_t)-1;
         rowoff[tid] = row < 0 ? (int64_t)-1 : is_a ? frag_row_offset(row, kp) : row * kp;
       }
       __syncthreads();
-      for (int s = 0; s < nseg; ++s) {
-        const int32_t* kps = kpre + (int64_t)s * (K + 1);
-        const int64_t P0 = s_off[s] + kps[kw0];
-        const int64_t P1 = last_win ? s_off[s + 1] : s_off[s] + kps[kw1];
-        const int64_t g_end = (P1 + 3) >> 2;
-        for (int64_t g = (P0 >> 2) + tid; g < g_end; g += kThreads) {
-          const uint4 e4 = *reinterpret_cast<const uint4*>(kmap + 4 * g);
-          const uint32_t ent[4] = {e4.x, e4.y, e4.z, e4.w};
+      const int gtot = s_pre[nseg];
+      for (int gb = 0; gb < gtot; gb += kThreads * kInFlight) {
+        // table entries of up to kInFlight groups per thread, loads first
+        uint4 e4[kInFlight];
+        int64_t gq[kInFlight];
+        int sq[kInFlight];
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) {
+          const int gi = min(gb + tid + j * kThreads, gtot - 1);
+          int lo = 0, hi = nseg - 1;  // segment of flat group gi: last s with s_pre[s] <= gi
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pre[mid] <= gi) lo = mid;
+            else hi = mid - 1;
+          }
+          sq[j] = lo;
+          gq[j] = (s_p0[lo] >> 2) + (gi - s_pre[lo]);
+          e4[j] = *reinterpret_cast<const uint4*>(kmap + 4 * gq[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) {
+          if (gb + tid + j * kThreads >= gtot) continue;
+          const int64_t g = gq[j], P0 = s_p0[sq[j]], P1 = s_p1[sq[j]];
+          const uint32_t ent[4] = {e4[j].x, e4[j].y, e4[j].z, e4[j].w};
           uint32_t adr[4], sh[4];
           bool inr[4];
 #pragma unroll
@@ -252,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
           }
         }
       }
-      __syncthreads();  // before rowoff is rewritten
+      __syncthreads();  // before rowoff and the segment ranges are rewritten
     }
   }
 }
