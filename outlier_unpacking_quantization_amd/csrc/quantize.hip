@@ -229,8 +229,8 @@ __device__ void select_from_hist(uint8_t* st, int64_t hist_off, int64_t nelem, i
 }
 
 // --- percentile histogram + fused selection ---------------------------------
-template <int DT, int NB>
-__global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int pass, int final_pass) {
+template <int DT, int NB, int PASS>
+__global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass) {
   using T = typename Elem<DT>::T;
   __shared__ uint32_t h[NB];
   __shared__ uint32_t smax;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int pass, int f
   }
   __syncthreads();
 
-  const uint32_t prefix = pass == 0 ? 0u : hd->sel_prefix;
+  const uint32_t prefix = PASS == 0 ? 0u : hd->sel_prefix;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   // work units: (stored row, 512-column tile); this workgroup takes a contiguous share
   const uint32_t ctiles = (uint32_t)ceil_div(a.scols, kColsPerTile);
@@ -261,36 +261,45 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int pass, int f
   const int64_t u0 = units * jp.local / jp.count, u1 = units * (jp.local + 1) / jp.count;
   uint32_t mx = 0;
   int bad = 0;
+  auto count = [&](uint32_t bits) {
+    const uint32_t k = bits & 0x7FFFFFFFu;
+    if constexpr (PASS == 0) {
+      mx = max(mx, k);
+      bad |= (k >= 0x7F800000u);
+      atomicAdd(&h[(k >> 16) & (NB - 1)], 1u);
+    } else if constexpr (PASS == 1) {
+      if ((k >> 16) == prefix) atomicAdd(&h[(k >> 8) & 0xFFu], 1u);
+    } else {
+      if ((k >> 8) == prefix) atomicAdd(&h[k & 0xFFu], 1u);
+    }
+  };
   for (int64_t ub = u0 + (int64_t)wave * kRowsInFlight; ub < u1; ub += (int64_t)nwave * kRowsInFlight) {
     uint32_t w[kRowsInFlight][8];
     int n[kRowsInFlight];
+    bool whole[kRowsInFlight];  // wave-uniform: the whole 512-column tile lies inside the row
 #pragma unroll
     for (int r = 0; r < kRowsInFlight; ++r) {
       const uint32_t u = (uint32_t)min64(ub + r, u1 - 1);  // clamped: loads stay unconditional
       const uint32_t sr = u / ctiles, ct = u - sr * ctiles;
       const int got = load8_bits<DT>(xb + (int64_t)sr * a.ld, (int64_t)ct * kColsPerTile + lane * 8, a.scols,
                                      a.vec_ok, w[r]);
-      n[r] = ub + r < u1 ? got : 0;
+      const bool live = ub + r < u1;
+      n[r] = live ? got : 0;
+      whole[r] = live && (int64_t)(ct + 1) * kColsPerTile <= a.scols;
     }
 #pragma unroll
-    for (int r = 0; r < kRowsInFlight; ++r)
+    for (int r = 0; r < kRowsInFlight; ++r) {
+      if (whole[r]) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < n[r]) {
-          const uint32_t k = w[r][j] & 0x7FFFFFFFu;
-          if (pass == 0) {
-            mx = max(mx, k);
-            bad |= (k >= 0x7F800000u);
-            atomicAdd(&h[(k >> 16) & (NB - 1)], 1u);
-          } else if (pass == 1) {
-            if ((k >> 16) == prefix) atomicAdd(&h[(k >> 8) & 0xFFu], 1u);
-          } else {
-            if ((k >> 8) == prefix) atomicAdd(&h[k & 0xFFu], 1u);
-          }
-        }
+        for (int j = 0; j < 8; ++j) count(w[r][j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < n[r]) count(w[r][j]);
       }
+    }
   }
-  if (pass == 0) {
+  if (PASS == 0) {
     mx = wave_max_u32(mx);
     bad = wave_max_i32(bad);
     if (lane == 0) {
@@ -303,24 +312,24 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int pass, int f
     const uint32_t c = h[i];
     if (c) atomicAdd(&gh[i], c);
   }
-  if (pass == 0 && threadIdx.x == 0) {
+  if (PASS == 0 && threadIdx.x == 0) {
     atomicMax(&hd->maxkey, smax);
     if (sbad) atomicOr(&hd->status, kStatusNonfinite);
   }
   // The last workgroup of this entry selects.  Every flush above is a
-  // device-scope atomic; a workgroup-scope release only has to wait until they
-  // are performed before the arrival counter moves (a device-scope release
-  // would also write back this XCD's whole L2, which costs tens of us across
-  // the grid).  The last workgroup then acquires at device scope, which drops
-  // stale cached lines before it reads the histogram.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  // device-scope atomic; each thread waits until its own have completed before
+  // the arrival counter moves (a device-scope release fence would also write
+  // back this XCD's whole L2, which costs tens of us across the grid).  The
+  // last workgroup then acquires at device scope, which drops stale cached
+  // lines before it reads the histogram.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) slast = atomicAdd(&hd->arrive, 1u) == (uint32_t)(jp.count - 1);
   __syncthreads();
   if (!slast) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x == 0) hd->arrive = 0;  // ready for the next pass (stream ordered)
-  select_from_hist(st, a.hist, a.srows * a.scols, pass, final_pass, a.beta, a.p_num, a.p_den, part, found, h);
+  select_from_hist(st, a.hist, a.srows * a.scols, PASS, final_pass, a.beta, a.p_num, a.p_den, part, found, h);
 }
 
 // --- fused RTN + outlier statistics -------------------------------------------
@@ -570,11 +579,13 @@ static int plan_hist(QuantJobs& J) {
 hipError_t launch_hist(int dtype, QuantJobs J, int pass, int final_pass, hipStream_t s) {
   const int grid = plan_hist(J);
   if (dtype == IMU_BF16) {
-    hipLaunchKernelGGL((hist_kernel<IMU_BF16, kHistBins>), dim3(grid), dim3(1024), 0, s, J, pass, final_pass);
+    hipLaunchKernelGGL((hist_kernel<IMU_BF16, kHistBins, 0>), dim3(grid), dim3(1024), 0, s, J, final_pass);
   } else if (pass == 0) {
-    hipLaunchKernelGGL((hist_kernel<IMU_F32, kHistBins>), dim3(grid), dim3(1024), 0, s, J, pass, final_pass);
+    hipLaunchKernelGGL((hist_kernel<IMU_F32, kHistBins, 0>), dim3(grid), dim3(1024), 0, s, J, final_pass);
+  } else if (pass == 1) {
+    hipLaunchKernelGGL((hist_kernel<IMU_F32, 256, 1>), dim3(grid), dim3(1024), 0, s, J, final_pass);
   } else {
-    hipLaunchKernelGGL((hist_kernel<IMU_F32, 256>), dim3(grid), dim3(1024), 0, s, J, pass, final_pass);
+    hipLaunchKernelGGL((hist_kernel<IMU_F32, 256, 2>), dim3(grid), dim3(1024), 0, s, J, final_pass);
   }
   return hipGetLastError();
 }
