@@ -33,6 +33,8 @@ namespace {
 
 constexpr int kColsPerTile = 512;  // 64 lanes x 8 elements
 constexpr int kRowsInFlight = 4;   // row loads issued per wave before use
+constexpr int kCountThreads = 512;    // threads of the counting kernel (tiles are 512 columns wide)
+constexpr int kResidualThreads = 256; // threads of the residual kernel
 
 // Raw 32-bit patterns (fp32 bits; bf16 widened) of the 8 elements starting at
 // column c0 of a stored row, and how many of them lie inside the row.  The
@@ -334,8 +336,8 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
 
 // --- fused RTN + outlier statistics -------------------------------------------
 // Tile: 512 stored columns x rows_per_wg stored rows.
-template <int DT, int BITS>
-__global__ __launch_bounds__(256) void round_count_kernel(QuantJobs J, int32_t* q0, int32_t* q1) {
+template <int DT, int BITS, bool QOUT>
+__global__ __launch_bounds__(kCountThreads) void round_count_kernel(QuantJobs J, int32_t* q0, int32_t* q1) {
   using T = typename Elem<DT>::T;
   constexpr float kThr = (float)(1 << (BITS - 1)) - 0.5f;  // |y| >= kThr <=> rne(y) out of range
   __shared__ int lcnt[kColsPerTile];
@@ -381,8 +383,12 @@ __global__ __launch_bounds__(256) void round_count_kernel(QuantJobs J, int32_t* 
   int tot = 0;
   float amax = 0.f;
   const int64_t R = a.srows, C = a.scols;
-  int32_t* qout = jp.op == 0 ? q0 : q1;
-  int32_t* qb = qout ? qout + b * R * C : nullptr;
+  int32_t* qb = nullptr;  // codes of this operand, if they were asked for
+  if constexpr (QOUT) {
+    int32_t* qo = jp.op == 0 ? q0 : q1;
+    if (qo) qb = qo + b * R * C;
+  }
+  const bool tile_whole = cbase + kColsPerTile <= a.scols;  // no element of this tile is past the row
   for (int64_t sb = r0 + (int64_t)wave * kRowsInFlight; sb < r1; sb += (int64_t)nwave * kRowsInFlight) {
     uint32_t w[kRowsInFlight][8];
     int n[kRowsInFlight];
@@ -394,26 +400,31 @@ __global__ __launch_bounds__(256) void round_count_kernel(QuantJobs J, int32_t* 
 #pragma unroll
     for (int rr = 0; rr < kRowsInFlight; ++rr) {
       const int64_t sr = sb + rr;
-      if (sr >= r1) break;  // uniform across the wave
+      if (sr >= r1) continue;  // uniform across the wave
       int lc = 0;
       float lm = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < n[rr]) {
-          const float y = __uint_as_float(w[rr][j]) * r;
-          const float ay = __builtin_fabsf(y);
-          const int o = ay >= kThr;
-          lc += o;
-          lm = __builtin_fmaxf(lm, ay);
-          ccnt[j] += o;
-          cmax[j] = __builtin_fmaxf(cmax[j], ay);
-          if (qb) {
-            const int64_t c = c0 + j;
-            const int32_t q = ay < 2147483648.0f ? (int32_t)__builtin_rintf(y) : 0;
-            if (!a.transposed) qb[sr * C + c] = q;
-            else qb[c * R + sr] = q;
-          }
+      auto elem = [&](int j) {
+        const float y = __uint_as_float(w[rr][j]) * r;
+        const float ay = __builtin_fabsf(y);
+        const int o = ay >= kThr;
+        lc += o;
+        lm = __builtin_fmaxf(lm, ay);
+        ccnt[j] += o;
+        cmax[j] = __builtin_fmaxf(cmax[j], ay);
+        if (QOUT && qb) {
+          const int64_t c = c0 + j;
+          const int32_t q = ay < 2147483648.0f ? (int32_t)__builtin_rintf(y) : 0;
+          if (!a.transposed) qb[sr * C + c] = q;
+          else qb[c * R + sr] = q;
         }
+      };
+      if (tile_whole) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) elem(j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < n[rr]) elem(j);
       }
       amax = __builtin_fmaxf(amax, lm);
       const int ld = lm < 2147483648.0f ? digits_of_max<BITS>(lm) : 1;
@@ -456,7 +467,7 @@ __global__ __launch_bounds__(256) void round_count_kernel(QuantJobs J, int32_t* 
 // srow_oob * srows > gamma * T.  srow_res gets the max over non-heavy columns,
 // scol_res the max over non-heavy rows.
 template <int DT, int BITS>
-__global__ __launch_bounds__(256) void residual_kernel(QuantJobs J) {
+__global__ __launch_bounds__(kResidualThreads) void residual_kernel(QuantJobs J) {
   using T = typename Elem<DT>::T;
   __shared__ uint32_t lmax[kColsPerTile];
   const JobPos jp = find_job(J, blockIdx.x);
@@ -491,6 +502,7 @@ __global__ __launch_bounds__(256) void residual_kernel(QuantJobs J) {
   float cmax[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) cmax[j] = -1.f;
+  const bool tile_whole = cbase + kColsPerTile <= a.scols;
   for (int64_t sb = r0 + (int64_t)wave * kRowsInFlight; sb < r1; sb += (int64_t)nwave * kRowsInFlight) {
     uint32_t w[kRowsInFlight][8];
     int n[kRowsInFlight];
@@ -507,15 +519,20 @@ __global__ __launch_bounds__(256) void residual_kernel(QuantJobs J) {
 #pragma unroll
     for (int rr = 0; rr < kRowsInFlight; ++rr) {
       const int64_t sr = sb + rr;
-      if (sr >= r1) break;  // uniform across the wave
+      if (sr >= r1) continue;  // uniform across the wave
       float lm = -1.f;
+      auto elem = [&](int j) {
+        const float ay = __builtin_fabsf(__uint_as_float(w[rr][j]) * r);
+        if (!colheavy[j]) lm = __builtin_fmaxf(lm, ay);
+        if (!rowheavy[rr]) cmax[j] = __builtin_fmaxf(cmax[j], ay);
+      };
+      if (tile_whole) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < n[rr]) {
-          const float ay = __builtin_fabsf(__uint_as_float(w[rr][j]) * r);
-          if (!colheavy[j]) lm = __builtin_fmaxf(lm, ay);
-          if (!rowheavy[rr]) cmax[j] = __builtin_fmaxf(cmax[j], ay);
-        }
+        for (int j = 0; j < 8; ++j) elem(j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < n[rr]) elem(j);
       }
       const int ld = lm < 0.f ? 0 : (lm < 2147483648.0f ? digits_of_max<BITS>(lm) : 1);
       const int rm = wave_max_small(ld);
@@ -591,9 +608,8 @@ hipError_t launch_hist(int dtype, QuantJobs J, int pass, int final_pass, hipStre
 }
 
 // Count kernels: tiles of 512 columns x rows_per_wg rows, about kCountWgs workgroups
-// in total so each column receives few atomics.
-static int plan_tiles(QuantJobs& J) {
-  constexpr int kCountWgs = 1024;
+// in total (fewer workgroups: fewer column atomics; more: more loads in flight).
+static int plan_tiles(QuantJobs& J, int kCountWgs) {
   double total = 0;
   for (int o = 0; o < J.nops; ++o) total += (double)J.op[o].s.srows * J.op[o].s.scols * J.op[o].batch;
   int begin = 0;
@@ -620,7 +636,10 @@ static hipError_t round_count_dt(int bits, const QuantJobs& J, int grid, int32_t
   switch (bits) {
 #define IMU_RC(B)                                                                                  \
   case B:                                                                                          \
-    hipLaunchKernelGGL((round_count_kernel<DT, B>), dim3(grid), dim3(256), 0, s, J, q0, q1);      \
+    if (q0 || q1)                                                                                  \
+      hipLaunchKernelGGL((round_count_kernel<DT, B, true>), dim3(grid), dim3(kCountThreads), 0, s, J, q0, q1); \
+    else                                                                                           \
+      hipLaunchKernelGGL((round_count_kernel<DT, B, false>), dim3(grid), dim3(kCountThreads), 0, s, J, q0, q1); \
     break;
     IMU_RC(2) IMU_RC(3) IMU_RC(4) IMU_RC(5) IMU_RC(6) IMU_RC(7) IMU_RC(8)
 #undef IMU_RC
@@ -631,7 +650,7 @@ static hipError_t round_count_dt(int bits, const QuantJobs& J, int grid, int32_t
 }
 
 hipError_t launch_round_count(int dtype, int bits, QuantJobs J, int32_t* q0, int32_t* q1, hipStream_t s) {
-  const int grid = plan_tiles(J);
+  const int grid = plan_tiles(J, 256);
   return dtype == IMU_BF16 ? round_count_dt<IMU_BF16>(bits, J, grid, q0, q1, s)
                            : round_count_dt<IMU_F32>(bits, J, grid, q0, q1, s);
 }
@@ -641,7 +660,7 @@ static hipError_t residual_dt(int bits, const QuantJobs& J, int grid, hipStream_
   switch (bits) {
 #define IMU_RS(B)                                                                                  \
   case B:                                                                                          \
-    hipLaunchKernelGGL((residual_kernel<DT, B>), dim3(grid), dim3(256), 0, s, J);                  \
+    hipLaunchKernelGGL((residual_kernel<DT, B>), dim3(grid), dim3(kResidualThreads), 0, s, J);     \
     break;
     IMU_RS(2) IMU_RS(3) IMU_RS(4) IMU_RS(5) IMU_RS(6) IMU_RS(7) IMU_RS(8)
 #undef IMU_RS
@@ -652,7 +671,7 @@ static hipError_t residual_dt(int bits, const QuantJobs& J, int grid, hipStream_
 }
 
 hipError_t launch_residual(int dtype, int bits, QuantJobs J, hipStream_t s) {
-  const int grid = plan_tiles(J);
+  const int grid = plan_tiles(J, 1024);  // more, shorter workgroups hide the per-row count loads
   return dtype == IMU_BF16 ? residual_dt<IMU_BF16>(bits, J, grid, s) : residual_dt<IMU_F32>(bits, J, grid, s);
 }
 
