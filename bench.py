@@ -30,6 +30,20 @@ INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0
 
 
+# HBM traffic of one GEMM launch on the default workload, from two rocprofv3
+# --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the
+# factor that maps the same counter onto the known bytes of a plain 256 MiB
+# device copy (bench.py --copy-calibration).  The readings belong to one
+# version of the GEMM source: when gemm.hip no longer hashes to `source_sha256`
+# the traffic is reported as null.
+GEMM_TRAFFIC = {
+    "source_sha256": "edcea43d38a8ebca62a821b4cd5f82c9f54d63a831967d57e954458cfdafff04",
+    "fetch_kib": 189893.9, "write_kib": 65536.0,        # counter readings per launch
+    "fetch_factor": 1.99980, "write_factor": 1.00000,  # copy calibration
+    "bytes_per_launch": 455973596,
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -38,7 +52,56 @@ def parse():
     ap.add_argument("--config", type=int, default=1, help="workload recipe index (default 1: LLaMA linear)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-repeats", type=int, default=1)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
+
+
+def gemm_source_sha() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "outlier_unpacking_quantization_amd", "csrc", "gemm.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+class HipEvents:
+    """Raw HIP events (timing enabled) through the HIP runtime torch has loaded."""
+
+    def __init__(self, n: int):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
+def copy_calibration():
+    import torch
+    n = 256 << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
 
 
 def device_matrix(op, torch, B):
@@ -84,6 +147,10 @@ def main():
               "the IM-Unpack path here is single-GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
     import torch
     from outlier_unpacking_quantization_amd import binding as B
     from outlier_unpacking_quantization_amd import workloads as W
@@ -103,12 +170,19 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    # the GEMM launches of every timed step are bracketed by a pair of HIP
+    # events recorded by the library on the launch stream
+    hev = HipEvents(2 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        B.set_gemm_events(hev.ev[2 * i], hev.ev[2 * i + 1])
         _, _, infos = step()
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / args.steps
+    B.set_gemm_events(None, None)
+    t_gemm = sum(hev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)) / 1000.0 / args.steps
+    hev.close()
     info = infos[0]
 
     # per-stage HIP events through the staged entry points (same kernels)
@@ -135,20 +209,12 @@ def main():
             acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(6)]
     stages_us = {n: round(float(v) * 1000.0 / reps, 2) for n, v in zip(names, acc)}
 
-    # dominant kernel: the unpacked int8 GEMM, timed alone over back-to-back launches
-    gc, gout = torch.empty_like(c), torch.empty_like(out)
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(3):
-        B.unpacked_gemm(a_u, b_u, p, sa, sb, plan)
-    g0.record()
-    greps = max(10, args.steps)
-    for _ in range(greps):
-        B.unpacked_gemm(a_u, b_u, p, sa, sb, plan)
-    g1.record()
-    torch.cuda.synchronize()
-    t_gemm = g0.elapsed_time(g1) / 1000.0 / greps
+    # dominant kernel: the unpacked int8 GEMM of the timed steps (events above)
     gemm_ops = 2.0 * info["m_u"] * info["k_u"] * info["n_u"]
     gemm_tops = gemm_ops / t_gemm / 1e12
+    traffic = None
+    if GEMM_TRAFFIC is not None and GEMM_TRAFFIC["source_sha256"] == gemm_source_sha():
+        traffic = GEMM_TRAFFIC["bytes_per_launch"]
 
     eff_tops = 2.0 * M * N * K / t_step / 1e12
     rec = {
@@ -175,7 +241,7 @@ def main():
         "stages_us": stages_us,
         "roofline": {"bound": "mfma", "kernel": "gemm_kernel (imu_unpacked_gemm)",
                      "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
                      "launch_us": round(t_gemm * 1e6, 2), "ops_per_launch": gemm_ops},
     }
     if not args.no_cpu_baseline:

@@ -222,6 +222,14 @@ const char* imu_status_string(imu_status s);
 const char* imu_last_error(void);
 /* Library version string. */
 const char* imu_version(void);
+/* Measurement hook for harnesses that time the GEMM inside a larger run: when
+ * `before` and `after` are non-NULL, every later imu_unpacked_gemm and
+ * imu_imunpack_matmul call on the calling thread records `before` on its stream
+ * right before its first GEMM launch and `after` right after its last one.
+ * Both NULL switches it off.  The events stay owned by the caller and must
+ * belong to the device the calls run on.  Returns IMU_ERR_INVALID_ARG if only
+ * one of the two is NULL. */
+imu_status imu_set_gemm_events(hipEvent_t before, hipEvent_t after);
 
 #ifdef __cplusplus
 }

@@ -111,6 +111,7 @@ def lib() -> ctypes.CDLL:
         "imu_status_string": (ctypes.c_char_p, [I32]),
         "imu_last_error": (ctypes.c_char_p, []),
         "imu_version": (ctypes.c_char_p, []),
+        "imu_set_gemm_events": (I32, [V, V]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -123,7 +124,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("imu_stats_bytes", "imu_stats_layout", "imu_plan_bytes", "imu_plan_layout",
             "imu_workspace_fixed_bytes", "imu_quantize_rtn", "imu_plan_unpack", "imu_unpack",
             "imu_unpacked_gemm", "imu_imunpack_matmul", "imu_status_string", "imu_last_error",
-            "imu_version")
+            "imu_version", "imu_set_gemm_events")
 
 
 def _check(status: int):
@@ -385,3 +386,8 @@ def imunpack_matmul(a, b, p: ImuParams, out: Optional[torch.Tensor] = None, c: O
 
 def version() -> str:
     return lib().imu_version().decode()
+
+
+def set_gemm_events(before: int | None, after: int | None) -> None:
+    """imu_set_gemm_events with raw hipEvent_t handles (None, None switches it off)."""
+    _check(lib().imu_set_gemm_events(ctypes.c_void_p(before), ctypes.c_void_p(after)))

@@ -15,6 +15,7 @@ using namespace imu;
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t g_gemm_ev[2] = {nullptr, nullptr};  // imu_set_gemm_events
 
 imu_status fail(imu_status s, const std::string& msg) {
   g_err = msg;
@@ -319,6 +320,7 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   const int64_t M = info[0].m, K = info[0].k, N = info[0].n;
   const StatsLayout la = stats_layout(M, K), lb = stats_layout(K, N);
   const PlanLayout pl = plan_layout(M, K, N, batch, p->bits);
+  if (g_gemm_ev[0]) IMU_HIP(hipEventRecord(g_gemm_ev[0], s));
   for (int64_t b = 0; b < batch; ++b) {
     const imu_plan_info& f = info[b];
     const uint8_t* pe = plan + pl.headers_bytes + b * pl.entry_stride;
@@ -352,6 +354,7 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
     }
     IMU_HIP(launch_gemm(g, s));
   }
+  if (g_gemm_ev[1]) IMU_HIP(hipEventRecord(g_gemm_ev[1], s));
   return IMU_OK;
 }
 
@@ -550,5 +553,13 @@ const char* imu_status_string(imu_status s) {
 const char* imu_last_error(void) { return g_err.c_str(); }
 
 const char* imu_version(void) { return "imunpack 0.1 (gfx950)"; }
+
+imu_status imu_set_gemm_events(hipEvent_t before, hipEvent_t after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(IMU_ERR_INVALID_ARG, "pass both events or neither");
+  g_gemm_ev[0] = before;
+  g_gemm_ev[1] = after;
+  return IMU_OK;
+}
 
 }  // extern "C"
