@@ -36,7 +36,7 @@ struct StatsHeader {
   uint32_t sel_prefix;  // radix-select state: key prefix found so far
   uint32_t sel_rank;    // rank still to find inside that prefix (1-based)
   unsigned long long total;  // T: out-of-range codes
-  uint32_t arrive;           // workgroups that finished the current histogram pass
+  uint32_t arrive;           // workgroups that finished the current pass (last-workgroup election, barriers)
   int32_t pad1;
   int64_t rows, cols;
 };

@@ -10,22 +10,23 @@
 // function of the per-line statistics, so it is deterministic.
 //
 // The lines (rows of A, columns of B, then k) are cut into chunks of
-// kPlanLines, one workgroup per chunk and batch entry:
+// kPlanLines, one workgroup per chunk and batch entry, in three launches:
 // (1) plan_sums: the depth of every line under each of the 4 candidates (packed
 //     bytes, kept for (2)) and the chunk's share of M'[4], N'[4], K'[4][4]; the
 //     last workgroup to finish adds the shares up and picks the pair.
 // (2) plan_counts: the chosen depth maps and, per chunk, the entries of every
 //     task (each level of A's rows or B's columns: lines deeper than the level;
-//     each exponent segment e of K': triples (k, v, v') with v + v' = e); the
-//     last workgroup turns them into level bases, padded segment offsets, the
-//     header sizes and each chunk's offset in every task.
-// (3) plan_write: each chunk scans its lines (a thread owns 4 consecutive
-//     lines, one block-wide scan per batch of tasks) and writes the level-major
-//     line maps, the per-segment prefixes over k and the K' position table used
-//     by the unpack kernels.
-// Records pass between the workgroups of one kernel as device-scope atomic
-// stores and loads (written through the XCD-local L2); the counter that elects
-// the last workgroup is the statistics header's, which is zero between passes.
+//     each exponent segment e of K': triples (k, v, v') with v + v' = e).
+// (3) plan_write: from all chunks' counts, each workgroup derives the level
+//     bases or padded segment offsets and its own offset in every task
+//     (workgroup 0 also writes the header sizes), then scans its lines (a
+//     thread owns 4 consecutive lines, one block-wide scan per batch of tasks)
+//     and writes the level-major line maps, the per-segment prefixes over k and
+//     the K' position table used by the unpack kernels.
+// Records exchanged inside one launch are written with device-scope atomic
+// stores (through the XCD-local L2) and read after a device-scope acquire; the
+// counter that elects the last workgroup is the statistics header's, which is
+// zero between passes.
 #include "common.h"
 #include "kernels.h"
 
@@ -47,13 +48,6 @@ __device__ inline void st_dev(long long* p, long long v) {
 __device__ inline void st_dev(int32_t* p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline long long ld_dev(const long long* p) {
-  return __hip_atomic_load(const_cast<long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline int32_t ld_dev(const int32_t* p) {
-  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Elects the workgroup that finishes last.  Every thread's earlier stores have
 // completed before the count is taken; the elected workgroup resets the
 // counter for the next kernel (stream ordered).
@@ -65,16 +59,6 @@ __device__ inline bool last_to_arrive(uint32_t* counter, uint32_t total, int* s_
   const bool last = *s_flag != 0;
   if (last && threadIdx.x == 0) *counter = 0;
   return last;
-}
-
-__device__ inline long long wave_sum_i64(long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    int lo = __shfl_xor((int)(v & 0xFFFFFFFFll), o, 64);
-    int hi = __shfl_xor((int)(v >> 32), o, 64);
-    v += ((long long)hi << 32) | (unsigned)lo;
-  }
-  return v;
 }
 
 // Block-wide exclusive scans of kTaskBatch counters per thread at once.
@@ -207,21 +191,44 @@ __device__ inline uint32_t* arrive_counter(const PlanArgs& a, int b) {
   return &reinterpret_cast<StatsHeader*>(const_cast<uint8_t*>(a.stats_a) + b * a.stats_stride_a)->arrive;
 }
 
-// --- (1) candidate depths and sizes; choice --------------------------------
-__global__ __launch_bounds__(kThreads) void plan_sums_kernel(PlanArgs a) {
-  __shared__ long long red[kWaves][24];
-  __shared__ long long tot[24];
-  __shared__ int s_flag;
-  const int b = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+// Shared memory of a planner workgroup, all phases.
+struct PlanShared {
+  long long red[kThreads / 24][24];
+  int red32[kWaves][16];
+  long long tot[24];
+  unsigned long long cost_hi[16], cost_lo[16];
+  int cost_ok[16];
+  int choice[2];
+  int flag;
+  int hist[(kMaxD + 1) * (kMaxD + 1)];  // depth histogram (rows/cols) or (dA, dB) pairs (k)
+  int smax[kWaves][4];
+  long long task_tot[3][kPlanTasks];    // per kind and task: entries of all chunks
+  int off[kPlanTasks];                  // this chunk's offset in every task of its kind
+  long long base[kPlanTasks];           // level bases (rows/cols) or segment offsets (k)
+  long long segoff[kMaxSeg + 1];        // padded segment offsets
+  long long end_rows[2];                // first row past the last level: A rows, B columns
+  long long m_base, n_base, m_alloc, n_alloc;
+  int lev[2], nseg;
+  int scan_tot[kWaves * kTaskBatch];
+};
+
+// --- (1) candidate depths of a chunk's lines and its share of the sizes -----
+__device__ void phase_sums(const PlanArgs& a, int b, int64_t w, PlanShared& S) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const PlanLayout& L = a.pl;
   const Entry E = entry_of(a, b);
   const Src A = src_of(a.stats_a + b * a.stats_stride_a, a.sla);
   const Src B = src_of(a.stats_b + b * a.stats_stride_b, a.slb);
-  const Chunk c = chunk_of(L, blockIdx.x);
+  const Chunk c = chunk_of(L, w);
   const int gamma = a.gamma;
-  long long acc[24];
+  if (w == 0 && t == 0)  // status of this plan; later failures are OR-ed in
+    E.ph->status = (int32_t)(reinterpret_cast<const StatsHeader*>(a.stats_a + b * a.stats_stride_a)->status |
+                             reinterpret_cast<const StatsHeader*>(a.stats_b + b * a.stats_stride_b)->status);
+  // a chunk's shares fit 32 bits (1024 lines, depths <= 32); only its kind's
+  // 4 (rows, columns) or 16 (k) sums are non-zero
+  int acc[16];
 #pragma unroll
-  for (int j = 0; j < 24; ++j) acc[j] = 0;
+  for (int j = 0; j < 16; ++j) acc[j] = 0;
   uint32_t dx[kPer], dy[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {  // clamped indices: all loads issued before use
@@ -244,97 +251,105 @@ __global__ __launch_bounds__(kThreads) void plan_sums_kernel(PlanArgs a) {
     } else if (c.kind == 1) {
       E.cand[L.M + i] = dx[j];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[4 + q] += pick(dx[j], q);
+      for (int q = 0; q < 4; ++q) acc[q] += pick(dx[j], q);
     } else {
       E.cand[L.M + L.N + i] = dx[j];
       E.cand[L.M + L.N + L.K + i] = dy[j];
 #pragma unroll
       for (int ca = 0; ca < 4; ++ca)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[8 + ca * 4 + cb] += pick(dx[j], ca) * pick(dy[j], cb);
+        for (int cb = 0; cb < 4; ++cb) acc[ca * 4 + cb] += pick(dx[j], ca) * pick(dy[j], cb);
     }
   }
+  const int nsum = c.kind == 2 ? 16 : 4;  // uniform over the workgroup
 #pragma unroll
-  for (int j = 0; j < 24; ++j) {
-    const long long v = wave_sum_i64(acc[j]);
-    if (lane == 0) red[wave][j] = v;
+  for (int j = 0; j < 16; ++j) {
+    if (j < nsum) {
+      const int v = wave_sum_i32(acc[j]);
+      if (lane == 0) S.red32[wave][j] = v;
+    }
   }
   __syncthreads();
-  PlanWgRecord* my = E.rec + blockIdx.x;
-  if (t < 24) {
+  if (t < 24) {  // record slots: [0,4) A rows, [4,8) B columns, [8,24) k pairs
+    const int first = c.kind == 0 ? 0 : c.kind == 1 ? 4 : 8;
     long long v = 0;
-    for (int w = 0; w < kWaves; ++w) v += red[w][t];
-    st_dev(&my->sum[t], v);
-  }
-  const uint32_t G = (uint32_t)(L.wg_a + L.wg_b + L.wg_k);
-  if (!last_to_arrive(arrive_counter(a, b), G, &s_flag)) return;
-
-  // the last workgroup: totals over all chunks, then the choice
-#pragma unroll
-  for (int j = 0; j < 24; ++j) acc[j] = 0;
-  for (uint32_t w = t; w < G; w += kThreads)
-#pragma unroll
-    for (int j = 0; j < 24; ++j) acc[j] += ld_dev(&E.rec[w].sum[j]);
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 24; ++j) {
-    const long long v = wave_sum_i64(acc[j]);
-    if (lane == 0) red[wave][j] = v;
-  }
-  __syncthreads();
-  if (t < 24) {
-    long long v = 0;
-    for (int w = 0; w < kWaves; ++w) v += red[w][t];
-    tot[t] = v;
-  }
-  __syncthreads();
-  if (t == 0) {
-    PlanHeader* ph = E.ph;
-    int best_a = -1, best_b = -1;
-    unsigned __int128 best = 0;
-    for (int ca = 0; ca < 4; ++ca)
-      for (int cb = 0; cb < 4; ++cb) {
-        const int slot = ca * 4 + cb;
-        if (!allowed(a.strat_a, ca) || !allowed(a.strat_b, cb)) {
-          ph->pair[slot][0] = ph->pair[slot][1] = ph->pair[slot][2] = -1;
-          continue;
-        }
-        const long long mu = tot[ca], ku = tot[8 + slot], nu = tot[4 + cb];
-        ph->pair[slot][0] = mu;
-        ph->pair[slot][1] = ku;
-        ph->pair[slot][2] = nu;
-        const unsigned __int128 cost =
-            (unsigned __int128)(unsigned long long)mu * (unsigned long long)ku * (unsigned long long)nu;
-        if (best_a < 0 || cost < best) {
-          best = cost;
-          best_a = ca;
-          best_b = cb;
-        }
-      }
-    ph->choice_a = best_a;
-    ph->choice_b = best_b;
-    ph->m_u = tot[best_a];
-    ph->k_u = tot[8 + best_a * 4 + best_b];
-    ph->n_u = tot[4 + best_b];
-    ph->status = (int32_t)(reinterpret_cast<const StatsHeader*>(a.stats_a + b * a.stats_stride_a)->status |
-                           reinterpret_cast<const StatsHeader*>(a.stats_b + b * a.stats_stride_b)->status);
+    if (t >= first && t < first + nsum)
+      for (int q = 0; q < kWaves; ++q) v += S.red32[q][t - first];
+    st_dev(&E.rec[w].sum[t], v);
   }
 }
 
-// --- (2) chosen depths, per-chunk task counts; bases, offsets, sizes --------
-__global__ __launch_bounds__(kThreads) void plan_counts_kernel(PlanArgs a) {
-  __shared__ int hist[(kMaxD + 1) * (kMaxD + 1)];  // depth histogram (rows/cols) or (dA, dB) pairs (k)
-  __shared__ int smax[kWaves][4];
-  __shared__ int s_flag;
-  __shared__ long long gt[2][kPlanTasks];  // lines deeper than u: A rows, B cols
-  __shared__ long long seg_len[kPlanTasks];
-  __shared__ int lev_s[2], nseg_s;
-  const int b = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+// Totals of all chunks' shares and the joint choice (S.choice).  With
+// write_header the workgroup also writes the choice and every pair's sizes.
+__device__ void choose(const PlanArgs& a, int b, int64_t G, bool write_header, PlanShared& S) {
+  const int t = threadIdx.x;
+  const Entry E = entry_of(a, b);
+  // the records were written through to memory before the election; after an
+  // acquire at device scope (drops stale cached lines) plain loads see them
+  // and can all be in flight at once
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  constexpr int kGroups = kThreads / 24;  // thread t adds value t % 24 of records t / 24 (mod kGroups)
+  if (t < kGroups * 24) {
+    const int j = t % 24, g = t / 24;
+    long long v = 0;
+    for (int64_t q = g; q < G; q += kGroups) v += E.rec[q].sum[j];
+    S.red[g][j] = v;
+  }
+  __syncthreads();
+  if (t < 24) {
+    long long v = 0;
+    for (int g = 0; g < kGroups; ++g) v += S.red[g][t];
+    S.tot[t] = v;
+  }
+  __syncthreads();
+  // cost of pair (ca, cb) = M'[ca] K'[ca][cb] N'[cb] < 2^88: M'K' < 2^59 is
+  // exact in 64 bits (M' < 2^29, K' < 2^30), its product with N' < 2^29 is
+  // kept as (high, low) 64-bit words
+  if (t < 16) {
+    const int ca = t >> 2, cb = t & 3;
+    const bool ok = allowed(a.strat_a, ca) && allowed(a.strat_b, cb);
+    const unsigned long long mk = (unsigned long long)S.tot[ca] * (unsigned long long)S.tot[8 + t];
+    const unsigned long long nu = (unsigned long long)S.tot[4 + cb];
+    S.cost_hi[t] = ok ? __umul64hi(mk, nu) : ~0ull;
+    S.cost_lo[t] = ok ? mk * nu : ~0ull;
+    S.cost_ok[t] = ok;
+    if (write_header) {
+      E.ph->pair[t][0] = ok ? S.tot[ca] : -1;
+      E.ph->pair[t][1] = ok ? S.tot[8 + t] : -1;
+      E.ph->pair[t][2] = ok ? S.tot[4 + cb] : -1;
+    }
+  }
+  __syncthreads();
+  if (t == 0) {  // smallest cost, ties to the first pair in A-major order
+    int best = -1;
+    for (int q = 0; q < 16; ++q) {
+      if (!S.cost_ok[q]) continue;
+      if (best < 0 || S.cost_hi[q] < S.cost_hi[best] ||
+          (S.cost_hi[q] == S.cost_hi[best] && S.cost_lo[q] < S.cost_lo[best]))
+        best = q;
+    }
+    const int best_a = best >> 2, best_b = best & 3;
+    S.choice[0] = best_a;
+    S.choice[1] = best_b;
+    if (write_header) {
+      PlanHeader* ph = E.ph;
+      ph->choice_a = best_a;
+      ph->choice_b = best_b;
+      ph->m_u = S.tot[best_a];
+      ph->k_u = S.tot[8 + best];
+      ph->n_u = S.tot[4 + best_b];
+    }
+  }
+  __syncthreads();
+}
+
+// --- (2) chosen depth maps and a chunk's entries per task -------------------
+__device__ void phase_counts(const PlanArgs& a, int b, int64_t w, int ca, int cb, PlanShared& S) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const PlanLayout& L = a.pl;
   const Entry E = entry_of(a, b);
-  const Chunk c = chunk_of(L, blockIdx.x);
-  const int ca = E.ph->choice_a, cb = E.ph->choice_b;
-  for (int i = t; i < (kMaxD + 1) * (kMaxD + 1); i += kThreads) hist[i] = 0;
+  const Chunk c = chunk_of(L, w);
+  for (int i = t; i < (kMaxD + 1) * (kMaxD + 1); i += kThreads) S.hist[i] = 0;
   __syncthreads();
   uint32_t dx[kPer], dy[kPer];
 #pragma unroll
@@ -356,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void plan_counts_kernel(PlanArgs a) {
       const int d = pick(dx[j], c.kind == 0 ? ca : cb);
       (c.kind == 0 ? E.da_r : E.db_c)[i] = d;
       m0 = max(m0, d);
-      atomicAdd(&hist[d], 1);
+      atomicAdd(&S.hist[d], 1);
     } else {
       const int x = pick(dx[j], ca), y = pick(dy[j], cb);
       E.da_c[i] = x;
@@ -364,125 +379,121 @@ __global__ __launch_bounds__(kThreads) void plan_counts_kernel(PlanArgs a) {
       m0 = max(m0, x);
       m1 = max(m1, y);
       m2 = max(m2, x + y - 2);
-      atomicAdd(&hist[x * (kMaxD + 1) + y], 1);
+      atomicAdd(&S.hist[x * (kMaxD + 1) + y], 1);
     }
   }
   m0 = wave_max_i32(m0);
   m1 = wave_max_i32(m1);
   m2 = wave_max_i32(m2);
   if (lane == 0) {
-    smax[wave][0] = m0;
-    smax[wave][1] = m1;
-    smax[wave][2] = m2;
+    S.smax[wave][0] = m0;
+    S.smax[wave][1] = m1;
+    S.smax[wave][2] = m2;
   }
   __syncthreads();
   int x_hi = 1, y_hi = 1;
-  for (int w = 0; w < kWaves; ++w) {
-    x_hi = max(x_hi, smax[w][0]);
-    y_hi = max(y_hi, smax[w][1]);
+  for (int q = 0; q < kWaves; ++q) {
+    x_hi = max(x_hi, S.smax[q][0]);
+    y_hi = max(y_hi, S.smax[q][1]);
   }
-  PlanWgRecord* my = E.rec + blockIdx.x;
+  PlanWgRecord* my = E.rec + w;
   if (t < kPlanTasks) {  // task counts of this chunk
     int v = 0;
     if (c.kind < 2) {
-      for (int d = t + 1; d <= x_hi; ++d) v += hist[d];  // lines with depth > t
+      for (int d = t + 1; d <= x_hi; ++d) v += S.hist[d];  // lines with depth > t
     } else {
       for (int x = 1; x <= x_hi; ++x)
-        for (int y = 1; y <= y_hi; ++y) v += hist[x * (kMaxD + 1) + y] * seg_count(x, y, t);
+        for (int y = 1; y <= y_hi; ++y) v += S.hist[x * (kMaxD + 1) + y] * seg_count(x, y, t);
     }
     st_dev(&my->cnt[t], v);
   }
   if (t < 3) {
     int v = t == 2 ? 0 : 1;
-    for (int w = 0; w < kWaves; ++w) v = max(v, smax[w][t]);
+    for (int q = 0; q < kWaves; ++q) v = max(v, S.smax[q][t]);
     st_dev(&my->mx[t], v);
   }
-  const uint32_t G = (uint32_t)(L.wg_a + L.wg_b + L.wg_k);
-  if (!last_to_arrive(arrive_counter(a, b), G, &s_flag)) return;
+}
 
-  // the last workgroup: per task, chunk offsets and totals (one thread per
-  // task and kind walks that kind's chunks in order)
+// Levels, segment count, per-task totals of every kind and this chunk's offset
+// in each task of its kind, from all chunks' records (written by the previous
+// launch); level bases (rows and
+// columns) or padded segment offsets (k).  With write_header the workgroup
+// also writes the header sizes.
+__device__ void layout(const PlanArgs& a, int b, int64_t w, bool write_header, PlanShared& S) {
+  const int t = threadIdx.x;
+  const PlanLayout& L = a.pl;
+  const Entry E = entry_of(a, b);
+  const Chunk me = chunk_of(L, w);
   const int64_t wk0[3] = {0, L.wg_a, L.wg_a + L.wg_b};
   const int64_t wkn[3] = {L.wg_a, L.wg_b, L.wg_k};
   for (int job = t; job < 3 * kPlanTasks; job += kThreads) {
     const int kind = job / kPlanTasks, task = job % kPlanTasks;
     long long run = 0;
     for (int64_t r = 0; r < wkn[kind]; ++r) {
-      PlanWgRecord* rc = E.rec + wk0[kind] + r;
-      rc->off[task] = (int32_t)run;  // read by the next kernel
-      run += ld_dev(&rc->cnt[task]);
+      if (kind == me.kind && r == me.rank) S.off[task] = (int)run;
+      run += E.rec[wk0[kind] + r].cnt[task];  // written by the previous launch
     }
-    if (kind < 2) gt[kind][task] = run;
-    else seg_len[task] = run;
+    S.task_tot[kind][task] = run;
   }
-  if (t < 3) {
+  if (t < 3) {  // lev_a (A rows), lev_b (B columns), emax (k)
+    const int kind = t, field = t == 2 ? 2 : 0;
     int v = t == 2 ? 0 : 1;
-    for (int64_t w = 0; w < (int64_t)G; ++w) {
-      const Chunk cw = chunk_of(L, w);
-      const int mxv = t == 0 ? ld_dev(&E.rec[w].mx[0]) : ld_dev(&E.rec[w].mx[t == 1 ? 0 : 2]);
-      if ((t == 0 && cw.kind == 0) || (t == 1 && cw.kind == 1) || (t == 2 && cw.kind == 2)) v = max(v, mxv);
-    }
-    if (t < 2) lev_s[t] = min(v, (int)L.levels);
-    else nseg_s = min(v, (int)L.segments - 1) + 1;
+    for (int64_t r = 0; r < wkn[kind]; ++r) v = max(v, E.rec[wk0[kind] + r].mx[field]);
+    if (t < 2) S.lev[t] = min(v, (int)L.levels);
+    else S.nseg = min(v, (int)L.segments - 1) + 1;
   }
   __syncthreads();
   if (t == 0) {
-    PlanHeader* ph = E.ph;
-    const int lev_a = lev_s[0], lev_b = lev_s[1], nseg = nseg_s;
-    const int64_t m_base = round_up(L.M, L.pad_m), n_base = round_up(L.N, L.pad_n);
-    long long end_a = m_base, end_b = n_base;
-    for (int u = 1; u < lev_a; ++u) end_a += gt[0][u];
-    for (int u = 1; u < lev_b; ++u) end_b += gt[1][u];
-    long long off = 0;
-    for (int s = 0; s < nseg; ++s) {
-      ph->seg_off[s] = off;
-      ph->seg_len[s] = (int32_t)seg_len[s];
-      off += round_up(seg_len[s], kKPad);
+    S.m_base = round_up(L.M, L.pad_m);
+    S.n_base = round_up(L.N, L.pad_n);
+    for (int kind = 0; kind < 2; ++kind) {
+      long long p = kind == 0 ? S.m_base : S.n_base;
+      for (int u = 1; u < S.lev[kind]; ++u) p += S.task_tot[kind][u];
+      S.end_rows[kind] = p;
     }
-    ph->seg_off[nseg] = off;
-    ph->n_seg = nseg;
-    ph->k_pad = off;
-    ph->m_base = m_base;
-    ph->n_base = n_base;
-    ph->m_alloc = round_up(end_a, L.pad_m);
-    ph->n_alloc = round_up(end_b, L.pad_n);
-    ph->lev_a = lev_a;
-    ph->lev_b = lev_b;
-    ph->emax = nseg - 1;
-  }
-}
-
-// --- (3) positions ----------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void plan_write_kernel(PlanArgs a) {
-  __shared__ int scan_tot[kWaves * kTaskBatch];
-  __shared__ long long base_s[kPlanTasks];  // level bases (rows/cols) or segment offsets (k)
-  __shared__ int off_s[kPlanTasks];
-  const int b = blockIdx.y, t = threadIdx.x;
-  const PlanLayout& L = a.pl;
-  const Entry E = entry_of(a, b);
-  const PlanHeader* ph = E.ph;
-  const Chunk c = chunk_of(L, blockIdx.x);
-  const int ntasks = c.kind == 0 ? ph->lev_a : c.kind == 1 ? ph->lev_b : ph->n_seg;
-  const PlanWgRecord* my = E.rec + blockIdx.x;
-  if (t < kPlanTasks) off_s[t] = my->off[t];
-  if (t == 0) {
-    if (c.kind < 2) {
-      // level u > 0 starts after the padded base and the levels 1..u-1, whose
-      // sizes are the totals of the previous chunks' last offsets + counts:
-      // recomputed here from the records of this kind's last chunk
-      const int64_t last = c.kind == 0 ? L.wg_a - 1 : L.wg_a + L.wg_b - 1;
-      const PlanWgRecord* lr = E.rec + last;
-      long long p = c.kind == 0 ? ph->m_base : ph->n_base;
-      base_s[0] = 0;
-      for (int u = 1; u < ntasks; ++u) {
-        base_s[u] = p;
-        p += (long long)lr->off[u] + lr->cnt[u];
+    S.m_alloc = round_up(S.end_rows[0], L.pad_m);
+    S.n_alloc = round_up(S.end_rows[1], L.pad_n);
+    long long off = 0;
+    for (int q = 0; q < S.nseg; ++q) {
+      S.segoff[q] = off;
+      off += round_up(S.task_tot[2][q], kKPad);
+    }
+    S.segoff[S.nseg] = off;
+    if (me.kind < 2) {
+      long long p = me.kind == 0 ? S.m_base : S.n_base;
+      S.base[0] = 0;
+      for (int u = 1; u < S.lev[me.kind]; ++u) {
+        S.base[u] = p;
+        p += S.task_tot[me.kind][u];
       }
     } else {
-      for (int s = 0; s < ntasks; ++s) base_s[s] = ph->seg_off[s];
+      for (int q = 0; q < S.nseg; ++q) S.base[q] = S.segoff[q];
+    }
+    if (write_header) {
+      PlanHeader* ph = E.ph;
+      for (int q = 0; q <= S.nseg; ++q) ph->seg_off[q] = S.segoff[q];
+      for (int q = 0; q < S.nseg; ++q) ph->seg_len[q] = (int32_t)S.task_tot[2][q];
+      ph->n_seg = S.nseg;
+      ph->k_pad = S.segoff[S.nseg];
+      ph->m_base = S.m_base;
+      ph->n_base = S.n_base;
+      ph->m_alloc = S.m_alloc;
+      ph->n_alloc = S.n_alloc;
+      ph->lev_a = S.lev[0];
+      ph->lev_b = S.lev[1];
+      ph->emax = S.nseg - 1;
     }
   }
   __syncthreads();
+}
+
+// --- (3) positions of a chunk's lines; workgroup 0 also writes the padding --
+__device__ void phase_write(const PlanArgs& a, int b, int64_t w, PlanShared& S) {
+  const int t = threadIdx.x;
+  const PlanLayout& L = a.pl;
+  const Entry E = entry_of(a, b);
+  const Chunk c = chunk_of(L, w);
+  const int ntasks = c.kind == 0 ? S.lev[0] : c.kind == 1 ? S.lev[1] : S.nseg;
   const int64_t i0 = min64(c.first + (int64_t)t * kPer, c.n), i1 = min64(i0 + kPer, c.n);
   int dA[kPer], dB[kPer];
 #pragma unroll
@@ -506,26 +517,26 @@ __global__ __launch_bounds__(kThreads) void plan_write_kernel(PlanArgs a) {
         if (l < nl) v += c.kind < 2 ? (dA[l] > tb + j) : seg_count(dA[l], dB[l], tb + j);
       cnt[j] = v;
     }
-    block_excl_scan_multi(cnt, ex, scan_tot);
+    block_excl_scan_multi(cnt, ex, S.scan_tot);
 #pragma unroll
     for (int j = 0; j < kTaskBatch; ++j) {
       const int task = tb + j;
       if (task >= ntasks) continue;
-      long long pos = ex[j] + off_s[task];  // position inside the task
+      long long pos = ex[j] + S.off[task];  // position inside the task
 #pragma unroll
       for (int l = 0; l < kPer; ++l) {
         if (l >= nl) continue;
         const int64_t i = i0 + l;
         if (c.kind < 2) {
           const bool live = dA[l] > task;
-          const long long p = base_s[task] + pos;
+          const long long p = S.base[task] + pos;
           (c.kind == 0 ? E.lvl_a : E.lvl_b)[(int64_t)task * c.n + i] = live ? (int32_t)p : -1;
           if (live) (c.kind == 0 ? E.amap : E.bmap)[p] = (int32_t)(i | ((int64_t)task << 24));
           pos += live;
         } else {
           const int cnt_l = seg_count(dA[l], dB[l], task);
           E.kpre[(int64_t)task * (L.K + 1) + i] = (int32_t)pos;
-          uint32_t* km = E.kmap + base_s[task] + pos;
+          uint32_t* km = E.kmap + S.base[task] + pos;
           const int lo = max(0, task - (dB[l] - 1));
           for (int v = 0; v < cnt_l; ++v) km[v] = kmap_pack(i, lo + v, task - lo - v, dA[l], dB[l]);
           pos += cnt_l;
@@ -533,31 +544,44 @@ __global__ __launch_bounds__(kThreads) void plan_write_kernel(PlanArgs a) {
       }
     }
   }
-  // padding (workgroup 0): rows between M and the padded base, after the last
-  // level up to the allocation, zero entries at the end of every segment, and
-  // the per-segment totals at kpre[s][K]
-  if (blockIdx.x == 0) {
-    __shared__ long long end_s[2];
-    if (t < 2) {
-      const int64_t last = t == 0 ? L.wg_a - 1 : L.wg_a + L.wg_b - 1;
-      const PlanWgRecord* lr = E.rec + last;
-      const int lev = t == 0 ? ph->lev_a : ph->lev_b;
-      long long p = t == 0 ? ph->m_base : ph->n_base;
-      for (int u = 1; u < lev; ++u) p += (long long)lr->off[u] + lr->cnt[u];
-      end_s[t] = p;
-    }
-    __syncthreads();
-    for (int64_t r = L.M + t; r < ph->m_base; r += kThreads) E.amap[r] = -1;
-    for (int64_t r = end_s[0] + t; r < ph->m_alloc; r += kThreads) E.amap[r] = -1;
-    for (int64_t r = L.N + t; r < ph->n_base; r += kThreads) E.bmap[r] = -1;
-    for (int64_t r = end_s[1] + t; r < ph->n_alloc; r += kThreads) E.bmap[r] = -1;
-    const int nseg = ph->n_seg;
-    for (int s = 0; s < nseg; ++s) {
-      const int64_t p0 = ph->seg_off[s] + ph->seg_len[s], p1 = ph->seg_off[s + 1];
+  if (w == 0) {
+    // rows between M and the padded base and after the last level up to the
+    // allocation, zero entries at the end of every segment, and the
+    // per-segment totals at kpre[s][K]
+    for (int64_t r = L.M + t; r < S.m_base; r += kThreads) E.amap[r] = -1;
+    for (int64_t r = S.end_rows[0] + t; r < S.m_alloc; r += kThreads) E.amap[r] = -1;
+    for (int64_t r = L.N + t; r < S.n_base; r += kThreads) E.bmap[r] = -1;
+    for (int64_t r = S.end_rows[1] + t; r < S.n_alloc; r += kThreads) E.bmap[r] = -1;
+    for (int q = 0; q < S.nseg; ++q) {
+      const int64_t p0 = S.segoff[q] + S.task_tot[2][q], p1 = S.segoff[q + 1];
       for (int64_t p = p0 + t; p < p1; p += kThreads) E.kmap[p] = kKmapPad;
     }
-    if (t < nseg) E.kpre[(int64_t)t * (L.K + 1) + L.K] = ph->seg_len[t];
+    if (t < S.nseg) E.kpre[(int64_t)t * (L.K + 1) + L.K] = (int32_t)S.task_tot[2][t];
   }
+}
+
+// The three launches.  Records a kernel's own workgroups exchange travel as
+// device-scope atomics; records of an earlier launch are read with plain loads.
+__global__ __launch_bounds__(kThreads) void plan_sums_kernel(PlanArgs a) {
+  __shared__ PlanShared S;
+  const int b = blockIdx.y;
+  const PlanLayout& L = a.pl;
+  const uint32_t G = (uint32_t)(L.wg_a + L.wg_b + L.wg_k);
+  phase_sums(a, b, blockIdx.x, S);
+  if (!last_to_arrive(arrive_counter(a, b), G, &S.flag)) return;
+  choose(a, b, G, true, S);
+}
+__global__ __launch_bounds__(kThreads) void plan_counts_kernel(PlanArgs a) {
+  __shared__ PlanShared S;
+  const int b = blockIdx.y;
+  const PlanHeader* ph = entry_of(a, b).ph;
+  phase_counts(a, b, blockIdx.x, ph->choice_a, ph->choice_b, S);
+}
+__global__ __launch_bounds__(kThreads) void plan_write_kernel(PlanArgs a) {
+  __shared__ PlanShared S;
+  const int b = blockIdx.y;
+  layout(a, b, blockIdx.x, blockIdx.x == 0, S);
+  phase_write(a, b, blockIdx.x, S);
 }
 
 }  // namespace

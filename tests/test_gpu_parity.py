@@ -68,6 +68,10 @@ def check_stats(st: B.Stats, q_entries, b: int, tag: str):
 
 @pytest.mark.parametrize("cfg", SMALL, ids=[_id(c) for c in SMALL])
 def test_staged_path_matches_oracle(cfg):
+    _staged(cfg)
+
+
+def _staged(cfg):
     pr = W.random_problem(**cfg)
     print(f"\n[case] {pr.name} a={pr.a.dtype}/{pr.a.layout} b={pr.b.layout} bits={pr.bits} beta={pr.beta} "
           f"strat={pr.strat_a}/{pr.strat_b} batch={pr.a.batch}", flush=True)
