@@ -11,21 +11,21 @@
 // unpacked row (i, u) and column (n, w) into C[i, n] with a further shift of
 // (bits-1)(u+w); all int32 arithmetic wraps modulo 2^32.
 //
-// Operands: A' (m_alloc x k_pad) and B'^T (n_alloc x k_pad), both K-contiguous.
-// Workgroup tile 256 x 128, four waves stacked along M, each owning 64 rows x
-// 128 columns (2 x 4 blocks of 32 x 32, 128 accumulator registers).  A wave's A
-// rows belong to it alone, and A' is stored in MFMA fragment order, so its A
-// fragments are contiguous 1 KB loads straight into registers; the B tile (128
-// x 128 bytes per K step, read 8 lanes per 128-byte row) is shared by the four
-// waves and goes through LDS, double-buffered, rows 144 bytes apart (16-byte
-// reads of 8 consecutive rows then touch disjoint banks).  Both operands are
-// prefetched two K steps ahead in a register ring (one wave per SIMD, so
-// latency is hidden by depth rather than by occupancy).  This keeps LDS
-// traffic at about 70% of its read bandwidth when the matrix cores run at peak,
-// where staging both operands through LDS would exceed it.  Segments are padded
-// to the K step, so a step never straddles two exponents.  Tiles are ordered in
-// groups of 8 tile rows and dealt to the 8 XCDs in contiguous runs, so the
-// workgroups sharing an XCD's L2 share A and B panels.
+// Operands: A' (m_alloc x k_pad) in MFMA fragment order and B'^T (n_alloc x
+// k_pad), both K-contiguous.  Workgroup tile 256 x 128, four waves stacked along
+// M, each owning 64 rows x 128 columns (2 x 4 blocks of 32 x 32, 128
+// accumulator registers).  A wave's A rows belong to it alone, so its A
+// fragments are contiguous 1 KB loads straight into registers, refilled one K
+// substep at a time one step ahead; the B tile (128 x 128 bytes per K step) is
+// shared by the four waves through LDS, double-buffered, rows 144 bytes apart
+// (16-byte reads of 8 consecutive rows touch disjoint banks), its global loads
+// two steps ahead.  B fragments are double-buffered by substep: the reads of
+// substep q+1 are issued before the MFMAs of substep q, and substep 0 of the
+// next step is read right after the barrier, under the MFMAs of substep 3.
+// Segments are padded to the K step, so a step never straddles two exponents.
+// Tiles are dealt to the 8 XCDs (hardware order w % 8) in contiguous runs of a
+// grouped order (groups of 4 tile rows), so the workgroups sharing an XCD's L2
+// share A and B panels.
 #include "common.h"
 #include "kernels.h"
 
@@ -36,21 +36,21 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 128, BK = 128;
+constexpr int FR = 2;  // 32-row A fragments per wave
+constexpr int BM = 128 * FR, BN = 128, BK = 128;
 constexpr int kThreads = 256;
 constexpr int BSTR = BK + 16;  // LDS bytes per staged B row
-constexpr int kGroupM = 8;     // tile rows per ordering group
+constexpr int kGroupM = 4;     // tile rows per ordering group
 constexpr int kXcds = 8;
-constexpr int kDepth = 2;     // K steps of A and B in flight per thread
 static_assert(BK == kKPad, "a K step must not straddle exponent segments");
 
 struct TileCoord {
   int tm, tn;
 };
 
-// Workgroup w of a launch over tiles_m x tiles_n tiles -> its tile.  Hardware
-// deals workgroups to XCDs round-robin (w % 8); XCD x gets the contiguous run of
-// tile ids [start(x), start(x) + count(x)) in grouped order.
+// Workgroup w of a launch over tiles_m x tiles_n tiles -> its tile.  XCD
+// x = w % 8 gets the contiguous run of ids [start(x), start(x) + count(x)) of the
+// order (group of kGroupM tile rows, column, row).
 __device__ inline TileCoord tile_of(int w, int tiles_m, int tiles_n) {
   const int T = tiles_m * tiles_n;
   const int x = w % kXcds, slot = w / kXcds;
@@ -63,13 +63,45 @@ __device__ inline TileCoord tile_of(int w, int tiles_m, int tiles_n) {
   return TileCoord{first_m + in % gm, in / gm};
 }
 
-__device__ inline void shift_acc(v16i (&acc)[2][4], int sh) {
+__device__ inline void shift_acc(v16i (&acc)[FR][4], int sh) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FR; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = sh >= 32 ? 0 : (int)((uint32_t)acc[i][j][r] << sh);
+}
+
+// Position in the walk over K' steps: segment s (walked from the highest
+// exponent down, empty segments skipped), K' offset k of the step and the end
+// of its segment.  The segment table is read through the constant address
+// space: the GEMM never writes it, so the loads are scalar and the cursors stay
+// in SGPRs (vector loads here would make the compiler wait for the operand
+// prefetches as well).
+struct Cursor {
+  int s;
+  int64_t k, end;
+};
+typedef __attribute__((address_space(4))) const int64_t* SegTable;
+__device__ inline void cursor_advance(Cursor& c, SegTable off) {
+  c.k += BK;
+  if (c.k >= c.end && c.s > 0) {
+    --c.s;
+    while (c.s > 0 && off[c.s] == off[c.s + 1]) --c.s;
+    c.k = off[c.s];
+    c.end = off[c.s + 1];
+    // finish the scalar loads here: left pending, they would make the loop
+    // wait on lgkmcnt(0) every step, which also drains the LDS reads in flight
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+  }
+}
+__device__ inline Cursor cursor_top(int nseg, SegTable off) {
+  Cursor c;
+  c.s = nseg - 1;
+  while (c.s > 0 && off[c.s] == off[c.s + 1]) --c.s;
+  c.k = off[c.s];
+  c.end = off[c.s + 1];
+  return c;
 }
 
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
@@ -85,131 +117,148 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t kp = g.k_pad;
-  const int64_t row0 = (int64_t)tc.tm * BM + wave * 64, col0 = (int64_t)tc.tn * BN;
+  const int64_t row0 = (int64_t)tc.tm * BM + wave * (32 * FR), col0 = (int64_t)tc.tn * BN;
   const int shift = g.bits - 1;
 
-  // A' is in fragment order: fragment f (rows row0 + 32f ..) of K substep q at
-  // step k is the contiguous 1 KB at block (row0/32 + f, k/32 + q); lane l holds
-  // bytes [16l, 16l + 16) of it.
+  // A' fragment f (rows row0 + 32f ..) of K substep q at step offset k is the
+  // contiguous 1 KB at block (row0/32 + f, k/32 + q); lane l holds bytes
+  // [16l, 16l + 16) of it.
   const int8_t* ga = g.a_u + frag_row_offset(row0, kp) + lane * 16;
-  const int64_t ga_f1 = (kp >> 5) * 1024;
+  const int64_t ga_f = (kp >> 5) * 1024;
   // B staging: thread copies rows br + 32j (j < 4), bytes [bc, bc + 16) of the step
   const int br = tid >> 3, bc = (tid & 7) * 16;
   const int8_t* gb = g.b_u + (col0 + br) * kp + bc;
   const int64_t gb_j = 32 * kp;
   const int sb_w = br * BSTR + bc;
-  // B fragment j (columns col0 + 32j + lane%32), substep q
+  // B fragment j (columns col0 + 32j + lane%32) of substep q
   const int sb_r = (lane & 31) * BSTR + 16 * (lane >> 5);
+  const int64_t k_last = kp - BK;  // loads past the walk re-read the last step (never used)
 
-  v16i acc[2][4];
+  v16i acc[FR][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FR; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16i{0};
 
-  // Segment cursors (wave-uniform): segments run from the highest exponent
-  // down; empty segments are skipped but still count in the shifts.
-  const int nseg = ph->n_seg;
-  const int64_t* off = ph->seg_off;
+  const SegTable off = (SegTable)ph->seg_off;
+  const int nseg = ((__attribute__((address_space(4))) const PlanHeader*)ph)->n_seg;
   const int64_t steps = kp / BK;
-  int ls = nseg - 1;  // load cursor
-  while (ls > 0 && off[ls] == off[ls + 1]) --ls;
-  int64_t lk = off[ls], lend = off[ls + 1];
-  int cs = ls;  // compute cursor
-  int64_t ck = lk, cend = lend;
-  auto advance = [&](int& s, int64_t& k, int64_t& end) {
-    k += BK;
-    if (k >= end && s > 0) {
-      --s;
-      while (s > 0 && off[s] == off[s + 1]) --s;
-      k = off[s];
-      end = off[s + 1];
-    }
-  };
+  Cursor cc = cursor_top(nseg, off);  // compute
+  Cursor la = cc, lb = cc;            // A loads (one step ahead), B loads (two ahead)
 
-  // Register ring over kDepth K steps: slot t holds the A fragments and the B
-  // staging registers of the steps j with j % kDepth == t, loaded kDepth steps
-  // before their use.  Loads past the last step re-read the last step (they
-  // stay unconditional so the ring stays in registers); that data is never used.
-  const int64_t k_last = kp - BK;
-  v4i ar[kDepth][4][2];
-  v4i bs[kDepth][4];
-#define IMU_LOAD(t)                                                                          \
-  {                                                                                          \
-    const int64_t k_ = min64(lk, k_last);                                                    \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                          \
-      ar[t][q][0] = *reinterpret_cast<const v4i*>(ga + k_ * 32 + 1024 * q);                  \
-      ar[t][q][1] = *reinterpret_cast<const v4i*>(ga + ga_f1 + k_ * 32 + 1024 * q);          \
-    }                                                                                        \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[t][j] =                                 \
-        *reinterpret_cast<const v4i*>(gb + j * gb_j + k_);                                   \
-    advance(ls, lk, lend);                                                                   \
+  v4i ar[4][FR];  // A fragments of the current step, refilled substep by substep
+  v4i bs[4];      // B staging registers
+  v4i bf[2][4];   // B fragments, double-buffered by substep
+#define IMU_LOAD_A(q, k)                                                                       \
+  {                                                                                            \
+    const int64_t k_ = min64((k), k_last);                                                     \
+    _Pragma("unroll") for (int f = 0; f < FR; ++f) ar[q][f] =                                  \
+        *reinterpret_cast<const v4i*>(ga + f * ga_f + k_ * 32 + 1024 * (q));                   \
   }
-#define IMU_STORE_B(t, buf) \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(&sB[buf][sb_w + j * 32 * BSTR]) = bs[t][j];
-#define IMU_STEP(t)                                                                              \
-  if (i0 + t < steps) {                                                                          \
-    const int64_t j_ = i0 + t;                                                                   \
-    if (cs != prev_s) {                                                                          \
-      shift_acc(acc, shift * (prev_s - cs));                                                     \
-      prev_s = cs;                                                                               \
-    }                                                                                            \
-    const int8_t* sbuf = sB[j_ & 1];                                                             \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                              \
-      v4i bf[4];                                                                                 \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) bf[j] =                                      \
-          *reinterpret_cast<const v4i*>(sbuf + sb_r + j * 32 * BSTR + 32 * q);                   \
-      _Pragma("unroll") for (int f = 0; f < 2; ++f)                                              \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
-        acc[f][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[t][q][f], bf[j], acc[f][j], 0, 0, 0); \
-    }                                                                                            \
-    IMU_STORE_B((t + 1) % kDepth, (j_ + 1) & 1);                                                 \
-    IMU_LOAD(t);                                                                                 \
-    __syncthreads();                                                                             \
-    advance(cs, ck, cend);                                                                       \
+#define IMU_LOAD_B(k)                                                                          \
+  {                                                                                            \
+    const int64_t k_ = min64((k), k_last);                                                     \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gb + j * gb_j + k_); \
   }
+#define IMU_STORE_B(buf) \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(&sB[buf][sb_w + j * 32 * BSTR]) = bs[j];
+#define IMU_READ_B(d, sbuf, q) \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) bf[d][j] = *reinterpret_cast<const v4i*>((sbuf) + sb_r + j * 32 * BSTR + 32 * (q));
+#define IMU_MFMA(d, q)                                                                             \
+  _Pragma("unroll") for (int f = 0; f < FR; ++f)                                                   \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
+    acc[f][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[q][f], bf[d][j], acc[f][j], 0, 0, 0);
 
-  static_assert(kDepth == 2, "the ring below is written out for two slots");
-  IMU_LOAD(0);
-  IMU_LOAD(1);
-  IMU_STORE_B(0, 0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) IMU_LOAD_A(q, la.k);
+  cursor_advance(la, off);
+  IMU_LOAD_B(lb.k);
+  cursor_advance(lb, off);
+  IMU_STORE_B(0);
+  IMU_LOAD_B(lb.k);
+  cursor_advance(lb, off);
   __syncthreads();
-  int prev_s = cs;
-  for (int64_t i0 = 0; i0 < steps; i0 += kDepth) {
-    IMU_STEP(0);
-    IMU_STEP(1);
+  IMU_READ_B(0, sB[0], 0);
+  int prev_s = cc.s;
+  for (int64_t i = 0; i < steps; ++i) {
+    if (cc.s != prev_s) {  // Horner: the exponents between the two segments
+      shift_acc(acc, shift * (prev_s - cc.s));
+      prev_s = cc.s;
+    }
+    const int8_t* sbuf = sB[i & 1];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      IMU_READ_B((q + 1) & 1, sbuf, q + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      IMU_MFMA(q & 1, q);
+      IMU_LOAD_A(q, la.k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    IMU_STORE_B((i + 1) & 1);  // B of step i+1 (loaded during step i-1)
+    IMU_LOAD_B(lb.k);          // B of step i+2
+    cursor_advance(lb, off);
+    __syncthreads();
+    IMU_READ_B(0, sB[(i + 1) & 1], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    IMU_MFMA(1, 3);
+    IMU_LOAD_A(3, la.k);
+    __builtin_amdgcn_sched_barrier(0);
+    cursor_advance(la, off);
+    cursor_advance(cc, off);
   }
-#undef IMU_LOAD
+#undef IMU_LOAD_A
+#undef IMU_LOAD_B
 #undef IMU_STORE_B
-#undef IMU_STEP
+#undef IMU_READ_B
+#undef IMU_MFMA
   if (prev_s > 0) shift_acc(acc, shift * prev_s);  // exponents below the last non-empty segment
 
   // epilogue: accumulator register r of lane l holds element
-  // (8*(r/4) + 4*(l/32) + r%4, l%32) of each 32x32 block
+  // (8*(r/4) + 4*(l/32) + r%4, l%32) of each 32x32 block.  Rows are visited one
+  // at a time (f, r/4, r%4) with the four column blocks j of the row, so only a
+  // row's pointers are live.
   const float sab = g.sa->s * g.sb->s;
+  const int64_t ldc = g.ldc;
+  const int64_t r_lane = row0 + 4 * (lane >> 5), c_lane = col0 + (lane & 31);
+  if (g.mode == 2) {  // extra tiles: every element lands on some C[i, n] with its shift
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < FR; ++f)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t gr = row0 + f * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t gc = col0 + j * 32 + (lane & 31);
-        const int32_t v = acc[f][j][r];
-        if (g.mode == 2) {
+        for (int r = 0; r < 16; ++r) {
+          const int64_t gr = r_lane + f * 32 + 8 * (r >> 2) + (r & 3);
+          const int64_t gc = c_lane + j * 32;
           const int32_t am = g.amap[gr], bm = g.bmap[gc];
           if (am < 0 || bm < 0) continue;
           const int sh = shift * ((am >> 24) + (bm >> 24));
           if (sh >= 32) continue;
-          atomicAdd(&g.c[(int64_t)(am & 0xFFFFFF) * g.ldc + (bm & 0xFFFFFF)], (int)((uint32_t)v << sh));
-        } else {
-          if (gr >= g.M || gc >= g.N) continue;
-          int32_t* cp = &g.c[gr * g.ldc + gc];
-          const int32_t cv = g.mode == 1 ? (int32_t)((uint32_t)*cp + (uint32_t)v) : v;
-          *cp = cv;
-          if (g.out) g.out[gr * g.ldc + gc] = (float)cv * sab;
+          atomicAdd(&g.c[(int64_t)(am & 0xFFFFFF) * ldc + (bm & 0xFFFFFF)], (int)((uint32_t)acc[f][j][r] << sh));
+        }
+    return;
+  }
+#pragma unroll
+  for (int f = 0; f < FR; ++f)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+#pragma unroll
+      for (int r3 = 0; r3 < 4; ++r3) {
+        const int r = 4 * r4 + r3;
+        const int64_t gr = r_lane + f * 32 + 8 * r4 + r3;
+        if (gr >= g.M) continue;
+        int32_t* crow = g.c + gr * ldc + c_lane;
+        float* orow = g.out ? g.out + gr * ldc + c_lane : nullptr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (c_lane + 32 * j >= g.N) continue;
+          const int32_t v = acc[f][j][r];
+          const int32_t cv = g.mode == 1 ? (int32_t)((uint32_t)crow[32 * j] + (uint32_t)v) : v;
+          crow[32 * j] = cv;
+          if (orow) orow[32 * j] = (float)cv * sab;
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 }  // namespace

@@ -72,6 +72,56 @@ __device__ inline int load8_bits(const typename Elem<DT>::T* row, int64_t c0, in
   return n;
 }
 
+// The same in two halves, so that the loads of the next rows can be in flight
+// while the current rows are processed: load_raw issues the loads (same
+// clamping as above) into a vector value (bf16: pairs packed low/high as in
+// memory), bits8 widens them once they are needed.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v8u __attribute__((ext_vector_type(8)));
+template <int DT>
+struct RawOf {
+  using V = v8u;
+};
+template <>
+struct RawOf<IMU_BF16> {
+  using V = v4u;
+};
+template <int DT>
+__device__ __forceinline__ typename RawOf<DT>::V load_raw(const typename Elem<DT>::T* row, int64_t c0,
+                                                          int64_t scols, int vec_ok) {
+  typename RawOf<DT>::V u = 0;
+  if (vec_ok) {
+    const int64_t cc = c0 < scols ? c0 : scols - 8;
+    const uint4 a = *reinterpret_cast<const uint4*>(row + cc);
+    u.s0 = a.x; u.s1 = a.y; u.s2 = a.z; u.s3 = a.w;
+    if constexpr (DT == IMU_F32) {
+      const uint4 b = *reinterpret_cast<const uint4*>(row + cc + 4);
+      u.s4 = b.x; u.s5 = b.y; u.s6 = b.z; u.s7 = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t c = min64(c0 + j, scols - 1);
+      if constexpr (DT == IMU_BF16) u[j >> 1] |= (uint32_t)row[c] << (16 * (j & 1));
+      else u[j] = __float_as_uint(row[c]);
+    }
+  }
+  return u;
+}
+template <int DT>
+__device__ __forceinline__ void bits8(typename RawOf<DT>::V u, uint32_t (&w)[8]) {
+  if constexpr (DT == IMU_BF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = u[j] << 16;
+      w[2 * j + 1] = u[j] & 0xFFFF0000u;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = u[j];
+  }
+}
+
 // Sum over the wave of a per-lane value in [0, 16), by bit planes of ballots.
 __device__ inline int wave_sum_small(int v) {
   int s = 0;
@@ -389,54 +439,71 @@ __global__ __launch_bounds__(kCountThreads) void round_count_kernel(QuantJobs J,
     if (qo) qb = qo + b * R * C;
   }
   const bool tile_whole = cbase + kColsPerTile <= a.scols;  // no element of this tile is past the row
-  for (int64_t sb = r0 + (int64_t)wave * kRowsInFlight; sb < r1; sb += (int64_t)nwave * kRowsInFlight) {
-    uint32_t w[kRowsInFlight][8];
-    int n[kRowsInFlight];
-#pragma unroll
-    for (int rr = 0; rr < kRowsInFlight; ++rr) {
-      const int got = load8_bits<DT>(xb + min64(sb + rr, r1 - 1) * a.ld, c0, a.scols, a.vec_ok, w[rr]);
-      n[rr] = sb + rr < r1 ? got : 0;
-    }
-#pragma unroll
-    for (int rr = 0; rr < kRowsInFlight; ++rr) {
-      const int64_t sr = sb + rr;
-      if (sr >= r1) continue;  // uniform across the wave
-      int lc = 0;
-      float lm = 0.f;
-      auto elem = [&](int j) {
-        const float y = __uint_as_float(w[rr][j]) * r;
-        const float ay = __builtin_fabsf(y);
-        const int o = ay >= kThr;
-        lc += o;
-        lm = __builtin_fmaxf(lm, ay);
-        ccnt[j] += o;
-        cmax[j] = __builtin_fmaxf(cmax[j], ay);
-        if (QOUT && qb) {
-          const int64_t c = c0 + j;
-          const int32_t q = ay < 2147483648.0f ? (int32_t)__builtin_rintf(y) : 0;
-          if (!a.transposed) qb[sr * C + c] = q;
-          else qb[c * R + sr] = q;
-        }
-      };
-      if (tile_whole) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) elem(j);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j < n[rr]) elem(j);
+  const int nin = (int)min64(max64(a.scols - c0, 0), 8);      // this lane's elements inside a row
+  // rows of one group: kRowsInFlight consecutive stored rows per wave; two
+  // groups alternate so that one group's loads fly while the other is counted
+#define IMU_ISSUE(g, sb_)                                                                          \
+  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr)                                      \
+      g[rr] = load_raw<DT>(xb + min64((sb_) + rr, r1 - 1) * a.ld, c0, a.scols, a.vec_ok);
+  // per row: RTN of its elements, out-of-range count and largest digit count;
+  // columns keep their counts and maxima in registers
+  auto row_stats = [&](const uint32_t (&w)[8], int64_t sr) __attribute__((always_inline)) {
+    int lc = 0;
+    float lm = 0.f;
+    auto elem = [&](int j) {
+      const float y = __uint_as_float(w[j]) * r;
+      const float ay = __builtin_fabsf(y);
+      const int o = ay >= kThr;
+      lc += o;
+      lm = __builtin_fmaxf(lm, ay);
+      ccnt[j] += o;
+      cmax[j] = __builtin_fmaxf(cmax[j], ay);
+      if (QOUT && qb) {
+        const int64_t c = c0 + j;
+        const int32_t q = ay < 2147483648.0f ? (int32_t)__builtin_rintf(y) : 0;
+        if (!a.transposed) qb[sr * C + c] = q;
+        else qb[c * R + sr] = q;
       }
-      amax = __builtin_fmaxf(amax, lm);
-      const int ld = lm < 2147483648.0f ? digits_of_max<BITS>(lm) : 1;
-      const int rc = wave_sum_small(lc);
-      const int rm = wave_max_small(ld);
-      if (lane == 0) {
-        if (rc) atomicAdd(&srow_oob[sr], rc);
-        atomicMax(&srow_max[sr], rm);
-        tot += rc;
-      }
+    };
+    if (tile_whole) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) elem(j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < nin) elem(j);
     }
+    amax = __builtin_fmaxf(amax, lm);
+    const int ld = lm < 2147483648.0f ? digits_of_max<BITS>(lm) : 1;
+    const int rc = wave_sum_small(lc);
+    const int rm = wave_max_small(ld);
+    if (lane == 0) {
+      if (rc) atomicAdd(&srow_oob[sr], rc);
+      atomicMax(&srow_max[sr], rm);
+      tot += rc;
+    }
+  };
+#define IMU_PROCESS(g, sb_)                                                                        \
+  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                   \
+    if ((sb_) + rr < r1) { /* uniform across the wave */                                           \
+      uint32_t w[8];                                                                               \
+      bits8<DT>(g[rr], w);                                                               \
+      row_stats(w, (sb_) + rr);                                                                    \
+    }                                                                                              \
   }
+  const int64_t gstep = (int64_t)nwave * kRowsInFlight;
+  typename RawOf<DT>::V g0[kRowsInFlight], g1[kRowsInFlight];
+  int64_t sb = r0 + (int64_t)wave * kRowsInFlight;
+  IMU_ISSUE(g0, sb);
+  for (; sb < r1; sb += 2 * gstep) {
+    IMU_ISSUE(g1, sb + gstep);
+    IMU_PROCESS(g0, sb);
+    if (sb + gstep >= r1) break;
+    IMU_ISSUE(g0, sb + 2 * gstep);
+    IMU_PROCESS(g1, sb + gstep);
+  }
+#undef IMU_ISSUE
+#undef IMU_PROCESS
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (cmax[j] >= 0.f) {
@@ -650,7 +717,7 @@ static hipError_t round_count_dt(int bits, const QuantJobs& J, int grid, int32_t
 }
 
 hipError_t launch_round_count(int dtype, int bits, QuantJobs J, int32_t* q0, int32_t* q1, hipStream_t s) {
-  const int grid = plan_tiles(J, 256);
+  const int grid = plan_tiles(J, 512);
   return dtype == IMU_BF16 ? round_count_dt<IMU_BF16>(bits, J, grid, q0, q1, s)
                            : round_count_dt<IMU_F32>(bits, J, grid, q0, q1, s);
 }
