@@ -86,11 +86,23 @@ __device__ inline uint32_t code_word(float x, float r) {
 
 // Two's-complement byte of the signed digit whose magnitude starts at bit sh1
 // of the sign-magnitude word w (sh1 = 1 + t (BITS-1) <= 31).
+// digit_signed leaves garbage above the low byte (callers that pack bytes with
+// v_perm only take the low byte).
 template <int BITS>
-__device__ inline uint32_t digit_byte(uint32_t w, uint32_t sh1) {
+__device__ inline uint32_t digit_signed(uint32_t w, uint32_t sh1) {
   const uint32_t d = (w >> sh1) & ((1u << (BITS - 1)) - 1u);
   const uint32_t sm = 0u - (w & 1u);
-  return ((d ^ sm) - sm) & 0xFFu;
+  return (d ^ sm) - sm;
+}
+template <int BITS>
+__device__ inline uint32_t digit_byte(uint32_t w, uint32_t sh1) {
+  return digit_signed<BITS>(w, sh1) & 0xFFu;
+}
+
+// A 64-bit value that every thread holds alike, as a scalar.
+__device__ inline int64_t uniform64(int64_t v) {
+  return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)v));
 }
 
 // Byte offset of entry b's unpacked operand in the buffer (entries in batch
@@ -234,6 +246,13 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
         rowoff[tid] = row < 0 ? (int64_t)-1 : is_a ? frag_row_offset(row, kp) : row * kp;
       }
       __syncthreads();
+      // row offsets as scalars (the same for every thread): held in SGPRs for
+      // 16 lines, re-read from LDS per use for 64
+      constexpr int LR = L <= 16 ? L : 1;
+      int64_t ros_s[LR];
+#pragma unroll
+      for (int i = 0; i < LR; ++i) ros_s[i] = uniform64(rowoff[i]);
+#define IMU_RO(i) (L <= 16 ? ros_s[(i) % LR] : uniform64(rowoff[i]))
       const int gtot = s_pre[nseg];
       for (int gb = 0; gb < gtot; gb += kThreads * kInFlight) {
         // table entries of up to kInFlight groups per thread, loads first
@@ -273,27 +292,34 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
             adr[c] = ok ? (uint32_t)slot(kk) : kZero;
             sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
           }
-          const bool full = inr[0] && inr[3];
-          const int64_t pos = is_a ? frag_pos_offset(4 * g) : 4 * g;
-#pragma unroll 8
-          for (int i = 0; i < L; ++i) {
-            const int64_t ro = rowoff[i];
-            if (ro < 0) continue;
-            const uint32_t* cl = codes + i * LS;
-            uint32_t dw = 0;
+          const uint32_t pos = (uint32_t)(is_a ? frag_pos_offset(4 * g) : 4 * g);
+          if (inr[0] && inr[3]) {  // the whole dword lies in the range: one store per line
 #pragma unroll
-            for (int c = 0; c < 4; ++c) dw |= digit_byte<BITS>(cl[adr[c]], sh[c]) << (8 * c);
-            int8_t* dst = out + ro + pos;
-            if (full) {
-              *reinterpret_cast<uint32_t*>(dst) = dw;
-            } else {
+            for (int i = 0; i < L; ++i) {
+              const int64_t ro = IMU_RO(i);
+              if (ro < 0) continue;  // uniform: row offsets are scalar
+              const uint32_t* cl = codes + i * LS;
+              const uint32_t b0 = digit_signed<BITS>(cl[adr[0]], sh[0]), b1 = digit_signed<BITS>(cl[adr[1]], sh[1]);
+              const uint32_t b2 = digit_signed<BITS>(cl[adr[2]], sh[2]), b3 = digit_signed<BITS>(cl[adr[3]], sh[3]);
+              // low bytes of b0..b3 -> bytes 0..3
+              const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u), hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+              *reinterpret_cast<uint32_t*>(out + ro + pos) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            }
+          } else {  // a window or range boundary cuts the dword: byte stores
+#pragma unroll 4
+            for (int i = 0; i < L; ++i) {
+              const int64_t ro = IMU_RO(i);
+              if (ro < 0) continue;
+              const uint32_t* cl = codes + i * LS;
+              int8_t* dst = out + ro + pos;
 #pragma unroll
               for (int c = 0; c < 4; ++c)
-                if (inr[c]) dst[c] = (int8_t)(uint8_t)(dw >> (8 * c));
+                if (inr[c]) dst[c] = (int8_t)(uint8_t)digit_byte<BITS>(cl[adr[c]], sh[c]);
             }
           }
         }
       }
+#undef IMU_RO
       __syncthreads();  // before rowoff and the segment ranges are rewritten
     }
   }
