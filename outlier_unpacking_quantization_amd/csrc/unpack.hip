@@ -41,6 +41,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTargetWgs = 2048;  // workgroups aimed for per launch (8 per CU)
 constexpr int kInFlight = 4;      // table loads a thread issues before using them
+constexpr uint32_t kDrop = 0x80000000u;     // store offset past any buffer: the store is dropped
+constexpr int kBufferFlags = 0x00020000;    // buffer descriptor word 3 (raw byte-addressed access)
 
 template <bool OC>
 struct Shape {
@@ -155,6 +157,11 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
   const int64_t start = entry_offset(a.plan, (int)gridDim.z, b, a.operand, a.after_a != 0);
   if (start < 0 || start + unpacked_entry_bytes(ph, a.operand) > a.cap) return;
   int8_t* out = a.out + start;
+  // this entry's bytes as a buffer when 32-bit offsets reach all of it
+  const int64_t entry_bytes = unpacked_entry_bytes(ph, a.operand);
+  const bool use_buf = entry_bytes < (int64_t)kDrop;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(out, (short)0, use_buf ? (int)entry_bytes : 0, kBufferFlags);
   const int64_t kp = ph->k_pad;
   const int nseg = ph->n_seg;
   const int tid = threadIdx.x;
@@ -171,7 +178,19 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
 
   for (int64_t w = w_begin; w < w_end; ++w) {
     const int64_t kw0 = w * W, kw1 = min64(kw0 + W, K);
+    const bool last_win = kw1 == K;
     __syncthreads();  // readers of the previous window are done
+    // Loads that do not depend on the staged codes are issued first, so one
+    // memory round trip covers them and the staging: this window's K' range of
+    // every segment, and the level-0 rows of the lines.
+    int64_t P0 = 0, P1 = 0;
+    if (tid < nseg) {
+      const int32_t* kps = kpre + (int64_t)tid * (K + 1);
+      P0 = s_off[tid] + kps[kw0];
+      P1 = last_win ? s_off[tid + 1] : s_off[tid] + kps[kw1];
+    }
+    int64_t row_u0 = -1;
+    if (tid < L && s_dout[tid] > 0) row_u0 = lvl[o0 + tid];
     if constexpr (!OC) {
       constexpr int G = W / 8;  // groups of 8 k per line
       constexpr int kIter = L * G / kThreads;
@@ -215,37 +234,31 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
         codes[i * LS + slot(kk)] = code_word(load_elem<DT>(xb + o * a.so + k * a.sk), r);
       }
     }
-    __syncthreads();
     // this window's K' positions: per segment the range [P0, P1), as groups of
     // 4 positions flattened over the segments (s_pre: first flat group of each
     // segment), so that all segments' groups are spread over all threads
-    const bool last_win = kw1 == K;
     if (tid <= nseg) {
-      int64_t P0 = 0, P1 = 0;
-      if (tid < nseg) {
-        const int32_t* kps = kpre + (int64_t)tid * (K + 1);
-        P0 = s_off[tid] + kps[kw0];
-        P1 = last_win ? s_off[tid + 1] : s_off[tid] + kps[kw1];
-      }
       s_p0[tid] = P0;
       s_p1[tid] = P1;
       s_ng[tid] = P1 > P0 ? (int)(((P1 + 3) >> 2) - (P0 >> 2)) : 0;
     }
+    if (tid < L) rowoff[tid] = row_u0 < 0 ? (int64_t)-1 : is_a ? frag_row_offset(row_u0, kp) : row_u0 * kp;
     __syncthreads();
-    if (tid == 0) {
+    if (tid <= nseg) {
       int run = 0;
-      for (int q = 0; q < nseg; ++q) {
-        s_pre[q] = run;
-        run += s_ng[q];
-      }
-      s_pre[nseg] = run;
+      for (int q = 0; q < tid; ++q) run += s_ng[q];
+      s_pre[tid] = run;
     }
+    __syncthreads();
     for (int u = 0; u < umax; ++u) {
-      if (tid < L) {
-        const int64_t row = s_dout[tid] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + o0 + tid] : (int64_t)-1;
-        rowoff[tid] = row < 0 ? (int64_t)-1 : is_a ? frag_row_offset(row, kp) : row * kp;
+      if (u > 0) {  // rows of the unpacked levels (rare): one more round trip each
+        __syncthreads();  // readers of the previous level's rowoff are done
+        if (tid < L) {
+          const int64_t row = s_dout[tid] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + o0 + tid] : (int64_t)-1;
+          rowoff[tid] = row < 0 ? (int64_t)-1 : is_a ? frag_row_offset(row, kp) : row * kp;
+        }
+        __syncthreads();
       }
-      __syncthreads();
       // row offsets as scalars (the same for every thread): held in SGPRs for
       // 16 lines, re-read from LDS per use for 64
       constexpr int LR = L <= 16 ? L : 1;
@@ -293,19 +306,48 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
             sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
           }
           const uint32_t pos = (uint32_t)(is_a ? frag_pos_offset(4 * g) : 4 * g);
-          if (inr[0] && inr[3]) {  // the whole dword lies in the range: one store per line
+          const bool full = inr[0] && inr[3];  // the whole dword lies in the range
+          if (use_buf) {
+            // Buffer stores at 32-bit offsets into this entry; absent rows and
+            // bytes outside the range get an offset past the end, which the
+            // hardware drops, so the lines form one branch-free block in which
+            // the LDS reads of later lines overlap the work on earlier ones.
+            if (full) {
+#pragma unroll(L <= 16 ? L : 8)
+              for (int i = 0; i < L; ++i) {
+                const int64_t ro = IMU_RO(i);
+                const uint32_t o = ro < 0 ? kDrop : (uint32_t)ro + pos;
+                const uint32_t* cl = codes + i * LS;
+                const uint32_t b0 = digit_signed<BITS>(cl[adr[0]], sh[0]), b1 = digit_signed<BITS>(cl[adr[1]], sh[1]);
+                const uint32_t b2 = digit_signed<BITS>(cl[adr[2]], sh[2]), b3 = digit_signed<BITS>(cl[adr[3]], sh[3]);
+                // low bytes of b0..b3 -> bytes 0..3
+                const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u), hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(hi, lo, 0x05040100u), rs, (int)o, 0, 0);
+              }
+            } else {
+#pragma unroll 4
+              for (int i = 0; i < L; ++i) {
+                const int64_t ro = IMU_RO(i);
+                const uint32_t* cl = codes + i * LS;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                  const uint32_t o = ro < 0 || !inr[c] ? kDrop : (uint32_t)ro + pos + c;
+                  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)digit_signed<BITS>(cl[adr[c]], sh[c]), rs, (int)o, 0, 0);
+                }
+              }
+            }
+          } else if (full) {  // entries of 2 GB and more: pointer stores, one line at a time
 #pragma unroll
             for (int i = 0; i < L; ++i) {
               const int64_t ro = IMU_RO(i);
               if (ro < 0) continue;  // uniform: row offsets are scalar
               const uint32_t* cl = codes + i * LS;
-              const uint32_t b0 = digit_signed<BITS>(cl[adr[0]], sh[0]), b1 = digit_signed<BITS>(cl[adr[1]], sh[1]);
-              const uint32_t b2 = digit_signed<BITS>(cl[adr[2]], sh[2]), b3 = digit_signed<BITS>(cl[adr[3]], sh[3]);
-              // low bytes of b0..b3 -> bytes 0..3
-              const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u), hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
-              *reinterpret_cast<uint32_t*>(out + ro + pos) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+              uint32_t dw = 0;
+#pragma unroll
+              for (int c = 0; c < 4; ++c) dw |= digit_byte<BITS>(cl[adr[c]], sh[c]) << (8 * c);
+              *reinterpret_cast<uint32_t*>(out + ro + pos) = dw;
             }
-          } else {  // a window or range boundary cuts the dword: byte stores
+          } else {
 #pragma unroll 4
             for (int i = 0; i < L; ++i) {
               const int64_t ro = IMU_RO(i);
