@@ -93,7 +93,7 @@ static_assert(offsetof(PlanHeader, seg_len) == 1000, "plan header layout");
 
 // The planner splits the lines (rows of A, columns of B, then k) into chunks
 // of kPlanLines, one workgroup each; every workgroup keeps a record.
-constexpr int kPlanLines = 1024;
+constexpr int kPlanLines = 512;
 constexpr int kPlanTasks = 64;  // >= max levels and >= max segments
 struct PlanWgRecord {
   long long sum[24];       // candidate sizes: M'[4], N'[4], K'[4][4] of this chunk

@@ -224,7 +224,7 @@ __device__ void phase_sums(const PlanArgs& a, int b, int64_t w, PlanShared& S) {
   if (w == 0 && t == 0)  // status of this plan; later failures are OR-ed in
     E.ph->status = (int32_t)(reinterpret_cast<const StatsHeader*>(a.stats_a + b * a.stats_stride_a)->status |
                              reinterpret_cast<const StatsHeader*>(a.stats_b + b * a.stats_stride_b)->status);
-  // a chunk's shares fit 32 bits (1024 lines, depths <= 32); only its kind's
+  // a chunk's shares fit 32 bits (kPlanLines lines, depths <= 32); only its kind's
   // 4 (rows, columns) or 16 (k) sums are non-zero
   int acc[16];
 #pragma unroll

@@ -325,32 +325,43 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
       if ((k >> 8) == prefix) atomicAdd(&h[k & 0xFFu], 1u);
     }
   };
-  for (int64_t ub = u0 + (int64_t)wave * kRowsInFlight; ub < u1; ub += (int64_t)nwave * kRowsInFlight) {
-    uint32_t w[kRowsInFlight][8];
-    int n[kRowsInFlight];
-    bool whole[kRowsInFlight];  // wave-uniform: the whole 512-column tile lies inside the row
-#pragma unroll
-    for (int r = 0; r < kRowsInFlight; ++r) {
-      const uint32_t u = (uint32_t)min64(ub + r, u1 - 1);  // clamped: loads stay unconditional
-      const uint32_t sr = u / ctiles, ct = u - sr * ctiles;
-      const int got = load8_bits<DT>(xb + (int64_t)sr * a.ld, (int64_t)ct * kColsPerTile + lane * 8, a.scols,
-                                     a.vec_ok, w[r]);
-      const bool live = ub + r < u1;
-      n[r] = live ? got : 0;
-      whole[r] = live && (int64_t)(ct + 1) * kColsPerTile <= a.scols;
-    }
-#pragma unroll
-    for (int r = 0; r < kRowsInFlight; ++r) {
-      if (whole[r]) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) count(w[r][j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j < n[r]) count(w[r][j]);
-      }
-    }
+  // two groups of kRowsInFlight units alternate: one group's loads fly while
+  // the other is counted
+  const int64_t ustep = (int64_t)nwave * kRowsInFlight;
+  typename RawOf<DT>::V g0[kRowsInFlight], g1[kRowsInFlight];
+#define IMU_ISSUE(g, ub_)                                                                          \
+  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                    \
+    const uint32_t u_ = (uint32_t)min64((ub_) + rr, u1 - 1); /* clamped: loads stay unconditional */ \
+    const uint32_t sr_ = u_ / ctiles, ct_ = u_ - sr_ * ctiles;                                      \
+    g[rr] = load_raw<DT>(xb + (int64_t)sr_ * a.ld, (int64_t)ct_ * kColsPerTile + lane * 8, a.scols, a.vec_ok); \
   }
+#define IMU_PROCESS(g, ub_)                                                                        \
+  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                   \
+    if ((ub_) + rr < u1) { /* uniform across the wave */                                           \
+      const uint32_t u_ = (uint32_t)((ub_) + rr);                                                  \
+      const uint32_t sr_ = u_ / ctiles, ct_ = u_ - sr_ * ctiles;                                   \
+      const int64_t c0_ = (int64_t)ct_ * kColsPerTile + lane * 8;                                  \
+      uint32_t w[8];                                                                               \
+      bits8<DT>(g[rr], w);                                                                         \
+      if ((int64_t)(ct_ + 1) * kColsPerTile <= a.scols) { /* the whole tile lies inside the row */ \
+        _Pragma("unroll") for (int j = 0; j < 8; ++j) count(w[j]);                                 \
+      } else {                                                                                     \
+        const int n_ = (int)min64(max64(a.scols - c0_, 0), 8);                                     \
+        _Pragma("unroll") for (int j = 0; j < 8; ++j) if (j < n_) count(w[j]);                     \
+      }                                                                                            \
+    }                                                                                              \
+  }
+  int64_t ub = u0 + (int64_t)wave * kRowsInFlight;
+  IMU_ISSUE(g0, ub);
+  for (; ub < u1; ub += 2 * ustep) {
+    IMU_ISSUE(g1, ub + ustep);
+    IMU_PROCESS(g0, ub);
+    if (ub + ustep >= u1) break;
+    IMU_ISSUE(g0, ub + 2 * ustep);
+    IMU_PROCESS(g1, ub + ustep);
+  }
+#undef IMU_ISSUE
+#undef IMU_PROCESS
   if (PASS == 0) {
     mx = wave_max_u32(mx);
     bad = wave_max_i32(bad);
@@ -570,42 +581,56 @@ __global__ __launch_bounds__(kResidualThreads) void residual_kernel(QuantJobs J)
 #pragma unroll
   for (int j = 0; j < 8; ++j) cmax[j] = -1.f;
   const bool tile_whole = cbase + kColsPerTile <= a.scols;
-  for (int64_t sb = r0 + (int64_t)wave * kRowsInFlight; sb < r1; sb += (int64_t)nwave * kRowsInFlight) {
-    uint32_t w[kRowsInFlight][8];
-    int n[kRowsInFlight];
-    bool rowheavy[kRowsInFlight];
-#pragma unroll
-    for (int rr = 0; rr < kRowsInFlight; ++rr) {
-      const bool ok = sb + rr < r1;
-      const int64_t sr = min64(sb + rr, r1 - 1);
-      const int got = load8_bits<DT>(xb + sr * a.ld, c0, a.scols, a.vec_ok, w[rr]);
-      const int oob = srow_oob[sr];
-      n[rr] = ok ? got : 0;
-      rowheavy[rr] = ok && (long long)oob * a.srows > gT;
-    }
-#pragma unroll
-    for (int rr = 0; rr < kRowsInFlight; ++rr) {
-      const int64_t sr = sb + rr;
-      if (sr >= r1) continue;  // uniform across the wave
-      float lm = -1.f;
-      auto elem = [&](int j) {
-        const float ay = __builtin_fabsf(__uint_as_float(w[rr][j]) * r);
-        if (!colheavy[j]) lm = __builtin_fmaxf(lm, ay);
-        if (!rowheavy[rr]) cmax[j] = __builtin_fmaxf(cmax[j], ay);
-      };
-      if (tile_whole) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) elem(j);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j < n[rr]) elem(j);
-      }
-      const int ld = lm < 0.f ? 0 : (lm < 2147483648.0f ? digits_of_max<BITS>(lm) : 1);
-      const int rm = wave_max_small(ld);
-      if (lane == 0 && rm) atomicMax(&srow_res[sr], rm);
-    }
+  const int nin = (int)min64(max64(a.scols - c0, 0), 8);  // this lane's elements inside a row
+  // two groups of kRowsInFlight rows alternate: one group's loads (elements
+  // and row counts) fly while the other is reduced
+#define IMU_ISSUE(g, oob, sb_)                                                                     \
+  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                    \
+    const int64_t sr_ = min64((sb_) + rr, r1 - 1);                                                  \
+    g[rr] = load_raw<DT>(xb + sr_ * a.ld, c0, a.scols, a.vec_ok);                                   \
+    oob[rr] = srow_oob[sr_];                                                                        \
   }
+  auto row_res = [&](const uint32_t (&w)[8], int64_t sr, bool rowheavy) __attribute__((always_inline)) {
+    float lm = -1.f;
+    auto elem = [&](int j) {
+      const float ay = __builtin_fabsf(__uint_as_float(w[j]) * r);
+      if (!colheavy[j]) lm = __builtin_fmaxf(lm, ay);
+      if (!rowheavy) cmax[j] = __builtin_fmaxf(cmax[j], ay);
+    };
+    if (tile_whole) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) elem(j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < nin) elem(j);
+    }
+    const int ld = lm < 0.f ? 0 : (lm < 2147483648.0f ? digits_of_max<BITS>(lm) : 1);
+    const int rm = wave_max_small(ld);
+    if (lane == 0 && rm) atomicMax(&srow_res[sr], rm);
+  };
+#define IMU_PROCESS(g, oob, sb_)                                                                   \
+  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                   \
+    if ((sb_) + rr < r1) { /* uniform across the wave */                                           \
+      uint32_t w[8];                                                                               \
+      bits8<DT>(g[rr], w);                                                                         \
+      row_res(w, (sb_) + rr, (long long)oob[rr] * a.srows > gT);                                   \
+    }                                                                                              \
+  }
+  const int64_t gstep = (int64_t)nwave * kRowsInFlight;
+  typename RawOf<DT>::V g0[kRowsInFlight], g1[kRowsInFlight];
+  int o0[kRowsInFlight], o1[kRowsInFlight];
+  int64_t sb = r0 + (int64_t)wave * kRowsInFlight;
+  IMU_ISSUE(g0, o0, sb);
+  for (; sb < r1; sb += 2 * gstep) {
+    IMU_ISSUE(g1, o1, sb + gstep);
+    IMU_PROCESS(g0, o0, sb);
+    if (sb + gstep >= r1) break;
+    IMU_ISSUE(g0, o0, sb + 2 * gstep);
+    IMU_PROCESS(g1, o1, sb + gstep);
+  }
+#undef IMU_ISSUE
+#undef IMU_PROCESS
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     if (cmax[j] >= 0.f) atomicMax(&lmax[lane * 8 + j], __float_as_uint(cmax[j]) + 1u);
