@@ -279,9 +279,9 @@ imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, 
 
 // Unpack one operand; M, K, N give the plan layout.  after_a: B' entries start
 // after all A' entries of x_u; cap: bytes available at x_u.
-imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, const uint8_t* stats,
+UnpackArgs unpack_args(const Operand& op, int operand, const imu_params* p, const uint8_t* stats,
                        const uint8_t* plan, int64_t M, int64_t K, int64_t N, int8_t* x_u, bool after_a,
-                       int64_t cap, hipStream_t s) {
+                       int64_t cap) {
   const StatsLayout L = stats_layout(op.R, op.C);
   const imu_matrix* x = op.m;
   UnpackArgs u{};
@@ -310,7 +310,14 @@ imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, cons
   u.out = x_u;
   u.after_a = after_a ? 1 : 0;
   u.cap = cap;
-  IMU_HIP(launch_unpack(op.dtype, p->bits, u, (int)x->batch, s));
+  return u;
+}
+
+imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, const uint8_t* stats,
+                       const uint8_t* plan, int64_t M, int64_t K, int64_t N, int8_t* x_u, bool after_a,
+                       int64_t cap, hipStream_t s) {
+  const UnpackArgs u = unpack_args(op, operand, p, stats, plan, M, K, N, x_u, after_a, cap);
+  IMU_HIP(launch_unpack(op.dtype, p->bits, &u, 1, (int)op.m->batch, s));
   return IMU_OK;
 }
 
@@ -524,8 +531,14 @@ imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const i
   IMU_TRY(stage_headers(plan, (size_t)batch * kPlanHeaderStride, stream, &hdrs));
   int8_t* region = reinterpret_cast<int8_t*>(w + fixed);
   const int64_t cap = (int64_t)ws_bytes - fixed;
-  IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap, stream));
-  IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap, stream));
+  if (oa.dtype == ob.dtype) {  // both operands in one launch
+    const UnpackArgs u[2] = {unpack_args(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap),
+                             unpack_args(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap)};
+    IMU_HIP(launch_unpack(oa.dtype, p->bits, u, 2, (int)batch, stream));
+  } else {
+    IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap, stream));
+    IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap, stream));
+  }
   IMU_HIP(hipEventSynchronize(g_stage.ev));
   int64_t a_bytes = 0, b_bytes = 0;
   IMU_TRY(finish_plan(oa, ob, hdrs, (int)batch, info, &a_bytes, &b_bytes));

@@ -46,7 +46,10 @@ struct UnpackArgs {
   int after_a;                  // 1: B' entries follow all A' entries of the buffer
   int64_t cap;                  // bytes available at out; entries that would not fit are skipped
 };
-hipError_t launch_unpack(int dtype, int bits, const UnpackArgs& a, int batch, hipStream_t s);
+// Operands of one dtype share a launch: launch_unpack takes one or two
+// UnpackArgs (A then B) and launches them together when their staging shape
+// matches (both inner-contiguous or both outer-contiguous), else one each.
+hipError_t launch_unpack(int dtype, int bits, const UnpackArgs* ops, int nops, int batch, hipStream_t s);
 
 // gemm.hip
 struct GemmArgs {

@@ -123,8 +123,25 @@ __device__ inline int64_t entry_offset(const uint8_t* plan, int batch, int b, in
   return off;
 }
 
+// The operands of one launch: workgroups [0, wgs[0]) serve op[0], the rest
+// op[1]; inside an operand, workgroup w covers line block w % nblk and window
+// group w / nblk (wpg windows each).
+struct UnpackJobs {
+  UnpackArgs op[2];
+  int nops;
+  int nblk[2], wgs[2], wpg[2];
+};
+
 template <int DT, int BITS, bool OC>
-__global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins_per_wg) {
+__global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
+  int bid = blockIdx.x, jo = 0;
+  if (J.nops > 1 && bid >= J.wgs[0]) {
+    bid -= J.wgs[0];
+    jo = 1;
+  }
+  const UnpackArgs& a = J.op[jo];
+  const int wins_per_wg = J.wpg[jo];
+  const int blk_x = bid % J.nblk[jo], blk_y = bid / J.nblk[jo];
   using T = typename Elem<DT>::T;
   constexpr int L = Shape<OC>::L, W = Shape<OC>::W, LS = Shape<OC>::LS;
   constexpr int D = (31 + BITS - 2) / (BITS - 1);
@@ -137,9 +154,9 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
   __shared__ int s_ng[kMaxSeg + 1], s_pre[kMaxSeg + 1];
 
   const int b = blockIdx.z;
-  const int64_t o0 = (int64_t)blockIdx.x * L;
+  const int64_t o0 = (int64_t)blk_x * L;
   const int64_t K = a.K, nwin = ceil_div(K, W);
-  const int64_t w_begin = (int64_t)blockIdx.y * wins_per_wg;
+  const int64_t w_begin = (int64_t)blk_y * wins_per_wg;
   const int64_t w_end = min64(w_begin + wins_per_wg, nwin);
   if (w_begin >= w_end) return;
   const T* xb = static_cast<const T*>(a.x) + b * a.bstride;
@@ -368,16 +385,31 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a, int wins
 }
 
 template <int DT, bool OC>
-hipError_t unpack_launch(int bits, const UnpackArgs& a, int batch, hipStream_t s) {
+hipError_t unpack_launch(int bits, const UnpackArgs* ops, int nops, int batch, hipStream_t s) {
   constexpr int L = Shape<OC>::L, W = Shape<OC>::W;
-  const int64_t nblk = ceil_div(a.n_outer, L), nwin = ceil_div(a.K, W);
-  const int64_t want_y = min64(nwin, max64(1, ceil_div(kTargetWgs, nblk * batch)));
-  const int64_t wpg = ceil_div(nwin, want_y);
-  dim3 grid((unsigned)nblk, (unsigned)ceil_div(nwin, wpg), (unsigned)batch);
+  UnpackJobs J{};
+  J.nops = nops;
+  int64_t total = 0;
+  for (int o = 0; o < nops; ++o) {
+    const UnpackArgs& a = ops[o];
+    J.op[o] = a;
+    const int64_t nblk = ceil_div(a.n_outer, L), nwin = ceil_div(a.K, W);
+    const int64_t want_y = min64(nwin, max64(1, ceil_div(kTargetWgs, nblk * batch)));
+    const int64_t wpg = ceil_div(nwin, want_y);
+    const int64_t wgs = nblk * ceil_div(nwin, wpg);
+    if (wgs > 0x3FFFFFFF || wpg > 0x7FFFFFFF) return hipErrorInvalidValue;
+    J.nblk[o] = (int)nblk;
+    J.wpg[o] = (int)wpg;
+    J.wgs[o] = (int)wgs;
+    total += wgs;
+  }
+  if (total == 0) return hipSuccess;
+  if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid((unsigned)total, 1, (unsigned)batch);
   switch (bits) {
 #define IMU_UP(B)                                                                                     \
   case B:                                                                                             \
-    hipLaunchKernelGGL((unpack_kernel<DT, B, OC>), grid, dim3(kThreads), 0, s, a, (int)wpg);          \
+    hipLaunchKernelGGL((unpack_kernel<DT, B, OC>), grid, dim3(kThreads), 0, s, J);                    \
     break;
     IMU_UP(2) IMU_UP(3) IMU_UP(4) IMU_UP(5) IMU_UP(6) IMU_UP(7) IMU_UP(8)
 #undef IMU_UP
@@ -388,14 +420,22 @@ hipError_t unpack_launch(int bits, const UnpackArgs& a, int batch, hipStream_t s
 }
 
 template <int DT>
-hipError_t unpack_dt(int bits, const UnpackArgs& a, int batch, hipStream_t s) {
-  return a.sk == 1 ? unpack_launch<DT, false>(bits, a, batch, s) : unpack_launch<DT, true>(bits, a, batch, s);
+hipError_t unpack_dt(int bits, const UnpackArgs* ops, int nops, int batch, hipStream_t s) {
+  // operands with the same staging shape share a launch
+  if (nops == 2 && (ops[0].sk == 1) != (ops[1].sk == 1)) {
+    hipError_t e = unpack_dt<DT>(bits, ops, 1, batch, s);
+    return e != hipSuccess ? e : unpack_dt<DT>(bits, ops + 1, 1, batch, s);
+  }
+  return ops[0].sk == 1 ? unpack_launch<DT, false>(bits, ops, nops, batch, s)
+                        : unpack_launch<DT, true>(bits, ops, nops, batch, s);
 }
 
 }  // namespace
 
-hipError_t launch_unpack(int dtype, int bits, const UnpackArgs& a, int batch, hipStream_t s) {
-  return dtype == IMU_BF16 ? unpack_dt<IMU_BF16>(bits, a, batch, s) : unpack_dt<IMU_F32>(bits, a, batch, s);
+hipError_t launch_unpack(int dtype, int bits, const UnpackArgs* ops, int nops, int batch, hipStream_t s) {
+  if (nops < 1 || nops > 2) return hipErrorInvalidValue;
+  return dtype == IMU_BF16 ? unpack_dt<IMU_BF16>(bits, ops, nops, batch, s)
+                           : unpack_dt<IMU_F32>(bits, ops, nops, batch, s);
 }
 
 }  // namespace imu
