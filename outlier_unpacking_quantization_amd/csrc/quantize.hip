@@ -12,12 +12,14 @@
 // all batch entries: a small job table gives each (operand, entry) a contiguous
 // range of workgroups.
 //
-// The statistics are formed in the float domain, which gives the same integers
-// as rounding every element: with y = fl32(x r) and S = 2^(bits-1) (even),
-// rne(y) needs two or more digits iff |y| >= S - 1/2, and the largest digit
-// count of a line is the digit count of rne(max |y|) (rne and the digit count
-// are monotone in |y|).  Row reductions use wave ballots; column reductions
-// stay in registers, then LDS, then one global atomic per column per workgroup.
+// The statistics give the same integers as rounding every element: with
+// y = fl32(x r) and S = 2^(bits-1) (even), rne(y) needs two or more digits iff
+// |y| >= S - 1/2, and the largest digit count of a line is the digit count of
+// rne(max |y|) (rne and the digit count are monotone in |y|).  Since
+// fl32(|x| r) is itself monotone in |x|, both are decided on integer magnitude
+// keys (see "magnitude keys" below) with one product per line.  Row reductions
+// use DPP; column reductions stay in registers, then LDS, then one global
+// atomic per column per workgroup.
 //
 // Percentile: one pass builds an exact 32768-bin histogram of the 15-bit
 // magnitude key per workgroup in LDS (128 KB), flushes the non-zero bins with
@@ -36,46 +38,13 @@ constexpr int kRowsInFlight = 4;   // row loads issued per wave before use
 constexpr int kCountThreads = 512;    // threads of the counting kernel (tiles are 512 columns wide)
 constexpr int kResidualThreads = 256; // threads of the residual kernel
 
-// Raw 32-bit patterns (fp32 bits; bf16 widened) of the 8 elements starting at
-// column c0 of a stored row, and how many of them lie inside the row.  The
-// loads are unconditional (indices clamped into the row) so that a caller can
-// issue several rows' loads back to back; elements past the row are garbage
-// and must be ignored through the returned count.
-template <int DT>
-__device__ inline int load8_bits(const typename Elem<DT>::T* row, int64_t c0, int64_t scols, int vec_ok,
-                                 uint32_t w[8]) {
-  const int n = (int)min64(max64(scols - c0, 0), 8);
-  if (vec_ok) {  // scols % 8 == 0: a lane's 8 elements are all inside or all outside
-    const int64_t cc = n ? c0 : scols - 8;
-    if constexpr (DT == IMU_BF16) {
-      const uint4 u = *reinterpret_cast<const uint4*>(row + cc);
-      const uint32_t p[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[2 * j] = p[j] << 16;
-        w[2 * j + 1] = p[j] & 0xFFFF0000u;
-      }
-    } else {
-      const uint4 a = *reinterpret_cast<const uint4*>(row + cc);
-      const uint4 b = *reinterpret_cast<const uint4*>(row + cc + 4);
-      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-      w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    }
-    return n;
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t c = min64(c0 + j, scols - 1);
-    if constexpr (DT == IMU_BF16) w[j] = (uint32_t)row[c] << 16;
-    else w[j] = __float_as_uint(row[c]);
-  }
-  return n;
-}
-
-// The same in two halves, so that the loads of the next rows can be in flight
-// while the current rows are processed: load_raw issues the loads (same
-// clamping as above) into a vector value (bf16: pairs packed low/high as in
-// memory), bits8 widens them once they are needed.
+// Raw 32-bit patterns of the 8 elements starting at column c0 of a stored row,
+// in two halves, so that the loads of the next rows can be in flight while the
+// current rows are processed: load_raw issues the loads into a vector value
+// (bf16: pairs packed low/high as in memory; fp32: the bits), bits8 widens
+// them (bf16 to fp32 bits) once they are needed.  The loads are unconditional
+// (indices clamped into the row) so that several rows' loads can be issued
+// back to back; elements past the row are garbage for the caller to ignore.
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v8u __attribute__((ext_vector_type(8)));
 template <int DT>
@@ -86,11 +55,15 @@ template <>
 struct RawOf<IMU_BF16> {
   using V = v4u;
 };
-template <int DT>
+// VEC (scols % 8 == 0 and aligned rows): one 16-byte load (two for fp32) per
+// lane; otherwise 8 element loads.  A compile-time choice, so that the
+// compiler can count the loads in flight exactly (a run-time branch between
+// the two makes it wait for all of them before any use).
+template <int DT, bool VEC>
 __device__ __forceinline__ typename RawOf<DT>::V load_raw(const typename Elem<DT>::T* row, int64_t c0,
-                                                          int64_t scols, int vec_ok) {
+                                                          int64_t scols) {
   typename RawOf<DT>::V u = 0;
-  if (vec_ok) {
+  if constexpr (VEC) {
     const int64_t cc = c0 < scols ? c0 : scols - 8;
     const uint4 a = *reinterpret_cast<const uint4*>(row + cc);
     u.s0 = a.x; u.s1 = a.y; u.s2 = a.z; u.s3 = a.w;
@@ -120,22 +93,6 @@ __device__ __forceinline__ void bits8(typename RawOf<DT>::V u, uint32_t (&w)[8])
 #pragma unroll
     for (int j = 0; j < 8; ++j) w[j] = u[j];
   }
-}
-
-// Sum over the wave of a per-lane value in [0, 16), by bit planes of ballots.
-__device__ inline int wave_sum_small(int v) {
-  int s = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) s += __popcll(__ballot((v >> b) & 1)) << b;
-  return s;
-}
-// Max over the wave of a per-lane value in [0, 32), bit by bit from the top.
-__device__ inline int wave_max_small(int v) {
-  int m = 0;
-#pragma unroll
-  for (int bit = 16; bit > 0; bit >>= 1)
-    if (__ballot(v >= m + bit)) m += bit;
-  return m;
 }
 
 // Digit count of rne(a) for a = max |x r| >= 0 (a finite and below 2^31).
@@ -280,8 +237,125 @@ __device__ void select_from_hist(uint8_t* st, int64_t hist_off, int64_t nelem, i
   }
 }
 
+// --- magnitude keys ---------------------------------------------------------
+// For r >= 0, fl32(|x| r) is non-decreasing in |x|, and so is the digit count
+// of its rounding.  The statistics therefore need no product per element:
+// rne(x r) is out of range exactly when |x| is at least the smallest
+// magnitude whose product reaches 2^(bits-1) - 1/2, and the largest digit
+// count of a line is the digit count of its largest |x| (one product per
+// line).  Magnitudes are compared as integer keys, the bit pattern without the
+// sign (which orders non-negative floats): bf16 keys have 15 bits and sit two
+// to a dword (packed 16-bit arithmetic), fp32 keys have 31.
+typedef uint16_t v2u16 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pk_add_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2u16, a) + __builtin_bit_cast(v2u16, b));
+}
+__device__ inline uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(v2u16, a), __builtin_bit_cast(v2u16, b)));
+}
+
+template <int DT>
+struct KeyOps {  // fp32: one 31-bit key per dword
+  static constexpr int NW = 8;  // dwords of a lane's 8 elements
+  static constexpr int NB = 31;
+  static constexpr uint32_t kMask = 0x7FFFFFFFu;
+  static __device__ float value(uint32_t k) { return __uint_as_float(k); }
+};
+template <>
+struct KeyOps<IMU_BF16> {  // bf16: two 15-bit keys per dword (element 2d low, 2d+1 high)
+  static constexpr int NW = 4;
+  static constexpr int NB = 15;
+  static constexpr uint32_t kMask = 0x7FFF7FFFu;
+  static __device__ float value(uint32_t k) { return __uint_as_float(k << 16); }
+};
+
+// Key masks of a lane whose first n of 8 elements lie inside the row.
+template <int DT>
+__device__ inline void key_masks(int n, uint32_t (&km)[KeyOps<DT>::NW]) {
+  if constexpr (DT == IMU_BF16) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) km[d] = (2 * d < n ? 0x7FFFu : 0u) | (2 * d + 1 < n ? 0x7FFF0000u : 0u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) km[j] = j < n ? 0x7FFFFFFFu : 0u;
+  }
+}
+
+// Smallest key k with fl32(value(k) r) >= thr (2^NB if there is none).  The
+// keys whose product stays below thr form a prefix of the key order (key 0 is
+// one of them: its product is 0), so its last element is found 6 bits at a
+// time, the 64 lanes trying the 64 values of the next 6 bits.
+template <int DT>
+__device__ inline uint32_t key_threshold(float r, float thr) {
+  constexpr int NB = KeyOps<DT>::NB;
+  const uint64_t lane = threadIdx.x & 63;
+  uint32_t p = 0;
+#pragma unroll
+  for (int s = (NB - 1) / 6 * 6; s >= 0; s -= 6) {
+    const uint64_t cand = p + (lane << s);
+    const bool under = cand < (1ull << NB) && KeyOps<DT>::value((uint32_t)cand) * r < thr;
+    p += (uint32_t)(__popcll(__ballot(under)) - 1) << s;
+  }
+  return p + 1;
+}
+
+// Reduction over the wave, returned as a scalar: butterflies inside each row
+// of 16 lanes (quad swaps, half-row and row mirrors), then the row broadcasts
+// leave the total in lane 63.  Rows the broadcast does not write receive 0,
+// the identity of the sums and maxima used here.
+#define IMU_DPP(v, ctrl, rows) (uint32_t) __builtin_amdgcn_update_dpp(0, (int)(v), ctrl, rows, 0xF, false)
+template <typename Op>
+__device__ inline uint32_t wave_reduce(uint32_t v, Op op) {
+  v = op(v, IMU_DPP(v, 0xB1, 0xF));   // lane ^ 1
+  v = op(v, IMU_DPP(v, 0x4E, 0xF));   // lane ^ 2
+  v = op(v, IMU_DPP(v, 0x141, 0xF));  // mirror inside 8 lanes
+  v = op(v, IMU_DPP(v, 0x140, 0xF));  // mirror inside 16 lanes
+  v = op(v, IMU_DPP(v, 0x142, 0xA));  // lane 15 of rows 0, 2 into rows 1, 3
+  v = op(v, IMU_DPP(v, 0x143, 0xC));  // lane 31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+#undef IMU_DPP
+struct AddU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct MaxU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+struct MaxPk16 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return pk_max_u16(a, b); }
+};
+
+// Wave-wide results of the kRowsInFlight = 4 rows of a group, as four
+// scalars.  Lane i (< 4) takes row i's value by selects on its lane bits, made
+// on values passed by value: selects between loads of one array or struct get
+// folded into an access indexed by lane, which the compiler stages in LDS.
+static_assert(kRowsInFlight == 4, "row groups of four");
+struct Row4 {
+  uint32_t v0, v1, v2, v3;
+};
+__device__ inline uint32_t pick4(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, int lane) {
+  return (lane & 2) ? ((lane & 1) ? v3 : v2) : ((lane & 1) ? v1 : v0);
+}
+#define IMU_PICK(r4, lane) pick4((r4).v0, (r4).v1, (r4).v2, (r4).v3, lane)
+// sums of per-lane counts below 2^16 / 64 (two rows to a dword)
+__device__ inline Row4 wave_sums4(const uint32_t (&c)[4]) {
+  const uint32_t a = wave_reduce(c[0] | c[1] << 16, AddU32()), b = wave_reduce(c[2] | c[3] << 16, AddU32());
+  return Row4{a & 0xFFFFu, a >> 16, b & 0xFFFFu, b >> 16};
+}
+template <int DT>
+__device__ inline Row4 wave_max_keys4(const uint32_t (&k)[4]) {
+  if constexpr (DT == IMU_BF16) {  // 15-bit keys, two rows to a dword
+    const uint32_t a = wave_reduce(k[0] | k[1] << 16, MaxPk16()), b = wave_reduce(k[2] | k[3] << 16, MaxPk16());
+    return Row4{a & 0xFFFFu, a >> 16, b & 0xFFFFu, b >> 16};
+  } else {
+    return Row4{wave_reduce(k[0], MaxU32()), wave_reduce(k[1], MaxU32()), wave_reduce(k[2], MaxU32()),
+                wave_reduce(k[3], MaxU32())};
+  }
+}
+
 // --- percentile histogram + fused selection ---------------------------------
-template <int DT, int NB, int PASS>
+template <int DT, int NB, int PASS, bool VEC>
 __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass) {
   using T = typename Elem<DT>::T;
   __shared__ uint32_t h[NB];
@@ -306,18 +380,18 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
   __syncthreads();
 
   const uint32_t prefix = PASS == 0 ? 0u : hd->sel_prefix;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, nwave = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // unit indices stay scalar
   // work units: (stored row, 512-column tile); this workgroup takes a contiguous share
   const uint32_t ctiles = (uint32_t)ceil_div(a.scols, kColsPerTile);
   const int64_t units = a.srows * (int64_t)ctiles;
   const int64_t u0 = units * jp.local / jp.count, u1 = units * (jp.local + 1) / jp.count;
-  uint32_t mx = 0;
-  int bad = 0;
+  uint32_t mx = 0;   // largest key (fp32 bit pattern without sign)
+  uint32_t mxp = 0;  // bf16: largest 15-bit keys of the packed path, two halves
   auto count = [&](uint32_t bits) {
     const uint32_t k = bits & 0x7FFFFFFFu;
     if constexpr (PASS == 0) {
       mx = max(mx, k);
-      bad |= (k >= 0x7F800000u);
       atomicAdd(&h[(k >> 16) & (NB - 1)], 1u);
     } else if constexpr (PASS == 1) {
       if ((k >> 16) == prefix) atomicAdd(&h[(k >> 8) & 0xFFu], 1u);
@@ -333,7 +407,7 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
   _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                    \
     const uint32_t u_ = (uint32_t)min64((ub_) + rr, u1 - 1); /* clamped: loads stay unconditional */ \
     const uint32_t sr_ = u_ / ctiles, ct_ = u_ - sr_ * ctiles;                                      \
-    g[rr] = load_raw<DT>(xb + (int64_t)sr_ * a.ld, (int64_t)ct_ * kColsPerTile + lane * 8, a.scols, a.vec_ok); \
+    g[rr] = load_raw<DT, VEC>(xb + (int64_t)sr_ * a.ld, (int64_t)ct_ * kColsPerTile + lane * 8, a.scols); \
   }
 #define IMU_PROCESS(g, ub_)                                                                        \
   _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                   \
@@ -344,7 +418,16 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
       uint32_t w[8];                                                                               \
       bits8<DT>(g[rr], w);                                                                         \
       if ((int64_t)(ct_ + 1) * kColsPerTile <= a.scols) { /* the whole tile lies inside the row */ \
-        _Pragma("unroll") for (int j = 0; j < 8; ++j) count(w[j]);                                 \
+        if constexpr (DT == IMU_BF16 && PASS == 0) { /* two 15-bit keys per dword */              \
+          _Pragma("unroll") for (int d = 0; d < 4; ++d) {                                          \
+            const uint32_t k_ = g[rr][d] & 0x7FFF7FFFu;                                            \
+            mxp = pk_max_u16(mxp, k_);                                                             \
+            atomicAdd(&h[k_ & 0xFFFFu], 1u);                                                       \
+            atomicAdd(&h[k_ >> 16], 1u);                                                           \
+          }                                                                                        \
+        } else {                                                                                   \
+          _Pragma("unroll") for (int j = 0; j < 8; ++j) count(w[j]);                               \
+        }                                                                                          \
       } else {                                                                                     \
         const int n_ = (int)min64(max64(a.scols - c0_, 0), 8);                                     \
         _Pragma("unroll") for (int j = 0; j < 8; ++j) if (j < n_) count(w[j]);                     \
@@ -363,11 +446,11 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
 #undef IMU_ISSUE
 #undef IMU_PROCESS
   if (PASS == 0) {
+    mx = max(mx, max(mxp & 0xFFFFu, mxp >> 16) << 16);
     mx = wave_max_u32(mx);
-    bad = wave_max_i32(bad);
     if (lane == 0) {
       atomicMax(&smax, mx);
-      if (bad) atomicOr(&sbad, 1);
+      if (mx >= 0x7F800000u) atomicOr(&sbad, 1);  // Inf or NaN
     }
   }
   __syncthreads();
@@ -396,15 +479,23 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
 }
 
 // --- fused RTN + outlier statistics -------------------------------------------
-// Tile: 512 stored columns x rows_per_wg stored rows.
-template <int DT, int BITS, bool QOUT>
+// Tile: 512 stored columns x rows_per_wg stored rows.  Per row a lane counts
+// its out-of-range keys and keeps their largest; the wave reduces a group of
+// kRowsInFlight rows at once (DPP) and lanes 0..3 post one row each.  Columns
+// keep counts and largest keys in registers (bf16: two columns per dword,
+// 16-bit counts, so a workgroup takes at most 65535 rows), then LDS, then one
+// global atomic per column per workgroup.  Codes, when asked for, are rounded
+// from the elements.
+template <int DT, int BITS, bool QOUT, bool VEC>
 __global__ __launch_bounds__(kCountThreads) void round_count_kernel(QuantJobs J, int32_t* q0, int32_t* q1) {
   using T = typename Elem<DT>::T;
+  using KO = KeyOps<DT>;
+  constexpr int NW = KO::NW;
   constexpr float kThr = (float)(1 << (BITS - 1)) - 0.5f;  // |y| >= kThr <=> rne(y) out of range
   __shared__ int lcnt[kColsPerTile];
-  __shared__ uint32_t lmax[kColsPerTile];  // max |y| as fp32 bits (monotone for y >= 0)
+  __shared__ uint32_t lmax[kColsPerTile];  // largest key + 1 (0: column not seen)
   __shared__ unsigned long long ltot;
-  __shared__ int lbad;
+  __shared__ uint32_t lamax;
   const JobPos jp = find_job(J, blockIdx.x);
   if (jp.count == 0) return;
   const QuantOp& op = J.op[jp.op];
@@ -419,30 +510,33 @@ __global__ __launch_bounds__(kCountThreads) void round_count_kernel(QuantJobs J,
   int32_t* scol_oob = reinterpret_cast<int32_t*>(st + a.scol_oob);
   int32_t* srow_max = reinterpret_cast<int32_t*>(st + a.srow_maxdig);
   int32_t* scol_max = reinterpret_cast<int32_t*>(st + a.scol_maxdig);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nwave = blockDim.x >> 6;
+  const int64_t cbase = ct * kColsPerTile;
+  const int64_t c0 = cbase + lane * 8;
+  const int64_t r0 = rb * op.rows_per_wg;
+  const int64_t r1 = min64(r0 + op.rows_per_wg, a.srows);
+  // the first two groups of rows are in flight while the workgroup sets up
+#define IMU_ISSUE(g, sb_)                                                                          \
+  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr)                                      \
+      g[rr] = load_raw<DT, VEC>(xb + min64((sb_) + rr, r1 - 1) * a.ld, c0, a.scols);
+  const int64_t gstep = (int64_t)nwave * kRowsInFlight;
+  typename RawOf<DT>::V g0[kRowsInFlight], g1[kRowsInFlight];
+  int64_t sb = r0 + (int64_t)wave * kRowsInFlight;
+  IMU_ISSUE(g0, sb);
+  IMU_ISSUE(g1, sb + gstep);
   for (int i = threadIdx.x; i < kColsPerTile; i += blockDim.x) {
     lcnt[i] = 0;
     lmax[i] = 0;
   }
   if (threadIdx.x == 0) {
     ltot = 0;
-    lbad = 0;
+    lamax = 0;
   }
   __syncthreads();
   const float r = hd->r;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  const int64_t cbase = ct * kColsPerTile;
-  const int64_t c0 = cbase + lane * 8;
-  const int64_t r0 = rb * op.rows_per_wg;
-  const int64_t r1 = min64(r0 + op.rows_per_wg, a.srows);
-  int ccnt[8];
-  float cmax[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    ccnt[j] = 0;
-    cmax[j] = -1.f;  // below any |y|; marks "no element seen"
-  }
-  int tot = 0;
-  float amax = 0.f;
+  const uint32_t kth = key_threshold<DT>(r, kThr);
+  const uint32_t cadd = (0x8000u - kth) * 0x10001u;  // bf16: a half of k + cadd reaches 0x8000 iff k >= kth
   const int64_t R = a.srows, C = a.scols;
   int32_t* qb = nullptr;  // codes of this operand, if they were asked for
   if constexpr (QOUT) {
@@ -451,102 +545,132 @@ __global__ __launch_bounds__(kCountThreads) void round_count_kernel(QuantJobs J,
   }
   const bool tile_whole = cbase + kColsPerTile <= a.scols;  // no element of this tile is past the row
   const int nin = (int)min64(max64(a.scols - c0, 0), 8);      // this lane's elements inside a row
-  // rows of one group: kRowsInFlight consecutive stored rows per wave; two
-  // groups alternate so that one group's loads fly while the other is counted
-#define IMU_ISSUE(g, sb_)                                                                          \
-  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr)                                      \
-      g[rr] = load_raw<DT>(xb + min64((sb_) + rr, r1 - 1) * a.ld, c0, a.scols, a.vec_ok);
-  // per row: RTN of its elements, out-of-range count and largest digit count;
-  // columns keep their counts and maxima in registers
-  auto row_stats = [&](const uint32_t (&w)[8], int64_t sr) __attribute__((always_inline)) {
-    int lc = 0;
-    float lm = 0.f;
-    auto elem = [&](int j) {
-      const float y = __uint_as_float(w[j]) * r;
-      const float ay = __builtin_fabsf(y);
-      const int o = ay >= kThr;
-      lc += o;
-      lm = __builtin_fmaxf(lm, ay);
-      ccnt[j] += o;
-      cmax[j] = __builtin_fmaxf(cmax[j], ay);
-      if (QOUT && qb) {
-        const int64_t c = c0 + j;
-        const int32_t q = ay < 2147483648.0f ? (int32_t)__builtin_rintf(y) : 0;
-        if (!a.transposed) qb[sr * C + c] = q;
-        else qb[c * R + sr] = q;
+  uint32_t km[NW];
+  key_masks<DT>(nin, km);
+  uint32_t ccnt[NW], cmx[NW];
+#pragma unroll
+  for (int d = 0; d < NW; ++d) {
+    ccnt[d] = 0;
+    cmx[d] = 0;
+  }
+  uint32_t amax = 0;  // largest key of the wave's rows
+  uint32_t tot = 0;   // out-of-range codes of the wave's rows
+  // one row: the lane's out-of-range count and largest key; column registers
+  // returns (count, largest key)
+  auto row_keys = [&](const typename RawOf<DT>::V& g, bool whole) __attribute__((always_inline)) {
+    uint32_t rc = 0, rm = 0;
+#pragma unroll
+    for (int d = 0; d < NW; ++d) {
+      const uint32_t k = g[d] & (whole ? KO::kMask : km[d]);
+      if constexpr (DT == IMU_BF16) {
+        const uint32_t m = pk_add_u16(k, cadd) & 0x80008000u;
+        rc += __popc(m);
+        ccnt[d] += m >> 15;
+        rm = pk_max_u16(rm, k);
+        cmx[d] = pk_max_u16(cmx[d], k);
+      } else {
+        const uint32_t o = k >= kth;
+        rc += o;
+        ccnt[d] += o;
+        rm = max(rm, k);
+        cmx[d] = max(cmx[d], k);
       }
-    };
-    if (tile_whole) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) elem(j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < nin) elem(j);
     }
-    amax = __builtin_fmaxf(amax, lm);
-    const int ld = lm < 2147483648.0f ? digits_of_max<BITS>(lm) : 1;
-    const int rc = wave_sum_small(lc);
-    const int rm = wave_max_small(ld);
-    if (lane == 0) {
-      if (rc) atomicAdd(&srow_oob[sr], rc);
-      atomicMax(&srow_max[sr], rm);
-      tot += rc;
+    if constexpr (DT == IMU_BF16) rm = max(rm & 0xFFFFu, rm >> 16);
+    return make_uint2(rc, rm);
+  };
+  auto row_codes = [&](const typename RawOf<DT>::V& g, int64_t sr) __attribute__((always_inline)) {
+    uint32_t w[8];
+    bits8<DT>(g, w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= nin) continue;
+      const float y = __uint_as_float(w[j]) * r;
+      const int32_t q = __builtin_fabsf(y) < 2147483648.0f ? (int32_t)__builtin_rintf(y) : 0;
+      const int64_t c = c0 + j;
+      if (!a.transposed) qb[sr * C + c] = q;
+      else qb[c * R + sr] = q;
     }
   };
+  // a group of rows: lane statistics, then wave totals posted by lanes 0..3
 #define IMU_PROCESS(g, sb_)                                                                        \
-  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                   \
-    if ((sb_) + rr < r1) { /* uniform across the wave */                                           \
-      uint32_t w[8];                                                                               \
-      bits8<DT>(g[rr], w);                                                               \
-      row_stats(w, (sb_) + rr);                                                                    \
+  {                                                                                                \
+    uint32_t rc_[kRowsInFlight], rm_[kRowsInFlight];                                               \
+    _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                 \
+      if ((sb_) + rr < r1) { /* uniform across the wave */                                         \
+        const uint2 v_ = row_keys(g[rr], tile_whole);                                              \
+        rc_[rr] = v_.x;                                                                            \
+        rm_[rr] = v_.y;                                                                            \
+        if (QOUT && qb) row_codes(g[rr], (sb_) + rr);                                              \
+      } else {                                                                                     \
+        rc_[rr] = 0;                                                                               \
+        rm_[rr] = 0;                                                                               \
+      }                                                                                            \
+    }                                                                                              \
+    const Row4 cnt_ = wave_sums4(rc_), key_ = wave_max_keys4<DT>(rm_);                             \
+    tot += cnt_.v0 + cnt_.v1 + cnt_.v2 + cnt_.v3;                                                  \
+    amax = max(amax, max(max(key_.v0, key_.v1), max(key_.v2, key_.v3)));                           \
+    if (lane < kRowsInFlight && (sb_) + lane < r1) {                                               \
+      const uint32_t c_ = IMU_PICK(cnt_, lane);                                                         \
+      const float f_ = KO::value(IMU_PICK(key_, lane)) * r;                                             \
+      if (c_) atomicAdd(&srow_oob[(sb_) + lane], (int)c_);                                         \
+      atomicMax(&srow_max[(sb_) + lane], f_ < 2147483648.0f ? digits_of_max<BITS>(f_) : 1);       \
     }                                                                                              \
   }
-  const int64_t gstep = (int64_t)nwave * kRowsInFlight;
-  typename RawOf<DT>::V g0[kRowsInFlight], g1[kRowsInFlight];
-  int64_t sb = r0 + (int64_t)wave * kRowsInFlight;
-  IMU_ISSUE(g0, sb);
+  // two groups alternate: one group's loads fly while the other is reduced
   for (; sb < r1; sb += 2 * gstep) {
-    IMU_ISSUE(g1, sb + gstep);
     IMU_PROCESS(g0, sb);
     if (sb + gstep >= r1) break;
-    IMU_ISSUE(g0, sb + 2 * gstep);
+    IMU_ISSUE(g0, sb + 2 * gstep);  // unconditional (rows clamped), so the loads in flight are known exactly
     IMU_PROCESS(g1, sb + gstep);
+    IMU_ISSUE(g1, sb + 3 * gstep);
   }
 #undef IMU_ISSUE
 #undef IMU_PROCESS
+  // columns: registers -> LDS (keys + 1, so that a seen column is non-zero)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (cmax[j] >= 0.f) {
-      if (ccnt[j]) atomicAdd(&lcnt[lane * 8 + j], ccnt[j]);
-      atomicMax(&lmax[lane * 8 + j], __float_as_uint(cmax[j]) + 1u);  // +1: seen even when |y| = 0
+  for (int d = 0; d < NW; ++d) {
+    if constexpr (DT == IMU_BF16) {
+      const int c = lane * 8 + 2 * d;
+      if (ccnt[d] & 0xFFFFu) atomicAdd(&lcnt[c], (int)(ccnt[d] & 0xFFFFu));
+      if (ccnt[d] >> 16) atomicAdd(&lcnt[c + 1], (int)(ccnt[d] >> 16));
+      atomicMax(&lmax[c], (cmx[d] & 0xFFFFu) + 1u);
+      atomicMax(&lmax[c + 1], (cmx[d] >> 16) + 1u);
+    } else {
+      const int c = lane * 8 + d;
+      if (ccnt[d]) atomicAdd(&lcnt[c], (int)ccnt[d]);
+      atomicMax(&lmax[c], cmx[d] + 1u);
     }
   }
-  if (lane == 0 && tot) atomicAdd(&ltot, (unsigned long long)tot);
-  if (!(amax < 2147483648.0f)) atomicOr(&lbad, 1);  // also catches NaN
+  if (lane == 0) {
+    if (tot) atomicAdd(&ltot, (unsigned long long)tot);
+    atomicMax(&lamax, amax);
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < kColsPerTile; i += blockDim.x) {
     const int64_t c = cbase + i;
     const uint32_t m = lmax[i];
     if (c < a.scols && m) {
-      const float cm = __uint_as_float(m - 1u);
+      const float f = KO::value(m - 1u) * r;
       if (lcnt[i]) atomicAdd(&scol_oob[c], lcnt[i]);
-      atomicMax(&scol_max[c], cm < 2147483648.0f ? digits_of_max<BITS>(cm) : 1);
+      atomicMax(&scol_max[c], f < 2147483648.0f ? digits_of_max<BITS>(f) : 1);
     }
   }
   if (threadIdx.x == 0) {
     if (ltot) atomicAdd(&hd->total, ltot);
-    if (lbad) atomicOr(&hd->status, kStatusRange);
+    if (KO::value(lamax) * r >= 2147483648.0f) atomicOr(&hd->status, kStatusRange);
   }
 }
 
 // --- Mix residual: largest digit count of each line outside heavy lines --------
 // A stored column is heavy when scol_oob * scols > gamma * T, a stored row when
 // srow_oob * srows > gamma * T.  srow_res gets the max over non-heavy columns,
-// scol_res the max over non-heavy rows.
-template <int DT, int BITS>
+// scol_res the max over non-heavy rows; both from largest keys, as above.
+template <int DT, int BITS, bool VEC>
 __global__ __launch_bounds__(kResidualThreads) void residual_kernel(QuantJobs J) {
   using T = typename Elem<DT>::T;
+  using KO = KeyOps<DT>;
+  constexpr int NW = KO::NW;
   __shared__ uint32_t lmax[kColsPerTile];
   const JobPos jp = find_job(J, blockIdx.x);
   if (jp.count == 0) return;
@@ -558,89 +682,115 @@ __global__ __launch_bounds__(kResidualThreads) void residual_kernel(QuantJobs J)
   const T* xb = static_cast<const T*>(a.x) + b * a.bstride;
   uint8_t* st = a.stats + b * a.stats_stride;
   const StatsHeader* hd = reinterpret_cast<const StatsHeader*>(st);
-  const int32_t* srow_oob = reinterpret_cast<const int32_t*>(st + a.srow_oob);
+  // row counts are read per row with uniform addresses: scalar loads (the
+  // counting kernel wrote them before this launch)
+  const __attribute__((address_space(4))) int32_t* srow_oob =
+      (const __attribute__((address_space(4))) int32_t*)(st + a.srow_oob);
   const int32_t* scol_oob = reinterpret_cast<const int32_t*>(st + a.scol_oob);
   int32_t* srow_res = reinterpret_cast<int32_t*>(st + a.srow_res);
   int32_t* scol_res = reinterpret_cast<int32_t*>(st + a.scol_res);
-  for (int i = threadIdx.x; i < kColsPerTile; i += blockDim.x) lmax[i] = 0;
-  __syncthreads();
-  const float r = hd->r;
-  const long long gT = (long long)a.gamma * (long long)hd->total;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nwave = blockDim.x >> 6;
   const int64_t cbase = ct * kColsPerTile;
   const int64_t c0 = cbase + lane * 8;
   const int64_t r0 = rb * op.rows_per_wg;
   const int64_t r1 = min64(r0 + op.rows_per_wg, a.srows);
-  bool colheavy[8];
+  // the first two groups of rows are in flight while the workgroup sets up
+#define IMU_ISSUE(g, sb_)                                                                          \
+  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr)                                      \
+      g[rr] = load_raw<DT, VEC>(xb + min64((sb_) + rr, r1 - 1) * a.ld, c0, a.scols);
+  const int64_t gstep = (int64_t)nwave * kRowsInFlight;
+  typename RawOf<DT>::V g0[kRowsInFlight], g1[kRowsInFlight];
+  int64_t sb = r0 + (int64_t)wave * kRowsInFlight;
+  IMU_ISSUE(g0, sb);
+  IMU_ISSUE(g1, sb + gstep);
+  for (int i = threadIdx.x; i < kColsPerTile; i += blockDim.x) lmax[i] = 0;
+  __syncthreads();
+  const float r = hd->r;
+  const long long gT = (long long)a.gamma * (long long)hd->total;
+  const int nin = (int)min64(max64(a.scols - c0, 0), 8);  // this lane's elements inside a row
+  uint32_t km[NW], lm[NW];  // key masks: elements inside the row; of those, the non-heavy columns
+  key_masks<DT>(nin, km);
+  bool light = false;  // the lane has a non-heavy column inside the row
+  int coob[8];          // column counts, loaded together (index clamped into the row)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) coob[j] = scol_oob[min64(c0 + j, a.scols - 1)];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t c = c0 + j;
-    colheavy[j] = c < a.scols && (long long)scol_oob[c] * a.scols > gT;
-  }
-  float cmax[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) cmax[j] = -1.f;
-  const bool tile_whole = cbase + kColsPerTile <= a.scols;
-  const int nin = (int)min64(max64(a.scols - c0, 0), 8);  // this lane's elements inside a row
-  // two groups of kRowsInFlight rows alternate: one group's loads (elements
-  // and row counts) fly while the other is reduced
-#define IMU_ISSUE(g, oob, sb_)                                                                     \
-  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                    \
-    const int64_t sr_ = min64((sb_) + rr, r1 - 1);                                                  \
-    g[rr] = load_raw<DT>(xb + sr_ * a.ld, c0, a.scols, a.vec_ok);                                   \
-    oob[rr] = srow_oob[sr_];                                                                        \
-  }
-  auto row_res = [&](const uint32_t (&w)[8], int64_t sr, bool rowheavy) __attribute__((always_inline)) {
-    float lm = -1.f;
-    auto elem = [&](int j) {
-      const float ay = __builtin_fabsf(__uint_as_float(w[j]) * r);
-      if (!colheavy[j]) lm = __builtin_fmaxf(lm, ay);
-      if (!rowheavy) cmax[j] = __builtin_fmaxf(cmax[j], ay);
-    };
-    if (tile_whole) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) elem(j);
+    const bool heavy = c < a.scols && (long long)coob[j] * a.scols > gT;
+    light |= j < nin && !heavy;
+    const uint32_t keep = heavy ? 0u : 0xFFFFFFFFu;
+    if constexpr (DT == IMU_BF16) {
+      if (j & 1) lm[j >> 1] = (lm[j >> 1] & 0xFFFFu) | (km[j >> 1] & keep & 0xFFFF0000u);
+      else lm[j >> 1] = km[j >> 1] & keep & 0xFFFFu;
     } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < nin) elem(j);
+      lm[j] = km[j] & keep;
     }
-    const int ld = lm < 0.f ? 0 : (lm < 2147483648.0f ? digits_of_max<BITS>(lm) : 1);
-    const int rm = wave_max_small(ld);
-    if (lane == 0 && rm) atomicMax(&srow_res[sr], rm);
-  };
-#define IMU_PROCESS(g, oob, sb_)                                                                   \
-  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                   \
-    if ((sb_) + rr < r1) { /* uniform across the wave */                                           \
-      uint32_t w[8];                                                                               \
-      bits8<DT>(g[rr], w);                                                                         \
-      row_res(w, (sb_) + rr, (long long)oob[rr] * a.srows > gT);                                   \
+  }
+  const bool rows_live = __ballot(light) != 0;  // some row residual is posted
+  uint32_t cmx[NW];
+#pragma unroll
+  for (int d = 0; d < NW; ++d) cmx[d] = 0;
+  bool col_seen = false;  // the wave took a non-heavy row
+#define IMU_PROCESS(g, sb_)                                                                        \
+  {                                                                                                \
+    uint32_t rm_[kRowsInFlight];                                                                   \
+    _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                 \
+      rm_[rr] = 0;                                                                                 \
+      if ((sb_) + rr < r1) { /* uniform across the wave */                                         \
+        const bool rheavy = (long long)srow_oob[(sb_) + rr] * a.srows > gT;                        \
+        uint32_t m_ = 0;                                                                           \
+        _Pragma("unroll") for (int d = 0; d < NW; ++d) {                                           \
+          if constexpr (DT == IMU_BF16) m_ = pk_max_u16(m_, g[rr][d] & lm[d]);                     \
+          else m_ = max(m_, g[rr][d] & lm[d]);                                                     \
+        }                                                                                          \
+        if (!rheavy) {                                                                             \
+          col_seen = true;                                                                         \
+          _Pragma("unroll") for (int d = 0; d < NW; ++d) {                                         \
+            if constexpr (DT == IMU_BF16) cmx[d] = pk_max_u16(cmx[d], g[rr][d] & km[d]);           \
+            else cmx[d] = max(cmx[d], g[rr][d] & km[d]);                                           \
+          }                                                                                        \
+        }                                                                                          \
+        if constexpr (DT == IMU_BF16) m_ = max(m_ & 0xFFFFu, m_ >> 16);                            \
+        rm_[rr] = m_;                                                                              \
+      }                                                                                            \
+    }                                                                                              \
+    if (rows_live) {                                                                               \
+      const Row4 key_ = wave_max_keys4<DT>(rm_);                                                   \
+      if (lane < kRowsInFlight && (sb_) + lane < r1) {                                             \
+        const float f_ = KO::value(IMU_PICK(key_, lane)) * r;                                           \
+        atomicMax(&srow_res[(sb_) + lane], f_ < 2147483648.0f ? digits_of_max<BITS>(f_) : 1);      \
+      }                                                                                            \
     }                                                                                              \
   }
-  const int64_t gstep = (int64_t)nwave * kRowsInFlight;
-  typename RawOf<DT>::V g0[kRowsInFlight], g1[kRowsInFlight];
-  int o0[kRowsInFlight], o1[kRowsInFlight];
-  int64_t sb = r0 + (int64_t)wave * kRowsInFlight;
-  IMU_ISSUE(g0, o0, sb);
   for (; sb < r1; sb += 2 * gstep) {
-    IMU_ISSUE(g1, o1, sb + gstep);
-    IMU_PROCESS(g0, o0, sb);
+    IMU_PROCESS(g0, sb);
     if (sb + gstep >= r1) break;
-    IMU_ISSUE(g0, o0, sb + 2 * gstep);
-    IMU_PROCESS(g1, o1, sb + gstep);
+    IMU_ISSUE(g0, sb + 2 * gstep);  // unconditional (rows clamped), so the loads in flight are known exactly
+    IMU_PROCESS(g1, sb + gstep);
+    IMU_ISSUE(g1, sb + 3 * gstep);
   }
 #undef IMU_ISSUE
 #undef IMU_PROCESS
+  if (col_seen) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (cmax[j] >= 0.f) atomicMax(&lmax[lane * 8 + j], __float_as_uint(cmax[j]) + 1u);
+    for (int d = 0; d < NW; ++d) {
+      if constexpr (DT == IMU_BF16) {
+        atomicMax(&lmax[lane * 8 + 2 * d], (cmx[d] & 0xFFFFu) + 1u);
+        atomicMax(&lmax[lane * 8 + 2 * d + 1], (cmx[d] >> 16) + 1u);
+      } else {
+        atomicMax(&lmax[lane * 8 + d], cmx[d] + 1u);
+      }
+    }
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < kColsPerTile; i += blockDim.x) {
     const int64_t c = cbase + i;
     const uint32_t m = lmax[i];
     if (c < a.scols && m) {
-      const float cm = __uint_as_float(m - 1u);
-      atomicMax(&scol_res[c], cm < 2147483648.0f ? digits_of_max<BITS>(cm) : 1);
+      const float f = KO::value(m - 1u) * r;
+      atomicMax(&scol_res[c], f < 2147483648.0f ? digits_of_max<BITS>(f) : 1);
     }
   }
 }
@@ -685,17 +835,30 @@ static int plan_hist(QuantJobs& J) {
   return begin;
 }
 
+// Whether every operand of a launch takes 16-byte row loads.
+static bool all_vec(const QuantJobs& J) {
+  bool v = true;
+  for (int o = 0; o < J.nops; ++o) v = v && J.op[o].s.vec_ok;
+  return v;
+}
+
+template <bool VEC>
+static void hist_vec(int dtype, const QuantJobs& J, int grid, int pass, int final_pass, hipStream_t s) {
+  if (dtype == IMU_BF16) {
+    hipLaunchKernelGGL((hist_kernel<IMU_BF16, kHistBins, 0, VEC>), dim3(grid), dim3(1024), 0, s, J, final_pass);
+  } else if (pass == 0) {
+    hipLaunchKernelGGL((hist_kernel<IMU_F32, kHistBins, 0, VEC>), dim3(grid), dim3(1024), 0, s, J, final_pass);
+  } else if (pass == 1) {
+    hipLaunchKernelGGL((hist_kernel<IMU_F32, 256, 1, VEC>), dim3(grid), dim3(1024), 0, s, J, final_pass);
+  } else {
+    hipLaunchKernelGGL((hist_kernel<IMU_F32, 256, 2, VEC>), dim3(grid), dim3(1024), 0, s, J, final_pass);
+  }
+}
+
 hipError_t launch_hist(int dtype, QuantJobs J, int pass, int final_pass, hipStream_t s) {
   const int grid = plan_hist(J);
-  if (dtype == IMU_BF16) {
-    hipLaunchKernelGGL((hist_kernel<IMU_BF16, kHistBins, 0>), dim3(grid), dim3(1024), 0, s, J, final_pass);
-  } else if (pass == 0) {
-    hipLaunchKernelGGL((hist_kernel<IMU_F32, kHistBins, 0>), dim3(grid), dim3(1024), 0, s, J, final_pass);
-  } else if (pass == 1) {
-    hipLaunchKernelGGL((hist_kernel<IMU_F32, 256, 1>), dim3(grid), dim3(1024), 0, s, J, final_pass);
-  } else {
-    hipLaunchKernelGGL((hist_kernel<IMU_F32, 256, 2>), dim3(grid), dim3(1024), 0, s, J, final_pass);
-  }
+  if (all_vec(J)) hist_vec<true>(dtype, J, grid, pass, final_pass, s);
+  else hist_vec<false>(dtype, J, grid, pass, final_pass, s);
   return hipGetLastError();
 }
 
@@ -712,7 +875,7 @@ static int plan_tiles(QuantJobs& J, int kCountWgs) {
     const int64_t want = max64((int64_t)(kCountWgs * el / total + 0.5), 1);  // workgroups for this operand
     int64_t rblocks = max64(want / (ctiles * q.batch), 1);
     int64_t rpw = ceil_div(q.s.srows, rblocks);
-    rpw = max64(rpw, 4);
+    rpw = min64(max64(rpw, 4), 32768);  // column counts of the bf16 path are 16-bit
     rblocks = ceil_div(q.s.srows, rpw);
     q.rows_per_wg = (int)rpw;
     q.wgs_per_entry = (int)(rblocks * ctiles);
@@ -728,10 +891,12 @@ static hipError_t round_count_dt(int bits, const QuantJobs& J, int grid, int32_t
   switch (bits) {
 #define IMU_RC(B)                                                                                  \
   case B:                                                                                          \
-    if (q0 || q1)                                                                                  \
-      hipLaunchKernelGGL((round_count_kernel<DT, B, true>), dim3(grid), dim3(kCountThreads), 0, s, J, q0, q1); \
+    if (q0 || q1) /* codes asked for: element loads for every shape */                           \
+      hipLaunchKernelGGL((round_count_kernel<DT, B, true, false>), dim3(grid), dim3(kCountThreads), 0, s, J, q0, q1); \
+    else if (all_vec(J))                                                                           \
+      hipLaunchKernelGGL((round_count_kernel<DT, B, false, true>), dim3(grid), dim3(kCountThreads), 0, s, J, q0, q1); \
     else                                                                                           \
-      hipLaunchKernelGGL((round_count_kernel<DT, B, false>), dim3(grid), dim3(kCountThreads), 0, s, J, q0, q1); \
+      hipLaunchKernelGGL((round_count_kernel<DT, B, false, false>), dim3(grid), dim3(kCountThreads), 0, s, J, q0, q1); \
     break;
     IMU_RC(2) IMU_RC(3) IMU_RC(4) IMU_RC(5) IMU_RC(6) IMU_RC(7) IMU_RC(8)
 #undef IMU_RC
@@ -752,7 +917,10 @@ static hipError_t residual_dt(int bits, const QuantJobs& J, int grid, hipStream_
   switch (bits) {
 #define IMU_RS(B)                                                                                  \
   case B:                                                                                          \
-    hipLaunchKernelGGL((residual_kernel<DT, B>), dim3(grid), dim3(kResidualThreads), 0, s, J);     \
+    if (all_vec(J))                                                                                \
+      hipLaunchKernelGGL((residual_kernel<DT, B, true>), dim3(grid), dim3(kResidualThreads), 0, s, J); \
+    else                                                                                           \
+      hipLaunchKernelGGL((residual_kernel<DT, B, false>), dim3(grid), dim3(kResidualThreads), 0, s, J); \
     break;
     IMU_RS(2) IMU_RS(3) IMU_RS(4) IMU_RS(5) IMU_RS(6) IMU_RS(7) IMU_RS(8)
 #undef IMU_RS
