@@ -86,6 +86,25 @@ __device__ inline uint32_t code_word(float x, float r) {
   return (m << 1) | (uint32_t)(q < 0);
 }
 
+// The four low digits of the RTN code of x as two's-complement bytes (digit t
+// in byte t), for codes with at most four digits (|q| < 2^(4 (BITS-1))).
+template <int BITS>
+__device__ inline uint32_t digit_word(float x, float r) {
+  bool bad = false;
+  const int32_t q = rtn_code(x, r, &bad);
+  const uint32_t m = q < 0 ? 0u - (uint32_t)q : (uint32_t)q;
+  uint32_t w;
+  if constexpr (BITS == 5) {  // nibbles -> bytes
+    const uint32_t p = __builtin_amdgcn_perm(m, m, 0x01010000u);  // bytes m0 m0 m1 m1
+    w = (p & 0x000F000Fu) | ((p >> 4) & 0x0F000F00u);
+  } else {
+    constexpr uint32_t kD = BITS - 1, kMask = (1u << kD) - 1u;
+    w = (m & kMask) | ((m >> kD) & kMask) << 8 | ((m >> (2 * kD)) & kMask) << 16 | ((m >> (3 * kD)) & kMask) << 24;
+  }
+  // negative codes: every byte d -> -d (bytes are at most 127, so 0x80 - d never borrows)
+  return q < 0 ? (0x80808080u - w) ^ 0x80808080u : w;
+}
+
 // Two's-complement byte of the signed digit whose magnitude starts at bit sh1
 // of the sign-magnitude word w (sh1 = 1 + t (BITS-1) <= 31).
 // digit_signed leaves garbage above the low byte (callers that pack bytes with
@@ -100,6 +119,9 @@ template <int BITS>
 __device__ inline uint32_t digit_byte(uint32_t w, uint32_t sh1) {
   return digit_signed<BITS>(w, sh1) & 0xFFu;
 }
+
+// Buffer-store offset of a row at byte offset ro (-1: absent row).
+__device__ inline uint32_t buf_row(int64_t ro) { return ro < 0 ? kDrop : (uint32_t)ro; }
 
 // A 64-bit value that every thread holds alike, as a scalar.
 __device__ inline int64_t uniform64(int64_t v) {
@@ -160,7 +182,15 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
   const int64_t w_end = min64(w_begin + wins_per_wg, nwin);
   if (w_begin >= w_end) return;
   const T* xb = static_cast<const T*>(a.x) + b * a.bstride;
-  const float r = reinterpret_cast<const StatsHeader*>(a.stats + b * a.stats_stride)->r;
+  const StatsHeader* sth = reinterpret_cast<const StatsHeader*>(a.stats + b * a.stats_stride);
+  const float r = sth->r;
+  // Codes of at most four digits (the largest |x| decides): the staging keeps
+  // each element's digits as bytes of one word, and the rows are assembled
+  // from byte reads.  Otherwise it keeps sign-magnitude codes and extracts
+  // digits per byte.  (Inner-contiguous shape only: the 64-line shape keeps
+  // one form, which holds its per-thread table entries in registers.)
+  const float fmax = __uint_as_float(sth->maxkey) * r;
+  const bool fast = !OC && fmax < 2147483648.0f && digit_count<BITS>((uint32_t)__builtin_rintf(fmax)) <= 4;
   const PlanLayout& P = a.pl;
   const uint8_t* pe = a.plan + P.headers_bytes + b * P.entry_stride;
   const PlanHeader* ph = reinterpret_cast<const PlanHeader*>(a.plan + b * kPlanHeaderStride);
@@ -208,49 +238,53 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
     }
     int64_t row_u0 = -1;
     if (tid < L && s_dout[tid] > 0) row_u0 = lvl[o0 + tid];
-    if constexpr (!OC) {
-      constexpr int G = W / 8;  // groups of 8 k per line
-      constexpr int kIter = L * G / kThreads;
-      static_assert(L * G % kThreads == 0, "staging split");
-      if (a.vec_ok && kw1 == kw0 + W) {
+    auto stage = [&](auto word) __attribute__((always_inline)) {
+      if constexpr (!OC) {
+        constexpr int G = W / 8;  // groups of 8 k per line
+        constexpr int kIter = L * G / kThreads;
+        static_assert(L * G % kThreads == 0, "staging split");
+        if (a.vec_ok && kw1 == kw0 + W) {
 #pragma unroll
-        for (int it = 0; it < kIter; ++it) {
-          const int item = tid + it * kThreads;
-          const int i = item / G, kk = (item % G) * 8;
-          const int64_t o = min64(o0 + i, a.n_outer - 1);
-          float v[8];
-          load8_vec<DT>(xb + o * a.so + kw0 + kk, v);
-          uint32_t* dst = &codes[i * LS + slot(kk)];
+          for (int it = 0; it < kIter; ++it) {
+            const int item = tid + it * kThreads;
+            const int i = item / G, kk = (item % G) * 8;
+            const int64_t o = min64(o0 + i, a.n_outer - 1);
+            float v[8];
+            load8_vec<DT>(xb + o * a.so + kw0 + kk, v);
+            uint32_t* dst = &codes[i * LS + slot(kk)];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) dst[j] = code_word(v[j], r);
+            for (int j = 0; j < 8; ++j) dst[j] = word(v[j]);
+          }
+        } else {
+#pragma unroll
+          for (int it = 0; it < kIter; ++it) {
+            const int item = tid + it * kThreads;
+            const int i = item / G, kk = (item % G) * 8;
+            const int64_t o = min64(o0 + i, a.n_outer - 1);
+            const T* line = xb + o * a.so;
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = load_elem<DT>(line + min64(kw0 + kk + j, K - 1) * a.sk);
+            uint32_t* dst = &codes[i * LS + slot(kk)];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = word(v[j]);
+          }
         }
       } else {
-#pragma unroll
+        constexpr int kIter = L * W / kThreads;
+        static_assert(L * W % kThreads == 0, "staging split");
+#pragma unroll 8
         for (int it = 0; it < kIter; ++it) {
           const int item = tid + it * kThreads;
-          const int i = item / G, kk = (item % G) * 8;
+          const int i = item % L, kk = item / L;
           const int64_t o = min64(o0 + i, a.n_outer - 1);
-          const T* line = xb + o * a.so;
-          float v[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = load_elem<DT>(line + min64(kw0 + kk + j, K - 1) * a.sk);
-          uint32_t* dst = &codes[i * LS + slot(kk)];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) dst[j] = code_word(v[j], r);
+          const int64_t k = min64(kw0 + kk, K - 1);
+          codes[i * LS + slot(kk)] = word(load_elem<DT>(xb + o * a.so + k * a.sk));
         }
       }
-    } else {
-      constexpr int kIter = L * W / kThreads;
-      static_assert(L * W % kThreads == 0, "staging split");
-#pragma unroll 8
-      for (int it = 0; it < kIter; ++it) {
-        const int item = tid + it * kThreads;
-        const int i = item % L, kk = item / L;
-        const int64_t o = min64(o0 + i, a.n_outer - 1);
-        const int64_t k = min64(kw0 + kk, K - 1);
-        codes[i * LS + slot(kk)] = code_word(load_elem<DT>(xb + o * a.so + k * a.sk), r);
-      }
-    }
+    };
+    if (fast) stage([&](float x) { return digit_word<BITS>(x, r); });
+    else stage([&](float x) { return code_word(x, r); });
     // this window's K' positions: per segment the range [P0, P1), as groups of
     // 4 positions flattened over the segments (s_pre: first flat group of each
     // segment), so that all segments' groups are spread over all threads
@@ -276,13 +310,16 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
         }
         __syncthreads();
       }
-      // row offsets as scalars (the same for every thread): held in SGPRs for
-      // 16 lines, re-read from LDS per use for 64
+      // row offsets as scalars (the same for every thread).  Buffer stores
+      // take 32-bit offsets, kDrop for an absent row (kDrop + pos stays past
+      // the end): held in SGPRs for 16 lines, re-read from LDS per use for 64.
+      // The pointer stores of huge entries re-read the 64-bit offsets.
       constexpr int LR = L <= 16 ? L : 1;
-      int64_t ros_s[LR];
+      uint32_t rb_s[LR];
 #pragma unroll
-      for (int i = 0; i < LR; ++i) ros_s[i] = uniform64(rowoff[i]);
-#define IMU_RO(i) (L <= 16 ? ros_s[(i) % LR] : uniform64(rowoff[i]))
+      for (int i = 0; i < LR; ++i) rb_s[i] = buf_row(uniform64(rowoff[i]));
+#define IMU_RB(i) (L <= 16 ? rb_s[(i) % LR] : buf_row(uniform64(rowoff[i])))
+#define IMU_RO(i) uniform64(rowoff[i])
       const int gtot = s_pre[nseg];
       for (int gb = 0; gb < gtot; gb += kThreads * kInFlight) {
         // table entries of up to kInFlight groups per thread, loads first
@@ -307,6 +344,8 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
           if (gb + tid + j * kThreads >= gtot) continue;
           const int64_t g = gq[j], P0 = s_p0[sq[j]], P1 = s_p1[sq[j]];
           const uint32_t ent[4] = {e4[j].x, e4[j].y, e4[j].z, e4[j].w};
+          // per position: word of the element and shift of digit t (codes),
+          // or byte t of the element's word (digit bytes, t < 4)
           uint32_t adr[4], sh[4];
           bool inr[4];
 #pragma unroll
@@ -318,67 +357,80 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
             const bool last = (e >> last_sh) & 1u;
             const int t = u == 0 ? kap : (last ? kap + u : D);
             const int kk = (int)((int64_t)(e & 0xFFFFFu) - kw0);
-            const bool ok = inr[c] && e != kKmapPad && t < D && kk >= 0 && kk < W;
-            adr[c] = ok ? (uint32_t)slot(kk) : kZero;
+            const bool ok = inr[c] && e != kKmapPad && t < (fast ? 4 : D) && kk >= 0 && kk < W;
+            adr[c] = fast ? (ok ? 4u * (uint32_t)slot(kk) + (uint32_t)t : 4u * kZero) : (ok ? (uint32_t)slot(kk) : kZero);
             sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
           }
           const uint32_t pos = (uint32_t)(is_a ? frag_pos_offset(4 * g) : 4 * g);
           const bool full = inr[0] && inr[3];  // the whole dword lies in the range
-          if (use_buf) {
-            // Buffer stores at 32-bit offsets into this entry; absent rows and
-            // bytes outside the range get an offset past the end, which the
-            // hardware drops, so the lines form one branch-free block in which
-            // the LDS reads of later lines overlap the work on earlier ones.
-            if (full) {
-#pragma unroll(L <= 16 ? L : 8)
-              for (int i = 0; i < L; ++i) {
-                const int64_t ro = IMU_RO(i);
-                const uint32_t o = ro < 0 ? kDrop : (uint32_t)ro + pos;
-                const uint32_t* cl = codes + i * LS;
-                const uint32_t b0 = digit_signed<BITS>(cl[adr[0]], sh[0]), b1 = digit_signed<BITS>(cl[adr[1]], sh[1]);
-                const uint32_t b2 = digit_signed<BITS>(cl[adr[2]], sh[2]), b3 = digit_signed<BITS>(cl[adr[3]], sh[3]);
-                // low bytes of b0..b3 -> bytes 0..3
-                const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u), hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(hi, lo, 0x05040100u), rs, (int)o, 0, 0);
-              }
-            } else {
-#pragma unroll 4
-              for (int i = 0; i < L; ++i) {
-                const int64_t ro = IMU_RO(i);
-                const uint32_t* cl = codes + i * LS;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                  const uint32_t o = ro < 0 || !inr[c] ? kDrop : (uint32_t)ro + pos + c;
-                  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)digit_signed<BITS>(cl[adr[c]], sh[c]), rs, (int)o, 0, 0);
-                }
-              }
-            }
-          } else if (full) {  // entries of 2 GB and more: pointer stores, one line at a time
-#pragma unroll
-            for (int i = 0; i < L; ++i) {
-              const int64_t ro = IMU_RO(i);
-              if (ro < 0) continue;  // uniform: row offsets are scalar
-              const uint32_t* cl = codes + i * LS;
-              uint32_t dw = 0;
-#pragma unroll
-              for (int c = 0; c < 4; ++c) dw |= digit_byte<BITS>(cl[adr[c]], sh[c]) << (8 * c);
-              *reinterpret_cast<uint32_t*>(out + ro + pos) = dw;
-            }
-          } else {
-#pragma unroll 4
-            for (int i = 0; i < L; ++i) {
-              const int64_t ro = IMU_RO(i);
-              if (ro < 0) continue;
-              const uint32_t* cl = codes + i * LS;
-              int8_t* dst = out + ro + pos;
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                if (inr[c]) dst[c] = (int8_t)(uint8_t)digit_byte<BITS>(cl[adr[c]], sh[c]);
-            }
+          // rows of the group: digit (low byte, two's complement) of position c
+          // in line cl from the digit bytes or from the sign-magnitude code
+#define IMU_EMIT_ROWS()                                                                                                           \
+          if (use_buf) {                                                                                                          \
+            /* Buffer stores at 32-bit offsets into this entry; absent rows and */                                                \
+            /* bytes outside the range get an offset past the end, which the */                                                   \
+            /* hardware drops, so the lines form one branch-free block in which */                                                \
+            /* the LDS reads of later lines overlap the work on earlier ones. */                                                  \
+            if (full) {                                                                                                           \
+_Pragma("unroll(L <= 16 ? L : 8)")                                                                                                \
+              for (int i = 0; i < L; ++i) {                                                                                       \
+                const uint32_t o = IMU_RB(i) + pos;                                                                               \
+                const uint32_t* cl = codes + i * LS;                                                                              \
+                const uint32_t b0 = IMU_DIG(cl, 0), b1 = IMU_DIG(cl, 1);                                                          \
+                const uint32_t b2 = IMU_DIG(cl, 2), b3 = IMU_DIG(cl, 3);                                                          \
+                /* low bytes of b0..b3 -> bytes 0..3 */                                                                           \
+                const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u), hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);  \
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(hi, lo, 0x05040100u), rs, (int)o, 0, 0);              \
+              }                                                                                                                   \
+            } else {                                                                                                              \
+_Pragma("unroll 4")                                                                                                               \
+              for (int i = 0; i < L; ++i) {                                                                                       \
+                const uint32_t rb = IMU_RB(i);                                                                                    \
+                const uint32_t* cl = codes + i * LS;                                                                              \
+_Pragma("unroll")                                                                                                                 \
+                for (int c = 0; c < 4; ++c) {                                                                                     \
+                  const uint32_t o = inr[c] ? rb + pos + c : kDrop;                                                               \
+                  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)IMU_DIG(cl, c), rs, (int)o, 0, 0);                                \
+                }                                                                                                                 \
+              }                                                                                                                   \
+            }                                                                                                                     \
+          } else if (full) { /* entries of 2 GB and more: pointer stores, one line at a time */                                   \
+_Pragma("unroll")                                                                                                                 \
+            for (int i = 0; i < L; ++i) {                                                                                         \
+              const int64_t ro = IMU_RO(i);                                                                                       \
+              if (ro < 0) continue; /* uniform: row offsets are scalar */                                                         \
+              const uint32_t* cl = codes + i * LS;                                                                                \
+              uint32_t dw = 0;                                                                                                    \
+_Pragma("unroll")                                                                                                                 \
+              for (int c = 0; c < 4; ++c) dw |= (IMU_DIG(cl, c) & 0xFFu) << (8 * c);                                              \
+              *reinterpret_cast<uint32_t*>(out + ro + pos) = dw;                                                                  \
+            }                                                                                                                     \
+          } else {                                                                                                                \
+_Pragma("unroll 4")                                                                                                               \
+            for (int i = 0; i < L; ++i) {                                                                                         \
+              const int64_t ro = IMU_RO(i);                                                                                       \
+              if (ro < 0) continue;                                                                                               \
+              const uint32_t* cl = codes + i * LS;                                                                                \
+              int8_t* dst = out + ro + pos;                                                                                       \
+_Pragma("unroll")                                                                                                                 \
+              for (int c = 0; c < 4; ++c)                                                                                         \
+                if (inr[c]) dst[c] = (int8_t)(uint8_t)(IMU_DIG(cl, c) & 0xFFu);                                                   \
+            }                                                                                                                     \
           }
+          if (fast) {
+#define IMU_DIG(cl, c) ((uint32_t)reinterpret_cast<const uint8_t*>(cl)[adr[c]])
+            IMU_EMIT_ROWS();
+#undef IMU_DIG
+          } else {
+#define IMU_DIG(cl, c) digit_signed<BITS>((cl)[adr[c]], sh[c])
+            IMU_EMIT_ROWS();
+#undef IMU_DIG
+          }
+#undef IMU_EMIT_ROWS
         }
       }
 #undef IMU_RO
+#undef IMU_RB
       __syncthreads();  // before rowoff and the segment ranges are rewritten
     }
   }

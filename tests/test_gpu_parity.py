@@ -71,8 +71,23 @@ def test_staged_path_matches_oracle(cfg):
     _staged(cfg)
 
 
+def test_wide_codes_match_oracle():
+    """Codes of five and more digits (|q| >= 2^16 at b=5) take the unpack
+    kernels' code-word staging; the other cases stay within four digits."""
+    pr = W.random_problem(seed=13, m=96, k=300, n=80, kind="gauss", dtype="f32")
+    rng = np.random.Generator(np.random.PCG64(13))
+    for op, scale in ((pr.a, 1e5), (pr.b, 3e4)):
+        flat = op.stored.reshape(-1)
+        idx = rng.choice(flat.size, 5, replace=False)
+        flat[idx] *= np.float32(scale)
+    _staged_problem(pr)
+
+
 def _staged(cfg):
-    pr = W.random_problem(**cfg)
+    _staged_problem(W.random_problem(**cfg))
+
+
+def _staged_problem(pr):
     print(f"\n[case] {pr.name} a={pr.a.dtype}/{pr.a.layout} b={pr.b.layout} bits={pr.bits} beta={pr.beta} "
           f"strat={pr.strat_a}/{pr.strat_b} batch={pr.a.batch}", flush=True)
     refs = G.oracle_entries(pr)
