@@ -239,6 +239,29 @@ __device__ inline int32_t digit_of(int32_t q, int t) {
   return q < 0 ? -(int32_t)d : (int32_t)d;
 }
 
+// Reduction over the wave, returned as a scalar: butterflies inside each row
+// of 16 lanes (quad swaps, half-row and row mirrors), then the row broadcasts
+// leave the total in lane 63.  Rows the broadcast does not write receive 0,
+// the identity of the sums and maxima used here.
+#define IMU_DPP(v, ctrl, rows) (uint32_t) __builtin_amdgcn_update_dpp(0, (int)(v), ctrl, rows, 0xF, false)
+template <typename Op>
+__device__ inline uint32_t wave_reduce(uint32_t v, Op op) {
+  v = op(v, IMU_DPP(v, 0xB1, 0xF));   // lane ^ 1
+  v = op(v, IMU_DPP(v, 0x4E, 0xF));   // lane ^ 2
+  v = op(v, IMU_DPP(v, 0x141, 0xF));  // mirror inside 8 lanes
+  v = op(v, IMU_DPP(v, 0x140, 0xF));  // mirror inside 16 lanes
+  v = op(v, IMU_DPP(v, 0x142, 0xA));  // lane 15 of rows 0, 2 into rows 1, 3
+  v = op(v, IMU_DPP(v, 0x143, 0xC));  // lane 31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+#undef IMU_DPP
+struct AddU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+struct MaxU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+
 __device__ inline int wave_sum_i32(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
