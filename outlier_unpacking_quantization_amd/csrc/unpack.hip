@@ -90,9 +90,14 @@ __device__ inline uint32_t code_word(float x, float r) {
 // in byte t), for codes with at most four digits (|q| < 2^(4 (BITS-1))).
 template <int BITS>
 __device__ inline uint32_t digit_word(float x, float r) {
-  bool bad = false;
-  const int32_t q = rtn_code(x, r, &bad);
-  const uint32_t m = q < 0 ? 0u - (uint32_t)q : (uint32_t)q;
+  const float y = x * r;  // the RTN product; q = rne(y)
+  uint32_t m;             // |q|
+  if constexpr (4 * (BITS - 1) <= 22) {
+    // |y| < 2^22: adding 1.5 * 2^23 leaves rne(|y|) in the low mantissa bits
+    m = __float_as_uint(__builtin_fabsf(y) + 12582912.0f) - 0x4B400000u;
+  } else {
+    m = (uint32_t)__builtin_rintf(__builtin_fabsf(y));
+  }
   uint32_t w;
   if constexpr (BITS == 5) {  // nibbles -> bytes
     const uint32_t p = __builtin_amdgcn_perm(m, m, 0x01010000u);  // bytes m0 m0 m1 m1
@@ -101,8 +106,10 @@ __device__ inline uint32_t digit_word(float x, float r) {
     constexpr uint32_t kD = BITS - 1, kMask = (1u << kD) - 1u;
     w = (m & kMask) | ((m >> kD) & kMask) << 8 | ((m >> (2 * kD)) & kMask) << 16 | ((m >> (3 * kD)) & kMask) << 24;
   }
-  // negative codes: every byte d -> -d (bytes are at most 127, so 0x80 - d never borrows)
-  return q < 0 ? (0x80808080u - w) ^ 0x80808080u : w;
+  // negative codes: every byte d -> -d (bytes are at most 127, so 0x80 - d
+  // never borrows); a zero code has zero bytes either way
+  const uint32_t neg = (uint32_t)((int32_t)__float_as_uint(y) >> 31);
+  return (w & ~neg) | (((0x80808080u - w) ^ 0x80808080u) & neg);
 }
 
 // Two's-complement byte of the signed digit whose magnitude starts at bit sh1
@@ -122,6 +129,23 @@ __device__ inline uint32_t digit_byte(uint32_t w, uint32_t sh1) {
 
 // Buffer-store offset of a row at byte offset ro (-1: absent row).
 __device__ inline uint32_t buf_row(int64_t ro) { return ro < 0 ? kDrop : (uint32_t)ro; }
+
+// Output dword of four positions: bytes c8[adr[0..3]] (digit bytes; loaded
+// into 16-bit halves, so one shift-or packs them) or the low bytes of the
+// digits extracted from sign-magnitude code words.
+typedef uint16_t v2u16 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t dword_of_bytes(const uint8_t* c8, const uint32_t (&adr)[4]) {
+  const v2u16 even = {c8[adr[0]], c8[adr[2]]}, odd = {c8[adr[1]], c8[adr[3]]};
+  return __builtin_bit_cast(uint32_t, even) | __builtin_bit_cast(uint32_t, odd) << 8;
+}
+template <int BITS>
+__device__ inline uint32_t dword_of_digits(const uint32_t* cl, const uint32_t (&adr)[4], const uint32_t (&sh)[4]) {
+  const uint32_t b0 = digit_signed<BITS>(cl[adr[0]], sh[0]), b1 = digit_signed<BITS>(cl[adr[1]], sh[1]);
+  const uint32_t b2 = digit_signed<BITS>(cl[adr[2]], sh[2]), b3 = digit_signed<BITS>(cl[adr[3]], sh[3]);
+  // low bytes of b0..b3 -> bytes 0..3
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u), hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
 
 // A 64-bit value that every thread holds alike, as a scalar.
 __device__ inline int64_t uniform64(int64_t v) {
@@ -376,11 +400,7 @@ _Pragma("unroll(L <= 16 ? L : 8)")                                              
               for (int i = 0; i < L; ++i) {                                                                                       \
                 const uint32_t o = IMU_RB(i) + pos;                                                                               \
                 const uint32_t* cl = codes + i * LS;                                                                              \
-                const uint32_t b0 = IMU_DIG(cl, 0), b1 = IMU_DIG(cl, 1);                                                          \
-                const uint32_t b2 = IMU_DIG(cl, 2), b3 = IMU_DIG(cl, 3);                                                          \
-                /* low bytes of b0..b3 -> bytes 0..3 */                                                                           \
-                const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u), hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);  \
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(hi, lo, 0x05040100u), rs, (int)o, 0, 0);              \
+                __builtin_amdgcn_raw_buffer_store_b32(IMU_DWORD(cl), rs, (int)o, 0, 0);                                           \
               }                                                                                                                   \
             } else {                                                                                                              \
 _Pragma("unroll 4")                                                                                                               \
@@ -419,11 +439,15 @@ _Pragma("unroll")                                                               
           }
           if (fast) {
 #define IMU_DIG(cl, c) ((uint32_t)reinterpret_cast<const uint8_t*>(cl)[adr[c]])
+#define IMU_DWORD(cl) dword_of_bytes(reinterpret_cast<const uint8_t*>(cl), adr)
             IMU_EMIT_ROWS();
+#undef IMU_DWORD
 #undef IMU_DIG
           } else {
 #define IMU_DIG(cl, c) digit_signed<BITS>((cl)[adr[c]], sh[c])
+#define IMU_DWORD(cl) dword_of_digits<BITS>(cl, adr, sh)
             IMU_EMIT_ROWS();
+#undef IMU_DWORD
 #undef IMU_DIG
           }
 #undef IMU_EMIT_ROWS
