@@ -13,6 +13,7 @@ namespace imu {
 // constants
 // ---------------------------------------------------------------------------
 constexpr int kHistBins = 32768;    // 15-bit magnitude key of bf16 (and the top of fp32)
+constexpr int kHistCoarse = 256;    // coarse counts (128 keys each) kept after the key bins
 constexpr int kKPad = 128;          // every exponent segment of K' is padded to this many bytes
 constexpr int kMaxSeg = 64;         // room for 2*max_digits(2)-1 = 61 segments
 constexpr int kStatusNonfinite = 1; // device status bits
@@ -64,7 +65,7 @@ inline StatsLayout stats_layout(int64_t R, int64_t C) {
   L.col_maxdig = take(4 * C);
   L.cr_rowdig = take(4 * R);
   L.rc_coldig = take(4 * C);
-  L.hist = take(4 * (int64_t)kHistBins);
+  L.hist = take(4 * (int64_t)(kHistBins + kHistCoarse));
   L.stride = o;
   return L;
 }

@@ -135,6 +135,62 @@ __device__ inline JobPos find_job(const QuantJobs& J, int bid) {
   return p;  // count 0: not reached for a consistent grid
 }
 
+// Inclusive scan of a 64-bit value over the 64 lanes of a wave.
+__device__ inline unsigned long long wave_incl_scan_u64(unsigned long long v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned lo = __shfl_up((unsigned)(v & 0xFFFFFFFFull), o, 64);
+    const unsigned hi = __shfl_up((unsigned)(v >> 32), o, 64);
+    if (lane >= o) v += ((unsigned long long)hi << 32) | lo;
+  }
+  return v;
+}
+
+// Result of a selection pass: the k-th smallest key lies in bin `bin`, with
+// `below` keys in lower bins.  Not final: the prefix and the rank left for the
+// next pass; final: kth, alpha (the largest |x| when kth is 0), r and s.
+__device__ inline void apply_selection(StatsHeader* hd, int pass, int final_pass, uint32_t bin,
+                                       unsigned long long below, unsigned long long k, int beta,
+                                       uint32_t maxkey, int status) {
+  if (bin == 0xFFFFFFFFu) {  // cannot happen for a consistent histogram
+    hd->status |= kStatusNonfinite;
+    status |= kStatusNonfinite;
+    bin = 0;
+    below = 0;
+  }
+  const uint32_t rank = (uint32_t)(k - below);
+  const uint32_t prefix = pass == 0 ? bin : ((hd->sel_prefix << 8) | bin);
+  if (!final_pass) {
+    hd->sel_prefix = prefix;
+    hd->sel_rank = rank;
+    return;
+  }
+  const uint32_t key = pass == 0 ? (prefix << 16) : prefix;  // pass 0 is final only for bf16
+  const float kth = __uint_as_float(key);
+  const float alpha = kth > 0.f ? kth : __uint_as_float(maxkey);
+  hd->kth = kth;
+  hd->alpha = alpha;
+  if (alpha > 0.f && !(status & kStatusNonfinite)) {
+    // a binary64 quotient rounded once more to binary32 is the correctly
+    // rounded binary32 quotient (53 >= 2*24 + 2)
+    hd->r = (float)((double)beta / (double)alpha);
+    hd->s = (float)((double)alpha / (double)beta);
+  } else {
+    hd->r = 0.f;
+    hd->s = 0.f;
+  }
+}
+
+// nearest rank: k = ceil(p_num * N / p_den), clamped to [1, N]
+__device__ inline unsigned long long nearest_rank(int64_t nelem, int p_num, int p_den) {
+  const unsigned long long num = (unsigned long long)p_num * (unsigned long long)nelem;
+  unsigned long long k = (num + (unsigned long long)p_den - 1) / (unsigned long long)p_den;
+  if (k < 1) k = 1;
+  if (k > (unsigned long long)nelem) k = nelem;
+  return k;
+}
+
 // Select the k-th smallest key of the global histogram (one workgroup of 1024).
 // pass 0: 32768 bins (key bits 30..16); pass 1/2: 256 bins (15..8 / 7..0).
 // The caller has passed an acquire fence after the arrival counter, so plain
@@ -150,11 +206,7 @@ __device__ void select_from_hist(uint8_t* st, int64_t hist_off, int64_t nelem, i
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   unsigned long long k;
   if (pass == 0) {
-    // nearest rank: k = ceil(p_num * N / p_den), clamped to [1, N]
-    unsigned long long num = (unsigned long long)p_num * (unsigned long long)nelem;
-    k = (num + (unsigned long long)p_den - 1) / (unsigned long long)p_den;
-    if (k < 1) k = 1;
-    if (k > (unsigned long long)nelem) k = nelem;
+    k = nearest_rank(nelem, p_num, p_den);
   } else {
     k = hd->sel_rank;
   }
@@ -200,37 +252,7 @@ __device__ void select_from_hist(uint8_t* st, int64_t hist_off, int64_t nelem, i
     }
   }
   __syncthreads();
-  if (t == 0) {
-    uint32_t bin = found[0];
-    unsigned long long below = part[16];
-    if (bin == 0xFFFFFFFFu) {  // cannot happen for a consistent histogram
-      hd->status |= kStatusNonfinite;
-      bin = 0;
-      below = 0;
-    }
-    const uint32_t rank = (uint32_t)(k - below);
-    const uint32_t prefix = pass == 0 ? bin : ((hd->sel_prefix << 8) | bin);
-    if (!final_pass) {
-      hd->sel_prefix = prefix;
-      hd->sel_rank = rank;
-    } else {
-      const uint32_t key = pass == 0 ? (prefix << 16) : prefix;  // pass 0 is final only for bf16
-      const float kth = __uint_as_float(key);
-      const float alpha = kth > 0.f ? kth : __uint_as_float(hd->maxkey);
-      const int status = hd->status;
-      hd->kth = kth;
-      hd->alpha = alpha;
-      if (alpha > 0.f && !(status & kStatusNonfinite)) {
-        // a binary64 quotient rounded once more to binary32 is the correctly
-        // rounded binary32 quotient (53 >= 2*24 + 2)
-        hd->r = (float)((double)beta / (double)alpha);
-        hd->s = (float)((double)alpha / (double)beta);
-      } else {
-        hd->r = 0.f;
-        hd->s = 0.f;
-      }
-    }
-  }
+  if (t == 0) apply_selection(hd, pass, final_pass, found[0], part[16], k, beta, hd->maxkey, hd->status);
   if (!final_pass) {
     __syncthreads();
     for (int i = t; i < 256; i += blockDim.x) gh[i] = 0;  // the next pass uses 256 bins
@@ -333,10 +355,46 @@ __device__ inline Row4 wave_max_keys4(const uint32_t (&k)[4]) {
 }
 
 // --- percentile histogram + fused selection ---------------------------------
+// Two-level selection of the first pass: besides the 32768 key bins, every
+// workgroup adds its counts per coarse bin of 128 keys to kHistCoarse global
+// counters (in the same flush), so the last workgroup reads 256 coarse counts,
+// then the 128 bins of the coarse bin holding rank k, instead of all 32768.
+static_assert(kHistCoarse * 128 == kHistBins, "two-level histogram");
+__device__ __forceinline__ void select_two_level(StatsHeader* hd, const uint32_t* gh, const uint32_t* coarse,
+                                                 int64_t nelem, int final_pass, int beta, int p_num, int p_den) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long k = nearest_rank(nelem, p_num, p_den);
+  uint32_t c4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c4[j] = coarse[4 * lane + j];
+  const unsigned long long csum = (unsigned long long)c4[0] + c4[1] + c4[2] + c4[3];
+  const unsigned long long cincl = wave_incl_scan_u64(csum);
+  unsigned long long run = cincl - csum;
+  const bool chit = run < k && k <= cincl;  // one lane for a consistent histogram
+  int j = 0;
+  if (chit)
+    while (j < 3 && run + c4[j] < k) run += c4[j++];
+  const unsigned long long chits = __ballot(chit);
+  const int csrc = chits ? __builtin_ctzll(chits) : 0;
+  const uint32_t cbin = (uint32_t)__shfl(4 * lane + j, csrc, 64);
+  const unsigned long long below = __shfl(run, csrc, 64);
+  // the 128 key bins of that coarse bin, two per lane
+  const uint32_t f0 = gh[cbin * 128 + 2 * lane], f1 = gh[cbin * 128 + 2 * lane + 1];
+  const unsigned long long fsum = (unsigned long long)f0 + f1;
+  const unsigned long long fincl = below + wave_incl_scan_u64(fsum), fexcl = fincl - fsum;
+  const bool fhit = chits && fexcl < k && k <= fincl;
+  const unsigned long long fhits = __ballot(fhit);
+  const int fsrc = fhits ? __builtin_ctzll(fhits) : 0;
+  const bool lo_half = fexcl + f0 >= k;
+  const uint32_t bin = (uint32_t)__shfl(cbin * 128 + 2 * lane + (lo_half ? 0 : 1), fsrc, 64);
+  const unsigned long long blw = __shfl(lo_half ? fexcl : fexcl + f0, fsrc, 64);
+  if (lane == 0) apply_selection(hd, 0, final_pass, fhits ? bin : 0xFFFFFFFFu, blw, k, beta, hd->maxkey, hd->status);
+}
+
 template <int DT, int NB, int PASS, bool VEC>
 __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass) {
   using T = typename Elem<DT>::T;
-  __shared__ uint32_t h[NB];
+  __shared__ __attribute__((aligned(16))) uint32_t h[NB];
   __shared__ uint32_t smax;
   __shared__ int sbad;
   __shared__ uint32_t slast;
@@ -350,7 +408,8 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
   StatsHeader* hd = reinterpret_cast<StatsHeader*>(st);
   uint32_t* gh = reinterpret_cast<uint32_t*>(st + a.hist);
 
-  for (int i = threadIdx.x; i < NB; i += blockDim.x) h[i] = 0;
+  static_assert(NB % 4 == 0, "16-byte clears");
+  for (int i = threadIdx.x; i < NB / 4; i += blockDim.x) reinterpret_cast<uint4*>(h)[i] = uint4{0, 0, 0, 0};
   if (threadIdx.x == 0) {
     smax = 0;
     sbad = 0;
@@ -432,9 +491,27 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
     }
   }
   __syncthreads();
+  // key bins: lane-consecutive bins, so that a wave's atomics fall on two
+  // 128-byte lines
   for (int i = threadIdx.x; i < NB; i += blockDim.x) {
     const uint32_t c = h[i];
     if (c) atomicAdd(&gh[i], c);
+  }
+  if constexpr (PASS == 0) {
+    // coarse counts: thread t sums bins [32t, 32t + 32) (16-byte reads, the
+    // chunk order rotated by lane so that 8 lanes read 8 different banks);
+    // four threads make one coarse bin, stored after the key bins
+    static_assert(NB == 32 * 1024, "one run of 32 bins per thread");
+    const int t = threadIdx.x;
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&h[32 * t + 4 * ((j + lane) & 7)]);
+      c += v.x + v.y + v.z + v.w;
+    }
+    c += __shfl_xor(c, 1, 64);
+    c += __shfl_xor(c, 2, 64);
+    if ((t & 3) == 0 && c) atomicAdd(&gh[NB + (t >> 2)], c);
   }
   if (PASS == 0 && threadIdx.x == 0) {
     atomicMax(&hd->maxkey, smax);
@@ -453,7 +530,15 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
   if (!slast) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x == 0) hd->arrive = 0;  // ready for the next pass (stream ordered)
-  select_from_hist(st, a.hist, a.srows * a.scols, PASS, final_pass, a.beta, a.p_num, a.p_den, part, found, h);
+  if constexpr (PASS == 0) {
+    if (wave == 0) select_two_level(hd, gh, gh + NB, a.srows * a.scols, final_pass, a.beta, a.p_num, a.p_den);
+    if (!final_pass) {  // the next pass uses the first 256 bins
+      __syncthreads();
+      for (int i = threadIdx.x; i < 256; i += blockDim.x) gh[i] = 0;
+    }
+  } else {
+    select_from_hist(st, a.hist, a.srows * a.scols, PASS, final_pass, a.beta, a.p_num, a.p_den, part, found, h);
+  }
 }
 
 // --- fused RTN + outlier statistics -------------------------------------------
@@ -794,9 +879,9 @@ hipError_t launch_fill_2d(int32_t* p, int64_t rows, int64_t cols, int64_t ld, hi
   return hipGetLastError();
 }
 
-// Histogram: about kHistWgs workgroups in total, shared in proportion to size.
-static int plan_hist(QuantJobs& J) {
-  constexpr int kHistWgs = 256;
+// Histogram: about `target` workgroups in total, shared in proportion to size
+// (at least one per batch entry).
+static int plan_hist(QuantJobs& J, int target) {
   double total = 0;
   for (int o = 0; o < J.nops; ++o) total += (double)J.op[o].s.srows * J.op[o].s.scols * J.op[o].batch;
   int begin = 0;
@@ -804,7 +889,7 @@ static int plan_hist(QuantJobs& J) {
     QuantOp& q = J.op[o];
     const double el = (double)q.s.srows * q.s.scols;
     const int64_t units = q.s.srows * ceil_div(q.s.scols, kColsPerTile);
-    int64_t per = (int64_t)(kHistWgs * el / total + 0.5);
+    int64_t per = (int64_t)(target * el / total + 0.5);
     per = min64(max64(per, 1), max64(units, 1));
     q.wgs_per_entry = (int)per;
     q.wg_begin = begin;
@@ -821,23 +906,22 @@ static bool all_vec(const QuantJobs& J) {
 }
 
 template <bool VEC>
-static void hist_vec(int dtype, const QuantJobs& J, int grid, int pass, int final_pass, hipStream_t s) {
-  if (dtype == IMU_BF16) {
+static hipError_t hist_vec(int dtype, QuantJobs& J, int pass, int final_pass, hipStream_t s) {
+  constexpr int kHistWgs = 256;
+  const int grid = plan_hist(J, kHistWgs);
+  if (dtype == IMU_BF16)
     hipLaunchKernelGGL((hist_kernel<IMU_BF16, kHistBins, 0, VEC>), dim3(grid), dim3(1024), 0, s, J, final_pass);
-  } else if (pass == 0) {
+  else if (pass == 0)
     hipLaunchKernelGGL((hist_kernel<IMU_F32, kHistBins, 0, VEC>), dim3(grid), dim3(1024), 0, s, J, final_pass);
-  } else if (pass == 1) {
+  else if (pass == 1)
     hipLaunchKernelGGL((hist_kernel<IMU_F32, 256, 1, VEC>), dim3(grid), dim3(1024), 0, s, J, final_pass);
-  } else {
+  else
     hipLaunchKernelGGL((hist_kernel<IMU_F32, 256, 2, VEC>), dim3(grid), dim3(1024), 0, s, J, final_pass);
-  }
+  return hipGetLastError();
 }
 
 hipError_t launch_hist(int dtype, QuantJobs J, int pass, int final_pass, hipStream_t s) {
-  const int grid = plan_hist(J);
-  if (all_vec(J)) hist_vec<true>(dtype, J, grid, pass, final_pass, s);
-  else hist_vec<false>(dtype, J, grid, pass, final_pass, s);
-  return hipGetLastError();
+  return all_vec(J) ? hist_vec<true>(dtype, J, pass, final_pass, s) : hist_vec<false>(dtype, J, pass, final_pass, s);
 }
 
 // Count kernels: tiles of 512 columns x rows_per_wg rows, about kCountWgs workgroups
