@@ -61,6 +61,17 @@ __device__ inline bool last_to_arrive(uint32_t* counter, uint32_t total, int* s_
   return last;
 }
 
+// Inclusive scan of a 64-bit value over the 64 lanes of a wave.
+__device__ inline long long wave_incl_scan_i64(long long v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
 // Block-wide exclusive scans of kTaskBatch counters per thread at once.
 __device__ inline void block_excl_scan_multi(const int* cnt, int* ex, int* tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -196,8 +207,6 @@ struct PlanShared {
   long long red[kThreads / 24][24];
   int red32[kWaves][16];
   long long tot[24];
-  unsigned long long cost_hi[16], cost_lo[16];
-  int cost_ok[16];
   int choice[2];
   int flag;
   int hist[(kMaxD + 1) * (kMaxD + 1)];  // depth histogram (rows/cols) or (dA, dB) pairs (k)
@@ -289,10 +298,15 @@ __device__ void choose(const PlanArgs& a, int b, int64_t G, bool write_header, P
   // and can all be in flight at once
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   constexpr int kGroups = kThreads / 24;  // thread t adds value t % 24 of records t / 24 (mod kGroups)
-  if (t < kGroups * 24) {
+  if (t < kGroups * 24) {  // loads of 4 records in flight at a time
     const int j = t % 24, g = t / 24;
     long long v = 0;
-    for (int64_t q = g; q < G; q += kGroups) v += E.rec[q].sum[j];
+    for (int64_t q0 = g; q0 < G; q0 += 4 * kGroups) {
+      long long w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = q0 + i * kGroups < G ? E.rec[q0 + i * kGroups].sum[j] : 0;
+      v += w[0] + w[1] + w[2] + w[3];
+    }
     S.red[g][j] = v;
   }
   __syncthreads();
@@ -305,39 +319,47 @@ __device__ void choose(const PlanArgs& a, int b, int64_t G, bool write_header, P
   // cost of pair (ca, cb) = M'[ca] K'[ca][cb] N'[cb] < 2^88: M'K' < 2^59 is
   // exact in 64 bits (M' < 2^29, K' < 2^30), its product with N' < 2^29 is
   // kept as (high, low) 64-bit words
-  if (t < 16) {
-    const int ca = t >> 2, cb = t & 3;
-    const bool ok = allowed(a.strat_a, ca) && allowed(a.strat_b, cb);
-    const unsigned long long mk = (unsigned long long)S.tot[ca] * (unsigned long long)S.tot[8 + t];
-    const unsigned long long nu = (unsigned long long)S.tot[4 + cb];
-    S.cost_hi[t] = ok ? __umul64hi(mk, nu) : ~0ull;
-    S.cost_lo[t] = ok ? mk * nu : ~0ull;
-    S.cost_ok[t] = ok;
-    if (write_header) {
-      E.ph->pair[t][0] = ok ? S.tot[ca] : -1;
-      E.ph->pair[t][1] = ok ? S.tot[8 + t] : -1;
-      E.ph->pair[t][2] = ok ? S.tot[4 + cb] : -1;
+  if (t < 64) {  // wave 0: lane q < 16 is pair (q >> 2, q & 3)
+    const int q = t, ca = q >> 2, cb = q & 3;
+    const bool ok = q < 16 && allowed(a.strat_a, ca) && allowed(a.strat_b, cb);
+    unsigned long long hi = ~0ull, lo = ~0ull;
+    if (ok) {
+      const unsigned long long mk = (unsigned long long)S.tot[ca] * (unsigned long long)S.tot[8 + q];
+      const unsigned long long nu = (unsigned long long)S.tot[4 + cb];
+      hi = __umul64hi(mk, nu);
+      lo = mk * nu;
     }
-  }
-  __syncthreads();
-  if (t == 0) {  // smallest cost, ties to the first pair in A-major order
-    int best = -1;
-    for (int q = 0; q < 16; ++q) {
-      if (!S.cost_ok[q]) continue;
-      if (best < 0 || S.cost_hi[q] < S.cost_hi[best] ||
-          (S.cost_hi[q] == S.cost_hi[best] && S.cost_lo[q] < S.cost_lo[best]))
-        best = q;
+    if (write_header && q < 16) {
+      E.ph->pair[q][0] = ok ? S.tot[ca] : -1;
+      E.ph->pair[q][1] = ok ? S.tot[8 + q] : -1;
+      E.ph->pair[q][2] = ok ? S.tot[4 + cb] : -1;
     }
-    const int best_a = best >> 2, best_b = best & 3;
-    S.choice[0] = best_a;
-    S.choice[1] = best_b;
-    if (write_header) {
-      PlanHeader* ph = E.ph;
-      ph->choice_a = best_a;
-      ph->choice_b = best_b;
-      ph->m_u = S.tot[best_a];
-      ph->k_u = S.tot[8 + best];
-      ph->n_u = S.tot[4 + best_b];
+    // smallest cost over the 16 lanes, ties to the first pair in A-major
+    // order: butterflies on (not allowed, high, low, index)
+    int best = ok ? q : 64 + q;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const unsigned long long ohi = __shfl_xor(hi, o, 64), olo = __shfl_xor(lo, o, 64);
+      const int obest = __shfl_xor(best, o, 64);
+      const bool take = ohi < hi || (ohi == hi && (olo < lo || (olo == lo && obest < best)));
+      if (take) {
+        hi = ohi;
+        lo = olo;
+        best = obest;
+      }
+    }
+    if (q == 0) {
+      const int best_a = (best & 15) >> 2, best_b = best & 3;
+      S.choice[0] = best_a;
+      S.choice[1] = best_b;
+      if (write_header) {
+        PlanHeader* ph = E.ph;
+        ph->choice_a = best_a;
+        ph->choice_b = best_b;
+        ph->m_u = S.tot[best_a];
+        ph->k_u = S.tot[8 + (best & 15)];
+        ph->n_u = S.tot[4 + best_b];
+      }
     }
   }
   __syncthreads();
@@ -426,62 +448,85 @@ __device__ void layout(const PlanArgs& a, int b, int64_t w, bool write_header, P
   const Chunk me = chunk_of(L, w);
   const int64_t wk0[3] = {0, L.wg_a, L.wg_a + L.wg_b};
   const int64_t wkn[3] = {L.wg_a, L.wg_b, L.wg_k};
+  // records written by the previous launch, read kBatch chunks at a time with
+  // all loads in flight (a plain loop would wait for each in turn)
+  constexpr int kBatch = 8;
   for (int job = t; job < 3 * kPlanTasks; job += kThreads) {
     const int kind = job / kPlanTasks, task = job % kPlanTasks;
     long long run = 0;
-    for (int64_t r = 0; r < wkn[kind]; ++r) {
-      if (kind == me.kind && r == me.rank) S.off[task] = (int)run;
-      run += E.rec[wk0[kind] + r].cnt[task];  // written by the previous launch
+    for (int64_t r0 = 0; r0 < wkn[kind]; r0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = r0 + j < wkn[kind] ? E.rec[wk0[kind] + r0 + j].cnt[task] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (kind == me.kind && r0 + j == me.rank) S.off[task] = (int)run;
+        run += v[j];
+      }
     }
     S.task_tot[kind][task] = run;
   }
   if (t < 3) {  // lev_a (A rows), lev_b (B columns), emax (k)
     const int kind = t, field = t == 2 ? 2 : 0;
-    int v = t == 2 ? 0 : 1;
-    for (int64_t r = 0; r < wkn[kind]; ++r) v = max(v, E.rec[wk0[kind] + r].mx[field]);
-    if (t < 2) S.lev[t] = min(v, (int)L.levels);
-    else S.nseg = min(v, (int)L.segments - 1) + 1;
+    int m = t == 2 ? 0 : 1;
+    for (int64_t r0 = 0; r0 < wkn[kind]; r0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = r0 + j < wkn[kind] ? E.rec[wk0[kind] + r0 + j].mx[field] : m;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) m = max(m, v[j]);
+    }
+    if (t < 2) S.lev[t] = min(m, (int)L.levels);
+    else S.nseg = min(m, (int)L.segments - 1) + 1;
   }
   __syncthreads();
-  if (t == 0) {
-    S.m_base = round_up(L.M, L.pad_m);
-    S.n_base = round_up(L.N, L.pad_n);
+  if (t < 64) {  // wave 0, lane = task: the prefixes below are wave scans
+    const int lane = t;
+    const long long m_base = round_up(L.M, L.pad_m), n_base = round_up(L.N, L.pad_n);
+    // level bases: base[u] = (padded base) + entries of the levels 1..u-1
+    long long base_k[2], end_k[2];
+#pragma unroll
     for (int kind = 0; kind < 2; ++kind) {
-      long long p = kind == 0 ? S.m_base : S.n_base;
-      for (int u = 1; u < S.lev[kind]; ++u) p += S.task_tot[kind][u];
-      S.end_rows[kind] = p;
+      const long long v = lane >= 1 && lane < S.lev[kind] ? S.task_tot[kind][lane] : 0;
+      const long long incl = wave_incl_scan_i64(v);
+      base_k[kind] = (kind == 0 ? m_base : n_base) + incl - v;
+      end_k[kind] = (kind == 0 ? m_base : n_base) + __shfl(incl, 63, 64);
     }
-    S.m_alloc = round_up(S.end_rows[0], L.pad_m);
-    S.n_alloc = round_up(S.end_rows[1], L.pad_n);
-    long long off = 0;
-    for (int q = 0; q < S.nseg; ++q) {
-      S.segoff[q] = off;
-      off += round_up(S.task_tot[2][q], kKPad);
+    // segment offsets: each segment padded to the K step (lanes from nseg on
+    // hold the total, so segoff[nseg] = k_pad)
+    const long long seg = lane < S.nseg ? round_up(S.task_tot[2][lane], kKPad) : 0;
+    const long long sincl = wave_incl_scan_i64(seg);
+    const long long k_pad = __shfl(sincl, 63, 64);
+    S.segoff[lane] = sincl - seg;
+    if (lane == 0) {
+      S.m_base = m_base;
+      S.n_base = n_base;
+      S.end_rows[0] = end_k[0];
+      S.end_rows[1] = end_k[1];
+      S.m_alloc = round_up(end_k[0], L.pad_m);
+      S.n_alloc = round_up(end_k[1], L.pad_n);
     }
-    S.segoff[S.nseg] = off;
-    if (me.kind < 2) {
-      long long p = me.kind == 0 ? S.m_base : S.n_base;
-      S.base[0] = 0;
-      for (int u = 1; u < S.lev[me.kind]; ++u) {
-        S.base[u] = p;
-        p += S.task_tot[me.kind][u];
-      }
-    } else {
-      for (int q = 0; q < S.nseg; ++q) S.base[q] = S.segoff[q];
-    }
+    if (me.kind < 2) S.base[lane] = lane == 0 ? 0 : (me.kind == 0 ? base_k[0] : base_k[1]);
+    else S.base[lane] = sincl - seg;
     if (write_header) {
       PlanHeader* ph = E.ph;
-      for (int q = 0; q <= S.nseg; ++q) ph->seg_off[q] = S.segoff[q];
-      for (int q = 0; q < S.nseg; ++q) ph->seg_len[q] = (int32_t)S.task_tot[2][q];
-      ph->n_seg = S.nseg;
-      ph->k_pad = S.segoff[S.nseg];
-      ph->m_base = S.m_base;
-      ph->n_base = S.n_base;
-      ph->m_alloc = S.m_alloc;
-      ph->n_alloc = S.n_alloc;
-      ph->lev_a = S.lev[0];
-      ph->lev_b = S.lev[1];
-      ph->emax = S.nseg - 1;
+      if (lane < S.nseg) {
+        ph->seg_off[lane] = sincl - seg;
+        ph->seg_len[lane] = (int32_t)S.task_tot[2][lane];
+      }
+      if (lane == 0) {
+        ph->seg_off[S.nseg] = k_pad;
+        ph->n_seg = S.nseg;
+        ph->k_pad = k_pad;
+        ph->m_base = m_base;
+        ph->n_base = n_base;
+        ph->m_alloc = round_up(end_k[0], L.pad_m);
+        ph->n_alloc = round_up(end_k[1], L.pad_n);
+        ph->lev_a = S.lev[0];
+        ph->lev_b = S.lev[1];
+        ph->emax = S.nseg - 1;
+      }
     }
   }
   __syncthreads();
