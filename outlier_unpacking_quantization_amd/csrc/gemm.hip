@@ -35,6 +35,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int FR = 2;  // 32-row A fragments per wave
 constexpr int BM = 128 * FR, BN = 128, BK = 128;
@@ -61,6 +62,27 @@ __device__ inline TileCoord tile_of(int w, int tiles_m, int tiles_n) {
   const int gm = min(kGroupM, tiles_m - first_m);
   const int in = id - group * kGroupM * tiles_n;
   return TileCoord{first_m + in % gm, in / gm};
+}
+
+// 4 x 4 transpose inside each quad of lanes: on entry lane c of the quad holds
+// x[i] = element (i, c), on exit x[i] = element (c, i).  Two exchanges: the
+// off-diagonal 2 x 2 blocks with lane c ^ 2, then the off-diagonal elements of
+// each 2 x 2 block with lane c ^ 1.
+__device__ inline void quad_transpose(int (&x)[4]) {
+  const bool hi = (threadIdx.x & 2) != 0, odd = (threadIdx.x & 1) != 0;
+  int s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = __builtin_amdgcn_mov_dpp(x[i], 0x4E, 0xF, 0xF, false);  // lane ^ 2
+  x[0] = hi ? s[2] : x[0];
+  x[1] = hi ? s[3] : x[1];
+  x[2] = hi ? x[2] : s[0];
+  x[3] = hi ? x[3] : s[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = __builtin_amdgcn_mov_dpp(x[i], 0xB1, 0xF, 0xF, false);  // lane ^ 1
+  x[0] = odd ? s[1] : x[0];
+  x[1] = odd ? x[1] : s[0];
+  x[2] = odd ? s[3] : x[2];
+  x[3] = odd ? x[3] : s[2];
 }
 
 __device__ inline void shift_acc(v16i (&acc)[FR][4], int sh) {
@@ -235,6 +257,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
           if (sh >= 32) continue;
           atomicAdd(&g.c[(int64_t)(am & 0xFFFFFF) * ldc + (bm & 0xFFFFFF)], (int)((uint32_t)acc[f][j][r] << sh));
         }
+    return;
+  }
+  // Base tiles.  A 4 x 4 transpose inside each quad of lanes turns the four
+  // rows r4 * 8 + 4 * (l / 32) + 0..3 held at column l % 32 into four
+  // consecutive columns of row ... + l % 4, so each lane stores 16 bytes and a
+  // store instruction covers eight full 128-byte row segments.  Needs 16-byte
+  // aligned rows and the whole tile inside N; otherwise one element per store.
+  const bool vec = (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(g.out) & 15) == 0 && col0 + BN <= g.N;
+  if (vec) {
+    const int64_t r_v = row0 + 4 * (lane >> 5) + (lane & 3), c_v = col0 + 4 * ((lane & 31) >> 2);
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int64_t gr = r_v + f * 32 + 8 * r4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int x[4] = {acc[f][j][4 * r4], acc[f][j][4 * r4 + 1], acc[f][j][4 * r4 + 2], acc[f][j][4 * r4 + 3]};
+          quad_transpose(x);
+          if (gr < g.M) {
+            v4u v = {(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
+            v4u* cp = reinterpret_cast<v4u*>(g.c + gr * ldc + c_v + 32 * j);
+            if (g.mode == 1) v += *cp;
+            *cp = v;
+            if (g.out) {
+              const float4 o = {(float)(int32_t)v.x * sab, (float)(int32_t)v.y * sab, (float)(int32_t)v.z * sab,
+                                (float)(int32_t)v.w * sab};
+              *reinterpret_cast<float4*>(g.out + gr * ldc + c_v + 32 * j) = o;
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     return;
   }
 #pragma unroll
