@@ -408,14 +408,6 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
   StatsHeader* hd = reinterpret_cast<StatsHeader*>(st);
   uint32_t* gh = reinterpret_cast<uint32_t*>(st + a.hist);
 
-  static_assert(NB % 4 == 0, "16-byte clears");
-  for (int i = threadIdx.x; i < NB / 4; i += blockDim.x) reinterpret_cast<uint4*>(h)[i] = uint4{0, 0, 0, 0};
-  if (threadIdx.x == 0) {
-    smax = 0;
-    sbad = 0;
-  }
-  __syncthreads();
-
   const uint32_t prefix = PASS == 0 ? 0u : hd->sel_prefix;
   const int lane = threadIdx.x & 63, nwave = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // unit indices stay scalar
@@ -473,6 +465,14 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
   }
   int64_t ub = u0 + (int64_t)wave * kRowsInFlight;
   IMU_ISSUE(g0, ub);
+  // the LDS histogram is cleared while the first loads fly
+  static_assert(NB % 4 == 0, "16-byte clears");
+  for (int i = threadIdx.x; i < NB / 4; i += blockDim.x) reinterpret_cast<uint4*>(h)[i] = uint4{0, 0, 0, 0};
+  if (threadIdx.x == 0) {
+    smax = 0;
+    sbad = 0;
+  }
+  __syncthreads();
   for (; ub < u1; ub += 2 * ustep) {
     IMU_ISSUE(g1, ub + ustep);
     IMU_PROCESS(g0, ub);
