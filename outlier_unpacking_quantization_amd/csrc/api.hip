@@ -155,7 +155,7 @@ imu_status quantize_ops(const Operand* const* ops, uint8_t* const* stats, int32_
 }
 
 imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
-                       uint8_t* stats_b, uint8_t* plan, hipStream_t s) {
+                       uint8_t* stats_b, uint8_t* plan, uint8_t* host_hdr, hipStream_t s) {
   const StatsLayout la = stats_layout(oa.R, oa.C), lb = stats_layout(ob.R, ob.C);
   const int batch = (int)oa.m->batch;
   for (int dt : {(int)IMU_BF16, (int)IMU_F32}) {
@@ -183,13 +183,15 @@ imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p
   pa.strat_a = p->strat_a;
   pa.strat_b = p->strat_b;
   pa.bits = p->bits;
+  pa.host_hdr = host_hdr;
   IMU_HIP(launch_plan(pa, s));
   return IMU_OK;
 }
 
-// Per-thread pinned staging buffer for the plan headers and an event marking
-// their arrival, so the host can wait for the headers alone while later
-// kernels keep the GPU busy.  Both live until the process ends.
+// Per-thread pinned buffer that the planner's last launch writes a copy of the
+// plan headers into, and an event recorded after that launch, so the host can
+// wait for the headers alone while later kernels keep the GPU busy.  Both live
+// until the process ends.
 struct HeaderStage {
   uint8_t* buf = nullptr;
   size_t bytes = 0;
@@ -198,7 +200,7 @@ struct HeaderStage {
 };
 thread_local HeaderStage g_stage;
 
-imu_status stage_headers(const uint8_t* plan, size_t bytes, hipStream_t s, const uint8_t** out) {
+imu_status header_stage(size_t bytes, uint8_t** out) {
   int dev = 0;
   IMU_HIP(hipGetDevice(&dev));
   HeaderStage& st = g_stage;
@@ -210,12 +212,22 @@ imu_status stage_headers(const uint8_t* plan, size_t bytes, hipStream_t s, const
   if (st.bytes < bytes) {
     void* p = nullptr;
     IMU_HIP(hipHostMalloc(&p, bytes, hipHostMallocDefault));
-    st.buf = static_cast<uint8_t*>(p);  // the previous buffer is not freed: a copy may still target it
-    st.bytes = bytes;
+    st.buf = static_cast<uint8_t*>(p);
+    st.bytes = bytes;  // the previous buffer is not freed: a launch may still write it
   }
-  IMU_HIP(hipMemcpyAsync(st.buf, plan, bytes, hipMemcpyDeviceToHost, s));
-  IMU_HIP(hipEventRecord(st.ev, s));
   *out = st.buf;
+  return IMU_OK;
+}
+
+// Plan launches with the host copy of the headers; returns that copy (valid
+// once g_stage.ev has completed).
+imu_status plan_staged(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
+                       uint8_t* stats_b, uint8_t* plan, hipStream_t s, const uint8_t** hdrs) {
+  uint8_t* buf = nullptr;
+  IMU_TRY(header_stage((size_t)oa.m->batch * kPlanHeaderStride, &buf));
+  IMU_TRY(plan_launch(oa, ob, p, stats_a, stats_b, plan, buf, s));
+  IMU_HIP(hipEventRecord(g_stage.ev, s));
+  *hdrs = buf;
   return IMU_OK;
 }
 
@@ -269,10 +281,9 @@ imu_status finish_plan(const Operand& oa, const Operand& ob, const uint8_t* hdrs
 
 imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
                      uint8_t* stats_b, uint8_t* plan, imu_plan_info* info, hipStream_t s) {
-  IMU_TRY(plan_launch(oa, ob, p, stats_a, stats_b, plan, s));
   const int batch = (int)oa.m->batch;
   const uint8_t* hdrs = nullptr;
-  IMU_TRY(stage_headers(plan, (size_t)batch * kPlanHeaderStride, s, &hdrs));
+  IMU_TRY(plan_staged(oa, ob, p, stats_a, stats_b, plan, s, &hdrs));
   IMU_HIP(hipEventSynchronize(g_stage.ev));
   return finish_plan(oa, ob, hdrs, batch, info, nullptr, nullptr);
 }
@@ -526,9 +537,8 @@ imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const i
   // the plan headers (staged to pinned memory) while they run, then checks the
   // workspace and sizes the GEMM launch.  If the plan failed or the workspace
   // is too small the unpack kernels write nothing.
-  IMU_TRY(plan_launch(oa, ob, p, stats_a, stats_b, plan, stream));
   const uint8_t* hdrs = nullptr;
-  IMU_TRY(stage_headers(plan, (size_t)batch * kPlanHeaderStride, stream, &hdrs));
+  IMU_TRY(plan_staged(oa, ob, p, stats_a, stats_b, plan, stream, &hdrs));
   int8_t* region = reinterpret_cast<int8_t*>(w + fixed);
   const int64_t cap = (int64_t)ws_bytes - fixed;
   if (oa.dtype == ob.dtype) {  // both operands in one launch

@@ -27,6 +27,7 @@ struct PlanArgs {
   uint8_t* plan;
   PlanLayout pl;
   int gamma, strat_a, strat_b, bits;
+  uint8_t* host_hdr;       // pinned host copy of the headers (kPlanHeaderStride per entry), or null
 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 

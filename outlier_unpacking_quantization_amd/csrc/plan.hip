@@ -510,22 +510,45 @@ __device__ void layout(const PlanArgs& a, int b, int64_t w, bool write_header, P
     if (me.kind < 2) S.base[lane] = lane == 0 ? 0 : (me.kind == 0 ? base_k[0] : base_k[1]);
     else S.base[lane] = sincl - seg;
     if (write_header) {
-      PlanHeader* ph = E.ph;
-      if (lane < S.nseg) {
-        ph->seg_off[lane] = sincl - seg;
-        ph->seg_len[lane] = (int32_t)S.task_tot[2][lane];
-      }
-      if (lane == 0) {
-        ph->seg_off[S.nseg] = k_pad;
-        ph->n_seg = S.nseg;
-        ph->k_pad = k_pad;
-        ph->m_base = m_base;
-        ph->n_base = n_base;
-        ph->m_alloc = round_up(end_k[0], L.pad_m);
-        ph->n_alloc = round_up(end_k[1], L.pad_n);
-        ph->lev_a = S.lev[0];
-        ph->lev_b = S.lev[1];
-        ph->emax = S.nseg - 1;
+      // the layout fields, into the header and into the host's copy (if any),
+      // which also gets the fields of the earlier launches: the host then waits
+      // for this launch alone, with no copy queued between it and the unpack
+      PlanHeader* hh = a.host_hdr ? reinterpret_cast<PlanHeader*>(a.host_hdr + b * kPlanHeaderStride) : nullptr;
+      auto put = [&](PlanHeader* h) __attribute__((always_inline)) {
+        if (lane < S.nseg) {
+          h->seg_off[lane] = sincl - seg;
+          h->seg_len[lane] = (int32_t)S.task_tot[2][lane];
+        }
+        if (lane == 0) {
+          h->seg_off[S.nseg] = k_pad;
+          h->n_seg = S.nseg;
+          h->k_pad = k_pad;
+          h->m_base = m_base;
+          h->n_base = n_base;
+          h->m_alloc = round_up(end_k[0], L.pad_m);
+          h->n_alloc = round_up(end_k[1], L.pad_n);
+          h->lev_a = S.lev[0];
+          h->lev_b = S.lev[1];
+          h->emax = S.nseg - 1;
+        }
+      };
+      put(E.ph);
+      if (hh) {
+        put(hh);
+        const PlanHeader* ph = E.ph;  // written by the earlier launches
+        if (lane < 16) {
+          hh->pair[lane][0] = ph->pair[lane][0];
+          hh->pair[lane][1] = ph->pair[lane][1];
+          hh->pair[lane][2] = ph->pair[lane][2];
+        }
+        if (lane == 0) {
+          hh->choice_a = ph->choice_a;
+          hh->choice_b = ph->choice_b;
+          hh->status = ph->status;
+          hh->m_u = ph->m_u;
+          hh->k_u = ph->k_u;
+          hh->n_u = ph->n_u;
+        }
       }
     }
   }

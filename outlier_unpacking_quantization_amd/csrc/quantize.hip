@@ -969,7 +969,7 @@ static hipError_t round_count_dt(int bits, const QuantJobs& J, int grid, int32_t
 }
 
 hipError_t launch_round_count(int dtype, int bits, QuantJobs J, int32_t* q0, int32_t* q1, hipStream_t s) {
-  const int grid = plan_tiles(J, 512);
+  const int grid = plan_tiles(J, 256);  // one workgroup per CU: fewer column flushes
   return dtype == IMU_BF16 ? round_count_dt<IMU_BF16>(bits, J, grid, q0, q1, s)
                            : round_count_dt<IMU_F32>(bits, J, grid, q0, q1, s);
 }
