@@ -65,20 +65,26 @@ def gemm_source_sha() -> str:
 
 
 class HipEvents:
-    """Raw HIP events (timing enabled) through the HIP runtime torch has loaded."""
+    """Raw HIP events (timing enabled) through the HIP runtime torch has loaded.
+
+    They are recorded with a device-scope release: a default event writes back
+    the L2 to system scope when it is recorded, which would leave the GPU idle
+    for microseconds inside every timed step."""
+
+    kReleaseToDevice = 0x40000000  # hipEventReleaseToDevice
 
     def __init__(self, n: int):
         import ctypes
         self.ct = ctypes
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             h = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(h), self.kReleaseToDevice) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.ev.append(h.value)
 
     def elapsed_ms(self, i: int, j: int) -> float:

@@ -2,6 +2,8 @@
 // carving, kernel launches and the one plan-header readback.  Contains no
 // kernels; the device work lives in quantize.hip, plan.hip, unpack.hip and
 // gemm.hip.
+#include <atomic>
+#include <cstddef>
 #include <cstdint>
 #include <cstring>
 #include <string>
@@ -155,7 +157,8 @@ imu_status quantize_ops(const Operand* const* ops, uint8_t* const* stats, int32_
 }
 
 imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
-                       uint8_t* stats_b, uint8_t* plan, uint8_t* host_hdr, hipStream_t s) {
+                       uint8_t* stats_b, uint8_t* plan, uint8_t* host_hdr, int64_t host_tag, hipEvent_t done,
+                       hipStream_t s) {
   const StatsLayout la = stats_layout(oa.R, oa.C), lb = stats_layout(ob.R, ob.C);
   const int batch = (int)oa.m->batch;
   for (int dt : {(int)IMU_BF16, (int)IMU_F32}) {
@@ -184,18 +187,25 @@ imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p
   pa.strat_b = p->strat_b;
   pa.bits = p->bits;
   pa.host_hdr = host_hdr;
-  IMU_HIP(launch_plan(pa, s));
+  pa.host_tag = host_tag;
+  IMU_HIP(launch_plan(pa, done, s));
   return IMU_OK;
 }
 
-// Per-thread pinned buffer that the planner's last launch writes a copy of the
-// plan headers into, and an event recorded after that launch, so the host can
-// wait for the headers alone while later kernels keep the GPU busy.  Both live
-// until the process ends.
+// Per-thread pinned, coherent host buffer that the planner's last launch
+// writes a copy of the plan headers into, each copy closed by a per-call tag,
+// and an event that completes with that launch (it is attached to the launch,
+// so no marker of its own sits between the planner and the unpack; it carries
+// no system-scope fence, which would write back the L2 and leave the GPU idle
+// for microseconds).  The host waits for the headers alone while later kernels
+// keep the GPU busy.  Buffer and events live until the process ends.
 struct HeaderStage {
-  uint8_t* buf = nullptr;
+  uint8_t* buf = nullptr;       // host address
+  uint8_t* dbuf = nullptr;      // the same memory as the device addresses it
   size_t bytes = 0;
-  hipEvent_t ev = nullptr;
+  hipEvent_t ev = nullptr;      // completes with the planner's last launch
+  hipEvent_t ev_sys = nullptr;  // fallback: an event with the system-scope fence
+  int64_t tag = 0;
   int dev = -1;
 };
 thread_local HeaderStage g_stage;
@@ -204,29 +214,66 @@ imu_status header_stage(size_t bytes, uint8_t** out) {
   int dev = 0;
   IMU_HIP(hipGetDevice(&dev));
   HeaderStage& st = g_stage;
-  if (st.ev && st.dev != dev) st.ev = nullptr;  // events belong to a device; the old one is kept alive
+  if (st.ev && st.dev != dev) {  // events and mappings belong to a device; the old ones are kept alive
+    st.ev = st.ev_sys = nullptr;
+    st.bytes = 0;
+  }
   if (!st.ev) {
-    IMU_HIP(hipEventCreateWithFlags(&st.ev, hipEventDisableTiming));
+    IMU_HIP(hipEventCreateWithFlags(&st.ev, hipEventDisableTiming | hipEventDisableSystemFence));
+    IMU_HIP(hipEventCreateWithFlags(&st.ev_sys, hipEventDisableTiming));
     st.dev = dev;
   }
   if (st.bytes < bytes) {
     void* p = nullptr;
-    IMU_HIP(hipHostMalloc(&p, bytes, hipHostMallocDefault));
+    IMU_HIP(hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocCoherent));
+    std::memset(p, 0, bytes);  // no stale tag
+    void* d = nullptr;
+    IMU_HIP(hipHostGetDevicePointer(&d, p, 0));
     st.buf = static_cast<uint8_t*>(p);
+    st.dbuf = static_cast<uint8_t*>(d);
     st.bytes = bytes;  // the previous buffer is not freed: a launch may still write it
   }
   *out = st.buf;
   return IMU_OK;
 }
 
+// Wait until the host copy of every entry's header carries this call's tag:
+// the planner's event, then a bounded poll of the tags.  Should they still be
+// missing (host memory not coherent with the GPU after all), an event with the
+// system-scope fence is recorded and waited for; a tag missing after that is an
+// error.
+imu_status wait_headers(int batch, hipStream_t s) {
+  HeaderStage& st = g_stage;
+  auto tagged = [&]() {
+    for (int b = 0; b < batch; ++b) {
+      const volatile int64_t* t = reinterpret_cast<const volatile int64_t*>(
+          st.buf + (size_t)b * kPlanHeaderStride + offsetof(PlanHeader, reserved));
+      if (*t != st.tag) return false;
+    }
+    return true;
+  };
+  IMU_HIP(hipEventSynchronize(st.ev));
+  for (int i = 0; i < 100000; ++i)
+    if (tagged()) {
+      std::atomic_thread_fence(std::memory_order_acquire);
+      return IMU_OK;
+    }
+  IMU_HIP(hipEventRecord(st.ev_sys, s));  // behind whatever was queued since: still correct
+  IMU_HIP(hipEventSynchronize(st.ev_sys));
+  if (!tagged()) return fail(IMU_ERR_HIP, "plan headers did not reach the host");
+  std::atomic_thread_fence(std::memory_order_acquire);
+  return IMU_OK;
+}
+
 // Plan launches with the host copy of the headers; returns that copy (valid
-// once g_stage.ev has completed).
+// once wait_headers has returned).
 imu_status plan_staged(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
                        uint8_t* stats_b, uint8_t* plan, hipStream_t s, const uint8_t** hdrs) {
   uint8_t* buf = nullptr;
   IMU_TRY(header_stage((size_t)oa.m->batch * kPlanHeaderStride, &buf));
-  IMU_TRY(plan_launch(oa, ob, p, stats_a, stats_b, plan, buf, s));
-  IMU_HIP(hipEventRecord(g_stage.ev, s));
+  HeaderStage& st = g_stage;
+  ++st.tag;
+  IMU_TRY(plan_launch(oa, ob, p, stats_a, stats_b, plan, st.dbuf, st.tag, st.ev, s));
   *hdrs = buf;
   return IMU_OK;
 }
@@ -284,7 +331,7 @@ imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, 
   const int batch = (int)oa.m->batch;
   const uint8_t* hdrs = nullptr;
   IMU_TRY(plan_staged(oa, ob, p, stats_a, stats_b, plan, s, &hdrs));
-  IMU_HIP(hipEventSynchronize(g_stage.ev));
+  IMU_TRY(wait_headers(batch, s));
   return finish_plan(oa, ob, hdrs, batch, info, nullptr, nullptr);
 }
 
@@ -549,7 +596,7 @@ imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const i
     IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap, stream));
     IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap, stream));
   }
-  IMU_HIP(hipEventSynchronize(g_stage.ev));
+  IMU_TRY(wait_headers((int)batch, stream));
   int64_t a_bytes = 0, b_bytes = 0;
   IMU_TRY(finish_plan(oa, ob, hdrs, (int)batch, info, &a_bytes, &b_bytes));
   const int64_t needed = fixed + a_bytes + b_bytes;

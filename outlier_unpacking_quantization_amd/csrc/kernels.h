@@ -28,8 +28,9 @@ struct PlanArgs {
   PlanLayout pl;
   int gamma, strat_a, strat_b, bits;
   uint8_t* host_hdr;       // pinned host copy of the headers (kPlanHeaderStride per entry), or null
+  int64_t host_tag;        // written last into reserved[0] of each host copy
 };
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_plan(const PlanArgs& a, hipEvent_t done, hipStream_t s);  // done: completes with the last launch, or null
 
 // unpack.hip
 struct UnpackArgs {

@@ -27,6 +27,8 @@
 // stores (through the XCD-local L2) and read after a device-scope acquire; the
 // counter that elects the last workgroup is the statistics header's, which is
 // zero between passes.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -514,41 +516,65 @@ __device__ void layout(const PlanArgs& a, int b, int64_t w, bool write_header, P
       // which also gets the fields of the earlier launches: the host then waits
       // for this launch alone, with no copy queued between it and the unpack
       PlanHeader* hh = a.host_hdr ? reinterpret_cast<PlanHeader*>(a.host_hdr + b * kPlanHeaderStride) : nullptr;
-      auto put = [&](PlanHeader* h) __attribute__((always_inline)) {
+      // put(h, st): every layout field, stored through st (plain stores for the
+      // device header, system-scope stores, which write through the caches,
+      // for the host copy)
+      auto put = [&](PlanHeader* h, auto st) __attribute__((always_inline)) {
         if (lane < S.nseg) {
-          h->seg_off[lane] = sincl - seg;
-          h->seg_len[lane] = (int32_t)S.task_tot[2][lane];
+          st(&h->seg_off[lane], (int64_t)(sincl - seg));
+          st(&h->seg_len[lane], (int32_t)S.task_tot[2][lane]);
         }
         if (lane == 0) {
-          h->seg_off[S.nseg] = k_pad;
-          h->n_seg = S.nseg;
-          h->k_pad = k_pad;
-          h->m_base = m_base;
-          h->n_base = n_base;
-          h->m_alloc = round_up(end_k[0], L.pad_m);
-          h->n_alloc = round_up(end_k[1], L.pad_n);
-          h->lev_a = S.lev[0];
-          h->lev_b = S.lev[1];
-          h->emax = S.nseg - 1;
+          st(&h->seg_off[S.nseg], (int64_t)k_pad);
+          st(&h->n_seg, (int32_t)S.nseg);
+          st(&h->k_pad, (int64_t)k_pad);
+          st(&h->m_base, (int64_t)m_base);
+          st(&h->n_base, (int64_t)n_base);
+          st(&h->m_alloc, (int64_t)round_up(end_k[0], L.pad_m));
+          st(&h->n_alloc, (int64_t)round_up(end_k[1], L.pad_n));
+          st(&h->lev_a, (int32_t)S.lev[0]);
+          st(&h->lev_b, (int32_t)S.lev[1]);
+          st(&h->emax, (int32_t)(S.nseg - 1));
         }
       };
-      put(E.ph);
+      put(E.ph, [](auto* p, auto v) __attribute__((always_inline)) { *p = v; });
       if (hh) {
-        put(hh);
-        const PlanHeader* ph = E.ph;  // written by the earlier launches
+        // fields of the earlier launches, all loaded before the first store
+        // (a load's wait would also wait for the slow host stores before it)
+        const PlanHeader* ph = E.ph;
+        int64_t pr[3] = {0, 0, 0}, mu = 0, ku = 0, nu = 0;
+        int32_t ca = 0, cb = 0, stt = 0;
         if (lane < 16) {
-          hh->pair[lane][0] = ph->pair[lane][0];
-          hh->pair[lane][1] = ph->pair[lane][1];
-          hh->pair[lane][2] = ph->pair[lane][2];
+          pr[0] = ph->pair[lane][0];
+          pr[1] = ph->pair[lane][1];
+          pr[2] = ph->pair[lane][2];
         }
         if (lane == 0) {
-          hh->choice_a = ph->choice_a;
-          hh->choice_b = ph->choice_b;
-          hh->status = ph->status;
-          hh->m_u = ph->m_u;
-          hh->k_u = ph->k_u;
-          hh->n_u = ph->n_u;
+          ca = ph->choice_a;
+          cb = ph->choice_b;
+          stt = ph->status;
+          mu = ph->m_u;
+          ku = ph->k_u;
+          nu = ph->n_u;
         }
+        auto sys = [](auto* p, auto v) __attribute__((always_inline)) {
+          __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        };
+        put(hh, sys);
+        if (lane < 16) {
+          sys(&hh->pair[lane][0], pr[0]);
+          sys(&hh->pair[lane][1], pr[1]);
+          sys(&hh->pair[lane][2], pr[2]);
+        }
+        if (lane == 0) {
+          sys(&hh->choice_a, ca);
+          sys(&hh->choice_b, cb);
+          sys(&hh->status, stt);
+          sys(&hh->m_u, mu);
+          sys(&hh->k_u, ku);
+          sys(&hh->n_u, nu);
+        }
+        // the tag follows at the end of the workgroup (host_tag_store)
       }
     }
   }
@@ -650,18 +676,29 @@ __global__ __launch_bounds__(kThreads) void plan_write_kernel(PlanArgs a) {
   const int b = blockIdx.y;
   layout(a, b, blockIdx.x, blockIdx.x == 0, S);
   phase_write(a, b, blockIdx.x, S);
+  // Workgroup 0 wrote the host copy of the header (wave 0, during the layout);
+  // long after, once those stores have completed, the tag closes the copy: a
+  // host that sees the tag sees the whole copy.
+  if (blockIdx.x == 0 && a.host_hdr && threadIdx.x < 64) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&reinterpret_cast<PlanHeader*>(a.host_hdr + b * kPlanHeaderStride)->reserved[0], a.host_tag,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+hipError_t launch_plan(const PlanArgs& a, hipEvent_t done, hipStream_t s) {
   const PlanLayout& L = a.pl;
   const int64_t G = L.wg_a + L.wg_b + L.wg_k;
   if (G <= 0 || G > 0x7FFFFFFF || L.batch < 1 || L.batch > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)G, (unsigned)L.batch);
   hipLaunchKernelGGL(plan_sums_kernel, grid, dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL(plan_counts_kernel, grid, dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(plan_write_kernel, grid, dim3(kThreads), 0, s, a);
+  // the event (if any) completes with this launch: no marker of its own in the stream
+  if (done) hipExtLaunchKernelGGL(plan_write_kernel, grid, dim3(kThreads), 0, s, nullptr, done, 0, a);
+  else hipLaunchKernelGGL(plan_write_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
