@@ -225,7 +225,9 @@ const char* imu_version(void);
 /* Measurement hook for harnesses that time the GEMM inside a larger run: when
  * `before` and `after` are non-NULL, every later imu_unpacked_gemm and
  * imu_imunpack_matmul call on the calling thread records `before` on its stream
- * right before its first GEMM launch and `after` right after its last one.
+ * right before its first GEMM launch and `after` right after its last one
+ * (when the call makes a single GEMM launch, the two are attached to that
+ * launch as its start and stop events, so they add no marker to the stream).
  * Both NULL switches it off.  The events stay owned by the caller and must
  * belong to the device the calls run on.  Returns IMU_ERR_INVALID_ARG if only
  * one of the two is NULL. */

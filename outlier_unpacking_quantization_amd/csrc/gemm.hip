@@ -26,6 +26,8 @@
 // Tiles are dealt to the 8 XCDs (hardware order w % 8) in contiguous runs of a
 // grouped order (groups of 4 tile rows), so the workgroups sharing an XCD's L2
 // share A and B panels.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -319,14 +321,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const int64_t rows = g.mode == 2 ? g.m_alloc : g.m_base;
   const int64_t cols = g.mode == 2 ? g.n_alloc : g.n_base;
   if (rows % BM || cols % BN) return hipErrorInvalidValue;
   const int64_t tiles = (rows / BM) * (cols / BN);
-  if (tiles == 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, g);
+  if (tiles == 0) {  // nothing to launch: the events still get recorded
+    if (start) hipEventRecord(start, s);
+    if (stop) hipEventRecord(stop, s);
+    return hipGetLastError();
+  }
+  if (start || stop) hipExtLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, start, stop, 0, g);
+  else hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 

@@ -70,6 +70,7 @@ struct GemmArgs {
   int bits;
   int mode;                // 0: base tiles, store C; 1: base tiles, add to C; 2: extra tiles, atomics
 };
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// start / stop: events recorded as the launch starts / ends (attached to it), or null
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace imu
