@@ -37,10 +37,10 @@ HBM_PEAK_GBS = 8000.0
 # version of the GEMM source: when gemm.hip no longer hashes to `source_sha256`
 # the traffic is reported as null.
 GEMM_TRAFFIC = {
-    "source_sha256": "80ec07662f7341acb2b6a49f71c93bd86991bb7462d8c5f08c5f2908eb00533d",
-    "fetch_kib": 152345.4, "write_kib": 65536.0,        # counter readings per launch
+    "source_sha256": "e2d5c60c8fdb113bcac261539518a6f90d6a2a925ce3066965086434b495ba5e",
+    "fetch_kib": 151384.9, "write_kib": 65536.0,        # counter readings per launch
     "fetch_factor": 1.99980, "write_factor": 1.00000,  # copy calibration
-    "bytes_per_launch": 379081043,
+    "bytes_per_launch": 377114156,
 }
 
 
