@@ -2,6 +2,7 @@
 // carving, kernel launches and the one plan-header readback.  Contains no
 // kernels; the device work lives in quantize.hip, plan.hip, unpack.hip and
 // gemm.hip.
+#include <algorithm>
 #include <atomic>
 #include <cstddef>
 #include <cstdint>
@@ -385,46 +386,56 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   const int64_t M = info[0].m, K = info[0].k, N = info[0].n;
   const StatsLayout la = stats_layout(M, K), lb = stats_layout(K, N);
   const PlanLayout pl = plan_layout(M, K, N, batch, p->bits);
-  // measurement events: attached to the launch itself when the call makes a
-  // single launch (no marker of their own in the stream), else recorded around
-  // all of the call's launches
-  const bool single = batch == 1 && info[0].m_alloc <= info[0].m_base && info[0].n_alloc <= info[0].n_base;
-  if (g_gemm_ev[0] && !single) IMU_HIP(hipEventRecord(g_gemm_ev[0], s));
+  if (batch > 65535) return fail(IMU_ERR_INVALID_ARG, "batch above 65535");
+  // one launch per pass serves every entry: the grid takes the largest entry
+  int64_t base_tiles = 0, extra_tiles = 0;
+  bool any_extras = false;
   for (int64_t b = 0; b < batch; ++b) {
     const imu_plan_info& f = info[b];
-    const uint8_t* pe = plan + pl.headers_bytes + b * pl.entry_stride;
-    GemmArgs g{};
-    g.a_u = a_u + f.a_offset;
-    g.b_u = b_u + f.b_offset;
-    g.hdr = plan + b * kPlanHeaderStride;
-    g.amap = reinterpret_cast<const int32_t*>(pe + pl.amap);
-    g.bmap = reinterpret_cast<const int32_t*>(pe + pl.bmap);
-    g.sa = reinterpret_cast<const StatsHeader*>(stats_a + b * la.stride);
-    g.sb = reinterpret_cast<const StatsHeader*>(stats_b + b * lb.stride);
-    g.c = c + b * cbs;
-    g.out = out ? out + b * cbs : nullptr;
-    g.ldc = ldc;
-    g.M = M;
-    g.N = N;
-    g.m_alloc = f.m_alloc;
-    g.n_alloc = f.n_alloc;
-    g.m_base = f.m_base;
-    g.n_base = f.n_base;
-    g.k_pad = f.k_pad;
-    g.bits = p->bits;
-    const bool extras = f.m_alloc > f.m_base || f.n_alloc > f.n_base;
-    if (extras) {
-      IMU_HIP(launch_fill_2d(g.c, M, N, ldc, s));
-      g.mode = 2;
-      IMU_HIP(launch_gemm(g, s));
-      g.mode = 1;
-    } else {
-      g.mode = 0;
+    if (f.m_base % 256 || f.n_base % 128 || f.m_alloc % 256 || f.n_alloc % 128)
+      return fail(IMU_ERR_INVALID_ARG, "plan sizes are not tile multiples");
+    base_tiles = std::max(base_tiles, (f.m_base / 256) * (f.n_base / 128));
+    if (f.m_alloc > f.m_base || f.n_alloc > f.n_base) {
+      any_extras = true;
+      extra_tiles = std::max(extra_tiles, (f.m_alloc / 256) * (f.n_alloc / 128));
     }
-    if (single) IMU_HIP(launch_gemm(g, s, g_gemm_ev[0], g_gemm_ev[1]));
-    else IMU_HIP(launch_gemm(g, s));
   }
-  if (g_gemm_ev[1] && !single) IMU_HIP(hipEventRecord(g_gemm_ev[1], s));
+  GemmArgs g{};
+  g.a_u = a_u;
+  g.b_u = b_u;
+  g.plan = plan;
+  g.headers_bytes = pl.headers_bytes;
+  g.entry_stride = pl.entry_stride;
+  g.amap_off = pl.amap;
+  g.bmap_off = pl.bmap;
+  g.stats_a = stats_a;
+  g.stats_b = stats_b;
+  g.stats_stride_a = la.stride;
+  g.stats_stride_b = lb.stride;
+  g.c = c;
+  g.out = out;
+  g.ldc = ldc;
+  g.cbs = cbs;
+  g.M = M;
+  g.N = N;
+  g.bits = p->bits;
+  // Measurement events: attached to the launch when the call makes a single
+  // one (no marker of their own in the stream), else recorded around all of
+  // the call's launches.
+  if (g_gemm_ev[0] && any_extras) IMU_HIP(hipEventRecord(g_gemm_ev[0], s));
+  if (any_extras) {
+    // extra tiles first: C cleared, their folds added with atomics; the base
+    // tiles of those entries then add their part and write the output
+    IMU_HIP(launch_fill_2d(c, M, N, ldc, (int)batch, cbs, s));
+    g.mode = 2;
+    IMU_HIP(launch_gemm(g, extra_tiles, (int)batch, s));
+    g.mode = 0;
+    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, s));
+    if (g_gemm_ev[1]) IMU_HIP(hipEventRecord(g_gemm_ev[1], s));
+  } else {
+    g.mode = 0;
+    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, s, g_gemm_ev[0], g_gemm_ev[1]));
+  }
   return IMU_OK;
 }
 

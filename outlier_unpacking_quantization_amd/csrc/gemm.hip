@@ -1,5 +1,6 @@
 // Low bit-width GEMM on the unpacked operands with the shift-and-accumulate
-// fold and the dequantization epilogue (gfx950, int8 MFMA).
+// fold and the dequantization epilogue (gfx950, int8 MFMA); one launch serves
+// every batch entry (blockIdx.y).
 //
 // Method: summary page "IM-Unpack: Training and Inference with Arbitrarily Low
 // Precision Integers", "Approach": the original integer GEMM is reproduced
@@ -128,30 +129,53 @@ __device__ inline Cursor cursor_top(int nseg, SegTable off) {
   return c;
 }
 
+typedef __attribute__((address_space(4))) const PlanHeader* HdrC;
+
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BSTR];
-  const PlanHeader* ph = reinterpret_cast<const PlanHeader*>(g.hdr);
-  const int64_t rows = g.mode == 2 ? g.m_alloc : g.m_base;
-  const int64_t cols = g.mode == 2 ? g.n_alloc : g.n_base;
+  // this workgroup's batch entry: sizes from its plan header (scalar loads)
+  const int entry = blockIdx.y;
+  const uint8_t* hdr = g.plan + (int64_t)entry * kPlanHeaderStride;
+  const HdrC ph = (HdrC)hdr;
+  const int64_t m_alloc = ph->m_alloc, n_alloc = ph->n_alloc, m_base = ph->m_base, n_base = ph->n_base;
+  const int64_t kp = ph->k_pad;
+  const bool extras = m_alloc > m_base || n_alloc > n_base;
+  if (g.mode == 2 && !extras) return;
+  const int mode = g.mode == 2 ? 2 : extras ? 1 : 0;
+  const int64_t rows = mode == 2 ? m_alloc : m_base;
+  const int64_t cols = mode == 2 ? n_alloc : n_base;
   const int tiles_m = (int)(rows / BM), tiles_n = (int)(cols / BN);
   if ((int)blockIdx.x >= tiles_m * tiles_n) return;
   const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n);
-  const bool base_tile = (int64_t)tc.tm * BM < g.m_base && (int64_t)tc.tn * BN < g.n_base;
-  if (g.mode == 2 && base_tile) return;
+  const bool base_tile = (int64_t)tc.tm * BM < m_base && (int64_t)tc.tn * BN < n_base;
+  if (mode == 2 && base_tile) return;
+  // the entry's operands follow those of the earlier entries
+  int64_t a_off = 0, b_off = 0;
+  for (int e = 0; e < entry; ++e) {
+    const HdrC h = (HdrC)(g.plan + (int64_t)e * kPlanHeaderStride);
+    a_off += round_up(h->m_alloc * h->k_pad, 256);
+    b_off += round_up(h->n_alloc * h->k_pad, 256);
+  }
+  const uint8_t* pe = g.plan + g.headers_bytes + entry * g.entry_stride;
+  const int32_t* amap = reinterpret_cast<const int32_t*>(pe + g.amap_off);
+  const int32_t* bmap = reinterpret_cast<const int32_t*>(pe + g.bmap_off);
+  const StatsHeader* sa = reinterpret_cast<const StatsHeader*>(g.stats_a + entry * g.stats_stride_a);
+  const StatsHeader* sb = reinterpret_cast<const StatsHeader*>(g.stats_b + entry * g.stats_stride_b);
+  int32_t* const c_e = g.c + entry * g.cbs;
+  float* const out_e = g.out ? g.out + entry * g.cbs : nullptr;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t kp = g.k_pad;
   const int64_t row0 = (int64_t)tc.tm * BM + wave * (32 * FR), col0 = (int64_t)tc.tn * BN;
   const int shift = g.bits - 1;
 
   // A' fragment f (rows row0 + 32f ..) of K substep q at step offset k is the
   // contiguous 1 KB at block (row0/32 + f, k/32 + q); lane l holds bytes
   // [16l, 16l + 16) of it.
-  const int8_t* ga = g.a_u + frag_row_offset(row0, kp) + lane * 16;
+  const int8_t* ga = g.a_u + a_off + frag_row_offset(row0, kp) + lane * 16;
   const int64_t ga_f = (kp >> 5) * 1024;
   // B staging: thread copies rows br + 32j (j < 4), bytes [bc, bc + 16) of the step
   const int br = tid >> 3, bc = (tid & 7) * 16;
-  const int8_t* gb = g.b_u + (col0 + br) * kp + bc;
+  const int8_t* gb = g.b_u + b_off + (col0 + br) * kp + bc;
   const int64_t gb_j = 32 * kp;
   const int sb_w = br * BSTR + bc;
   // B fragment j (columns col0 + 32j + lane%32) of substep q
@@ -165,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) acc[i][j] = v16i{0};
 
   const SegTable off = (SegTable)ph->seg_off;
-  const int nseg = ((__attribute__((address_space(4))) const PlanHeader*)ph)->n_seg;
+  const int nseg = ph->n_seg;
   const int64_t steps = kp / BK;
   Cursor cc = cursor_top(nseg, off);  // compute
   Cursor la = cc, lb = cc;            // A loads (one step ahead), B loads (two ahead)
@@ -241,10 +265,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // (8*(r/4) + 4*(l/32) + r%4, l%32) of each 32x32 block.  Rows are visited one
   // at a time (f, r/4, r%4) with the four column blocks j of the row, so only a
   // row's pointers are live.
-  const float sab = g.sa->s * g.sb->s;
+  const float sab = sa->s * sb->s;
   const int64_t ldc = g.ldc;
   const int64_t r_lane = row0 + 4 * (lane >> 5), c_lane = col0 + (lane & 31);
-  if (g.mode == 2) {  // extra tiles: every element lands on some C[i, n] with its shift
+  if (mode == 2) {  // extra tiles: every element lands on some C[i, n] with its shift
 #pragma unroll
     for (int f = 0; f < FR; ++f)
 #pragma unroll
@@ -253,11 +277,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
         for (int r = 0; r < 16; ++r) {
           const int64_t gr = r_lane + f * 32 + 8 * (r >> 2) + (r & 3);
           const int64_t gc = c_lane + j * 32;
-          const int32_t am = g.amap[gr], bm = g.bmap[gc];
+          const int32_t am = amap[gr], bm = bmap[gc];
           if (am < 0 || bm < 0) continue;
           const int sh = shift * ((am >> 24) + (bm >> 24));
           if (sh >= 32) continue;
-          atomicAdd(&g.c[(int64_t)(am & 0xFFFFFF) * ldc + (bm & 0xFFFFFF)], (int)((uint32_t)acc[f][j][r] << sh));
+          atomicAdd(&c_e[(int64_t)(am & 0xFFFFFF) * ldc + (bm & 0xFFFFFF)], (int)((uint32_t)acc[f][j][r] << sh));
         }
     return;
   }
@@ -266,8 +290,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // consecutive columns of row ... + l % 4, so each lane stores 16 bytes and a
   // store instruction covers eight full 128-byte row segments.  Needs 16-byte
   // aligned rows and the whole tile inside N; otherwise one element per store.
-  const bool vec = (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(g.out) & 15) == 0 && col0 + BN <= g.N;
+  const bool vec = (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c_e) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(out_e) & 15) == 0 && col0 + BN <= g.N;
   if (vec) {
     const int64_t r_v = row0 + 4 * (lane >> 5) + (lane & 3), c_v = col0 + 4 * ((lane & 31) >> 2);
 #pragma unroll
@@ -281,13 +305,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
           quad_transpose(x);
           if (gr < g.M) {
             v4u v = {(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
-            v4u* cp = reinterpret_cast<v4u*>(g.c + gr * ldc + c_v + 32 * j);
-            if (g.mode == 1) v += *cp;
+            v4u* cp = reinterpret_cast<v4u*>(c_e + gr * ldc + c_v + 32 * j);
+            if (mode == 1) v += *cp;
             *cp = v;
-            if (g.out) {
+            if (out_e) {
               const float4 o = {(float)(int32_t)v.x * sab, (float)(int32_t)v.y * sab, (float)(int32_t)v.z * sab,
                                 (float)(int32_t)v.w * sab};
-              *reinterpret_cast<float4*>(g.out + gr * ldc + c_v + 32 * j) = o;
+              *reinterpret_cast<float4*>(out_e + gr * ldc + c_v + 32 * j) = o;
             }
           }
         }
@@ -304,13 +328,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
         const int r = 4 * r4 + r3;
         const int64_t gr = r_lane + f * 32 + 8 * r4 + r3;
         if (gr >= g.M) continue;
-        int32_t* crow = g.c + gr * ldc + c_lane;
-        float* orow = g.out ? g.out + gr * ldc + c_lane : nullptr;
+        int32_t* crow = c_e + gr * ldc + c_lane;
+        float* orow = out_e ? out_e + gr * ldc + c_lane : nullptr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (c_lane + 32 * j >= g.N) continue;
           const int32_t v = acc[f][j][r];
-          const int32_t cv = g.mode == 1 ? (int32_t)((uint32_t)crow[32 * j] + (uint32_t)v) : v;
+          const int32_t cv = mode == 1 ? (int32_t)((uint32_t)crow[32 * j] + (uint32_t)v) : v;
           crow[32 * j] = cv;
           if (orow) orow[32 * j] = (float)cv * sab;
         }
@@ -321,19 +345,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  const int64_t rows = g.mode == 2 ? g.m_alloc : g.m_base;
-  const int64_t cols = g.mode == 2 ? g.n_alloc : g.n_base;
-  if (rows % BM || cols % BN) return hipErrorInvalidValue;
-  const int64_t tiles = (rows / BM) * (cols / BN);
-  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (tiles == 0) {  // nothing to launch: the events still get recorded
+hipError_t launch_gemm(const GemmArgs& g, int64_t tiles_x, int batch, hipStream_t s, hipEvent_t start,
+                       hipEvent_t stop) {
+  if (tiles_x > 0x7FFFFFFF || batch < 1 || batch > 65535) return hipErrorInvalidValue;
+  if (tiles_x <= 0) {  // nothing to launch: the events still get recorded
     if (start) hipEventRecord(start, s);
     if (stop) hipEventRecord(stop, s);
     return hipGetLastError();
   }
-  if (start || stop) hipExtLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, start, stop, 0, g);
-  else hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, g);
+  const dim3 grid((unsigned)tiles_x, (unsigned)batch);
+  if (start || stop) hipExtLaunchKernelGGL(gemm_kernel, grid, dim3(kThreads), 0, s, start, stop, 0, g);
+  else hipLaunchKernelGGL(gemm_kernel, grid, dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ __host__ __device__ inline int64_t unpacked_entry_bytes(const PlanHeader* h, int
 
 // quantize.hip
 hipError_t launch_fill_u32(void* p, uint32_t v, int64_t nwords, hipStream_t s);
-hipError_t launch_fill_2d(int32_t* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
+hipError_t launch_fill_2d(int32_t* p, int64_t rows, int64_t cols, int64_t ld, int batch, int64_t bstride, hipStream_t s);
 hipError_t launch_hist(int dtype, QuantJobs J, int pass, int final_pass, hipStream_t s);
 hipError_t launch_round_count(int dtype, int bits, QuantJobs J, int32_t* q0, int32_t* q1, hipStream_t s);
 hipError_t launch_residual(int dtype, int bits, QuantJobs J, hipStream_t s);
@@ -55,22 +55,28 @@ hipError_t launch_unpack(int dtype, int bits, const UnpackArgs* ops, int nops, i
 
 // gemm.hip
 struct GemmArgs {
+  // one launch serves every batch entry (blockIdx.y); an entry's sizes come
+  // from its plan header, its A' / B'^T from the sum of the earlier entries'
+  // sizes (entries consecutive in a_u and in b_u)
   const int8_t* a_u;
   const int8_t* b_u;
-  const uint8_t* hdr;      // this entry's plan header
-  const int32_t* amap;
-  const int32_t* bmap;
-  const StatsHeader* sa;
-  const StatsHeader* sb;
+  const uint8_t* plan;        // plan buffer (headers, then per-entry arrays)
+  int64_t headers_bytes, entry_stride, amap_off, bmap_off;  // PlanLayout of the plan
+  const uint8_t* stats_a;
+  const uint8_t* stats_b;
+  int64_t stats_stride_a, stats_stride_b;
   int32_t* c;
   float* out;
-  int64_t ldc;
+  int64_t ldc, cbs;           // C / out row stride and batch stride
   int64_t M, N;
-  int64_t m_alloc, n_alloc, m_base, n_base, k_pad;
   int bits;
-  int mode;                // 0: base tiles, store C; 1: base tiles, add to C; 2: extra tiles, atomics
+  int mode;                   // 2: extra tiles (atomics); else base tiles (per entry: store C, or add to
+                              // C when the entry has extra tiles)
 };
-// start / stop: events recorded as the launch starts / ends (attached to it), or null
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// tiles_x: the largest tile count of an entry for this mode; batch entries on
+// blockIdx.y.  start / stop: events recorded as the launch starts / ends
+// (attached to it), or null
+hipError_t launch_gemm(const GemmArgs& a, int64_t tiles_x, int batch, hipStream_t s, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
 
 }  // namespace imu

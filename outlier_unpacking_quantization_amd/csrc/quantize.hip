@@ -107,7 +107,8 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
   for (; i < n; i += step) p[i] = v;
 }
 
-__global__ void fill_2d_kernel(int32_t* p, int64_t rows, int64_t cols, int64_t ld) {
+__global__ void fill_2d_kernel(int32_t* p, int64_t rows, int64_t cols, int64_t ld, int64_t bstride) {
+  p += blockIdx.z * bstride;
   for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
     for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < cols;
          c += (int64_t)gridDim.x * blockDim.x)
@@ -872,10 +873,13 @@ hipError_t launch_fill_u32(void* p, uint32_t v, int64_t nwords, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fill_2d(int32_t* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t s) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  dim3 grid((unsigned)min64(ceil_div(cols, 256), 64), (unsigned)min64(rows, 4096));
-  hipLaunchKernelGGL(fill_2d_kernel, grid, dim3(256), 0, s, p, rows, cols, ld);
+hipError_t launch_fill_2d(int32_t* p, int64_t rows, int64_t cols, int64_t ld, int batch, int64_t bstride,
+                          hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
+  if (batch > 65535) return hipErrorInvalidValue;
+  const int64_t per = max64(1, 4096 / batch);  // row blocks per entry
+  dim3 grid((unsigned)min64(ceil_div(cols, 256), 64), (unsigned)min64(rows, per), (unsigned)batch);
+  hipLaunchKernelGGL(fill_2d_kernel, grid, dim3(256), 0, s, p, rows, cols, ld, bstride);
   return hipGetLastError();
 }
 
