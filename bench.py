@@ -216,13 +216,13 @@ def main():
     stages_us = {n: round(float(v) * 1000.0 / reps, 2) for n, v in zip(names, acc)}
 
     # dominant kernel: the unpacked int8 GEMM of the timed steps (events above)
-    gemm_ops = 2.0 * info["m_u"] * info["k_u"] * info["n_u"]
+    gemm_ops = sum(2.0 * f["m_u"] * f["k_u"] * f["n_u"] for f in infos)  # every batch entry
     gemm_tops = gemm_ops / t_gemm / 1e12
     traffic = None
     if GEMM_TRAFFIC is not None and GEMM_TRAFFIC["source_sha256"] == gemm_source_sha():
         traffic = GEMM_TRAFFIC["bytes_per_launch"]
 
-    eff_tops = 2.0 * M * N * K / t_step / 1e12
+    eff_tops = 2.0 * M * N * K * pr.a.batch / t_step / 1e12
     rec = {
         "metric": METRIC,
         "value": round(eff_tops, 3),
@@ -240,7 +240,7 @@ def main():
                                f"({pr.b.layout}), beta={pr.beta} b={pr.bits} p={pr.p_num}/{pr.p_den} "
                                f"{pr.strat_a}/{pr.strat_b}",
                    "M": M, "K": K, "N": N, "batch": pr.a.batch},
-        "unpack_ratio": round(info["unpack_ratio"], 4),
+        "unpack_ratio": round(sum(f["m_u"] * f["k_u"] * f["n_u"] for f in infos) / (pr.a.batch * M * K * N), 4),
         "plan": {"choice": list(info["choice"]), "m_u": info["m_u"], "k_u": info["k_u"], "n_u": info["n_u"],
                  "k_pad": info["k_pad"], "segments": info["n_seg"]},
         "gemm_pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
