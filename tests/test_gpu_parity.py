@@ -83,6 +83,19 @@ def test_wide_codes_match_oracle():
     _staged_problem(pr)
 
 
+def test_batch_entries_with_and_without_extra_tiles():
+    """One GEMM launch per pass serves every batch entry: here entry 0 has no
+    out-of-range code (its plan has no extra rows or columns) while entry 1's
+    heavy hitters unpack B into extra columns, so the extra-tile pass and the
+    base pass see entries of both kinds."""
+    pr = W.random_problem(seed=14, m=200, k=300, n=140, kind="gauss", dtype="f32", batch=2,
+                          strat_a="col", strat_b="col")
+    rng = np.random.Generator(np.random.PCG64(14))
+    for op in (pr.a, pr.b):
+        op.stored[0] = rng.choice(np.array([-1.0, 1.0], np.float32), size=op.stored[0].shape)
+    _staged_problem(pr)
+
+
 def _staged(cfg):
     _staged_problem(W.random_problem(**cfg))
 
