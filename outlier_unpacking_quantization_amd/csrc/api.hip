@@ -388,16 +388,22 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   const PlanLayout pl = plan_layout(M, K, N, batch, p->bits);
   if (batch > 65535) return fail(IMU_ERR_INVALID_ARG, "batch above 65535");
   // one launch per pass serves every entry: the grid takes the largest entry
+  // Entries with extra rows fold their extra tiles with atomics (C cleared
+  // first, then the atomic pass, then the base tiles add); entries with extra
+  // columns only fold them inside the base pass (each tile also multiplies the
+  // levels of its own columns) and store C once.
   int64_t base_tiles = 0, extra_tiles = 0;
-  bool any_extras = false;
+  bool any_rowx = false, any_colonly = false;
   for (int64_t b = 0; b < batch; ++b) {
     const imu_plan_info& f = info[b];
     if (f.m_base % 256 || f.n_base % 128 || f.m_alloc % 256 || f.n_alloc % 128)
       return fail(IMU_ERR_INVALID_ARG, "plan sizes are not tile multiples");
     base_tiles = std::max(base_tiles, (f.m_base / 256) * (f.n_base / 128));
-    if (f.m_alloc > f.m_base || f.n_alloc > f.n_base) {
-      any_extras = true;
+    if (f.m_alloc > f.m_base) {
+      any_rowx = true;
       extra_tiles = std::max(extra_tiles, (f.m_alloc / 256) * (f.n_alloc / 128));
+    } else if (f.n_alloc > f.n_base) {
+      any_colonly = true;
     }
   }
   GemmArgs g{};
@@ -408,6 +414,8 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   g.entry_stride = pl.entry_stride;
   g.amap_off = pl.amap;
   g.bmap_off = pl.bmap;
+  g.db_c_off = pl.db_c;
+  g.lvl_b_off = pl.lvl_b;
   g.stats_a = stats_a;
   g.stats_b = stats_b;
   g.stats_stride_a = la.stride;
@@ -422,19 +430,17 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   // Measurement events: attached to the launch when the call makes a single
   // one (no marker of their own in the stream), else recorded around all of
   // the call's launches.
-  if (g_gemm_ev[0] && any_extras) IMU_HIP(hipEventRecord(g_gemm_ev[0], s));
-  if (any_extras) {
-    // extra tiles first: C cleared, their folds added with atomics; the base
-    // tiles of those entries then add their part and write the output
+  if (g_gemm_ev[0] && any_rowx) IMU_HIP(hipEventRecord(g_gemm_ev[0], s));
+  if (any_rowx) {
     IMU_HIP(launch_fill_2d(c, M, N, ldc, (int)batch, cbs, s));
     g.mode = 2;
-    IMU_HIP(launch_gemm(g, extra_tiles, (int)batch, s));
+    IMU_HIP(launch_gemm(g, extra_tiles, (int)batch, false, s));
     g.mode = 0;
-    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, s));
+    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, any_colonly, s));
     if (g_gemm_ev[1]) IMU_HIP(hipEventRecord(g_gemm_ev[1], s));
   } else {
     g.mode = 0;
-    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, s, g_gemm_ev[0], g_gemm_ev[1]));
+    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, any_colonly, s, g_gemm_ev[0], g_gemm_ev[1]));
   }
   return IMU_OK;
 }

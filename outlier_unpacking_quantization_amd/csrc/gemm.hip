@@ -129,19 +129,74 @@ __device__ inline Cursor cursor_top(int nseg, SegTable off) {
   return c;
 }
 
-typedef __attribute__((address_space(4))) const PlanHeader* HdrC;
+// The walk of a tile that also folds extra columns (levels w > 0 of its own
+// columns): pairs (level w, segment s) in decreasing order of the combined
+// exponent w + s, each over its segment's K' steps, so one Horner accumulator
+// holds sum 2^((bits-1)(s+w)) P_(w,s).  Empty segments are skipped; once the
+// walk is over, k keeps growing (loads clamp it).
+struct FoldCursor {
+  int s, w, sum;
+  int64_t k, end;
+};
+__device__ inline bool fold_next_pair(FoldCursor& c, int nseg, int nlev, SegTable off) {
+  int s = c.s, w = c.w, sum = c.sum;
+  for (;;) {
+    if (w + 1 <= min(nlev - 1, sum)) {
+      ++w;
+    } else {
+      if (sum == 0) return false;
+      --sum;
+      w = max(0, sum - (nseg - 1));
+    }
+    s = sum - w;
+    if (off[s] != off[s + 1]) break;
+  }
+  c.s = s;
+  c.w = w;
+  c.sum = sum;
+  c.k = off[s];
+  c.end = off[s + 1];
+  return true;
+}
+__device__ inline void fold_advance(FoldCursor& c, int nseg, int nlev, SegTable off) {
+  c.k += BK;
+  if (c.k >= c.end && fold_next_pair(c, nseg, nlev, off))
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only (see cursor_advance)
+}
+__device__ inline FoldCursor fold_top(int nseg, int nlev, SegTable off) {
+  FoldCursor c;
+  c.w = nlev - 1;
+  c.sum = (nseg - 1) + (nlev - 1);
+  c.s = nseg - 1;
+  c.k = off[c.s];
+  c.end = off[c.s + 1];
+  if (c.k == c.end) fold_next_pair(c, nseg, nlev, off);
+  return c;
+}
 
+typedef __attribute__((address_space(4))) const PlanHeader* HdrC;
+constexpr int kMaxLevels = 32;  // digits of an int32 code in base 2^(bits-1), bits >= 2: at most 31
+
+// FOLD: the base pass also folds the extra columns of entries whose plan has
+// extra columns only (their levels w > 0 land on the tile's own columns), so
+// those entries need no atomic pass.
+template <bool FOLD>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BSTR];
+  __shared__ int32_t s_lvl[kMaxLevels - 1][BN];  // FOLD: B'^T row of (column, level w >= 1), -1 if none
+  __shared__ int s_nlev;
   // this workgroup's batch entry: sizes from its plan header (scalar loads)
   const int entry = blockIdx.y;
   const uint8_t* hdr = g.plan + (int64_t)entry * kPlanHeaderStride;
   const HdrC ph = (HdrC)hdr;
   const int64_t m_alloc = ph->m_alloc, n_alloc = ph->n_alloc, m_base = ph->m_base, n_base = ph->n_base;
   const int64_t kp = ph->k_pad;
-  const bool extras = m_alloc > m_base || n_alloc > n_base;
-  if (g.mode == 2 && !extras) return;
-  const int mode = g.mode == 2 ? 2 : extras ? 1 : 0;
+  const bool rowx = m_alloc > m_base, colx = n_alloc > n_base;
+  // the atomic pass serves entries with extra rows (and their extra columns);
+  // entries with extra columns only fold them in the base pass
+  if (g.mode == 2 && !rowx) return;
+  const int mode = g.mode == 2 ? 2 : rowx ? 1 : 0;
+  const bool colfold = FOLD && g.mode != 2 && !rowx && colx;
   const int64_t rows = mode == 2 ? m_alloc : m_base;
   const int64_t cols = mode == 2 ? n_alloc : n_base;
   const int tiles_m = (int)(rows / BM), tiles_n = (int)(cols / BN);
@@ -177,6 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int br = tid >> 3, bc = (tid & 7) * 16;
   const int8_t* gb = g.b_u + b_off + (col0 + br) * kp + bc;
   const int64_t gb_j = 32 * kp;
+  const int8_t* gbase = g.b_u + b_off + bc;
   const int sb_w = br * BSTR + bc;
   // B fragment j (columns col0 + 32j + lane%32) of substep q
   const int sb_r = (lane & 31) * BSTR + 16 * (lane >> 5);
@@ -190,9 +246,63 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 
   const SegTable off = (SegTable)ph->seg_off;
   const int nseg = ph->n_seg;
-  const int64_t steps = kp / BK;
-  Cursor cc = cursor_top(nseg, off);  // compute
-  Cursor la = cc, lb = cc;            // A loads (one step ahead), B loads (two ahead)
+  // levels of the tile's columns (1 unless this entry folds extra columns)
+  int nlev = 1;
+  int64_t gbo[4];    // byte offsets of the B staging rows at lb's level (FOLD)
+  uint32_t bvm = 0xF, bvl = 0xF;  // rows present at lb's level / in the last load (FOLD)
+  if constexpr (FOLD) {
+    if (colfold) {
+      const int32_t* dbc = reinterpret_cast<const int32_t*>(pe + g.db_c_off);
+      const int32_t* lvlb = reinterpret_cast<const int32_t*>(pe + g.lvl_b_off);
+      if (tid == 0) s_nlev = 1;
+      __syncthreads();
+      if (tid < BN && col0 + tid < g.N) atomicMax(&s_nlev, min(dbc[col0 + tid], kMaxLevels));
+      __syncthreads();
+      nlev = s_nlev;
+      for (int i = tid; i < (nlev - 1) * BN; i += kThreads) {
+        const int w = 1 + i / BN;
+        const int64_t n = col0 + i % BN;
+        s_lvl[w - 1][i % BN] = n < g.N ? lvlb[(int64_t)w * g.N + n] : -1;
+      }
+      __syncthreads();
+    }
+  }
+  // B staging rows of level w for this thread (FOLD); absent ones re-read the
+  // level-0 row and are zeroed when stored
+  auto set_level = [&](int w) __attribute__((always_inline)) {
+    bvm = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = br + 32 * j;
+      int64_t r = col0 + c;
+      if (w > 0) {
+        const int32_t x = s_lvl[w - 1][c];
+        if (x >= 0) r = x;
+        bvm |= (uint32_t)(x >= 0) << j;
+      } else {
+        bvm |= 1u << j;
+      }
+      gbo[j] = r * kp;
+    }
+  };
+  if constexpr (FOLD) set_level(0);
+  const int64_t steps = kp / BK * nlev;
+  using Cur = std::conditional_t<FOLD, FoldCursor, Cursor>;
+  auto top = [&]() __attribute__((always_inline)) {
+    if constexpr (FOLD) return fold_top(nseg, nlev, off);
+    else return cursor_top(nseg, off);
+  };
+  auto adv = [&](Cur& c) __attribute__((always_inline)) {
+    if constexpr (FOLD) fold_advance(c, nseg, nlev, off);
+    else cursor_advance(c, off);
+  };
+  auto expo = [](const Cur& c) __attribute__((always_inline)) {
+    if constexpr (FOLD) return c.sum;
+    else return c.s;
+  };
+  Cur cc = top();        // compute
+  Cur la = cc, lb = cc;  // A loads (one step ahead), B loads (two ahead)
+  int lbw = 0;           // level of lb's rows (FOLD)
 
   v4i ar[4][FR];  // A fragments of the current step, refilled substep by substep
   v4i bs[4];      // B staging registers
@@ -206,10 +316,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 #define IMU_LOAD_B(k)                                                                          \
   {                                                                                            \
     const int64_t k_ = min64((k), k_last);                                                     \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gb + j * gb_j + k_); \
+    if constexpr (FOLD) {                                                                      \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gbase + gbo[j] + k_); \
+      bvl = bvm;                                                                               \
+    } else {                                                                                   \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gb + j * gb_j + k_); \
+    }                                                                                          \
   }
-#define IMU_STORE_B(buf) \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(&sB[buf][sb_w + j * 32 * BSTR]) = bs[j];
+#define IMU_STORE_B(buf)                                                                       \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(&sB[buf][sb_w + j * 32 * BSTR]) = \
+      (!FOLD || ((bvl >> j) & 1u)) ? bs[j] : v4i{0, 0, 0, 0};
+#define IMU_ADV_B()                                                                            \
+  {                                                                                            \
+    adv(lb);                                                                                   \
+    if constexpr (FOLD) {                                                                      \
+      if (lb.w != lbw) {                                                                       \
+        lbw = lb.w;                                                                            \
+        set_level(lbw);                                                                        \
+      }                                                                                        \
+    }                                                                                          \
+  }
 #define IMU_READ_B(d, sbuf, q) \
   _Pragma("unroll") for (int j = 0; j < 4; ++j) bf[d][j] = *reinterpret_cast<const v4i*>((sbuf) + sb_r + j * 32 * BSTR + 32 * (q));
 #define IMU_MFMA(d, q)                                                                             \
@@ -219,19 +345,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 
 #pragma unroll
   for (int q = 0; q < 4; ++q) IMU_LOAD_A(q, la.k);
-  cursor_advance(la, off);
+  adv(la);
+  if constexpr (FOLD) set_level(lb.w), lbw = lb.w;
   IMU_LOAD_B(lb.k);
-  cursor_advance(lb, off);
+  IMU_ADV_B();
   IMU_STORE_B(0);
   IMU_LOAD_B(lb.k);
-  cursor_advance(lb, off);
+  IMU_ADV_B();
   __syncthreads();
   IMU_READ_B(0, sB[0], 0);
-  int prev_s = cc.s;
+  int prev_s = expo(cc);
   for (int64_t i = 0; i < steps; ++i) {
-    if (cc.s != prev_s) {  // Horner: the exponents between the two segments
-      shift_acc(acc, shift * (prev_s - cc.s));
-      prev_s = cc.s;
+    if (expo(cc) != prev_s) {  // Horner: the exponents between the two steps
+      shift_acc(acc, shift * (prev_s - expo(cc)));
+      prev_s = expo(cc);
     }
     const int8_t* sbuf = sB[i & 1];
 #pragma unroll
@@ -244,21 +371,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     }
     IMU_STORE_B((i + 1) & 1);  // B of step i+1 (loaded during step i-1)
     IMU_LOAD_B(lb.k);          // B of step i+2
-    cursor_advance(lb, off);
+    IMU_ADV_B();
     __syncthreads();
     IMU_READ_B(0, sB[(i + 1) & 1], 0);
     __builtin_amdgcn_sched_barrier(0);
     IMU_MFMA(1, 3);
     IMU_LOAD_A(3, la.k);
     __builtin_amdgcn_sched_barrier(0);
-    cursor_advance(la, off);
-    cursor_advance(cc, off);
+    adv(la);
+    adv(cc);
   }
 #undef IMU_LOAD_A
 #undef IMU_LOAD_B
 #undef IMU_STORE_B
 #undef IMU_READ_B
 #undef IMU_MFMA
+#undef IMU_ADV_B
   if (prev_s > 0) shift_acc(acc, shift * prev_s);  // exponents below the last non-empty segment
 
   // epilogue: accumulator register r of lane l holds element
@@ -345,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, int64_t tiles_x, int batch, hipStream_t s, hipEvent_t start,
+hipError_t launch_gemm(const GemmArgs& g, int64_t tiles_x, int batch, bool fold, hipStream_t s, hipEvent_t start,
                        hipEvent_t stop) {
   if (tiles_x > 0x7FFFFFFF || batch < 1 || batch > 65535) return hipErrorInvalidValue;
   if (tiles_x <= 0) {  // nothing to launch: the events still get recorded
@@ -354,8 +482,13 @@ hipError_t launch_gemm(const GemmArgs& g, int64_t tiles_x, int batch, hipStream_
     return hipGetLastError();
   }
   const dim3 grid((unsigned)tiles_x, (unsigned)batch);
-  if (start || stop) hipExtLaunchKernelGGL(gemm_kernel, grid, dim3(kThreads), 0, s, start, stop, 0, g);
-  else hipLaunchKernelGGL(gemm_kernel, grid, dim3(kThreads), 0, s, g);
+  if (fold) {
+    if (start || stop) hipExtLaunchKernelGGL(gemm_kernel<true>, grid, dim3(kThreads), 0, s, start, stop, 0, g);
+    else hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(kThreads), 0, s, g);
+  } else {
+    if (start || stop) hipExtLaunchKernelGGL(gemm_kernel<false>, grid, dim3(kThreads), 0, s, start, stop, 0, g);
+    else hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(kThreads), 0, s, g);
+  }
   return hipGetLastError();
 }
 

@@ -61,7 +61,7 @@ struct GemmArgs {
   const int8_t* a_u;
   const int8_t* b_u;
   const uint8_t* plan;        // plan buffer (headers, then per-entry arrays)
-  int64_t headers_bytes, entry_stride, amap_off, bmap_off;  // PlanLayout of the plan
+  int64_t headers_bytes, entry_stride, amap_off, bmap_off, db_c_off, lvl_b_off;  // PlanLayout of the plan
   const uint8_t* stats_a;
   const uint8_t* stats_b;
   int64_t stats_stride_a, stats_stride_b;
@@ -70,13 +70,15 @@ struct GemmArgs {
   int64_t ldc, cbs;           // C / out row stride and batch stride
   int64_t M, N;
   int bits;
-  int mode;                   // 2: extra tiles (atomics); else base tiles (per entry: store C, or add to
-                              // C when the entry has extra tiles)
+  int mode;                   // 2: extra tiles of entries with extra rows (atomics); else base tiles (per
+                              // entry: add to C after that pass, or store C, folding extra columns)
 };
 // tiles_x: the largest tile count of an entry for this mode; batch entries on
 // blockIdx.y.  start / stop: events recorded as the launch starts / ends
 // (attached to it), or null
-hipError_t launch_gemm(const GemmArgs& a, int64_t tiles_x, int batch, hipStream_t s, hipEvent_t start = nullptr,
-                       hipEvent_t stop = nullptr);
+// fold: the base pass also folds the extra columns of entries with extra
+// columns only (required whenever such an entry is present)
+hipError_t launch_gemm(const GemmArgs& a, int64_t tiles_x, int batch, bool fold, hipStream_t s,
+                       hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace imu
