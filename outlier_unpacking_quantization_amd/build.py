@@ -26,6 +26,10 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source additions.  The GEMM's main loop runs measurably slower (about 3%)
+# when the placement of earlier code leaves its header unaligned, so its loops
+# start on 64-byte boundaries.
+EXTRA_FLAGS = {"gemm.hip": ["-falign-loops=64"]}
 
 
 def _run(cmd):
@@ -44,7 +48,7 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for cmd, r in zip(cmds, ex.map(_run, cmds)):
             if verbose:
