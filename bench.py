@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 # version of the GEMM source: when gemm.hip no longer hashes to `source_sha256`
 # the traffic is reported as null.
 GEMM_TRAFFIC = {
-    "source_sha256": "1ecc4408eac33976d464c1394943940c01b31126a2f09ecbe8ee4d843aa6b3b1",
+    "source_sha256": "b0c90ad389bb716c95a04f6ff421f972ccaa545c176c29e7f1ad0ee076859aca",
     "fetch_kib": 151760.6, "write_kib": 65536.0,        # counter readings per launch
     "fetch_factor": 1.99980, "write_factor": 1.00000,  # copy calibration
     "bytes_per_launch": 377883038,

@@ -8,9 +8,14 @@
 // accumulation.  Here every digit is int8 and the products run on
 // v_mfma_i32_32x32x32_i8.  K' is split into exponent segments; walking them from
 // the highest exponent down, acc = acc * 2^(bits-1) + P_e (Horner), so one set
-// of int32 accumulators holds sum_e 2^((bits-1)e) P_e.  The epilogue folds the
-// unpacked row (i, u) and column (n, w) into C[i, n] with a further shift of
-// (bits-1)(u+w); all int32 arithmetic wraps modulo 2^32.
+// of int32 accumulators holds sum_e 2^((bits-1)e) P_e.  The unpacked row (i, u)
+// and column (n, w) fold into C[i, n] with a further shift of (bits-1)(u+w);
+// all int32 arithmetic wraps modulo 2^32.  Extra columns (w > 0) of a plan
+// without extra rows are folded inside the base tile of their original
+// columns: the shift is one more exponent, so the tile walks (level, segment)
+// pairs by combined exponent under the same Horner accumulator, with the B'^T
+// rows of level w staged into the LDS slots of their own columns.  Extra rows
+// fold in a separate pass of extra tiles with atomic adds.
 //
 // Operands: A' (m_alloc x k_pad) in MFMA fragment order and B'^T (n_alloc x
 // k_pad), both K-contiguous.  Workgroup tile 256 x 128, four waves stacked along
