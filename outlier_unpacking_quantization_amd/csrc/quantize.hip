@@ -759,15 +759,20 @@ __global__ __launch_bounds__(kResidualThreads) void residual_kernel(QuantJobs J)
   const int64_t c0 = cbase + lane * 8;
   const int64_t r0 = rb * op.rows_per_wg;
   const int64_t r1 = min64(r0 + op.rows_per_wg, a.srows);
-  // the first two groups of rows are in flight while the workgroup sets up
-#define IMU_ISSUE(g, sb_)                                                                          \
-  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr)                                      \
-      g[rr] = load_raw<DT, VEC>(xb + min64((sb_) + rr, r1 - 1) * a.ld, c0, a.scols);
+  // the first two groups of rows are in flight while the workgroup sets up;
+  // a group's row counts are loaded with its elements, so the loop never
+  // waits on a count of its own
+#define IMU_ISSUE(g, ro, sb_)                                                                      \
+  _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                   \
+    g[rr] = load_raw<DT, VEC>(xb + min64((sb_) + rr, r1 - 1) * a.ld, c0, a.scols);                  \
+    ro[rr] = srow_oob[min64((sb_) + rr, r1 - 1)];                                                  \
+  }
   const int64_t gstep = (int64_t)nwave * kRowsInFlight;
   typename RawOf<DT>::V g0[kRowsInFlight], g1[kRowsInFlight];
+  int32_t ro0[kRowsInFlight], ro1[kRowsInFlight];  // row counts of the two groups
   int64_t sb = r0 + (int64_t)wave * kRowsInFlight;
-  IMU_ISSUE(g0, sb);
-  IMU_ISSUE(g1, sb + gstep);
+  IMU_ISSUE(g0, ro0, sb);
+  IMU_ISSUE(g1, ro1, sb + gstep);
   for (int i = threadIdx.x; i < kColsPerTile; i += blockDim.x) lmax[i] = 0;
   __syncthreads();
   const float r = hd->r;
@@ -797,13 +802,13 @@ __global__ __launch_bounds__(kResidualThreads) void residual_kernel(QuantJobs J)
 #pragma unroll
   for (int d = 0; d < NW; ++d) cmx[d] = 0;
   bool col_seen = false;  // the wave took a non-heavy row
-#define IMU_PROCESS(g, sb_)                                                                        \
+#define IMU_PROCESS(g, ro, sb_)                                                                    \
   {                                                                                                \
     uint32_t rm_[kRowsInFlight];                                                                   \
     _Pragma("unroll") for (int rr = 0; rr < kRowsInFlight; ++rr) {                                 \
       rm_[rr] = 0;                                                                                 \
       if ((sb_) + rr < r1) { /* uniform across the wave */                                         \
-        const bool rheavy = (long long)srow_oob[(sb_) + rr] * a.srows > gT;                        \
+        const bool rheavy = (long long)ro[rr] * a.srows > gT;                                      \
         uint32_t m_ = 0;                                                                           \
         _Pragma("unroll") for (int d = 0; d < NW; ++d) {                                           \
           if constexpr (DT == IMU_BF16) m_ = pk_max_u16(m_, g[rr][d] & lm[d]);                     \
@@ -829,11 +834,11 @@ __global__ __launch_bounds__(kResidualThreads) void residual_kernel(QuantJobs J)
     }                                                                                              \
   }
   for (; sb < r1; sb += 2 * gstep) {
-    IMU_PROCESS(g0, sb);
+    IMU_PROCESS(g0, ro0, sb);
     if (sb + gstep >= r1) break;
-    IMU_ISSUE(g0, sb + 2 * gstep);  // unconditional (rows clamped), so the loads in flight are known exactly
-    IMU_PROCESS(g1, sb + gstep);
-    IMU_ISSUE(g1, sb + 3 * gstep);
+    IMU_ISSUE(g0, ro0, sb + 2 * gstep);  // unconditional (rows clamped), so the loads in flight are known exactly
+    IMU_PROCESS(g1, ro1, sb + gstep);
+    IMU_ISSUE(g1, ro1, sb + 3 * gstep);
   }
 #undef IMU_ISSUE
 #undef IMU_PROCESS
