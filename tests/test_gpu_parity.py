@@ -96,6 +96,21 @@ def test_batch_entries_with_and_without_extra_tiles():
     _staged_problem(pr)
 
 
+def test_batch_mixing_extra_rows_and_folded_extra_columns():
+    """A (row unpacking) is all in range in entry 0, so that entry has extra
+    columns only (from B, column unpacking) and folds them inside its base
+    tiles, while entry 1 also has extra rows and takes the atomic pass: both
+    kinds share the two GEMM launches."""
+    pr = W.random_problem(seed=15, m=260, k=200, n=300, kind="gauss", dtype="f32", batch=2,
+                          strat_a="row", strat_b="col")
+    rng = np.random.Generator(np.random.PCG64(15))
+    pr.a.stored[0] = rng.choice(np.array([-1.0, 1.0], np.float32), size=pr.a.stored[0].shape)
+    refs = G.oracle_entries(pr)
+    assert refs[0].plan.choice.m_u == 260 and refs[0].plan.choice.n_u > 300
+    assert refs[1].plan.choice.m_u > 260 and refs[1].plan.choice.n_u > 300
+    _staged_problem(pr)
+
+
 def _staged(cfg):
     _staged_problem(W.random_problem(**cfg))
 
