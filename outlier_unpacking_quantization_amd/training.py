@@ -1,0 +1,80 @@
+"""Quantized-training linear layer: y = x W^T, whose three GEMMs per step
+(forward, data gradient, weight gradient) each run the whole IM-Unpack path
+through ``imu_imunpack_matmul``.
+
+Method: summary page "IM-Unpack: Training and Inference with Arbitrarily Low
+Precision Integers", summary paragraph and "Key results": the page trains
+models with the GEMMs of the forward and the backward pass replaced by their
+low bit-width integer versions, which IM-Unpack computes exactly from the RTN
+codes of the operands (no clipping of heavy hitters).  Each product below is
+one such GEMM:
+
+    forward          y  = x  @ W^T     A = x  (tokens x d_in),   B = W^T
+    data gradient    dx = dy @ W       A = dy (tokens x d_out),  B = W
+    weight gradient  dW = dy^T @ x     A = dy^T,                 B = x
+
+Every operand is quantized per matrix for the product it enters (its own
+percentile scale), transposes are views (no copies), and the incoming
+gradient enters as float32, so no rounding happens before its RTN.  The
+outputs are the dequantized float32 products; autograd receives them in the
+dtype of the tensor they belong to.  Quantized tensors are not shared between
+the three products (each call quantizes its operands again).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import binding as B
+
+
+def linear_forward(x: torch.Tensor, w: torch.Tensor, p: B.ImuParams,
+                   ws: Optional[B.Workspace] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(y float32, C int32) of y = x @ W^T; x: (tokens, d_in), w: (d_out, d_in)."""
+    out, c, _ = B.imunpack_matmul(B.Matrix(x), B.Matrix(w, "transposed"), p, ws=ws)
+    return out[0], c[0]
+
+
+def linear_data_grad(dy: torch.Tensor, w: torch.Tensor, p: B.ImuParams,
+                     ws: Optional[B.Workspace] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(dx float32, C int32) of dx = dy @ W; dy: (tokens, d_out), w: (d_out, d_in)."""
+    out, c, _ = B.imunpack_matmul(B.Matrix(dy), B.Matrix(w), p, ws=ws)
+    return out[0], c[0]
+
+
+def linear_weight_grad(dy: torch.Tensor, x: torch.Tensor, p: B.ImuParams,
+                       ws: Optional[B.Workspace] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(dW float32, C int32) of dW = dy^T @ x; dy: (tokens, d_out), x: (tokens, d_in)."""
+    out, c, _ = B.imunpack_matmul(B.Matrix(dy, "transposed"), B.Matrix(x), p, ws=ws)
+    return out[0], c[0]
+
+
+class IMUnpackLinearFunction(torch.autograd.Function):
+    """y = x @ W^T with the forward and both gradients computed by IM-Unpack."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, p: B.ImuParams, ws: Optional[B.Workspace]):
+        if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+            raise B.ImunpackError(B.ERR_INVALID_ARG, "x must be (tokens, d_in) and w (d_out, d_in)")
+        x, w = x.contiguous(), w.contiguous()
+        ctx.save_for_backward(x, w)
+        ctx.p, ctx.ws = p, ws
+        return linear_forward(x, w, p, ws)[0]
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        x, w = ctx.saved_tensors
+        dy = dy.to(torch.float32).contiguous()
+        dx = dw = None
+        if ctx.needs_input_grad[0]:
+            dx = linear_data_grad(dy, w, ctx.p, ctx.ws)[0].to(x.dtype)
+        if ctx.needs_input_grad[1]:
+            dw = linear_weight_grad(dy, x, ctx.p, ctx.ws)[0].to(w.dtype)
+        return dx, dw, None, None
+
+
+def imunpack_linear(x: torch.Tensor, w: torch.Tensor, p: B.ImuParams,
+                    ws: Optional[B.Workspace] = None) -> torch.Tensor:
+    """y = x @ W^T (float32) with IM-Unpack in the forward and the backward pass."""
+    return IMUnpackLinearFunction.apply(x, w, p, ws)

@@ -130,3 +130,13 @@ def test_binding_matrix_marshalling():
         B.Matrix(torch.zeros((4, 4), dtype=torch.float64)).c()
     with pytest.raises(B.ImunpackError):
         B.Matrix(torch.zeros((4, 4)).t()).c()  # non-unit last stride
+
+
+def test_training_wrapper_rejects_bad_shapes():
+    torch = pytest.importorskip("torch")
+    from outlier_unpacking_quantization_amd import training as T
+    p = B.params(beta=31, bits=4)
+    with pytest.raises(B.ImunpackError):
+        T.imunpack_linear(torch.zeros(4, 3), torch.zeros(5, 2), p)
+    with pytest.raises(B.ImunpackError):
+        T.imunpack_linear(torch.zeros(4, 3, 2), torch.zeros(5, 3), p)
