@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--config", type=int, default=1, help="workload recipe index (default 1: LLaMA linear)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-repeats", type=int, default=1)
+    ap.add_argument("--training-step", action="store_true",
+                    help="time the quantized-training linear step (forward, data gradient, weight gradient) "
+                         "at the training workload size instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -145,6 +148,49 @@ def cpu_baseline(pr, repeats: int):
                       f"host cpus={os.cpu_count()}"}
 
 
+def training_step(args):
+    """One step = the three GEMMs of a linear layer's training step (forward,
+    data gradient, weight gradient), each the whole IM-Unpack path, on the
+    training workload (8192 tokens, 768 -> 3072, beta=31, b=4, Mix)."""
+    import torch
+    from outlier_unpacking_quantization_amd import binding as B
+    from outlier_unpacking_quantization_amd import training as T
+    from outlier_unpacking_quantization_amd import workloads as W
+
+    fwd, dgrad, _ = W.training()
+    dev = "cuda"
+    bf = lambda st: torch.from_numpy(np.ascontiguousarray(st[0]).view(np.int16)).view(torch.bfloat16).to(dev)
+    x = bf(fwd.a.stored)          # tokens x d_in
+    w = bf(fwd.b.stored)          # d_out x d_in (W^T stored transposed)
+    dy = bf(dgrad.a.stored).float()  # tokens x d_out, entering as float32
+    tokens, d_in = x.shape
+    d_out = w.shape[0]
+    p = B.params(beta=fwd.beta, bits=fwd.bits)
+    ws = B.Workspace(dev)
+
+    def step():
+        T.linear_forward(x, w, p, ws)
+        T.linear_data_grad(dy, w, p, ws)
+        T.linear_weight_grad(dy, x, p, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / args.steps
+    ops = 3 * 2.0 * tokens * d_in * d_out
+    print(json.dumps({"metric": "effective int-TOPS of a quantized-training linear step (fwd + dgrad + wgrad)",
+                      "value": round(ops / t / 1e12, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True,
+                      "dtype": "i8", "data": "synthetic",
+                      "config": {"workload": f"training linear: X {tokens}x{d_in} bf16, W {d_out}x{d_in} bf16, "
+                                             f"dY {tokens}x{d_out} (float32 from bf16), beta={fwd.beta} b={fwd.bits} "
+                                             "p=95/100 mix/mix"}}))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -155,6 +201,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.training_step:
+        training_step(args)
         return
 
     import torch
