@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -389,21 +390,35 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   if (batch > 65535) return fail(IMU_ERR_INVALID_ARG, "batch above 65535");
   // one launch per pass serves every entry: the grid takes the largest entry
   // Entries with extra rows fold their extra tiles with atomics (C cleared
-  // first, then the atomic pass, then the base tiles add); entries with extra
+  // first, then the atomic pass, then the base tiles add).  Entries with extra
   // columns only fold them inside the base pass (each tile also multiplies the
-  // levels of its own columns) and store C once.
-  int64_t base_tiles = 0, extra_tiles = 0;
-  bool any_rowx = false, any_colonly = false;
+  // levels of its own columns) and store C once, provided the base tiles of
+  // the call fill the GPU: with fewer tiles than CUs the folded work would sit
+  // on a few CUs, and the atomic pass spreads it over the extra tiles instead.
+  int64_t base_tiles = 0, base_total = 0;
   for (int64_t b = 0; b < batch; ++b) {
     const imu_plan_info& f = info[b];
     if (f.m_base % 256 || f.n_base % 128 || f.m_alloc % 256 || f.n_alloc % 128)
       return fail(IMU_ERR_INVALID_ARG, "plan sizes are not tile multiples");
     base_tiles = std::max(base_tiles, (f.m_base / 256) * (f.n_base / 128));
-    if (f.m_alloc > f.m_base) {
-      any_rowx = true;
+    base_total += (f.m_base / 256) * (f.n_base / 128);
+  }
+  int dev = 0, cus = 0;
+  IMU_HIP(hipGetDevice(&dev));
+  IMU_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  // IMU_FOLD_COLUMNS=1 / 0 forces the choice (both give the same result)
+  const char* fe = std::getenv("IMU_FOLD_COLUMNS");
+  const bool fold_cols = fe && fe[0] == '1' ? true : fe && fe[0] == '0' ? false : base_total >= cus;
+  int64_t extra_tiles = 0;
+  bool any_atomic = false, any_fold = false;
+  for (int64_t b = 0; b < batch; ++b) {
+    const imu_plan_info& f = info[b];
+    const bool rowx = f.m_alloc > f.m_base, colx = f.n_alloc > f.n_base;
+    if (rowx || (colx && !fold_cols)) {
+      any_atomic = true;
       extra_tiles = std::max(extra_tiles, (f.m_alloc / 256) * (f.n_alloc / 128));
-    } else if (f.n_alloc > f.n_base) {
-      any_colonly = true;
+    } else if (colx) {
+      any_fold = true;
     }
   }
   GemmArgs g{};
@@ -427,20 +442,21 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   g.M = M;
   g.N = N;
   g.bits = p->bits;
+  g.fold_cols = fold_cols ? 1 : 0;
   // Measurement events: attached to the launch when the call makes a single
   // one (no marker of their own in the stream), else recorded around all of
   // the call's launches.
-  if (g_gemm_ev[0] && any_rowx) IMU_HIP(hipEventRecord(g_gemm_ev[0], s));
-  if (any_rowx) {
+  if (g_gemm_ev[0] && any_atomic) IMU_HIP(hipEventRecord(g_gemm_ev[0], s));
+  if (any_atomic) {
     IMU_HIP(launch_fill_2d(c, M, N, ldc, (int)batch, cbs, s));
     g.mode = 2;
     IMU_HIP(launch_gemm(g, extra_tiles, (int)batch, false, s));
     g.mode = 0;
-    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, any_colonly, s));
+    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, any_fold, s));
     if (g_gemm_ev[1]) IMU_HIP(hipEventRecord(g_gemm_ev[1], s));
   } else {
     g.mode = 0;
-    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, any_colonly, s, g_gemm_ev[0], g_gemm_ev[1]));
+    IMU_HIP(launch_gemm(g, base_tiles, (int)batch, any_fold, s, g_gemm_ev[0], g_gemm_ev[1]));
   }
   return IMU_OK;
 }

@@ -197,11 +197,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int64_t m_alloc = ph->m_alloc, n_alloc = ph->n_alloc, m_base = ph->m_base, n_base = ph->n_base;
   const int64_t kp = ph->k_pad;
   const bool rowx = m_alloc > m_base, colx = n_alloc > n_base;
-  // the atomic pass serves entries with extra rows (and their extra columns);
-  // entries with extra columns only fold them in the base pass
-  if (g.mode == 2 && !rowx) return;
-  const int mode = g.mode == 2 ? 2 : rowx ? 1 : 0;
-  const bool colfold = FOLD && g.mode != 2 && !rowx && colx;
+  // the atomic pass serves entries with extra rows (and their extra columns),
+  // and entries with extra columns only unless those are folded in the base
+  // pass (g.fold_cols)
+  const bool atomic_entry = rowx || (colx && !g.fold_cols);
+  if (g.mode == 2 && !atomic_entry) return;
+  const int mode = g.mode == 2 ? 2 : atomic_entry ? 1 : 0;
+  const bool colfold = FOLD && g.mode != 2 && !atomic_entry && colx;
   const int64_t rows = mode == 2 ? m_alloc : m_base;
   const int64_t cols = mode == 2 ? n_alloc : n_base;
   const int tiles_m = (int)(rows / BM), tiles_n = (int)(cols / BN);

@@ -70,8 +70,9 @@ struct GemmArgs {
   int64_t ldc, cbs;           // C / out row stride and batch stride
   int64_t M, N;
   int bits;
-  int mode;                   // 2: extra tiles of entries with extra rows (atomics); else base tiles (per
+  int mode;                   // 2: extra tiles of the entries folded by atomics; else base tiles (per
                               // entry: add to C after that pass, or store C, folding extra columns)
+  int fold_cols;              // entries with extra columns only fold them in the base pass
 };
 // tiles_x: the largest tile count of an entry for this mode; batch entries on
 // blockIdx.y.  start / stop: events recorded as the launch starts / ends

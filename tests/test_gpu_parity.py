@@ -83,11 +83,14 @@ def test_wide_codes_match_oracle():
     _staged_problem(pr)
 
 
-def test_batch_entries_with_and_without_extra_tiles():
+@pytest.mark.parametrize("fold", ["1", "0"], ids=["fold_columns", "atomic_columns"])
+def test_batch_entries_with_and_without_extra_tiles(fold, monkeypatch):
     """One GEMM launch per pass serves every batch entry: here entry 0 has no
     out-of-range code (its plan has no extra rows or columns) while entry 1's
     heavy hitters unpack B into extra columns, so the extra-tile pass and the
-    base pass see entries of both kinds."""
+    base pass see entries of both kinds.  Run with the extra columns folded
+    inside the base tiles and with the atomic pass (IMU_FOLD_COLUMNS)."""
+    monkeypatch.setenv("IMU_FOLD_COLUMNS", fold)
     pr = W.random_problem(seed=14, m=200, k=300, n=140, kind="gauss", dtype="f32", batch=2,
                           strat_a="col", strat_b="col")
     rng = np.random.Generator(np.random.PCG64(14))
@@ -96,11 +99,13 @@ def test_batch_entries_with_and_without_extra_tiles():
     _staged_problem(pr)
 
 
-def test_batch_mixing_extra_rows_and_folded_extra_columns():
+def test_batch_mixing_extra_rows_and_folded_extra_columns(monkeypatch):
     """A (row unpacking) is all in range in entry 0, so that entry has extra
     columns only (from B, column unpacking) and folds them inside its base
     tiles, while entry 1 also has extra rows and takes the atomic pass: both
-    kinds share the two GEMM launches."""
+    kinds share the two GEMM launches (folding forced: the problem has fewer
+    base tiles than the GPU has CUs)."""
+    monkeypatch.setenv("IMU_FOLD_COLUMNS", "1")
     pr = W.random_problem(seed=15, m=260, k=200, n=300, kind="gauss", dtype="f32", batch=2,
                           strat_a="row", strat_b="col")
     rng = np.random.Generator(np.random.PCG64(15))
