@@ -37,10 +37,10 @@ HBM_PEAK_GBS = 8000.0
 # version of the GEMM source: when gemm.hip no longer hashes to `source_sha256`
 # the traffic is reported as null.
 GEMM_TRAFFIC = {
-    "source_sha256": "b0c90ad389bb716c95a04f6ff421f972ccaa545c176c29e7f1ad0ee076859aca",
-    "fetch_kib": 151760.6, "write_kib": 65536.0,        # counter readings per launch
+    "source_sha256": "9f179b4b771cddb04e32901c9ce05bb9939bf615b38f57d1d4242e0c8bdcd7b9",
+    "fetch_kib": 151790.0, "write_kib": 65536.0,        # counter readings per launch
     "fetch_factor": 1.99980, "write_factor": 1.00000,  # copy calibration
-    "bytes_per_launch": 377883038,
+    "bytes_per_launch": 377943480,
 }
 
 
