@@ -195,7 +195,12 @@ imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p,
  * element (i,u),(n,w) then adds acc << ((bits-1)(u+w)) into C[i,n] (mod 2^32).
  * c: int32 M x N row-major per entry (ldc elements per row, entries
  * c_batch_stride apart).  out (optional): fl32(fl32(C) * fl32(s_A * s_B)),
- * same layout as c.  The caller's info must come from the same plan. */
+ * same layout as c.  The caller's info must come from the same plan.
+ * Extra columns of a plan without extra rows are folded inside the tiles of
+ * their original columns when the call's output tiles (256 x 128) are at least
+ * as many as the GPU's CUs, else in a pass of extra tiles with atomic adds (as
+ * extra rows always are); the environment variable IMU_FOLD_COLUMNS=1 or 0
+ * forces either way.  The result is the same. */
 imu_status imu_unpacked_gemm(const int8_t* a_u, const int8_t* b_u, const imu_params* p,
                              const void* stats_a, const void* stats_b, const void* plan,
                              const imu_plan_info* info, int64_t batch, int32_t* c, int64_t ldc,
