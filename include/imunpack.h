@@ -10,9 +10,9 @@
  * (summary paragraph, "Problem").  Out-of-range integers are unpacked into
  * several in-range b-bit integers placed in extra rows or columns, chosen per
  * matrix from outlier counts (row, column or Mix unpacking; "Approach" and the
- * unpack-ratio rows of the table), and low bit-width GEMMs on the unpacked
- * matrices followed by bit-shift scaling and accumulation give the original
- * integer product exactly ("Approach").
+ * unpack-ratio rows of the table); products of the unpacked narrow-integer
+ * matrices, multiplied by powers of two and summed, equal the original integer
+ * product ("Approach").
  *
  * Conventions (all entry points)
  * ------------------------------
@@ -188,7 +188,7 @@ imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p,
                       int8_t* x_u, hipStream_t stream);
 
 /* Low bit-width GEMMs on the unpacked operands with the shift-and-accumulate
- * fold and dequantization ("Approach": bit-shift scaling and accumulation
+ * fold and dequantization ("Approach": power-of-two scaling and summation
  * reproduce the integer GEMM exactly).  For each exponent segment e the int8
  * MFMA product P_e = A'[:,K'_e] . B'[K'_e,:] is accumulated as
  * acc = acc * 2^(bits-1) + P_e (from the highest e down); each unpacked

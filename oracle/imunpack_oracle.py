@@ -12,10 +12,11 @@ Low Precision Integers" (atlas.scime.ai).  The page fixes what is computed:
   p=95%, beta=15/31; p=100% restricts every value to the range);
 * heavy hitters stay as out-of-range integers, they are not clipped
   (summary paragraph and "Problem");
-* out-of-range integers are decomposed into several in-range low bit-width
-  integers by row or column unpacking chosen per matrix from outlier counts,
-  and low bit-width GEMMs followed by bit-shift scaling and accumulation
-  reproduce the original integer GEMM exactly ("Approach");
+* each out-of-range integer is split into several in-range narrow integers
+  held in added rows or columns, the row/column choice made for each matrix
+  from how many outliers its lines hold; narrow-integer products, each
+  multiplied by a power of two and summed, then give back the integer product
+  without error ("Approach");
 * the Mix strategy beats every fixed row/column pairing ("Measured effects"
   table, unpack-ratio rows).
 
@@ -375,7 +376,7 @@ def exact_matmul(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 def segment_products(Ap: np.ndarray, Bp: np.ndarray, trip: np.ndarray, bits: int,
                      big: bool = False) -> np.ndarray:
     """O11: P_e = A'[:, K'_e] @ B'[K'_e, :] for every exponent segment e, then
-    P = sum_e S**e * P_e (the bit-shift scaling of the "Approach" section)."""
+    P = sum_e S**e * P_e (power-of-two scaling and summation, "Approach" section)."""
     S = digit_base(bits)
     P = np.zeros((Ap.shape[0], Bp.shape[1]), object if big else np.int64)
     for e in np.unique(trip[:, 3]) if trip.size else []:

@@ -3,9 +3,9 @@
 // every batch entry (blockIdx.y).
 //
 // Method: summary page "IM-Unpack: Training and Inference with Arbitrarily Low
-// Precision Integers", "Approach": the original integer GEMM is reproduced
-// exactly by low bit-width integer GEMMs followed by bit-shift scaling and
-// accumulation.  Here every digit is int8 and the products run on
+// Precision Integers", "Approach": products of the narrow-integer unpacked
+// matrices, multiplied by powers of two and summed, give the integer product of
+// the original operands with no error.  Here every digit is int8 and the products run on
 // v_mfma_i32_32x32x32_i8.  K' is split into exponent segments; walking them from
 // the highest exponent down, acc = acc * 2^(bits-1) + P_e (Horner), so one set
 // of int32 accumulators holds sum_e 2^((bits-1)e) P_e.  The unpacked row (i, u)

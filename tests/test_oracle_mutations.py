@@ -14,6 +14,7 @@ from oracle import imunpack_oracle as O
 from tests import test_oracle_pins as P
 
 PINS = [
+    P.test_widen_every_bf16_pattern,
     P.test_percentile_matches_sorted_bruteforce,
     P.test_scale_is_correctly_rounded_division,
     P.test_rtn_matches_exact_rational_rounding,
@@ -58,6 +59,20 @@ def _rank_floor(count, p_num, p_den):
 def _digit_unsigned(q, bits, t):
     S = 1 << (bits - 1)
     return (np.abs(np.asarray(q, np.int64)) // (S ** t)) % S
+
+
+def _widen_shift_15(stored, dtype):
+    if dtype == "bf16":
+        bits = np.asarray(stored, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+        return bits.view(np.float32)
+    return np.asarray(stored, dtype=np.float32)
+
+
+def _widen_through_f16(stored, dtype):
+    # reads the stored half-word as IEEE binary16 instead of bfloat16
+    if dtype == "bf16":
+        return np.asarray(stored, dtype=np.uint16).view(np.float16).astype(np.float32)
+    return np.asarray(stored, dtype=np.float32)
 
 
 def _placement_outer_first(t, d_k):
@@ -131,6 +146,8 @@ def _exact_matmul_drop_last_column(a, b):
 
 
 MUTATIONS = {
+    "widen_shift_15": ("widen", _widen_shift_15),
+    "widen_reads_binary16": ("widen", _widen_through_f16),
     "rtn_half_up": ("rtn", _rtn_half_up),
     "percentile_floor_rank": ("percentile_rank", _rank_floor),
     "digit_drops_sign": ("digit", _digit_unsigned),

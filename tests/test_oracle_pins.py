@@ -85,6 +85,52 @@ def solve(a, b, **kw):
 
 
 # ---------------------------------------------------------------------------
+# input widening (bf16 operands of the linear, attention and training GEMMs)
+# ---------------------------------------------------------------------------
+
+def bf16_value(bits: int) -> float:
+    """Value of a bfloat16 bit pattern from the format's definition: 1 sign bit,
+    8 exponent bits (bias 127), 7 fraction bits; exponent 0 is subnormal
+    (2^-126 * f/128), exponent 255 is Inf (f = 0) or NaN."""
+    s = -1.0 if bits >> 15 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return s * math.inf if f == 0 else math.nan
+    if e == 0:
+        return s * math.ldexp(f, -126 - 7)
+    return s * math.ldexp(128 + f, e - 127 - 7)
+
+
+def test_widen_every_bf16_pattern():
+    """All 65536 bf16 patterns: the oracle's widening equals the value the
+    format defines (±0, subnormals, the largest finite values, Inf, NaN) and
+    torch's own bfloat16 -> float32 conversion."""
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.widen(bits, "bf16")
+    assert got.dtype == np.float32 and got.shape == bits.shape
+    ref = np.array([bf16_value(int(b)) for b in bits], dtype=np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].astype(np.float64), ref[~nan])
+    # signed zeros keep their sign; the extremes land where the format puts them
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0x0000]) and got[0x8000] == 0
+    assert got[0x0001] == np.float32(2.0 ** -133) and got[0x007F] == np.float32(127 * 2.0 ** -133)
+    assert got[0x7F7F] == np.float32((2 - 2.0 ** -7) * 2.0 ** 127) and got[0xFF7F] == -got[0x7F7F]
+    assert got[0x7F80] == np.inf and got[0xFF80] == -np.inf
+    t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(np.isnan(t), nan)
+    assert np.array_equal(t[~nan].view(np.uint32), got[~nan].view(np.uint32))
+    # 2-D operands widen element by element, in their stored orientation
+    m = bits[:4096].reshape(64, 64)
+    assert np.array_equal(O.widen(m, "bf16").ravel().view(np.uint32), got[:4096].view(np.uint32))
+    assert np.array_equal(O.widen(m.T, "bf16"), O.widen(m, "bf16").T)
+    f = np.array([[1.5, -2.25]], np.float32)
+    assert O.widen(f, "f32") is not None and np.array_equal(O.widen(f, "f32"), f)
+
+
+# ---------------------------------------------------------------------------
 # O1 percentile, O2 scale, O3 RTN
 # ---------------------------------------------------------------------------
 
