@@ -17,15 +17,26 @@
  * Conventions (all entry points)
  * ------------------------------
  * - Every data pointer is a DEVICE pointer unless marked "host".  The caller
- *   owns every buffer; no entry point allocates or frees memory.
+ *   owns every buffer.  No entry point allocates or frees memory (device, pinned
+ *   or host heap): imu_init allocates, once per device, the pinned host buffer
+ *   the plan headers are read back through and two events, and imu_release
+ *   frees them.  imu_plan_unpack, imu_unpacked_gemm and imu_imunpack_matmul
+ *   need imu_init on the calling thread's current device first (else
+ *   IMU_ERR_INVALID_ARG).
  * - All work is enqueued on `stream` (HIP stream; 0 = the null stream).  Only
  *   imu_plan_unpack and imu_imunpack_matmul wait for the device, once each, to
- *   read the plan header (the unpacked sizes are data dependent).
+ *   read the plan header (the unpacked sizes are data dependent).  Calls on one
+ *   device from several host threads take turns between the planner launch and
+ *   that read (they share the device's header buffer).
  * - Argument errors are returned synchronously and nothing is enqueued.
  *   Conditions found on the device (non-finite input, |x.r| >= 2^31) are
  *   latched in the operand's statistics and returned at the next wait.
  * - The integer result C is defined modulo 2^32 (two's complement int32),
- *   which equals the exact product whenever it fits in int32.
+ *   which equals the exact product whenever it fits in int32.  There is no
+ *   overflow status: the int8 x int8 -> int32 MFMA products and the int32
+ *   shift-and-add fold never form the product in wider integers, so an exact
+ *   overflow test would need a second, wider product.  A caller can bound
+ *   |C| <= K * max|q_A| * max|q_B| from the statistics headers (maxkey and r).
  * - Batched operands (batch > 1) are independent problems: each batch entry
  *   has its own percentile scale, plan and unpacked sizes.
  * - Calls on one stream are ordered; calls that share a workspace must not
@@ -129,6 +140,21 @@ typedef struct {
   int64_t levels, segments;          /* array extents used above */
   int64_t m_alloc_max, n_alloc_max;
 } imu_plan_view;
+
+/* ---- set-up ------------------------------------------------------------------ */
+
+/* Set-up for the calling thread's current device: a pinned, coherent host
+ * buffer that receives the plan headers of up to max_batch batch entries per
+ * call (2 KB each), two events, and the device's compute-unit count.  Call once
+ * per device before the entry points that need it; calling again is cheap and
+ * grows the buffer if max_batch is larger (waiting for the device first).
+ * A call with more batch entries than the buffer holds returns
+ * IMU_ERR_UNSUPPORTED.  Thread-safe.  max_batch in [1, 65535]. */
+imu_status imu_init(int64_t max_batch);
+/* Frees what imu_init allocated for the current device, after waiting for the
+ * device (no call of the library may be in flight on it).  A later entry point
+ * on that device needs imu_init again.  A no-op when nothing was set up. */
+imu_status imu_release(void);
 
 /* ---- sizes and layouts (host only, no device work) ------------------------ */
 

@@ -12,6 +12,7 @@ fallback implementation.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 from dataclasses import dataclass
@@ -112,6 +113,8 @@ def lib() -> ctypes.CDLL:
         "imu_last_error": (ctypes.c_char_p, []),
         "imu_version": (ctypes.c_char_p, []),
         "imu_set_gemm_events": (I32, [V, V]),
+        "imu_init": (I32, [I64]),
+        "imu_release": (I32, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -121,15 +124,45 @@ def lib() -> ctypes.CDLL:
     return L
 
 
-EXPORTED = ("imu_stats_bytes", "imu_stats_layout", "imu_plan_bytes", "imu_plan_layout",
-            "imu_workspace_fixed_bytes", "imu_quantize_rtn", "imu_plan_unpack", "imu_unpack",
-            "imu_unpacked_gemm", "imu_imunpack_matmul", "imu_status_string", "imu_last_error",
+EXPORTED = ("imu_init", "imu_release", "imu_stats_bytes", "imu_stats_layout", "imu_plan_bytes",
+            "imu_plan_layout", "imu_workspace_fixed_bytes", "imu_quantize_rtn", "imu_plan_unpack",
+            "imu_unpack", "imu_unpacked_gemm", "imu_imunpack_matmul", "imu_status_string", "imu_last_error",
             "imu_version", "imu_set_gemm_events")
 
 
 def _check(status: int):
     if status != OK:
         raise ImunpackError(status, lib().imu_last_error().decode())
+
+
+# batch entries imu_init has set up per device index (the library's per-device
+# context: pinned header buffer and events)
+_ready = {}
+_MIN_BATCH = 256
+
+
+def ensure_init(device, batch: int = 1) -> None:
+    """imu_init for `device` (a torch device or index) with room for `batch`
+    entries; the first call also registers imu_release for interpreter exit."""
+    idx = torch.device(device).index if not isinstance(device, int) else device
+    if idx is None:
+        idx = torch.cuda.current_device()
+    if _ready.get(idx, 0) >= batch:
+        return
+    want = max(batch, _MIN_BATCH, _ready.get(idx, 0))
+    with torch.cuda.device(idx):
+        _check(lib().imu_init(want))
+    if not _ready:
+        atexit.register(release_all)
+    _ready[idx] = want
+
+
+def release_all() -> None:
+    """imu_release on every device set up through this binding."""
+    for idx in list(_ready):
+        with torch.cuda.device(idx):
+            lib().imu_release()
+        del _ready[idx]
 
 
 def _stream(stream) -> int:
@@ -303,6 +336,7 @@ def plan_unpack(a, b, p: ImuParams, stats_a: Stats, stats_b: Stats, stream=None)
     a, b = _as_matrix(a), _as_matrix(b)
     pl = Plan(a, b, p)
     ma, mb = a.c(), b.c()
+    ensure_init(a.stored.device, ma.batch)
     _check(lib().imu_plan_unpack(ctypes.byref(ma), ctypes.byref(mb), ctypes.byref(p), _ptr(stats_a.buf),
                                  _ptr(stats_b.buf), _ptr(pl.buf), pl.info, ctypes.c_void_p(_stream(stream))))
     return pl
@@ -331,6 +365,7 @@ def unpacked_gemm(a_u: torch.Tensor, b_u: torch.Tensor, p: ImuParams, stats_a: S
     """int8 MFMA GEMMs + shift-and-accumulate fold + dequant (imu_unpacked_gemm).
     Returns (C int32, out float32) shaped (batch, M, N)."""
     dev = a_u.device
+    ensure_init(dev, plan.batch)
     c = torch.empty((plan.batch, plan.M, plan.N), dtype=torch.int32, device=dev)
     out = torch.empty((plan.batch, plan.M, plan.N), dtype=torch.float32, device=dev) if want_out else None
     _check(lib().imu_unpacked_gemm(_ptr(a_u), _ptr(b_u), ctypes.byref(p), _ptr(stats_a.buf), _ptr(stats_b.buf),
@@ -361,6 +396,7 @@ def imunpack_matmul(a, b, p: ImuParams, out: Optional[torch.Tensor] = None, c: O
     a, b = _as_matrix(a), _as_matrix(b)
     ma, mb = a.c(), b.c()
     dev = a.stored.device
+    ensure_init(dev, ma.batch)
     shape = (ma.batch, ma.rows, mb.cols)
     if c is None:
         c = torch.empty(shape, dtype=torch.int32, device=dev)

@@ -1,15 +1,16 @@
-// C ABI of the IM-Unpack integer GEMM library: argument validation, buffer
-// carving, kernel launches and the one plan-header readback.  Contains no
-// kernels; the device work lives in quantize.hip, plan.hip, unpack.hip and
-// gemm.hip.
+// C ABI of the IM-Unpack integer GEMM library: set-up of the per-device
+// context, argument validation, buffer carving, kernel launches and the one
+// plan-header readback.  Contains no kernels; the device work lives in
+// quantize.hip, plan.hip, unpack.hip and gemm.hip.
 #include <algorithm>
 #include <atomic>
+#include <cstdarg>
 #include <cstddef>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <string>
-#include <vector>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -18,18 +19,23 @@ using namespace imu;
 
 namespace {
 
-thread_local std::string g_err;
+// Detail of the last error on this thread.  Formatted into a fixed buffer, so
+// that no entry point allocates host memory either.
+thread_local char g_err[512];
 thread_local hipEvent_t g_gemm_ev[2] = {nullptr, nullptr};  // imu_set_gemm_events
 
-imu_status fail(imu_status s, const std::string& msg) {
-  g_err = msg;
+__attribute__((format(printf, 2, 3))) imu_status fail(imu_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
   return s;
 }
 
 #define IMU_HIP(call)                                                                              \
   do {                                                                                             \
     hipError_t e_ = (call);                                                                        \
-    if (e_ != hipSuccess) return fail(IMU_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+    if (e_ != hipSuccess) return fail(IMU_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_));        \
   } while (0)
 
 #define IMU_TRY(call)                                                                              \
@@ -50,20 +56,20 @@ struct Operand {
 };
 
 imu_status check_matrix(const imu_matrix* x, const char* name, Operand* op) {
-  if (!x) return fail(IMU_ERR_INVALID_ARG, std::string(name) + " is NULL");
-  if (!x->data) return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".data is NULL");
+  if (!x) return fail(IMU_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!x->data) return fail(IMU_ERR_INVALID_ARG, "%s.data is NULL", name);
   if (x->dtype != IMU_F32 && x->dtype != IMU_BF16)
-    return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".dtype must be IMU_F32 or IMU_BF16");
+    return fail(IMU_ERR_INVALID_ARG, "%s.dtype must be IMU_F32 or IMU_BF16", name);
   if (x->layout != IMU_NORMAL && x->layout != IMU_TRANSPOSED)
-    return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".layout must be IMU_NORMAL or IMU_TRANSPOSED");
+    return fail(IMU_ERR_INVALID_ARG, "%s.layout must be IMU_NORMAL or IMU_TRANSPOSED", name);
   if (x->rows < 1 || x->cols < 1)
-    return fail(IMU_ERR_INVALID_ARG, std::string(name) + " must have rows >= 1 and cols >= 1");
+    return fail(IMU_ERR_INVALID_ARG, "%s must have rows >= 1 and cols >= 1", name);
   if (x->rows > kMaxLine || x->cols > kMaxLine)
-    return fail(IMU_ERR_UNSUPPORTED, std::string(name) + ": rows and cols must be below 2^24");
+    return fail(IMU_ERR_UNSUPPORTED, "%s: rows and cols must be below 2^24", name);
   if ((unsigned long long)x->rows * (unsigned long long)x->cols >= (1ull << 32))
-    return fail(IMU_ERR_UNSUPPORTED, std::string(name) + ": rows*cols must be below 2^32");
+    return fail(IMU_ERR_UNSUPPORTED, "%s: rows*cols must be below 2^32", name);
   if (x->batch < 1 || x->batch > 65535)
-    return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".batch must be in [1, 65535]");
+    return fail(IMU_ERR_INVALID_ARG, "%s.batch must be in [1, 65535]", name);
   op->m = x;
   op->R = x->rows;
   op->C = x->cols;
@@ -72,9 +78,9 @@ imu_status check_matrix(const imu_matrix* x, const char* name, Operand* op) {
   op->scols = op->tr ? x->rows : x->cols;
   op->dtype = x->dtype;
   op->elem = x->dtype == IMU_F32 ? 4 : 2;
-  if (x->ld < op->scols) return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".ld is below the stored row length");
+  if (x->ld < op->scols) return fail(IMU_ERR_INVALID_ARG, "%s.ld is below the stored row length", name);
   if (x->batch > 1 && x->batch_stride < (op->srows - 1) * x->ld + op->scols)
-    return fail(IMU_ERR_INVALID_ARG, std::string(name) + ".batch_stride overlaps batch entries");
+    return fail(IMU_ERR_INVALID_ARG, "%s.batch_stride overlaps batch entries", name);
   return IMU_OK;
 }
 
@@ -194,48 +200,47 @@ imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p
   return IMU_OK;
 }
 
-// Per-thread pinned, coherent host buffer that the planner's last launch
-// writes a copy of the plan headers into, each copy closed by a per-call tag,
-// and an event that completes with that launch (it is attached to the launch,
-// so no marker of its own sits between the planner and the unpack; it carries
-// no system-scope fence, which would write back the L2 and leave the GPU idle
-// for microseconds).  The host waits for the headers alone while later kernels
-// keep the GPU busy.  Buffer and events live until the process ends.
-struct HeaderStage {
-  uint8_t* buf = nullptr;       // host address
+
+// ---------------------------------------------------------------------------
+// per-device context (imu_init / imu_release)
+// ---------------------------------------------------------------------------
+// The planner's last launch writes a copy of the plan headers straight into
+// pinned, coherent host memory, each copy closed by a per-call tag, and an
+// event completes with that launch (it is attached to the launch, so no marker
+// of its own sits between the planner and the unpack; it carries no
+// system-scope fence, which would write back the L2 and leave the GPU idle for
+// microseconds).  The host waits for the headers alone while later kernels
+// keep the GPU busy.  imu_init allocates the buffer and the events once per
+// device; imu_release frees them.  Calls on one device from several host
+// threads share the buffer and take turns (the mutex) from the planner launch
+// to the header read.
+constexpr int kMaxDevices = 64;
+struct DeviceCtx {
+  std::mutex mu;
+  bool live = false;
+  uint8_t* buf = nullptr;       // host address of the header copies
   uint8_t* dbuf = nullptr;      // the same memory as the device addresses it
-  size_t bytes = 0;
+  int64_t cap = 0;              // batch entries the buffer holds
   hipEvent_t ev = nullptr;      // completes with the planner's last launch
   hipEvent_t ev_sys = nullptr;  // fallback: an event with the system-scope fence
   int64_t tag = 0;
-  int dev = -1;
+  int cus = 0;                  // compute units of the device
 };
-thread_local HeaderStage g_stage;
+DeviceCtx g_ctx[kMaxDevices];
+std::mutex g_init_mu;  // imu_init / imu_release
 
-imu_status header_stage(size_t bytes, uint8_t** out) {
+// The context of the calling thread's current device, or an error when
+// imu_init has not set it up (or its buffer is too small for `batch`).
+imu_status current_ctx(int64_t batch, DeviceCtx** out) {
   int dev = 0;
   IMU_HIP(hipGetDevice(&dev));
-  HeaderStage& st = g_stage;
-  if (st.ev && st.dev != dev) {  // events and mappings belong to a device; the old ones are kept alive
-    st.ev = st.ev_sys = nullptr;
-    st.bytes = 0;
-  }
-  if (!st.ev) {
-    IMU_HIP(hipEventCreateWithFlags(&st.ev, hipEventDisableTiming | hipEventDisableSystemFence));
-    IMU_HIP(hipEventCreateWithFlags(&st.ev_sys, hipEventDisableTiming));
-    st.dev = dev;
-  }
-  if (st.bytes < bytes) {
-    void* p = nullptr;
-    IMU_HIP(hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocCoherent));
-    std::memset(p, 0, bytes);  // no stale tag
-    void* d = nullptr;
-    IMU_HIP(hipHostGetDevicePointer(&d, p, 0));
-    st.buf = static_cast<uint8_t*>(p);
-    st.dbuf = static_cast<uint8_t*>(d);
-    st.bytes = bytes;  // the previous buffer is not freed: a launch may still write it
-  }
-  *out = st.buf;
+  if (dev < 0 || dev >= kMaxDevices) return fail(IMU_ERR_UNSUPPORTED, "device %d beyond the library's %d", dev, kMaxDevices);
+  DeviceCtx& c = g_ctx[dev];
+  if (!c.live) return fail(IMU_ERR_INVALID_ARG, "imu_init was not called for device %d", dev);
+  if (batch > c.cap)
+    return fail(IMU_ERR_UNSUPPORTED, "batch %lld above the %lld entries imu_init set up on device %d",
+                (long long)batch, (long long)c.cap, dev);
+  *out = &c;
   return IMU_OK;
 }
 
@@ -244,8 +249,7 @@ imu_status header_stage(size_t bytes, uint8_t** out) {
 // missing (host memory not coherent with the GPU after all), an event with the
 // system-scope fence is recorded and waited for; a tag missing after that is an
 // error.
-imu_status wait_headers(int batch, hipStream_t s) {
-  HeaderStage& st = g_stage;
+imu_status wait_headers(DeviceCtx& st, int batch, hipStream_t s) {
   auto tagged = [&]() {
     for (int b = 0; b < batch; ++b) {
       const volatile int64_t* t = reinterpret_cast<const volatile int64_t*>(
@@ -267,16 +271,13 @@ imu_status wait_headers(int batch, hipStream_t s) {
   return IMU_OK;
 }
 
-// Plan launches with the host copy of the headers; returns that copy (valid
-// once wait_headers has returned).
-imu_status plan_staged(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
+// Plan launches with the host copy of the headers (the caller holds st.mu);
+// returns that copy (valid once wait_headers has returned).
+imu_status plan_staged(DeviceCtx& st, const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
                        uint8_t* stats_b, uint8_t* plan, hipStream_t s, const uint8_t** hdrs) {
-  uint8_t* buf = nullptr;
-  IMU_TRY(header_stage((size_t)oa.m->batch * kPlanHeaderStride, &buf));
-  HeaderStage& st = g_stage;
   ++st.tag;
   IMU_TRY(plan_launch(oa, ob, p, stats_a, stats_b, plan, st.dbuf, st.tag, st.ev, s));
-  *hdrs = buf;
+  *hdrs = st.buf;
   return IMU_OK;
 }
 
@@ -289,12 +290,6 @@ imu_status finish_plan(const Operand& oa, const Operand& ob, const uint8_t* hdrs
   for (int b = 0; b < batch; ++b) {
     const PlanHeader* h = reinterpret_cast<const PlanHeader*>(hdrs + (size_t)b * kPlanHeaderStride);
     status |= h->status;
-    aoff += unpacked_entry_bytes(h, 0);
-  }
-  const int64_t a_all = aoff;
-  aoff = 0;
-  for (int b = 0; b < batch; ++b) {
-    const PlanHeader* h = reinterpret_cast<const PlanHeader*>(hdrs + (size_t)b * kPlanHeaderStride);
     if (info) {
       imu_plan_info& f = info[b];
       std::memset(&f, 0, sizeof(f));
@@ -321,7 +316,7 @@ imu_status finish_plan(const Operand& oa, const Operand& ob, const uint8_t* hdrs
     aoff += unpacked_entry_bytes(h, 0);
     boff += unpacked_entry_bytes(h, 1);
   }
-  if (a_total) *a_total = a_all;
+  if (a_total) *a_total = aoff;
   if (b_total) *b_total = boff;
   if (status & kStatusNonfinite) return fail(IMU_ERR_NONFINITE, "an input element is NaN or Inf");
   if (status & kStatusRange) return fail(IMU_ERR_RANGE, "|x * r| >= 2^31 for some element");
@@ -331,9 +326,12 @@ imu_status finish_plan(const Operand& oa, const Operand& ob, const uint8_t* hdrs
 imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
                      uint8_t* stats_b, uint8_t* plan, imu_plan_info* info, hipStream_t s) {
   const int batch = (int)oa.m->batch;
+  DeviceCtx* st = nullptr;
+  IMU_TRY(current_ctx(batch, &st));
+  std::lock_guard<std::mutex> lock(st->mu);
   const uint8_t* hdrs = nullptr;
-  IMU_TRY(plan_staged(oa, ob, p, stats_a, stats_b, plan, s, &hdrs));
-  IMU_TRY(wait_headers(batch, s));
+  IMU_TRY(plan_staged(*st, oa, ob, p, stats_a, stats_b, plan, s, &hdrs));
+  IMU_TRY(wait_headers(*st, batch, s));
   return finish_plan(oa, ob, hdrs, batch, info, nullptr, nullptr);
 }
 
@@ -381,10 +379,17 @@ imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, cons
   return IMU_OK;
 }
 
+// Tile-relevant sizes of one batch entry's plan.
+struct EntrySizes {
+  int64_t m_base, n_base, m_alloc, n_alloc;
+};
+
+// GEMM launches for `batch` entries whose sizes come from get(b) (the staged
+// host headers or the caller's info).
+template <class Get>
 imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, const uint8_t* stats_a,
-                     const uint8_t* stats_b, const uint8_t* plan, const imu_plan_info* info,
-                     int64_t batch, int32_t* c, int64_t ldc, int64_t cbs, float* out, hipStream_t s) {
-  const int64_t M = info[0].m, K = info[0].k, N = info[0].n;
+                     const uint8_t* stats_b, const uint8_t* plan, int64_t M, int64_t K, int64_t N, int64_t batch,
+                     Get get, int32_t* c, int64_t ldc, int64_t cbs, float* out, hipStream_t s) {
   const StatsLayout la = stats_layout(M, K), lb = stats_layout(K, N);
   const PlanLayout pl = plan_layout(M, K, N, batch, p->bits);
   if (batch > 65535) return fail(IMU_ERR_INVALID_ARG, "batch above 65535");
@@ -397,22 +402,25 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   // on a few CUs, and the atomic pass spreads it over the extra tiles instead.
   int64_t base_tiles = 0, base_total = 0;
   for (int64_t b = 0; b < batch; ++b) {
-    const imu_plan_info& f = info[b];
+    const EntrySizes f = get(b);
     if (f.m_base % 256 || f.n_base % 128 || f.m_alloc % 256 || f.n_alloc % 128)
       return fail(IMU_ERR_INVALID_ARG, "plan sizes are not tile multiples");
     base_tiles = std::max(base_tiles, (f.m_base / 256) * (f.n_base / 128));
     base_total += (f.m_base / 256) * (f.n_base / 128);
   }
-  int dev = 0, cus = 0;
-  IMU_HIP(hipGetDevice(&dev));
-  IMU_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  int cus = 0;
+  {
+    DeviceCtx* ctx = nullptr;
+    IMU_TRY(current_ctx(0, &ctx));
+    cus = ctx->cus;
+  }
   // IMU_FOLD_COLUMNS=1 / 0 forces the choice (both give the same result)
   const char* fe = std::getenv("IMU_FOLD_COLUMNS");
   const bool fold_cols = fe && fe[0] == '1' ? true : fe && fe[0] == '0' ? false : base_total >= cus;
   int64_t extra_tiles = 0;
   bool any_atomic = false, any_fold = false;
   for (int64_t b = 0; b < batch; ++b) {
-    const imu_plan_info& f = info[b];
+    const EntrySizes f = get(b);
     const bool rowx = f.m_alloc > f.m_base, colx = f.n_alloc > f.n_base;
     if (rowx || (colx && !fold_cols)) {
       any_atomic = true;
@@ -476,9 +484,118 @@ int64_t fixed_bytes(const Operand& oa, const Operand& ob, const imu_params* p) {
          round_up(plan_layout(oa.R, oa.C, ob.C, batch, p->bits).total, 256);
 }
 
+// The whole path on a caller-provided workspace (see imu_imunpack_matmul).
+imu_status matmul_impl(const Operand& oa, const Operand& ob, const imu_params* p, int32_t* c, float* out,
+                       uint8_t* w, int64_t ws_bytes, size_t* ws_needed, imu_plan_info* info, hipStream_t stream) {
+  const int64_t batch = oa.m->batch;
+  const int64_t fixed = fixed_bytes(oa, ob, p);
+  if (ws_needed) *ws_needed = (size_t)fixed;
+  if (!w || ws_bytes < fixed)
+    return fail(IMU_ERR_WORKSPACE, "workspace of %lld bytes below the fixed part (statistics and plan) of %lld",
+                (long long)ws_bytes, (long long)fixed);
+  DeviceCtx* st = nullptr;
+  IMU_TRY(current_ctx(batch, &st));
+  uint8_t* stats_a = w;
+  uint8_t* stats_b = stats_a + round_up(stats_layout(oa.R, oa.C).stride * batch, 256);
+  uint8_t* plan = stats_b + round_up(stats_layout(ob.R, ob.C).stride * batch, 256);
+  // statistics of A and B are adjacent: clear both with one launch
+  IMU_HIP(launch_fill_u32(stats_a, 0u, (int64_t)(plan - stats_a) / 4, stream));
+  const Operand* ops[2] = {&oa, &ob};
+  uint8_t* stv[2] = {stats_a, stats_b};
+  int32_t* q[2] = {nullptr, nullptr};
+  IMU_TRY(quantize_ops(ops, stv, q, 2, p, stream, true));
+  // The unpack kernels take their sizes and placement from the plan on the
+  // device, so they are queued right behind the plan; the host waits only for
+  // the plan headers (staged to pinned memory) while they run, then checks the
+  // workspace and sizes the GEMM launch.  If the plan failed or the workspace
+  // is too small the unpack kernels write nothing.
+  std::lock_guard<std::mutex> lock(st->mu);
+  const uint8_t* hdrs = nullptr;
+  IMU_TRY(plan_staged(*st, oa, ob, p, stats_a, stats_b, plan, stream, &hdrs));
+  int8_t* region = reinterpret_cast<int8_t*>(w + fixed);
+  const int64_t cap = ws_bytes - fixed;
+  if (oa.dtype == ob.dtype) {  // both operands in one launch
+    const UnpackArgs u[2] = {unpack_args(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap),
+                             unpack_args(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap)};
+    IMU_HIP(launch_unpack(oa.dtype, p->bits, u, 2, (int)batch, stream));
+  } else {
+    IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap, stream));
+    IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap, stream));
+  }
+  IMU_TRY(wait_headers(*st, (int)batch, stream));
+  int64_t a_bytes = 0, b_bytes = 0;
+  IMU_TRY(finish_plan(oa, ob, hdrs, (int)batch, info, &a_bytes, &b_bytes));
+  const int64_t needed = fixed + a_bytes + b_bytes;
+  if (ws_needed) *ws_needed = (size_t)needed;
+  if (ws_bytes < needed)
+    return fail(IMU_ERR_WORKSPACE, "workspace of %lld bytes below the %lld this plan needs", (long long)ws_bytes,
+                (long long)needed);
+  int8_t* a_u = region;
+  int8_t* b_u = region + a_bytes;
+  auto sizes = [hdrs](int64_t b) {
+    const PlanHeader* h = reinterpret_cast<const PlanHeader*>(hdrs + (size_t)b * kPlanHeaderStride);
+    return EntrySizes{h->m_base, h->n_base, h->m_alloc, h->n_alloc};
+  };
+  return gemm_impl(a_u, b_u, p, stats_a, stats_b, plan, oa.R, oa.C, ob.C, batch, sizes, c, ob.C, oa.R * ob.C, out,
+                   stream);
+}
+
 }  // namespace
 
 extern "C" {
+
+imu_status imu_init(int64_t max_batch) {
+  if (max_batch < 1 || max_batch > 65535) return fail(IMU_ERR_INVALID_ARG, "max_batch must be in [1, 65535]");
+  int dev = 0;
+  IMU_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(IMU_ERR_UNSUPPORTED, "device %d beyond the library's %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_init_mu);
+  DeviceCtx& c = g_ctx[dev];
+  std::lock_guard<std::mutex> l(c.mu);
+  if (!c.live) {
+    IMU_HIP(hipEventCreateWithFlags(&c.ev, hipEventDisableTiming | hipEventDisableSystemFence));
+    IMU_HIP(hipEventCreateWithFlags(&c.ev_sys, hipEventDisableTiming));
+    IMU_HIP(hipDeviceGetAttribute(&c.cus, hipDeviceAttributeMultiprocessorCount, dev));
+    c.live = true;
+  }
+  if (c.cap < max_batch) {
+    if (c.buf) {  // no planner launch may still write the old buffer
+      IMU_HIP(hipDeviceSynchronize());
+      IMU_HIP(hipHostFree(c.buf));
+      c.buf = c.dbuf = nullptr;
+      c.cap = 0;
+    }
+    const size_t bytes = (size_t)max_batch * kPlanHeaderStride;
+    void* h = nullptr;
+    IMU_HIP(hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocCoherent));
+    std::memset(h, 0, bytes);  // no stale tag
+    void* d = nullptr;
+    IMU_HIP(hipHostGetDevicePointer(&d, h, 0));
+    c.buf = static_cast<uint8_t*>(h);
+    c.dbuf = static_cast<uint8_t*>(d);
+    c.cap = max_batch;
+  }
+  return IMU_OK;
+}
+
+imu_status imu_release(void) {
+  int dev = 0;
+  IMU_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return IMU_OK;
+  std::lock_guard<std::mutex> g(g_init_mu);
+  DeviceCtx& c = g_ctx[dev];
+  std::lock_guard<std::mutex> l(c.mu);
+  if (!c.live) return IMU_OK;
+  IMU_HIP(hipDeviceSynchronize());  // nothing may still write the buffer or signal the events
+  if (c.buf) IMU_HIP(hipHostFree(c.buf));
+  IMU_HIP(hipEventDestroy(c.ev));
+  IMU_HIP(hipEventDestroy(c.ev_sys));
+  c.buf = c.dbuf = nullptr;
+  c.cap = 0;
+  c.ev = c.ev_sys = nullptr;
+  c.live = false;
+  return IMU_OK;
+}
 
 size_t imu_stats_bytes(const imu_matrix* x) {
   Operand op;
@@ -587,8 +704,12 @@ imu_status imu_unpacked_gemm(const int8_t* a_u, const int8_t* b_u, const imu_par
   if (ldc < info[0].n) return fail(IMU_ERR_INVALID_ARG, "ldc is below N");
   if (batch > 1 && c_batch_stride < (info[0].m - 1) * ldc + info[0].n)
     return fail(IMU_ERR_INVALID_ARG, "c_batch_stride overlaps batch entries");
+  auto sizes = [info](int64_t b) {
+    return EntrySizes{info[b].m_base, info[b].n_base, info[b].m_alloc, info[b].n_alloc};
+  };
   return gemm_impl(a_u, b_u, p, static_cast<const uint8_t*>(stats_a), static_cast<const uint8_t*>(stats_b),
-                   static_cast<const uint8_t*>(plan), info, batch, c, ldc, c_batch_stride, out, stream);
+                   static_cast<const uint8_t*>(plan), info[0].m, info[0].k, info[0].n, batch, sizes, c, ldc,
+                   c_batch_stride, out, stream);
 }
 
 imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const imu_params* p, int32_t* c,
@@ -597,52 +718,8 @@ imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const i
   Operand oa, ob;
   IMU_TRY(check_pair(a, b, p, &oa, &ob));
   if (!c) return fail(IMU_ERR_INVALID_ARG, "c is NULL");
-  const int64_t batch = a->batch;
-  const int64_t fixed = fixed_bytes(oa, ob, p);
-  if (ws_needed) *ws_needed = (size_t)fixed;
-  if (!ws || (int64_t)ws_bytes < fixed)
-    return fail(IMU_ERR_WORKSPACE, "workspace below the fixed part (statistics and plan)");
-  uint8_t* w = static_cast<uint8_t*>(ws);
-  uint8_t* stats_a = w;
-  uint8_t* stats_b = stats_a + round_up(stats_layout(oa.R, oa.C).stride * batch, 256);
-  uint8_t* plan = stats_b + round_up(stats_layout(ob.R, ob.C).stride * batch, 256);
-  // statistics of A and B are adjacent: clear both with one launch
-  IMU_HIP(launch_fill_u32(stats_a, 0u, (int64_t)(plan - stats_a) / 4, stream));
-  const Operand* ops[2] = {&oa, &ob};
-  uint8_t* st[2] = {stats_a, stats_b};
-  int32_t* q[2] = {nullptr, nullptr};
-  IMU_TRY(quantize_ops(ops, st, q, 2, p, stream, true));
-  std::vector<imu_plan_info> local;
-  if (!info) {
-    local.resize((size_t)batch);
-    info = local.data();
-  }
-  // The unpack kernels take their sizes and placement from the plan on the
-  // device, so they are queued right behind the plan; the host waits only for
-  // the plan headers (staged to pinned memory) while they run, then checks the
-  // workspace and sizes the GEMM launch.  If the plan failed or the workspace
-  // is too small the unpack kernels write nothing.
-  const uint8_t* hdrs = nullptr;
-  IMU_TRY(plan_staged(oa, ob, p, stats_a, stats_b, plan, stream, &hdrs));
-  int8_t* region = reinterpret_cast<int8_t*>(w + fixed);
-  const int64_t cap = (int64_t)ws_bytes - fixed;
-  if (oa.dtype == ob.dtype) {  // both operands in one launch
-    const UnpackArgs u[2] = {unpack_args(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap),
-                             unpack_args(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap)};
-    IMU_HIP(launch_unpack(oa.dtype, p->bits, u, 2, (int)batch, stream));
-  } else {
-    IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap, stream));
-    IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap, stream));
-  }
-  IMU_TRY(wait_headers((int)batch, stream));
-  int64_t a_bytes = 0, b_bytes = 0;
-  IMU_TRY(finish_plan(oa, ob, hdrs, (int)batch, info, &a_bytes, &b_bytes));
-  const int64_t needed = fixed + a_bytes + b_bytes;
-  if (ws_needed) *ws_needed = (size_t)needed;
-  if ((int64_t)ws_bytes < needed) return fail(IMU_ERR_WORKSPACE, "workspace below the unpacked operands' size");
-  int8_t* a_u = region;
-  int8_t* b_u = region + a_bytes;
-  return gemm_impl(a_u, b_u, p, stats_a, stats_b, plan, info, batch, c, ob.C, oa.R * ob.C, out, stream);
+  if (ws_bytes > (size_t)INT64_MAX) return fail(IMU_ERR_INVALID_ARG, "ws_bytes above 2^63");
+  return matmul_impl(oa, ob, p, c, out, static_cast<uint8_t*>(ws), (int64_t)ws_bytes, ws_needed, info, stream);
 }
 
 const char* imu_status_string(imu_status s) {
@@ -658,9 +735,9 @@ const char* imu_status_string(imu_status s) {
   return "unknown status";
 }
 
-const char* imu_last_error(void) { return g_err.c_str(); }
+const char* imu_last_error(void) { return g_err; }
 
-const char* imu_version(void) { return "imunpack 0.1 (gfx950)"; }
+const char* imu_version(void) { return "imunpack 0.2 (gfx950)"; }
 
 imu_status imu_set_gemm_events(hipEvent_t before, hipEvent_t after) {
   if ((before == nullptr) != (after == nullptr))

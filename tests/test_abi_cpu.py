@@ -31,10 +31,16 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) >= 13
+    assert len(names) >= 16
     for n in names:
         assert hasattr(lib, n), f"{n} declared in imunpack.h but not exported"
     assert set(B.EXPORTED) == set(names)
+
+
+def test_init_validates_before_touching_a_device(lib):
+    for bad in (0, -1, 65536):
+        assert lib.imu_init(bad) == B.ERR_INVALID_ARG
+        assert b"max_batch" in lib.imu_last_error()
 
 
 def test_version_and_status_strings(lib):

@@ -284,3 +284,51 @@ def test_full_size_workload(idx, sub):
         assert np.array_equal(c[e].cpu().numpy(), ref.C32), (pr.name, e)
         assert G.ulp_diff(out[e].cpu().numpy(), ref.out) <= 1, (pr.name, e)
     print(f"[full] {pr.name} ok ratio={infos[0]['unpack_ratio']:.3f} choice={infos[0]['choice']}", flush=True)
+
+
+def test_full_size_fp32_gradient_operand():
+    """The training data gradient at full size with the gradient entering as
+    float32 (Student-t draws, not bf16-rounded), so the percentile takes the
+    fp32 route (16-bit key prefix, then two 256-bin refinements) over 25.2 M
+    elements, in the launch configuration of the training step."""
+    rng = np.random.Generator(np.random.PCG64(1104))
+    dy = W.gradients(rng, 8192, 3072)
+    w = W.config(4)[1].b  # W (3072 x 768, bf16) as it enters dY @ W
+    print("\n[full-f32] dY 8192x3072 f32 @ W 3072x768 bf16", flush=True)
+    a = B.Matrix(torch.from_numpy(dy).to("cuda"))
+    b = G.to_device(w)
+    p = B.params(beta=31, bits=4)
+    out, c, infos = B.imunpack_matmul(a, b, p, ws=B.Workspace("cuda"))
+    torch.cuda.synchronize()
+    ref = O.imunpack_matmul(dy, G.logical_f32(w, 0), 31, 4, 95, 100, unpacked=False)
+    ch = ref.plan.choice
+    assert infos[0]["choice"] == (ch.cand_a, ch.cand_b)
+    assert (infos[0]["m_u"], infos[0]["k_u"], infos[0]["n_u"]) == (ch.m_u, ch.k_u, ch.n_u)
+    assert np.array_equal(c[0].cpu().numpy(), ref.C32)
+    assert G.ulp_diff(out[0].cpu().numpy(), ref.out) <= 1
+    # the scale itself, through the staged entry point
+    st = B.quantize_rtn(a, p)
+    h = st.header(0)
+    assert h["alpha_bits"] == G.f32_bits(ref.qa.scale.alpha) and h["r_bits"] == G.f32_bits(ref.qa.scale.r)
+    assert h["total"] == ref.qa.stats.total
+
+
+def test_entry_points_need_init_and_release_frees():
+    """imu_release frees the device's context; the planner then refuses to run
+    until imu_init sets it up again (through the binding here)."""
+    pr = W.random_problem(31, 96, 130, 70, kind="gauss", dtype="f32")
+    a, b = G.to_device(pr.a), G.to_device(pr.b)
+    p = G.params_of(pr)
+    out1, c1, _ = B.imunpack_matmul(a, b, p)
+    torch.cuda.synchronize()
+    B.release_all()
+    sa, sb = B.quantize_rtn(a, p), B.quantize_rtn(b, p)
+    pl = B.Plan(a, b, p)
+    ma, mb = a.c(), b.c()
+    import ctypes
+    st = B.lib().imu_plan_unpack(ctypes.byref(ma), ctypes.byref(mb), ctypes.byref(p), B._ptr(sa.buf),
+                                 B._ptr(sb.buf), B._ptr(pl.buf), pl.info,
+                                 ctypes.c_void_p(B._stream(None)))
+    assert st == B.ERR_INVALID_ARG and b"imu_init" in B.lib().imu_last_error()
+    out2, c2, _ = B.imunpack_matmul(a, b, p)  # the binding sets the device up again
+    assert torch.equal(c1, c2) and torch.equal(out1, out2)
