@@ -242,6 +242,24 @@ imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const i
                                int32_t* c, float* out, void* ws, size_t ws_bytes,
                                size_t* ws_needed, imu_plan_info* info, hipStream_t stream);
 
+/* imu_imunpack_matmul without a workspace argument, for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * allocation).  Statistics, plan and unpacked operands live in a static device
+ * array of the library, imu_noalloc_scratch_bytes() = 128 MiB per GPU, held
+ * from module load until the process ends; its address on each device is
+ * looked up by imu_init, which must have run on the current device.  The call
+ * itself allocates nothing.  A problem that needs more than the array returns
+ * IMU_ERR_WORKSPACE (*ws_needed, if not NULL, holds the size it needs; the
+ * unpack kernels then write nothing).  Every call on a GPU uses that GPU's one
+ * array and leaves the last call's contents in it: calls that overlap in time
+ * on one GPU (other streams, other host threads) race on it.  Results equal
+ * imu_imunpack_matmul's. */
+imu_status imu_imunpack_matmul_noalloc(const imu_matrix* a, const imu_matrix* b, const imu_params* p,
+                                       int32_t* c, float* out, size_t* ws_needed, imu_plan_info* info,
+                                       hipStream_t stream);
+/* Size in bytes of the static array imu_imunpack_matmul_noalloc works in. */
+size_t imu_noalloc_scratch_bytes(void);
+
 /* Fixed part of the imu_imunpack_matmul workspace (statistics and plan); the
  * unpacked operands need sum over entries of (m_alloc + n_alloc) * k_pad more. */
 size_t imu_workspace_fixed_bytes(const imu_matrix* a, const imu_matrix* b, const imu_params* p);

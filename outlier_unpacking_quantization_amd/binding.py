@@ -113,6 +113,9 @@ def lib() -> ctypes.CDLL:
         "imu_last_error": (ctypes.c_char_p, []),
         "imu_version": (ctypes.c_char_p, []),
         "imu_set_gemm_events": (I32, [V, V]),
+        "imu_imunpack_matmul_noalloc": (I32, [P(ImuMatrix), P(ImuMatrix), P(ImuParams), V, V, P(S),
+                                              P(ImuPlanInfo), V]),
+        "imu_noalloc_scratch_bytes": (S, []),
         "imu_init": (I32, [I64]),
         "imu_release": (I32, []),
     }
@@ -127,7 +130,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("imu_init", "imu_release", "imu_stats_bytes", "imu_stats_layout", "imu_plan_bytes",
             "imu_plan_layout", "imu_workspace_fixed_bytes", "imu_quantize_rtn", "imu_plan_unpack",
             "imu_unpack", "imu_unpacked_gemm", "imu_imunpack_matmul", "imu_status_string", "imu_last_error",
-            "imu_version", "imu_set_gemm_events")
+            "imu_version", "imu_set_gemm_events", "imu_imunpack_matmul_noalloc", "imu_noalloc_scratch_bytes")
 
 
 def _check(status: int):
@@ -418,6 +421,27 @@ def imunpack_matmul(a, b, p: ImuParams, out: Optional[torch.Tensor] = None, c: O
         _check(st)
         return (out if want_out else None), c, [info[i].as_dict() for i in range(ma.batch)]
     _check(ERR_WORKSPACE)
+
+
+def imunpack_matmul_noalloc(a, b, p: ImuParams, out: Optional[torch.Tensor] = None,
+                            c: Optional[torch.Tensor] = None, want_out: bool = True, stream=None):
+    """The whole path in the library's static scratch (imu_imunpack_matmul_noalloc):
+    no workspace argument.  Returns (out float32 or None, C int32, [info dict])."""
+    a, b = _as_matrix(a), _as_matrix(b)
+    ma, mb = a.c(), b.c()
+    dev = a.stored.device
+    ensure_init(dev, ma.batch)
+    shape = (ma.batch, ma.rows, mb.cols)
+    if c is None:
+        c = torch.empty(shape, dtype=torch.int32, device=dev)
+    if want_out and out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    info = (ImuPlanInfo * ma.batch)()
+    need = ctypes.c_size_t(0)
+    _check(lib().imu_imunpack_matmul_noalloc(ctypes.byref(ma), ctypes.byref(mb), ctypes.byref(p), _ptr(c),
+                                             _ptr(out) if want_out else None, ctypes.byref(need), info,
+                                             ctypes.c_void_p(_stream(stream))))
+    return (out if want_out else None), c, [info[i].as_dict() for i in range(ma.batch)]
 
 
 def version() -> str:

@@ -225,8 +225,16 @@ struct DeviceCtx {
   hipEvent_t ev_sys = nullptr;  // fallback: an event with the system-scope fence
   int64_t tag = 0;
   int cus = 0;                  // compute units of the device
+  uint8_t* scratch = nullptr;   // this device's copy of `scratch` (imu_imunpack_matmul_noalloc)
 };
 DeviceCtx g_ctx[kMaxDevices];
+
+// Workspace of imu_imunpack_matmul_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes its name to a
+// kernel (on the host the name is only a stand-in); imu_init looks up each
+// device's address with hipGetSymbolAddress and keeps it in the context.
+constexpr size_t kNoallocScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 std::mutex g_init_mu;  // imu_init / imu_release
 
 // The context of the calling thread's current device, or an error when
@@ -556,6 +564,9 @@ imu_status imu_init(int64_t max_batch) {
     IMU_HIP(hipEventCreateWithFlags(&c.ev, hipEventDisableTiming | hipEventDisableSystemFence));
     IMU_HIP(hipEventCreateWithFlags(&c.ev_sys, hipEventDisableTiming));
     IMU_HIP(hipDeviceGetAttribute(&c.cus, hipDeviceAttributeMultiprocessorCount, dev));
+    void* sp = nullptr;
+    IMU_HIP(hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)));
+    c.scratch = static_cast<uint8_t*>(sp);
     c.live = true;
   }
   if (c.cap < max_batch) {
@@ -593,6 +604,7 @@ imu_status imu_release(void) {
   c.buf = c.dbuf = nullptr;
   c.cap = 0;
   c.ev = c.ev_sys = nullptr;
+  c.scratch = nullptr;
   c.live = false;
   return IMU_OK;
 }
@@ -721,6 +733,23 @@ imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const i
   if (ws_bytes > (size_t)INT64_MAX) return fail(IMU_ERR_INVALID_ARG, "ws_bytes above 2^63");
   return matmul_impl(oa, ob, p, c, out, static_cast<uint8_t*>(ws), (int64_t)ws_bytes, ws_needed, info, stream);
 }
+
+imu_status imu_imunpack_matmul_noalloc(const imu_matrix* a, const imu_matrix* b, const imu_params* p, int32_t* c,
+                                       float* out, size_t* ws_needed, imu_plan_info* info, hipStream_t stream) {
+  Operand oa, ob;
+  IMU_TRY(check_pair(a, b, p, &oa, &ob));
+  if (!c) return fail(IMU_ERR_INVALID_ARG, "c is NULL");
+  DeviceCtx* st = nullptr;
+  IMU_TRY(current_ctx(a->batch, &st));
+  const imu_status r = matmul_impl(oa, ob, p, c, out, st->scratch, (int64_t)kNoallocScratchBytes, ws_needed, info,
+                                   stream);
+  if (r == IMU_ERR_WORKSPACE)
+    return fail(IMU_ERR_WORKSPACE, "the problem needs more than the library's fixed %zu-byte scratch (%s)",
+                kNoallocScratchBytes, "use imu_imunpack_matmul with a workspace");
+  return r;
+}
+
+size_t imu_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
 
 const char* imu_status_string(imu_status s) {
   switch (s) {
