@@ -1,16 +1,21 @@
 """Benchmark of the IM-Unpack integer GEMM path on one MI355X.
 
-A step is one call of imu_imunpack_matmul on the LLaMA-7B-shaped linear
-workload (X 2048x4096 bf16 times W^T with W 4096x4096 bf16, beta=15, b=5,
-p=95%, Mix unpacking): percentile scale, RTN + outlier counts, Mix residuals,
-plan (one device->host header read), digit unpacking of both operands, int8
-MFMA GEMM with shift-and-accumulate fold and dequantization.  Inputs are
-resident in HBM before the timed region.
+A step is one call of imu_imunpack_matmul: percentile scale, RTN + outlier
+counts, Mix residuals, plan (one device->host header read), digit unpacking
+of both operands, int8 MFMA GEMM with shift-and-accumulate fold and
+dequantization.  The default workload is the MLP up-projection (X 2048x4096
+bf16 times W^T with W 11008x4096 bf16, beta=31, b=4, p=95%, Mix unpacking),
+the largest single-GPU configuration; --config 1 selects the LLaMA-7B-shaped
+linear layer.  Inputs are resident in HBM before the timed region.
 
 The printed JSON line reports effective int-TOPS on the original shape
-(2*M*N*K / step time), the unpack ratio, the GEMM's share of the dense int8
-MFMA peak (roofline object), per-stage times from HIP events, and the CPU
-oracle timed on the host cores (cpu_baseline).  Only one GPU is supported.
+(2*M*N*K / step time) over back-to-back (warm) steps, the same steps with the
+L2 and the 256 MB MALL flushed before each (cold, a 512 MiB write between the
+steps, outside their events), the unpack ratio of Mix and of the four fixed
+row/column pairings (next to the ratios the IM-Unpack page reports for
+LLaMA-7B, as context), the GEMM's share of the dense int8 MFMA peak (roofline
+object), per-stage times from HIP events, and the CPU oracle timed on the host
+cores on a sampled block (cpu_baseline).  Only one GPU is supported.
 """
 from __future__ import annotations
 
@@ -28,20 +33,20 @@ sys.path.insert(0, ROOT)
 METRIC = "effective int-TOPS (orig M·N·K) + unpack ratio + % int8 MFMA peak, 1×MI355X"
 INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 512 << 20  # written between cold steps: more than the 256 MB MALL and the 8 x 4 MB L2
 
+# Unpack ratios the IM-Unpack summary page reports ("Measured effects" table,
+# unpack-ratio rows: LLaMA-7B linear-layer GEMMs, beta=15, b=5).  Context only:
+# those matrices are not available, the synthetic workloads are not them.
+PAGE_RATIOS = {"mix": 1.06, "row/row": 2.02, "row/col": 5.36, "col/row": 1.64, "col/col": 4.01}
 
-# HBM traffic of one GEMM launch on the default workload, from two rocprofv3
-# --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the
-# factor that maps the same counter onto the known bytes of a plain 256 MiB
-# device copy (bench.py --copy-calibration).  The readings belong to one
-# version of the GEMM source: when gemm.hip no longer hashes to `source_sha256`
-# the traffic is reported as null.
-GEMM_TRAFFIC = {
-    "source_sha256": "9f179b4b771cddb04e32901c9ce05bb9939bf615b38f57d1d4242e0c8bdcd7b9",
-    "fetch_kib": 151790.0, "write_kib": 65536.0,        # counter readings per launch
-    "fetch_factor": 1.99980, "write_factor": 1.00000,  # copy calibration
-    "bytes_per_launch": 377943480,
-}
+# HBM traffic of one GEMM launch per workload, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the factor
+# that maps the same counter onto the known bytes of a plain 256 MiB device
+# copy (bench.py --copy-calibration).  The readings belong to one version of
+# the GEMM source: when gemm.hip no longer hashes to `source_sha256` the
+# traffic is reported as null.
+GEMM_TRAFFIC = {}
 
 
 def parse():
@@ -49,9 +54,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, help="workload recipe index (default 1: LLaMA linear)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload recipe index (default 2: MLP up-projection; 1: LLaMA-shaped linear)")
+    ap.add_argument("--cold-steps", type=int, default=20, help="steps timed after a cache flush each")
+    ap.add_argument("--pair-steps", type=int, default=5, help="timed steps of each fixed row/column pairing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-repeats", type=int, default=1)
+    ap.add_argument("--only-steps", action="store_true",
+                    help="run the warm steps only (no cold, per-stage, fixed-pair or CPU legs): for profiler runs")
     ap.add_argument("--training-step", action="store_true",
                     help="time the quantized-training linear step (forward, data gradient, weight gradient) "
                          "at the training workload size instead")
@@ -90,6 +99,10 @@ class HipEvents:
                 raise RuntimeError("hipEventCreateWithFlags failed")
             self.ev.append(h.value)
 
+    def record(self, i: int, stream: int) -> None:
+        if self.hip.hipEventRecord(self.ct.c_void_p(self.ev[i]), self.ct.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed_ms(self, i: int, j: int) -> float:
         ms = self.ct.c_float()
         if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[i], self.ev[j]) != 0:
@@ -123,29 +136,58 @@ def device_matrix(op, torch, B):
     return B.Matrix(t[0] if op.batch == 1 else t, op.layout)
 
 
-def cpu_baseline(pr, repeats: int):
-    """The oracle as it stands, on the whole workload (all stages, unpacked GEMM included)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(pr, rows: int = 256, col_frac: int = 8):
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the workload: quantization (percentile, RTN, counts) and the plan of the
+    full operands, then the low bit-width route (unpack, segment GEMMs, fold)
+    for the output block of the first `rows` rows and the first N/col_frac
+    columns, checked against the direct product of that block.  The per-block
+    time is scaled to all of C (the route's work is proportional to the output
+    block at fixed K), so `value` is the oracle's effective int-TOPS on the
+    whole problem."""
     from oracle import imunpack_oracle as O
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = os.cpu_count() or 1
+    M, K, N = pr.mnk
+    ms, ns = min(rows, M), max(1, N // col_frac)
     a = O.widen(pr.a.logical_bits(0), pr.a.dtype)
     b = O.widen(pr.b.logical_bits(0), pr.b.dtype)
-    times = []
-    for _ in range(repeats):
-        t0 = time.perf_counter()
-        O.imunpack_matmul(a, b, pr.beta, pr.bits, pr.p_num, pr.p_den, pr.strat_a, pr.strat_b, pr.gamma,
-                          unpacked=True)
-        times.append(time.perf_counter() - t0)
-    M, K, N = pr.mnk
-    t = min(times)
-    return {"value": round(2.0 * M * N * K / t / 1e12, 6), "unit": "TOPS", "cores": int(blas_threads),
+    t0 = time.perf_counter()
+    qa = O.quantize(a, pr.beta, pr.p_num, pr.p_den, pr.bits)
+    qb = O.quantize(b, pr.beta, pr.p_num, pr.p_den, pr.bits)
+    pl = O.plan(qa, qb, pr.strat_a, pr.strat_b, pr.gamma)
+    t_qp = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    da_r, db_c = pl.da_r[:ms], pl.db_c[:ns]
+    rows_a, cols_b = O.level_lines(da_r), O.level_lines(db_c)
+    Ap = O.unpack_a(qa.q[:ms], pr.bits, da_r, pl.da_c, pl.db_r, rows_a, pl.trip)
+    Bp = O.unpack_b(qb.q[:, :ns], pr.bits, pl.db_r, db_c, pl.da_c, cols_b, pl.trip)
+    P = O.segment_products(Ap, Bp, pl.trip, pr.bits)
+    Cb = O.fold(P, rows_a, cols_b, ms, ns, pr.bits)
+    t_blk = time.perf_counter() - t1
+    if not np.array_equal(Cb, O.direct_product(qa.q[:ms], qb.q[:, :ns])):
+        raise AssertionError("oracle: sampled unpacked block differs from the direct product")
+    t_est = t_qp + t_blk * (M * N) / (ms * ns)
+    return {"value": round(2.0 * M * N * K / t_est / 1e12, 6), "unit": "TOPS", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"whole {pr.name} problem ({M}x{K} @ {K}x{N}), every oracle stage incl. the unpacked "
-                      f"GEMM + fold, best of {repeats}; {t:.2f} s; numpy/BLAS threads={blas_threads}, "
-                      f"host cpus={os.cpu_count()}"}
+            "sample": f"{pr.name}: quantize + plan of the full operands ({t_qp:.2f} s), then unpack + segment "
+                      f"GEMMs + fold for the C block of rows 0..{ms - 1} x columns 0..{ns - 1} ({t_blk:.2f} s, "
+                      f"checked against the direct product), scaled by {M * N / (ms * ns):.0f} to all of C; "
+                      f"numpy/BLAS threads={blas_threads}, host cpus={os.cpu_count()}, cpu '{cpu_model()}'"}
 
 
 def training_step(args):
@@ -212,21 +254,26 @@ def main():
 
     pr = W.config(args.config)[0]
     M, K, N = pr.mnk
+    nb = pr.a.batch
     a = device_matrix(pr.a, torch, B)
     b = device_matrix(pr.b, torch, B)
-    p = B.params(beta=pr.beta, bits=pr.bits, p=(pr.p_num, pr.p_den), strat_a=pr.strat_a,
-                 strat_b=pr.strat_b, gamma=pr.gamma)
-    ws = B.Workspace("cuda")
-    c = torch.empty((pr.a.batch, M, N), dtype=torch.int32, device="cuda")
-    out = torch.empty((pr.a.batch, M, N), dtype=torch.float32, device="cuda")
 
-    def step():
-        return B.imunpack_matmul(a, b, p, out=out, c=c, ws=ws)
+    def prm(sa, sb):
+        return B.params(beta=pr.beta, bits=pr.bits, p=(pr.p_num, pr.p_den), strat_a=sa, strat_b=sb,
+                        gamma=pr.gamma)
+
+    p = prm(pr.strat_a, pr.strat_b)
+    ws = B.Workspace("cuda")
+    c = torch.empty((nb, M, N), dtype=torch.int32, device="cuda")
+    out = torch.empty((nb, M, N), dtype=torch.float32, device="cuda")
+
+    def step(pp=p):
+        return B.imunpack_matmul(a, b, pp, out=out, c=c, ws=ws)
 
     for _ in range(args.warmup):
         step()
-    # the GEMM launches of every timed step are bracketed by a pair of HIP
-    # events recorded by the library on the launch stream
+    # warm: back-to-back steps, the GEMM launches of every step bracketed by a
+    # pair of HIP events the library records on the launch stream
     hev = HipEvents(2 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -239,6 +286,32 @@ def main():
     t_gemm = sum(hev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)) / 1000.0 / args.steps
     hev.close()
     info = infos[0]
+
+    if args.only_steps:
+        print(json.dumps({"workload": pr.name, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": round(t_step * 1e3, 4), "gemm_us": round(t_gemm * 1e6, 2)}))
+        return
+
+    # cold: a 512 MiB write before each step evicts the L2s and the MALL; the
+    # step's own events start after it
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    nc = max(1, args.cold_steps)
+    sev, gev = HipEvents(2 * nc), HipEvents(2 * nc)
+    sh = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    for i in range(nc):
+        flush.fill_(i & 0xFF)
+        sev.record(2 * i, sh)
+        B.set_gemm_events(gev.ev[2 * i], gev.ev[2 * i + 1])
+        step()
+        sev.record(2 * i + 1, sh)
+    torch.cuda.synchronize()
+    B.set_gemm_events(None, None)
+    cold_step = float(np.median([sev.elapsed_ms(2 * i, 2 * i + 1) for i in range(nc)])) / 1000.0
+    cold_gemm = float(np.median([gev.elapsed_ms(2 * i, 2 * i + 1) for i in range(nc)])) / 1000.0
+    sev.close()
+    gev.close()
+    del flush
 
     # per-stage HIP events through the staged entry points (same kernels)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
@@ -263,18 +336,39 @@ def main():
         if it:
             acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(6)]
     stages_us = {n: round(float(v) * 1000.0 / reps, 2) for n, v in zip(names, acc)}
+    del sa, sb, plan, a_u, b_u
 
-    # dominant kernel: the unpacked int8 GEMM of the timed steps (events above)
+    # the four fixed row/column pairings: unpack ratio (the Mix plan's table
+    # holds the sizes of every pair) and the whole step with that strategy
+    base_mnk = M * K * N
+    ratios = {"mix": round(info["m_u"] * info["k_u"] * info["n_u"] / base_mnk, 4)}
+    pair_ms = {}
+    for sa_, sb_ in (("row", "row"), ("row", "col"), ("col", "row"), ("col", "col")):
+        key = f"{sa_}/{sb_}"
+        mu, ku, nu = info["pairs"][(sa_, sb_)]
+        ratios[key] = round(mu * ku * nu / base_mnk, 4)
+        pp = prm(sa_, sb_)
+        for _ in range(2):
+            _, _, pinfo = step(pp)
+        if (pinfo[0]["m_u"], pinfo[0]["k_u"], pinfo[0]["n_u"]) != (mu, ku, nu):
+            raise AssertionError(f"fixed pairing {key}: sizes differ from the Mix plan's table")
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(max(1, args.pair_steps)):
+            step(pp)
+        torch.cuda.synchronize()
+        pair_ms[key] = round((time.perf_counter() - t1) / max(1, args.pair_steps) * 1e3, 4)
+
+    # dominant kernel: the unpacked int8 GEMM of the warm steps (events above)
     gemm_ops = sum(2.0 * f["m_u"] * f["k_u"] * f["n_u"] for f in infos)  # every batch entry
     gemm_tops = gemm_ops / t_gemm / 1e12
-    traffic = None
-    if GEMM_TRAFFIC is not None and GEMM_TRAFFIC["source_sha256"] == gemm_source_sha():
-        traffic = GEMM_TRAFFIC["bytes_per_launch"]
+    tr = GEMM_TRAFFIC.get(pr.name)
+    traffic = tr["bytes_per_launch"] if tr and tr["source_sha256"] == gemm_source_sha() else None
 
-    eff_tops = 2.0 * M * N * K * pr.a.batch / t_step / 1e12
+    eff = lambda t: 2.0 * M * N * K * nb / t / 1e12  # noqa: E731
     rec = {
         "metric": METRIC,
-        "value": round(eff_tops, 3),
+        "value": round(eff(t_step), 3),
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
@@ -288,8 +382,17 @@ def main():
         "config": {"workload": f"{pr.name}: A {M}x{K} {pr.a.dtype} ({pr.a.layout}) @ B {K}x{N} {pr.b.dtype} "
                                f"({pr.b.layout}), beta={pr.beta} b={pr.bits} p={pr.p_num}/{pr.p_den} "
                                f"{pr.strat_a}/{pr.strat_b}",
-                   "M": M, "K": K, "N": N, "batch": pr.a.batch},
-        "unpack_ratio": round(sum(f["m_u"] * f["k_u"] * f["n_u"] for f in infos) / (pr.a.batch * M * K * N), 4),
+                   "M": M, "K": K, "N": N, "batch": nb},
+        "warm": {"ms_per_step": round(t_step * 1e3, 4), "tops": round(eff(t_step), 3),
+                 "gemm_us": round(t_gemm * 1e6, 2)},
+        "cold": {"ms_per_step": round(cold_step * 1e3, 4), "tops": round(eff(cold_step), 3),
+                 "gemm_us": round(cold_gemm * 1e6, 2), "steps": nc,
+                 "flush": f"{FLUSH_BYTES >> 20} MiB written before each step, outside its events (median)"},
+        "unpack_ratio": round(sum(f["m_u"] * f["k_u"] * f["n_u"] for f in infos) / (nb * base_mnk), 4),
+        "unpack_ratios": ratios,
+        "pair_ms_per_step": pair_ms,
+        "page_unpack_ratios": {"values": PAGE_RATIOS,
+                               "note": "IM-Unpack page, LLaMA-7B linear layers, beta=15 b=5: context only"},
         "plan": {"choice": list(info["choice"]), "m_u": info["m_u"], "k_u": info["k_u"], "n_u": info["n_u"],
                  "k_pad": info["k_pad"], "segments": info["n_seg"]},
         "gemm_pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
@@ -300,7 +403,7 @@ def main():
                      "launch_us": round(t_gemm * 1e6, 2), "ops_per_launch": gemm_ops},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(pr, args.cpu_repeats)
+        rec["cpu_baseline"] = cpu_baseline(pr)
     print(json.dumps(rec))
 
 

@@ -206,7 +206,11 @@ imu_status imu_plan_unpack(const imu_matrix* a, const imu_matrix* b, const imu_p
  * block then K' block, block (rb, c) at byte (rb * k_pad/32 + c) * 1024; inside
  * a block, bytes [16h, 16h + 16) of the block's row r are at 16 * (r + 32h)
  * (h = 0, 1).  Rows are level-major (original lines
- * first, then level 1 lines, ...); columns are the exponent segments of K'
+ * first, then level 1 lines, ...).  A's rows keep their index order inside a
+ * level; B's columns (the rows of B'^T) are in depth order, descending depth
+ * then index: row j < N of B'^T is the column at position j of that order, and
+ * level w >= 1 of the column at position j is row n_base + (columns deeper than
+ * 1, ..., w-1, summed) + j.  Columns are the exponent segments of K'
  * (e = v + v' ascending, then k, then v), each padded with zero bytes to a
  * multiple of 128.  Every byte of the valid rows is written. */
 imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p,

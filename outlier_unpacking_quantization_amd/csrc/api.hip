@@ -4,6 +4,7 @@
 // quantize.hip, plan.hip, unpack.hip and gemm.hip.
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstddef>
 #include <cstdint>
@@ -445,8 +446,6 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   g.entry_stride = pl.entry_stride;
   g.amap_off = pl.amap;
   g.bmap_off = pl.bmap;
-  g.db_c_off = pl.db_c;
-  g.lvl_b_off = pl.lvl_b;
   g.stats_a = stats_a;
   g.stats_b = stats_b;
   g.stats_stride_a = la.stride;
@@ -459,6 +458,23 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   g.N = N;
   g.bits = p->bits;
   g.fold_cols = fold_cols ? 1 : 0;
+  // Tile order: each XCD takes a run of tiles covering G tile rows; its L2
+  // then fills G row panels of A' and about T / (8 G) column panels of B'^T,
+  // which is least near G = sqrt(T BN / (8 BM)) (rounded to a power of two).
+  {
+    int64_t tm = 1, tn = 1;
+    for (int64_t b = 0; b < batch; ++b) {
+      const EntrySizes f = get(b);
+      if ((f.m_base / 256) * (f.n_base / 128) >= tm * tn) {
+        tm = f.m_base / 256;
+        tn = f.n_base / 128;
+      }
+    }
+    const double ideal = std::sqrt((double)(tm * tn) * 128.0 / (8.0 * 256.0));
+    int gsz = 1;
+    while (gsz * 2 <= tm && std::log2(gsz * 2.0) <= std::log2(std::max(ideal, 1.0)) + 0.5) gsz *= 2;
+    g.group_m = gsz;
+  }
   // Measurement events: attached to the launch when the call makes a single
   // one (no marker of their own in the stream), else recorded around all of
   // the call's launches.

@@ -83,6 +83,13 @@ struct PlanHeader {
   int64_t seg_off[kMaxSeg + 1];
   int32_t seg_len[kMaxSeg];
   int64_t reserved[8];
+  // B's columns in depth order (descending depth, then column index): slot j
+  // of level w holds the column at position j of that order, for
+  // j < lvcnt_b[w] (the columns deeper than w; lvcnt_b[0] = N), as B'^T row
+  // lvbase_b[w] + j (lvbase_b[0] = 0).  b_perm: the order is not the identity.
+  int32_t lvcnt_b[32];
+  int64_t lvbase_b[32];
+  int32_t b_perm, pad1;
 };
 constexpr int64_t kPlanHeaderStride = 2048;
 static_assert(sizeof(PlanHeader) <= kPlanHeaderStride, "plan header");

@@ -14,8 +14,13 @@
 // without extra rows are folded inside the base tile of their original
 // columns: the shift is one more exponent, so the tile walks (level, segment)
 // pairs by combined exponent under the same Horner accumulator, with the B'^T
-// rows of level w staged into the LDS slots of their own columns.  Extra rows
-// fold in a separate pass of extra tiles with atomic adds.
+// rows of level w staged into the LDS slots of their own columns.  The plan
+// puts B's columns in depth order (descending, then by index), so a tile's
+// 128 columns share their depth except at the few tiles where the depth
+// changes, the tile runs only the levels its columns have, and level w's rows
+// of the tile are contiguous in B'^T; the epilogue stores each column through
+// the order's map.  Extra rows fold in a separate pass of extra tiles with
+// atomic adds.
 //
 // Operands: A' (m_alloc x k_pad) in MFMA fragment order and B'^T (n_alloc x
 // k_pad), both K-contiguous.  Workgroup tile 256 x 128, four waves stacked along
@@ -30,8 +35,10 @@
 // next step is read right after the barrier, under the MFMAs of substep 3.
 // Segments are padded to the K step, so a step never straddles two exponents.
 // Tiles are dealt to the 8 XCDs (hardware order w % 8) in contiguous runs of a
-// grouped order (groups of 4 tile rows), so the workgroups sharing an XCD's L2
-// share A and B panels.
+// grouped order (groups of G tile rows, G chosen by the host to minimise the
+// L2 fills), so the workgroups sharing an XCD's L2 share A and B panels; inside
+// a group the tile columns are taken in residue classes mod 8, which spreads
+// the deep (costly) columns over all runs.
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -49,7 +56,6 @@ constexpr int FR = 2;  // 32-row A fragments per wave
 constexpr int BM = 128 * FR, BN = 128, BK = 128;
 constexpr int kThreads = 256;
 constexpr int BSTR = BK + 16;  // LDS bytes per staged B row
-constexpr int kGroupM = 4;     // tile rows per ordering group
 constexpr int kXcds = 8;
 static_assert(BK == kKPad, "a K step must not straddle exponent segments");
 
@@ -57,19 +63,34 @@ struct TileCoord {
   int tm, tn;
 };
 
+// Tile column at position j of a group's column order: the residue classes
+// of the column index mod 8 in turn (0, 8, 16, ..., then 1, 9, ...).  B's
+// columns are in depth order, so the deepest (costliest) tile columns come
+// first; taking the classes in turn gives every XCD's run a share of each
+// depth, and the tiles of a run still share their A and B panels.
+__device__ inline int col_interleave(int j, int n) {
+  const int q = n >> 3, r = n & 7;  // classes c < r hold q + 1 columns, the others q
+  if (j < r * (q + 1)) {
+    const int c = j / (q + 1);
+    return c + 8 * (j - c * (q + 1));
+  }
+  const int jj = j - r * (q + 1), c = jj / q;  // q >= 1 here, since j < n
+  return r + c + 8 * (jj - c * q);
+}
+
 // Workgroup w of a launch over tiles_m x tiles_n tiles -> its tile.  XCD
 // x = w % 8 gets the contiguous run of ids [start(x), start(x) + count(x)) of the
-// order (group of kGroupM tile rows, column, row).
-__device__ inline TileCoord tile_of(int w, int tiles_m, int tiles_n) {
+// order (group of G tile rows, interleaved column, row).
+__device__ inline TileCoord tile_of(int w, int tiles_m, int tiles_n, int G) {
   const int T = tiles_m * tiles_n;
   const int x = w % kXcds, slot = w / kXcds;
   const int per = T / kXcds, rem = T % kXcds;
   const int id = x * per + min(x, rem) + slot;
-  const int group = id / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(kGroupM, tiles_m - first_m);
-  const int in = id - group * kGroupM * tiles_n;
-  return TileCoord{first_m + in % gm, in / gm};
+  const int group = id / (G * tiles_n);
+  const int first_m = group * G;
+  const int gm = min(G, tiles_m - first_m);
+  const int in = id - group * G * tiles_n;
+  return TileCoord{first_m + in % gm, col_interleave(in / gm, tiles_n)};
 }
 
 // 4 x 4 transpose inside each quad of lanes: on entry lane c of the quad holds
@@ -143,6 +164,7 @@ struct FoldCursor {
   int s, w, sum;
   int64_t k, end;
 };
+typedef __attribute__((address_space(4))) const PlanHeader* HdrC;
 __device__ inline bool fold_next_pair(FoldCursor& c, int nseg, int nlev, SegTable off) {
   int s = c.s, w = c.w, sum = c.sum;
   for (;;) {
@@ -179,7 +201,6 @@ __device__ inline FoldCursor fold_top(int nseg, int nlev, SegTable off) {
   return c;
 }
 
-typedef __attribute__((address_space(4))) const PlanHeader* HdrC;
 constexpr int kMaxLevels = 32;  // digits of an int32 code in base 2^(bits-1), bits >= 2: at most 31
 
 // FOLD: the base pass also folds the extra columns of entries whose plan has
@@ -188,8 +209,6 @@ constexpr int kMaxLevels = 32;  // digits of an int32 code in base 2^(bits-1), b
 template <bool FOLD>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BSTR];
-  __shared__ int32_t s_lvl[kMaxLevels - 1][BN];  // FOLD: B'^T row of (column, level w >= 1), -1 if none
-  __shared__ int s_nlev;
   // this workgroup's batch entry: sizes from its plan header (scalar loads)
   const int entry = blockIdx.y;
   const uint8_t* hdr = g.plan + (int64_t)entry * kPlanHeaderStride;
@@ -208,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int64_t cols = mode == 2 ? n_alloc : n_base;
   const int tiles_m = (int)(rows / BM), tiles_n = (int)(cols / BN);
   if ((int)blockIdx.x >= tiles_m * tiles_n) return;
-  const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n);
+  const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n, g.group_m);
   const bool base_tile = (int64_t)tc.tm * BM < m_base && (int64_t)tc.tn * BN < n_base;
   if (mode == 2 && base_tile) return;
   // the entry's operands follow those of the earlier entries
@@ -258,38 +277,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   int64_t gbo[4];    // byte offsets of the B staging rows at lb's level (FOLD)
   uint32_t bvm = 0xF, bvl = 0xF;  // rows present at lb's level / in the last load (FOLD)
   if constexpr (FOLD) {
-    if (colfold) {
-      const int32_t* dbc = reinterpret_cast<const int32_t*>(pe + g.db_c_off);
-      const int32_t* lvlb = reinterpret_cast<const int32_t*>(pe + g.lvl_b_off);
-      if (tid == 0) s_nlev = 1;
-      __syncthreads();
-      if (tid < BN && col0 + tid < g.N) atomicMax(&s_nlev, min(dbc[col0 + tid], kMaxLevels));
-      __syncthreads();
-      nlev = s_nlev;
-      for (int i = tid; i < (nlev - 1) * BN; i += kThreads) {
-        const int w = 1 + i / BN;
-        const int64_t n = col0 + i % BN;
-        s_lvl[w - 1][i % BN] = n < g.N ? lvlb[(int64_t)w * g.N + n] : -1;
-      }
-      __syncthreads();
-    }
+    // levels present in the tile: B's columns are in depth order, so level w
+    // is present iff some slot of the tile lies below lvcnt_b[w]
+    if (colfold)
+      while (nlev < kMaxLevels && (int64_t)ph->lvcnt_b[nlev] > col0) ++nlev;
   }
-  // B staging rows of level w for this thread (FOLD); absent ones re-read the
-  // level-0 row and are zeroed when stored
+  // B staging rows of level w for this thread (FOLD): slot col0 + c of level
+  // w > 0 is B'^T row lvbase_b[w] + col0 + c; slots past lvcnt_b[w] are absent
+  // (their column has fewer levels): they re-read the tile's first row of that
+  // level, which is present, and are zeroed when stored
   auto set_level = [&](int w) __attribute__((always_inline)) {
     bvm = 0;
+    const int64_t cnt = w == 0 ? n_alloc : (int64_t)ph->lvcnt_b[w];
+    const int64_t base = w == 0 ? 0 : ph->lvbase_b[w];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = br + 32 * j;
-      int64_t r = col0 + c;
-      if (w > 0) {
-        const int32_t x = s_lvl[w - 1][c];
-        if (x >= 0) r = x;
-        bvm |= (uint32_t)(x >= 0) << j;
-      } else {
-        bvm |= 1u << j;
-      }
-      gbo[j] = r * kp;
+      const bool live = col0 + c < cnt;
+      gbo[j] = (base + col0 + (live ? c : 0)) * kp;
+      bvm |= (uint32_t)live << j;
     }
   };
   if constexpr (FOLD) set_level(0);
@@ -307,6 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     if constexpr (FOLD) return c.sum;
     else return c.s;
   };
+
   Cur cc = top();        // compute
   Cur la = cc, lb = cc;  // A loads (one step ahead), B loads (two ahead)
   int lbw = 0;           // level of lb's rows (FOLD)
@@ -425,7 +432,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // consecutive columns of row ... + l % 4, so each lane stores 16 bytes and a
   // store instruction covers eight full 128-byte row segments.  Needs 16-byte
   // aligned rows and the whole tile inside N; otherwise one element per store.
-  const bool vec = (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c_e) & 15) == 0 &&
+  // With B's columns in depth order (b_perm) the tile's slots map to scattered
+  // columns of C: element stores through the column map.
+  const bool bperm = ph->b_perm != 0;
+  const bool vec = !bperm && (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c_e) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(out_e) & 15) == 0 && col0 + BN <= g.N;
   if (vec) {
     const int64_t r_v = row0 + 4 * (lane >> 5) + (lane & 3), c_v = col0 + 4 * ((lane & 31) >> 2);
@@ -454,6 +464,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
       }
     return;
   }
+  // column of C held by this lane in block j (slot c_lane + 32 j), -1 past N
+  int64_t cmapx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t slot = c_lane + 32 * j;
+    cmapx[j] = slot >= g.N ? -1 : bperm ? (int64_t)(bmap[slot] & 0xFFFFFF) : slot;
+  }
 #pragma unroll
   for (int f = 0; f < FR; ++f)
 #pragma unroll
@@ -463,15 +480,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
         const int r = 4 * r4 + r3;
         const int64_t gr = r_lane + f * 32 + 8 * r4 + r3;
         if (gr >= g.M) continue;
-        int32_t* crow = c_e + gr * ldc + c_lane;
-        float* orow = out_e ? out_e + gr * ldc + c_lane : nullptr;
+        int32_t* crow = c_e + gr * ldc;
+        float* orow = out_e ? out_e + gr * ldc : nullptr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (c_lane + 32 * j >= g.N) continue;
+          if (cmapx[j] < 0) continue;
           const int32_t v = acc[f][j][r];
-          const int32_t cv = mode == 1 ? (int32_t)((uint32_t)crow[32 * j] + (uint32_t)v) : v;
-          crow[32 * j] = cv;
-          if (orow) orow[32 * j] = (float)cv * sab;
+          const int32_t cv = mode == 1 ? (int32_t)((uint32_t)crow[cmapx[j]] + (uint32_t)v) : v;
+          crow[cmapx[j]] = cv;
+          if (orow) orow[cmapx[j]] = (float)cv * sab;
         }
       }
       __builtin_amdgcn_sched_barrier(0);

@@ -61,7 +61,7 @@ struct GemmArgs {
   const int8_t* a_u;
   const int8_t* b_u;
   const uint8_t* plan;        // plan buffer (headers, then per-entry arrays)
-  int64_t headers_bytes, entry_stride, amap_off, bmap_off, db_c_off, lvl_b_off;  // PlanLayout of the plan
+  int64_t headers_bytes, entry_stride, amap_off, bmap_off;  // PlanLayout of the plan
   const uint8_t* stats_a;
   const uint8_t* stats_b;
   int64_t stats_stride_a, stats_stride_b;
@@ -73,6 +73,7 @@ struct GemmArgs {
   int mode;                   // 2: extra tiles of the entries folded by atomics; else base tiles (per
                               // entry: add to C after that pass, or store C, folding extra columns)
   int fold_cols;              // entries with extra columns only fold them in the base pass
+  int group_m;                // tile rows per group of the workgroup -> tile order (power of two)
 };
 // tiles_x: the largest tile count of an entry for this mode; batch entries on
 // blockIdx.y.  start / stop: events recorded as the launch starts / ends

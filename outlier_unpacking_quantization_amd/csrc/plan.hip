@@ -20,9 +20,13 @@
 // (3) plan_write: from all chunks' counts, each workgroup derives the level
 //     bases or padded segment offsets and its own offset in every task
 //     (workgroup 0 also writes the header sizes), then scans its lines (a
-//     thread owns 4 consecutive lines, one block-wide scan per batch of tasks)
+//     thread owns 2 consecutive lines, one block-wide scan per batch of tasks)
 //     and writes the level-major line maps, the per-segment prefixes over k and
-//     the K' position table used by the unpack kernels.
+//     the K' position table used by the unpack kernels.  B's columns are laid
+//     out in depth order (descending depth, then index; a counting sort whose
+//     classes are the depths), so the GEMM's tiles hold columns of one depth.
+//     The header records the columns deeper than each level and each level's
+//     first row.
 // Records exchanged inside one launch are written with device-scope atomic
 // stores (through the XCD-local L2) and read after a device-scope acquire; the
 // counter that elects the last workgroup is the statistics header's, which is
@@ -538,6 +542,18 @@ __device__ void layout(const PlanArgs& a, int b, int64_t w, bool write_header, P
         }
       };
       put(E.ph, [](auto* p, auto v) __attribute__((always_inline)) { *p = v; });
+      // B's depth order (device header only: the GEMM reads it): lines deeper
+      // than each level and the first B'^T row of each level; the order is a
+      // permutation unless every column has the same depth
+      if (lane < 32) {
+        E.ph->lvcnt_b[lane] = (int32_t)S.task_tot[1][lane];
+        E.ph->lvbase_b[lane] = lane == 0 ? 0 : (int64_t)base_k[1];
+      }
+      {
+        const long long exact = lane >= 1 && lane <= S.lev[1] ? S.task_tot[1][lane - 1] - S.task_tot[1][lane] : 0;
+        const bool mixed = __ballot(exact > 0 && exact < L.N) != 0;
+        if (lane == 0) E.ph->b_perm = mixed ? 1 : 0;
+      }
       if (hh) {
         // fields of the earlier launches, all loaded before the first store
         // (a load's wait would also wait for the slow host stores before it)
@@ -601,7 +617,43 @@ __device__ void phase_write(const PlanArgs& a, int b, int64_t w, PlanShared& S) 
     }
   }
   const int nl = (int)(i1 - i0);
-  for (int tb = 0; tb < ntasks; tb += kTaskBatch) {
+  if (c.kind == 1) {
+    // B's columns in depth order: descending depth, then column index.  Task t
+    // is the class of depth t + 1; a column of depth d sits at position
+    // (columns deeper than d) + (earlier chunks' columns of depth d) + (its rank
+    // in this chunk's class), and level u < d of it at B'^T row base[u] + that
+    // position (base[0] = 0): the columns deeper than u lead the order.
+    for (int tb = 0; tb < ntasks; tb += kTaskBatch) {
+      int cnt[kTaskBatch], ex[kTaskBatch];
+#pragma unroll
+      for (int j = 0; j < kTaskBatch; ++j) {
+        int v = 0;
+#pragma unroll
+        for (int l = 0; l < kPer; ++l)
+          if (l < nl) v += dA[l] == tb + j + 1;
+        cnt[j] = v;
+      }
+      block_excl_scan_multi(cnt, ex, S.scan_tot);
+#pragma unroll
+      for (int j = 0; j < kTaskBatch; ++j) {
+        const int d = tb + j + 1;
+        if (d > ntasks) continue;
+        long long pos = S.task_tot[1][d] + (S.off[d - 1] - S.off[d]) + ex[j];
+#pragma unroll
+        for (int l = 0; l < kPer; ++l) {
+          if (l >= nl || dA[l] != d) continue;
+          const int64_t i = i0 + l;
+          for (int u = 0; u < ntasks; ++u) {
+            const long long row = u == 0 ? pos : S.base[u] + pos;
+            E.lvl_b[(int64_t)u * c.n + i] = u < d ? (int32_t)row : -1;
+            if (u < d) E.bmap[row] = (int32_t)(i | ((int64_t)u << 24));
+          }
+          ++pos;
+        }
+      }
+    }
+  }
+  for (int tb = 0; tb < (c.kind == 1 ? 0 : ntasks); tb += kTaskBatch) {
     int cnt[kTaskBatch], ex[kTaskBatch];
 #pragma unroll
     for (int j = 0; j < kTaskBatch; ++j) {

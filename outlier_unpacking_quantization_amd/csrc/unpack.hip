@@ -195,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
   __shared__ uint32_t codes[L * LS];
   __shared__ int64_t rowoff[L];  // row part of the byte offset of row (line, level u), -1 if absent
   __shared__ int s_dout[L];
+  __shared__ int32_t s_line[L];  // operand line staged in slot i
   __shared__ int64_t s_off[kMaxSeg + 1];
   __shared__ int64_t s_p0[kMaxSeg + 1], s_p1[kMaxSeg + 1];
   __shared__ int s_ng[kMaxSeg + 1], s_pre[kMaxSeg + 1];
@@ -240,7 +241,14 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
 
   for (int s = tid; s <= nseg; s += kThreads) s_off[s] = ph->seg_off[s];
   if (tid < L) {
-    s_dout[tid] = o0 + tid < a.n_outer ? dout[o0 + tid] : 0;
+    // B's lines (columns) in the plan's depth order (inner-contiguous shape):
+    // slot o0 + i holds the column at that position, so a workgroup's lines
+    // share their depth; otherwise the lines in index order
+    int64_t line = min64(o0 + tid, a.n_outer - 1);
+    if (!OC && !is_a && ph->b_perm && o0 + tid < a.n_outer)
+      line = reinterpret_cast<const int32_t*>(pe + P.bmap)[o0 + tid] & 0xFFFFFF;
+    s_line[tid] = (int32_t)line;
+    s_dout[tid] = o0 + tid < a.n_outer ? dout[line] : 0;
     codes[tid * LS + kZero] = 0u;
   }
   __syncthreads();
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
       P1 = last_win ? s_off[tid + 1] : s_off[tid] + kps[kw1];
     }
     int64_t row_u0 = -1;
-    if (tid < L && s_dout[tid] > 0) row_u0 = lvl[o0 + tid];
+    if (tid < L && s_dout[tid] > 0) row_u0 = lvl[s_line[tid]];
     auto stage = [&](auto word) __attribute__((always_inline)) {
       if constexpr (!OC) {
         constexpr int G = W / 8;  // groups of 8 k per line
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
           for (int it = 0; it < kIter; ++it) {
             const int item = tid + it * kThreads;
             const int i = item / G, kk = (item % G) * 8;
-            const int64_t o = min64(o0 + i, a.n_outer - 1);
+            const int64_t o = s_line[i];
             float v[8];
             load8_vec<DT>(xb + o * a.so + kw0 + kk, v);
             uint32_t* dst = &codes[i * LS + slot(kk)];
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
           for (int it = 0; it < kIter; ++it) {
             const int item = tid + it * kThreads;
             const int i = item / G, kk = (item % G) * 8;
-            const int64_t o = min64(o0 + i, a.n_outer - 1);
+            const int64_t o = s_line[i];
             const T* line = xb + o * a.so;
             float v[8];
 #pragma unroll
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
       if (u > 0) {  // rows of the unpacked levels (rare): one more round trip each
         __syncthreads();  // readers of the previous level's rowoff are done
         if (tid < L) {
-          const int64_t row = s_dout[tid] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + o0 + tid] : (int64_t)-1;
+          const int64_t row = s_dout[tid] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + s_line[tid]] : (int64_t)-1;
           rowoff[tid] = row < 0 ? (int64_t)-1 : is_a ? frag_row_offset(row, kp) : row * kp;
         }
         __syncthreads();

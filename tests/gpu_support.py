@@ -59,6 +59,24 @@ def padded_line_index(lines: np.ndarray, n_orig: int, base: int) -> np.ndarray:
     return np.where(idx < n_orig, idx, idx - n_orig + base)
 
 
+def depth_order_col_index(cols: np.ndarray, db_c: np.ndarray, base: int) -> np.ndarray:
+    """Canonical level-major B' column (n, w) -> row of B'^T as the HIP path
+    lays it out (include/imunpack.h): the columns in depth order (descending
+    depth, ties by index); level 0 at rows 0..N-1 in that order, level w >= 1 at
+    base + (columns deeper than 1..w-1) + the column's position in the order."""
+    d = np.asarray(db_c, np.int64)
+    order = np.lexsort((np.arange(d.size), -d))  # depth descending, then index
+    pos = np.empty(d.size, np.int64)
+    pos[order] = np.arange(d.size)
+    dmax = int(d.max()) if d.size else 1
+    deeper = np.array([int((d > w).sum()) for w in range(dmax + 1)], np.int64)
+    lvbase = np.zeros(dmax + 1, np.int64)
+    for w in range(2, dmax + 1):
+        lvbase[w] = lvbase[w - 1] + deeper[w - 1]
+    n, w = cols[:, 0], cols[:, 1]
+    return np.where(w == 0, pos[n], base + lvbase[np.minimum(w, dmax)] + pos[n])
+
+
 def padded_k_index(trip: np.ndarray) -> np.ndarray:
     """Canonical K' index (sorted by e, k, v) -> padded column."""
     sizes = np.bincount(trip[:, 3]) if trip.size else np.zeros(0, int)

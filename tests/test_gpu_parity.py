@@ -163,7 +163,9 @@ def _staged_problem(pr):
                          info["m_alloc"], kp)
         B_g = b_u[info["b_offset"]:info["b_offset"] + info["n_alloc"] * kp].view(info["n_alloc"], kp).cpu().numpy()
         rows = G.padded_line_index(pl.rows_a, M, info["m_base"])
-        cols = G.padded_line_index(pl.cols_b, N, info["n_base"])
+        cols = G.depth_order_col_index(pl.cols_b, pl.db_c, info["n_base"])
+        bmap = plan.array("bmap", e).cpu().numpy()
+        assert np.array_equal(bmap[cols], pl.cols_b[:, 0] | (pl.cols_b[:, 1] << 24)), f"{tag} B' row map"
         kidx = G.padded_k_index(pl.trip)
         assert np.array_equal(A_g[np.ix_(rows, kidx)], ref.Ap), f"{tag} A'"
         assert np.array_equal(B_g[np.ix_(cols, kidx)], ref.Bp.T), f"{tag} B'^T"
