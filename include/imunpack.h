@@ -102,6 +102,18 @@ typedef struct {
   int32_t strat_a, strat_b;
 } imu_params;
 
+/* Statistics of one operand prepared ahead of a call by imu_prepare_operand
+ * (a weight reused across inference calls, or a training tensor that enters
+ * several GEMMs).  stats = NULL: the call computes them itself.
+ * transposed = 1: they were prepared for the transpose of the operand's
+ * logical matrix (W prepared once, used as W in one GEMM and as W^T in
+ * another); the row and column statistics then swap roles. */
+typedef struct {
+  const void* stats;
+  int32_t transposed;
+  int32_t pad_;
+} imu_prepared;
+
 /* Host-side summary of one batch entry's plan, filled by imu_plan_unpack. */
 typedef struct {
   int64_t m, k, n;           /* original sizes M, K, N of this problem */
@@ -263,6 +275,28 @@ imu_status imu_imunpack_matmul_noalloc(const imu_matrix* a, const imu_matrix* b,
                                        hipStream_t stream);
 /* Size in bytes of the static array imu_imunpack_matmul_noalloc works in. */
 size_t imu_noalloc_scratch_bytes(void);
+
+/* Statistics of one operand for later calls: the percentile scale, RTN
+ * codes' out-of-range counts and largest digit counts (as imu_quantize_rtn)
+ * and the Mix residuals of both line directions (what imu_plan_unpack adds for
+ * a Mix operand), into `stats` (imu_stats_bytes(x) bytes, contents replaced).
+ * The same quantization serves every GEMM the matrix enters with the same
+ * beta, p, bits and gamma ("Key results": LLaMA inference with fixed weights;
+ * training, where one tensor enters the forward and a gradient GEMM).
+ * Asynchronous; device-detected errors surface at the call that uses them. */
+imu_status imu_prepare_operand(const imu_matrix* x, const imu_params* p, void* stats, hipStream_t stream);
+
+/* imu_imunpack_matmul with the statistics of A and/or B prepared by
+ * imu_prepare_operand: the call skips those operands' quantization passes
+ * (percentile, counts, residual) and only reads their statistics.  Each
+ * prepared buffer must describe this operand's data (or its transpose, with
+ * transposed = 1), with the same dtype and the same beta, p, bits and gamma;
+ * results equal imu_imunpack_matmul's.  pre_a / pre_b may be NULL.  Calls may
+ * share a prepared buffer, also concurrently. */
+imu_status imu_imunpack_matmul_prepared(const imu_matrix* a, const imu_matrix* b, const imu_params* p,
+                                        const imu_prepared* pre_a, const imu_prepared* pre_b, int32_t* c,
+                                        float* out, void* ws, size_t ws_bytes, size_t* ws_needed,
+                                        imu_plan_info* info, hipStream_t stream);
 
 /* Fixed part of the imu_imunpack_matmul workspace (statistics and plan); the
  * unpacked operands need sum over entries of (m_alloc + n_alloc) * k_pad more. */

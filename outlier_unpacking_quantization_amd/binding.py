@@ -48,6 +48,10 @@ class ImuParams(ctypes.Structure):
                 ("strat_b", ctypes.c_int32)]
 
 
+class ImuPrepared(ctypes.Structure):
+    _fields_ = [("stats", ctypes.c_void_p), ("transposed", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+
+
 class ImuPlanInfo(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int64), ("k", ctypes.c_int64), ("n", ctypes.c_int64),
                 ("m_u", ctypes.c_int64), ("k_u", ctypes.c_int64), ("n_u", ctypes.c_int64),
@@ -116,6 +120,9 @@ def lib() -> ctypes.CDLL:
         "imu_imunpack_matmul_noalloc": (I32, [P(ImuMatrix), P(ImuMatrix), P(ImuParams), V, V, P(S),
                                               P(ImuPlanInfo), V]),
         "imu_noalloc_scratch_bytes": (S, []),
+        "imu_prepare_operand": (I32, [P(ImuMatrix), P(ImuParams), V, V]),
+        "imu_imunpack_matmul_prepared": (I32, [P(ImuMatrix), P(ImuMatrix), P(ImuParams), P(ImuPrepared),
+                                               P(ImuPrepared), V, V, V, S, P(S), P(ImuPlanInfo), V]),
         "imu_init": (I32, [I64]),
         "imu_release": (I32, []),
     }
@@ -130,7 +137,8 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("imu_init", "imu_release", "imu_stats_bytes", "imu_stats_layout", "imu_plan_bytes",
             "imu_plan_layout", "imu_workspace_fixed_bytes", "imu_quantize_rtn", "imu_plan_unpack",
             "imu_unpack", "imu_unpacked_gemm", "imu_imunpack_matmul", "imu_status_string", "imu_last_error",
-            "imu_version", "imu_set_gemm_events", "imu_imunpack_matmul_noalloc", "imu_noalloc_scratch_bytes")
+            "imu_version", "imu_set_gemm_events", "imu_imunpack_matmul_noalloc", "imu_noalloc_scratch_bytes",
+            "imu_prepare_operand", "imu_imunpack_matmul_prepared")
 
 
 def _check(status: int):
@@ -442,6 +450,58 @@ def imunpack_matmul_noalloc(a, b, p: ImuParams, out: Optional[torch.Tensor] = No
                                              _ptr(out) if want_out else None, ctypes.byref(need), info,
                                              ctypes.c_void_p(_stream(stream))))
     return (out if want_out else None), c, [info[i].as_dict() for i in range(ma.batch)]
+
+
+def prepare_operand(x, p: ImuParams, stream=None) -> Stats:
+    """Statistics of one operand for later calls (imu_prepare_operand): scale,
+    counts and the Mix residuals of both line directions."""
+    x = _as_matrix(x)
+    st = Stats(x)
+    _check(lib().imu_prepare_operand(ctypes.byref(x.c()), ctypes.byref(p), _ptr(st.buf),
+                                     ctypes.c_void_p(_stream(stream))))
+    return st
+
+
+def _prepared(pre) -> Optional[ImuPrepared]:
+    """None, a Stats (used as prepared) or a (Stats, transposed) pair."""
+    if pre is None:
+        return None
+    st, tr = pre if isinstance(pre, tuple) else (pre, False)
+    return ImuPrepared(st.buf.data_ptr(), 1 if tr else 0, 0)
+
+
+def imunpack_matmul_prepared(a, b, p: ImuParams, pre_a=None, pre_b=None, out: Optional[torch.Tensor] = None,
+                             c: Optional[torch.Tensor] = None, want_out: bool = True,
+                             ws: Optional[Workspace] = None, stream=None):
+    """imu_imunpack_matmul_prepared: pre_a / pre_b are None, a Stats from
+    prepare_operand, or (Stats, transposed).  Returns (out or None, C, [info])."""
+    a, b = _as_matrix(a), _as_matrix(b)
+    ma, mb = a.c(), b.c()
+    dev = a.stored.device
+    ensure_init(dev, ma.batch)
+    shape = (ma.batch, ma.rows, mb.cols)
+    if c is None:
+        c = torch.empty(shape, dtype=torch.int32, device=dev)
+    if want_out and out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _default_ws.setdefault(str(dev), Workspace(dev))
+    pa, pb = _prepared(pre_a), _prepared(pre_b)
+    info = (ImuPlanInfo * ma.batch)()
+    need = ctypes.c_size_t(0)
+    for _ in range(3):
+        buf = ws.buf
+        st = lib().imu_imunpack_matmul_prepared(ctypes.byref(ma), ctypes.byref(mb), ctypes.byref(p),
+                                                ctypes.byref(pa) if pa else None, ctypes.byref(pb) if pb else None,
+                                                _ptr(c), _ptr(out) if want_out else None,
+                                                _ptr(buf) if buf.numel() else None, buf.numel(), ctypes.byref(need),
+                                                info, ctypes.c_void_p(_stream(stream)))
+        if st == ERR_WORKSPACE:
+            ws.ensure(need.value)
+            continue
+        _check(st)
+        return (out if want_out else None), c, [info[i].as_dict() for i in range(ma.batch)]
+    _check(ERR_WORKSPACE)
 
 
 def version() -> str:

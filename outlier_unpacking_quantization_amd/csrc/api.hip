@@ -165,23 +165,47 @@ imu_status quantize_ops(const Operand* const* ops, uint8_t* const* stats, int32_
   return IMU_OK;
 }
 
-imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
-                       uint8_t* stats_b, uint8_t* plan, uint8_t* host_hdr, int64_t host_tag, hipEvent_t done,
+// Statistics of one operand as the planner reads them: computed in this call
+// (layout of the operand's own shape), or prepared by imu_prepare_operand,
+// possibly for the operand's transpose (then the row and column arrays swap
+// roles: a row of the operand is a column of the matrix they describe).
+struct StatsRef {
+  uint8_t* stats;
+  StatsLayout L;
+  bool prepared;
+};
+
+StatsLayout transposed_layout(int64_t R, int64_t C) {
+  StatsLayout L = stats_layout(C, R);
+  std::swap(L.row_oob, L.col_oob);
+  std::swap(L.row_maxdig, L.col_maxdig);
+  std::swap(L.cr_rowdig, L.rc_coldig);
+  L.R = R;
+  L.C = C;
+  return L;
+}
+
+// Mix residuals of the operands whose statistics were computed in this call,
+// then the planner's launches (the plan headers must be zero: see PlanArgs).
+imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p, const StatsRef& ra,
+                       const StatsRef& rb, uint8_t* plan, uint8_t* host_hdr, int64_t host_tag, hipEvent_t done,
                        hipStream_t s) {
-  const StatsLayout la = stats_layout(oa.R, oa.C), lb = stats_layout(ob.R, ob.C);
   const int batch = (int)oa.m->batch;
   for (int dt : {(int)IMU_BF16, (int)IMU_F32}) {
     QuantJobs J{};
-    if (p->strat_a == IMU_MIX && oa.dtype == dt) {
-      J.op[J.nops].s = stream_args(oa, stats_a, la, p);
+    if (p->strat_a == IMU_MIX && oa.dtype == dt && !ra.prepared) {
+      J.op[J.nops].s = stream_args(oa, ra.stats, ra.L, p);
       J.op[J.nops++].batch = batch;
     }
-    if (p->strat_b == IMU_MIX && ob.dtype == dt) {
-      J.op[J.nops].s = stream_args(ob, stats_b, lb, p);
+    if (p->strat_b == IMU_MIX && ob.dtype == dt && !rb.prepared) {
+      J.op[J.nops].s = stream_args(ob, rb.stats, rb.L, p);
       J.op[J.nops++].batch = batch;
     }
     if (J.nops) IMU_HIP(launch_residual(dt, p->bits, J, s));
   }
+  uint8_t* stats_a = ra.stats;
+  uint8_t* stats_b = rb.stats;
+  const StatsLayout &la = ra.L, &lb = rb.L;
   PlanArgs pa{};
   pa.stats_a = stats_a;
   pa.stats_b = stats_b;
@@ -282,10 +306,10 @@ imu_status wait_headers(DeviceCtx& st, int batch, hipStream_t s) {
 
 // Plan launches with the host copy of the headers (the caller holds st.mu);
 // returns that copy (valid once wait_headers has returned).
-imu_status plan_staged(DeviceCtx& st, const Operand& oa, const Operand& ob, const imu_params* p, uint8_t* stats_a,
-                       uint8_t* stats_b, uint8_t* plan, hipStream_t s, const uint8_t** hdrs) {
+imu_status plan_staged(DeviceCtx& st, const Operand& oa, const Operand& ob, const imu_params* p, const StatsRef& ra,
+                       const StatsRef& rb, uint8_t* plan, hipStream_t s, const uint8_t** hdrs) {
   ++st.tag;
-  IMU_TRY(plan_launch(oa, ob, p, stats_a, stats_b, plan, st.dbuf, st.tag, st.ev, s));
+  IMU_TRY(plan_launch(oa, ob, p, ra, rb, plan, st.dbuf, st.tag, st.ev, s));
   *hdrs = st.buf;
   return IMU_OK;
 }
@@ -339,7 +363,9 @@ imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, 
   IMU_TRY(current_ctx(batch, &st));
   std::lock_guard<std::mutex> lock(st->mu);
   const uint8_t* hdrs = nullptr;
-  IMU_TRY(plan_staged(*st, oa, ob, p, stats_a, stats_b, plan, s, &hdrs));
+  const StatsRef ra{stats_a, stats_layout(oa.R, oa.C), false}, rb{stats_b, stats_layout(ob.R, ob.C), false};
+  IMU_HIP(launch_fill_u32(plan, 0u, plan_layout(oa.R, oa.C, ob.C, batch, p->bits).headers_bytes / 4, s));
+  IMU_TRY(plan_staged(*st, oa, ob, p, ra, rb, plan, s, &hdrs));
   IMU_TRY(wait_headers(*st, batch, s));
   return finish_plan(oa, ob, hdrs, batch, info, nullptr, nullptr);
 }
@@ -509,8 +535,10 @@ int64_t fixed_bytes(const Operand& oa, const Operand& ob, const imu_params* p) {
 }
 
 // The whole path on a caller-provided workspace (see imu_imunpack_matmul).
+// pre_a / pre_b: prepared statistics (imu_imunpack_matmul_prepared) or null.
 imu_status matmul_impl(const Operand& oa, const Operand& ob, const imu_params* p, int32_t* c, float* out,
-                       uint8_t* w, int64_t ws_bytes, size_t* ws_needed, imu_plan_info* info, hipStream_t stream) {
+                       uint8_t* w, int64_t ws_bytes, size_t* ws_needed, imu_plan_info* info, hipStream_t stream,
+                       const imu_prepared* pre_a = nullptr, const imu_prepared* pre_b = nullptr) {
   const int64_t batch = oa.m->batch;
   const int64_t fixed = fixed_bytes(oa, ob, p);
   if (ws_needed) *ws_needed = (size_t)fixed;
@@ -519,15 +547,30 @@ imu_status matmul_impl(const Operand& oa, const Operand& ob, const imu_params* p
                 (long long)ws_bytes, (long long)fixed);
   DeviceCtx* st = nullptr;
   IMU_TRY(current_ctx(batch, &st));
-  uint8_t* stats_a = w;
-  uint8_t* stats_b = stats_a + round_up(stats_layout(oa.R, oa.C).stride * batch, 256);
-  uint8_t* plan = stats_b + round_up(stats_layout(ob.R, ob.C).stride * batch, 256);
-  // statistics of A and B are adjacent: clear both with one launch
-  IMU_HIP(launch_fill_u32(stats_a, 0u, (int64_t)(plan - stats_a) / 4, stream));
-  const Operand* ops[2] = {&oa, &ob};
-  uint8_t* stv[2] = {stats_a, stats_b};
-  int32_t* q[2] = {nullptr, nullptr};
-  IMU_TRY(quantize_ops(ops, stv, q, 2, p, stream, true));
+  uint8_t* ws_a = w;
+  uint8_t* ws_b = ws_a + round_up(stats_layout(oa.R, oa.C).stride * batch, 256);
+  uint8_t* plan = ws_b + round_up(stats_layout(ob.R, ob.C).stride * batch, 256);
+  auto ref = [&](const Operand& o, uint8_t* own, const imu_prepared* pre) {
+    if (pre && pre->stats)
+      return StatsRef{static_cast<uint8_t*>(const_cast<void*>(pre->stats)),
+                      pre->transposed ? transposed_layout(o.R, o.C) : stats_layout(o.R, o.C), true};
+    return StatsRef{own, stats_layout(o.R, o.C), false};
+  };
+  const StatsRef ra = ref(oa, ws_a, pre_a), rb = ref(ob, ws_b, pre_b);
+  uint8_t* const stats_a = ra.stats;
+  uint8_t* const stats_b = rb.stats;
+  // the statistics of A and B and the plan headers are adjacent: one clear
+  IMU_HIP(launch_fill_u32(ws_a, 0u, (int64_t)(plan - ws_a + plan_layout(oa.R, oa.C, ob.C, batch, p->bits).headers_bytes) / 4,
+                          stream));
+  {
+    const Operand* ops[2];
+    uint8_t* stv[2];
+    int32_t* q[2] = {nullptr, nullptr};
+    int n = 0;
+    if (!ra.prepared) ops[n] = &oa, stv[n++] = stats_a;
+    if (!rb.prepared) ops[n] = &ob, stv[n++] = stats_b;
+    if (n) IMU_TRY(quantize_ops(ops, stv, q, n, p, stream, true));
+  }
   // The unpack kernels take their sizes and placement from the plan on the
   // device, so they are queued right behind the plan; the host waits only for
   // the plan headers (staged to pinned memory) while they run, then checks the
@@ -535,7 +578,7 @@ imu_status matmul_impl(const Operand& oa, const Operand& ob, const imu_params* p
   // is too small the unpack kernels write nothing.
   std::lock_guard<std::mutex> lock(st->mu);
   const uint8_t* hdrs = nullptr;
-  IMU_TRY(plan_staged(*st, oa, ob, p, stats_a, stats_b, plan, stream, &hdrs));
+  IMU_TRY(plan_staged(*st, oa, ob, p, ra, rb, plan, stream, &hdrs));
   int8_t* region = reinterpret_cast<int8_t*>(w + fixed);
   const int64_t cap = ws_bytes - fixed;
   if (oa.dtype == ob.dtype) {  // both operands in one launch
@@ -748,6 +791,39 @@ imu_status imu_imunpack_matmul(const imu_matrix* a, const imu_matrix* b, const i
   if (!c) return fail(IMU_ERR_INVALID_ARG, "c is NULL");
   if (ws_bytes > (size_t)INT64_MAX) return fail(IMU_ERR_INVALID_ARG, "ws_bytes above 2^63");
   return matmul_impl(oa, ob, p, c, out, static_cast<uint8_t*>(ws), (int64_t)ws_bytes, ws_needed, info, stream);
+}
+
+imu_status imu_prepare_operand(const imu_matrix* x, const imu_params* p, void* stats, hipStream_t stream) {
+  Operand op;
+  IMU_TRY(check_matrix(x, "x", &op));
+  IMU_TRY(check_params(p));
+  if (!stats) return fail(IMU_ERR_INVALID_ARG, "stats is NULL");
+  uint8_t* st = static_cast<uint8_t*>(stats);
+  const Operand* ops[1] = {&op};
+  uint8_t* stv[1] = {st};
+  int32_t* q[1] = {nullptr};
+  IMU_TRY(quantize_ops(ops, stv, q, 1, p, stream, false));
+  QuantJobs J{};
+  J.op[0].s = stream_args(op, st, stats_layout(op.R, op.C), p);
+  J.op[0].batch = (int)x->batch;
+  J.nops = 1;
+  IMU_HIP(launch_residual(op.dtype, p->bits, J, stream));
+  return IMU_OK;
+}
+
+imu_status imu_imunpack_matmul_prepared(const imu_matrix* a, const imu_matrix* b, const imu_params* p,
+                                        const imu_prepared* pre_a, const imu_prepared* pre_b, int32_t* c,
+                                        float* out, void* ws, size_t ws_bytes, size_t* ws_needed,
+                                        imu_plan_info* info, hipStream_t stream) {
+  Operand oa, ob;
+  IMU_TRY(check_pair(a, b, p, &oa, &ob));
+  if (!c) return fail(IMU_ERR_INVALID_ARG, "c is NULL");
+  if (ws_bytes > (size_t)INT64_MAX) return fail(IMU_ERR_INVALID_ARG, "ws_bytes above 2^63");
+  for (const imu_prepared* pr : {pre_a, pre_b})
+    if (pr && pr->transposed != 0 && pr->transposed != 1)
+      return fail(IMU_ERR_INVALID_ARG, "imu_prepared.transposed must be 0 or 1");
+  return matmul_impl(oa, ob, p, c, out, static_cast<uint8_t*>(ws), (int64_t)ws_bytes, ws_needed, info, stream,
+                     pre_a, pre_b);
 }
 
 imu_status imu_imunpack_matmul_noalloc(const imu_matrix* a, const imu_matrix* b, const imu_params* p, int32_t* c,

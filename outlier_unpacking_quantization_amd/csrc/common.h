@@ -82,7 +82,7 @@ struct PlanHeader {
   int64_t pair[16][3];
   int64_t seg_off[kMaxSeg + 1];
   int32_t seg_len[kMaxSeg];
-  int64_t reserved[8];
+  int64_t reserved[8];  // [0]: tag closing the host copy; [1]: the planner's arrival counter
   // B's columns in depth order (descending depth, then column index): slot j
   // of level w holds the column at position j of that order, for
   // j < lvcnt_b[w] (the columns deeper than w; lvcnt_b[0] = N), as B'^T row

@@ -19,7 +19,7 @@ hipError_t launch_round_count(int dtype, int bits, QuantJobs J, int32_t* q0, int
 hipError_t launch_residual(int dtype, int bits, QuantJobs J, hipStream_t s);
 
 // plan.hip
-struct PlanArgs {
+struct PlanArgs {  // the plan headers must be zero when the planner starts (arrival counter)
   const uint8_t* stats_a;
   const uint8_t* stats_b;
   int64_t stats_stride_a, stats_stride_b;

@@ -29,8 +29,8 @@
 //     first row.
 // Records exchanged inside one launch are written with device-scope atomic
 // stores (through the XCD-local L2) and read after a device-scope acquire; the
-// counter that elects the last workgroup is the statistics header's, which is
-// zero between passes.
+// counter that elects the last workgroup is a word of the plan header, which
+// the caller clears before the first launch.
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -204,8 +204,11 @@ __device__ inline Entry entry_of(const PlanArgs& a, int b) {
   return x;
 }
 
+// Arrival counter of the planner's first launch: a word of the entry's own
+// plan header (the statistics may be shared, read-only, between calls).  The
+// caller clears the headers before the planner runs.
 __device__ inline uint32_t* arrive_counter(const PlanArgs& a, int b) {
-  return &reinterpret_cast<StatsHeader*>(const_cast<uint8_t*>(a.stats_a) + b * a.stats_stride_a)->arrive;
+  return reinterpret_cast<uint32_t*>(&reinterpret_cast<PlanHeader*>(a.plan + b * kPlanHeaderStride)->reserved[1]);
 }
 
 // Shared memory of a planner workgroup, all phases.
