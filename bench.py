@@ -46,7 +46,14 @@ PAGE_RATIOS = {"mix": 1.06, "row/row": 2.02, "row/col": 5.36, "col/row": 1.64, "
 # copy (bench.py --copy-calibration).  The readings belong to one version of
 # the GEMM source: when gemm.hip no longer hashes to `source_sha256` the
 # traffic is reported as null.
-GEMM_TRAFFIC = {}
+GEMM_TRAFFIC = {
+    "mlp_up": {"source_sha256": "3752f4af7ba000e27b52101e2888cd22142d51f65326a3b55044c0810b40d844",
+               "fetch_kib": 2074048.3, "write_kib": 385111.6, "fetch_factor": 1.9998, "write_factor": 1.0000,
+               "bytes_per_launch": 4641580432},
+    "llama_linear": {"source_sha256": "3752f4af7ba000e27b52101e2888cd22142d51f65326a3b55044c0810b40d844",
+                     "fetch_kib": 151235.7, "write_kib": 65536.0, "fetch_factor": 1.9998, "write_factor": 1.0000,
+                     "bytes_per_launch": 376808605},
+}
 
 
 def parse():
