@@ -130,6 +130,17 @@ def rtn(x32: np.ndarray, r: np.float32) -> np.ndarray:
     return np.rint(y).astype(np.int64)
 
 
+def rtn_clipped(x32: np.ndarray, r: np.float32, beta: int) -> np.ndarray:
+    """The clipping quantizer of the page's ablation rows ("Measured effects":
+    clipping at the 99.5-percentile costs accuracy; p = 100% with beta = 255
+    restricts every value to the range): the RTN code of fl32(x * r), rounded
+    half to even, then clamped to [-beta, beta].  A product that overflows
+    binary32 is clamped like any other code beyond beta."""
+    with np.errstate(over="ignore"):
+        y = np.asarray(x32, dtype=np.float32) * np.float32(r)
+    return np.clip(np.rint(y), -beta, beta).astype(np.int64)
+
+
 # ----------------------------------------------------------------------------
 # O4-O5: digits and outlier statistics   (page: "Approach")
 # ----------------------------------------------------------------------------
@@ -432,9 +443,13 @@ class Quantized:
     stats: LineStats
 
 
-def quantize(x32: np.ndarray, beta: int, p_num: int, p_den: int, bits: int) -> Quantized:
+def quantize(x32: np.ndarray, beta: int, p_num: int, p_den: int, bits: int, clip: bool = False) -> Quantized:
+    """O1-O5 for one matrix; `clip` selects the clipping quantizer (rtn_clipped)."""
     sc = percentile_scale(x32, beta, p_num, p_den)
-    q = rtn(x32, sc.r) if sc.alpha > 0 else np.zeros(x32.shape, np.int64)
+    if sc.alpha == 0:
+        q = np.zeros(x32.shape, np.int64)
+    else:
+        q = rtn_clipped(x32, sc.r, beta) if clip else rtn(x32, sc.r)
     n = digit_count(q, bits)
     return Quantized(sc, q, n, line_stats(n))
 
@@ -483,7 +498,7 @@ class Result:
 
 def imunpack_matmul(a32: np.ndarray, b32: np.ndarray, beta: int, bits: int, p_num: int = 95,
                     p_den: int = 100, strat_a: str = "mix", strat_b: str = "mix",
-                    gamma: int = 2, unpacked: bool = True) -> Result:
+                    gamma: int = 2, unpacked: bool = True, clip: bool = False) -> Result:
     """The whole path for one (non-batched) problem C = A @ B.
 
     With ``unpacked`` the low bit-width route (O9-O12) is run as well and its
@@ -494,8 +509,8 @@ def imunpack_matmul(a32: np.ndarray, b32: np.ndarray, beta: int, bits: int, p_nu
         raise OracleError(ERR_INVALID_ARG, "bits must be in [2, 8]")
     if beta < 1 or not (0 < p_num <= p_den):
         raise OracleError(ERR_INVALID_ARG, "beta >= 1 and 0 < p <= 1 required")
-    qa = quantize(a32, beta, p_num, p_den, bits)
-    qb = quantize(b32, beta, p_num, p_den, bits)
+    qa = quantize(a32, beta, p_num, p_den, bits, clip)
+    qb = quantize(b32, beta, p_num, p_den, bits, clip)
     pl = plan(qa, qb, strat_a, strat_b, gamma)
     M, K = qa.q.shape
     N = qb.q.shape[1]

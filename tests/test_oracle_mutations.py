@@ -29,6 +29,8 @@ PINS = [
     P.test_int32_wraps_modulo_2_32,
     P.test_dequant_is_three_binary32_roundings,
     P.test_hand_worked_examples,
+    P.test_clipping_quantizer_is_rounding_then_clamp,
+    P.test_clipped_path_is_in_range_when_beta_fits,
 ]
 PARAMS = {
     "test_percentile_matches_sorted_bruteforce": {"p": (95, 100)},
@@ -145,7 +147,14 @@ def _exact_matmul_drop_last_column(a, b):
     return c
 
 
+def _clip_dropped(x32, r, beta):
+    with np.errstate(over="ignore"):
+        y = np.asarray(x32, np.float32) * np.float32(r)
+    return np.rint(np.nan_to_num(y, posinf=2.0 ** 31 - 1, neginf=-(2.0 ** 31 - 1))).astype(np.int64)
+
+
 MUTATIONS = {
+    "clip_dropped": ("rtn_clipped", _clip_dropped),
     "widen_shift_15": ("widen", _widen_shift_15),
     "widen_reads_binary16": ("widen", _widen_through_f16),
     "rtn_half_up": ("rtn", _rtn_half_up),

@@ -553,3 +553,64 @@ def test_invalid_parameters():
         with pytest.raises(O.OracleError) as e:
             solve(a, a, **kw)
         assert e.value.code == O.ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# quantizer variants of the page's ablation rows ("Measured effects":
+# p = 100% with beta = 255; clipping at the 99.5-percentile)
+# ---------------------------------------------------------------------------
+
+def _rne(x: Fraction) -> int:
+    """Round an exact rational half to even."""
+    n = math.floor(x)
+    rem = x - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n
+
+
+def test_clipping_quantizer_is_rounding_then_clamp():
+    rng = np.random.default_rng(71)
+    for trial in range(40):
+        x = (rng.standard_normal((5, 7)) * 4).astype(np.float32)
+        x[rng.random(x.shape) < 0.1] *= 300
+        if trial % 4 == 0:  # exact halves
+            x = (np.round(x * 2) / 2).astype(np.float32)
+        beta = int(rng.choice([1, 3, 7, 15, 31, 255]))
+        r = np.float32(rng.choice([1.0, 0.5, 2.0, rng.uniform(0.1, 9.0)]))
+        q = O.rtn_clipped(x, r, beta)
+        for v, got in zip(x.ravel(), q.ravel()):
+            y = Fraction(float(f32_round(Fraction(float(v)) * Fraction(float(r)))))
+            assert got == max(-beta, min(beta, _rne(y))), (v, r, beta)
+    # a product that overflows binary32 is clamped too
+    big = np.array([[3e38, -3e38, 1.0]], np.float32)
+    assert O.rtn_clipped(big, np.float32(10.0), 15).tolist() == [[15, -15, 10]]
+
+
+def test_clipped_path_is_in_range_when_beta_fits():
+    """beta = 15 at b = 5 with clipping: every code is in range, so no line is
+    unpacked (ratio 1) and C is the product of the clipped codes."""
+    rng = np.random.default_rng(72)
+    a = rng.standard_normal((40, 50)).astype(np.float32)
+    b = rng.standard_normal((50, 30)).astype(np.float32)
+    a.flat[rng.choice(a.size, 25, replace=False)] *= 40.0  # heavy hitters above the 99.5-percentile
+    b.flat[rng.choice(b.size, 20, replace=False)] *= -30.0
+    res = O.imunpack_matmul(a, b, 15, 5, 995, 1000, clip=True)
+    assert res.unpack_ratio == 1.0
+    assert np.abs(res.qa.q).max() == 15 and np.abs(res.qb.q).max() == 15
+    assert res.C.tolist() == brute_matmul(res.qa.q, res.qb.q)
+    plain = O.imunpack_matmul(a, b, 15, 5, 995, 1000)
+    assert plain.unpack_ratio > 1.0  # the same input unclipped has heavy hitters
+
+
+def test_p100_beta255_maps_the_largest_magnitude_to_beta():
+    rng = np.random.default_rng(73)
+    a = (rng.standard_normal((7, 10)) * 2).astype(np.float32)
+    b = rng.standard_normal((10, 6)).astype(np.float32)
+    for bits in (5, 8):
+        res = O.imunpack_matmul(a, b, 255, bits, 100, 100)
+        assert float(res.qa.scale.alpha) == float(np.abs(a).max())
+        assert np.abs(res.qa.q).max() == 255 and np.abs(res.qb.q).max() == 255
+        assert res.C.tolist() == brute_matmul(res.qa.q, res.qb.q)
+        S = 2 ** (bits - 1)
+        assert res.qa.n.max() == (2 if 255 >= S else 1)
