@@ -432,6 +432,24 @@ def main():
         torch.cuda.synchronize()
         pair_ms[key] = round((time.perf_counter() - t1) / max(1, args.pair_steps) * 1e3, 4)
 
+    # quantizer variants of the page's ablation rows on the same operands: p =
+    # 100% with beta = 255, and clipping at the 99.5-percentile
+    variants = {}
+    for key, vb, vp, vclip in (("p100_beta255", 255, (100, 100), False), ("clip_p995", pr.beta, (995, 1000), True)):
+        pv = B.params(beta=vb, bits=pr.bits, p=vp, strat_a=pr.strat_a, strat_b=pr.strat_b, gamma=pr.gamma,
+                      clip=vclip)
+        for _ in range(2):
+            _, _, vinfo = step(pv)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(max(1, args.pair_steps)):
+            step(pv)
+        torch.cuda.synchronize()
+        tv = (time.perf_counter() - t1) / max(1, args.pair_steps)
+        variants[key] = {"beta": vb, "p": f"{vp[0]}/{vp[1]}", "clip": vclip,
+                         "unpack_ratio": round(vinfo[0]["unpack_ratio"], 4),
+                         "ms_per_step": round(tv * 1e3, 4), "tops": round(2.0 * M * N * K * nb / tv / 1e12, 3)}
+
     # dominant kernel: the unpacked int8 GEMM of the warm steps (events above)
     gemm_ops = sum(2.0 * f["m_u"] * f["k_u"] * f["n_u"] for f in infos)  # every batch entry
     gemm_tops = gemm_ops / t_gemm / 1e12
@@ -464,6 +482,7 @@ def main():
         "unpack_ratio": round(sum(f["m_u"] * f["k_u"] * f["n_u"] for f in infos) / (nb * base_mnk), 4),
         "unpack_ratios": ratios,
         "pair_ms_per_step": pair_ms,
+        "quantizer_variants": variants,
         "page_unpack_ratios": {"values": PAGE_RATIOS,
                                "note": "IM-Unpack page, LLaMA-7B linear layers, beta=15 b=5: context only"},
         "plan": {"choice": list(info["choice"]), "m_u": info["m_u"], "k_u": info["k_u"], "n_u": info["n_u"],

@@ -100,6 +100,10 @@ typedef struct {
 typedef struct {
   int32_t beta, p_num, p_den, bits, gamma;
   int32_t strat_a, strat_b;
+  int32_t clip; /* 0: RTN codes are never clipped (IM-Unpack); 1: the clipping
+                   quantizer of the page's ablation rows ("Measured effects":
+                   clipping at the 99.5-percentile): q = clamp(rne(fl32(x r)),
+                   -beta, beta), so no code exceeds beta and none is an error */
 } imu_params;
 
 /* Statistics of one operand prepared ahead of a call by imu_prepare_operand

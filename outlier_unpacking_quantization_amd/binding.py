@@ -45,7 +45,7 @@ class ImuMatrix(ctypes.Structure):
 class ImuParams(ctypes.Structure):
     _fields_ = [("beta", ctypes.c_int32), ("p_num", ctypes.c_int32), ("p_den", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("gamma", ctypes.c_int32), ("strat_a", ctypes.c_int32),
-                ("strat_b", ctypes.c_int32)]
+                ("strat_b", ctypes.c_int32), ("clip", ctypes.c_int32)]
 
 
 class ImuPrepared(ctypes.Structure):
@@ -237,8 +237,8 @@ class Matrix:
 
 
 def params(beta: int = 15, bits: int = 5, p: Tuple[int, int] = (95, 100), strat_a: str = "mix",
-           strat_b: str = "mix", gamma: int = 2) -> ImuParams:
-    return ImuParams(beta, p[0], p[1], bits, gamma, STRATEGY[strat_a], STRATEGY[strat_b])
+           strat_b: str = "mix", gamma: int = 2, clip: bool = False) -> ImuParams:
+    return ImuParams(beta, p[0], p[1], bits, gamma, STRATEGY[strat_a], STRATEGY[strat_b], 1 if clip else 0)
 
 
 def _as_matrix(x) -> Matrix:

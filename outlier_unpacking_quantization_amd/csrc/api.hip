@@ -92,6 +92,7 @@ imu_status check_params(const imu_params* p) {
   if (p->p_den < 1 || p->p_den > 1000000) return fail(IMU_ERR_INVALID_ARG, "p_den must be in [1, 1e6]");
   if (p->p_num < 1 || p->p_num > p->p_den) return fail(IMU_ERR_INVALID_ARG, "p = p_num/p_den must be in (0, 1]");
   if (p->gamma < 0 || p->gamma > 1000000) return fail(IMU_ERR_INVALID_ARG, "gamma must be in [0, 1e6]");
+  if (p->clip != 0 && p->clip != 1) return fail(IMU_ERR_INVALID_ARG, "clip must be 0 or 1");
   for (int s : {p->strat_a, p->strat_b})
     if (s != IMU_ROW && s != IMU_COL && s != IMU_MIX)
       return fail(IMU_ERR_INVALID_ARG, "strategy must be IMU_ROW, IMU_COL or IMU_MIX");
@@ -133,6 +134,7 @@ StreamArgs stream_args(const Operand& op, uint8_t* stats, const StatsLayout& L, 
   s.p_num = p->p_num;
   s.p_den = p->p_den;
   s.gamma = p->gamma;
+  s.clip = p->clip;
   return s;
 }
 
@@ -403,6 +405,8 @@ UnpackArgs unpack_args(const Operand& op, int operand, const imu_params* p, cons
   u.out = x_u;
   u.after_a = after_a ? 1 : 0;
   u.cap = cap;
+  u.beta = p->beta;
+  u.clip = p->clip;
   return u;
 }
 

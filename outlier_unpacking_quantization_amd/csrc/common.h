@@ -227,6 +227,15 @@ __device__ inline int digit_count(uint32_t m) {
   return bl == 0 ? 1 : 1 + (bl - 1) / (BITS - 1);
 }
 
+// Digit count of the largest code of a line whose largest |x r| is f (f >= 0):
+// rne(f), clamped to beta when clipping; without clipping f >= 2^31 is a
+// range error reported elsewhere (1 is returned).
+template <int BITS>
+__device__ inline int line_digits(float f, int clip, int beta) {
+  if (clip) return digit_count<BITS>(f >= (float)beta ? (uint32_t)beta : (uint32_t)__builtin_rintf(f));
+  return f < 2147483648.0f ? digit_count<BITS>((uint32_t)__builtin_rintf(f)) : 1;
+}
+
 // RTN code of x: one binary32 product, round half to even.  Sets *bad when the
 // code does not fit int32 (|x r| >= 2^31, including Inf/NaN products).
 __device__ inline int32_t rtn_code(float x, float r, bool* bad) {
@@ -299,6 +308,7 @@ struct StreamArgs {       // one operand traversed in stored orientation
   int64_t srow_oob, scol_oob, srow_maxdig, scol_maxdig, srow_res, scol_res, hist;
   int transposed;  // logical = stored^T
   int beta, p_num, p_den, gamma;
+  int clip;        // codes clamped to [-beta, beta] (clipping quantizer)
 };
 
 // Work split of the streaming kernels: operand o owns workgroups

@@ -46,6 +46,7 @@ struct UnpackArgs {
   PlanLayout pl;
   int8_t* out;                  // start of the unpacked buffer (all batch entries)
   int after_a;                  // 1: B' entries follow all A' entries of the buffer
+  int beta, clip;               // clipping quantizer: codes clamped to [-beta, beta]
   int64_t cap;                  // bytes available at out; entries that would not fit are skipped
 };
 // Operands of one dtype share a launch: launch_unpack takes one or two

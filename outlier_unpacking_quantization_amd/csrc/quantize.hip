@@ -95,11 +95,6 @@ __device__ __forceinline__ void bits8(typename RawOf<DT>::V u, uint32_t (&w)[8])
   }
 }
 
-// Digit count of rne(a) for a = max |x r| >= 0 (a finite and below 2^31).
-template <int BITS>
-__device__ inline int digits_of_max(float a) {
-  return digit_count<BITS>((uint32_t)__builtin_rintf(a));
-}
 
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
   int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -599,7 +594,9 @@ __global__ __launch_bounds__(kCountThreads) void round_count_kernel(QuantJobs J,
   }
   __syncthreads();
   const float r = hd->r;
-  const uint32_t kth = key_threshold<DT>(r, kThr);
+  // clipping at beta < 2^(bits-1) leaves every code in range: no key reaches
+  const bool never_oob = a.clip && a.beta < (1 << (BITS - 1));
+  const uint32_t kth = never_oob ? (1u << KO::NB) : key_threshold<DT>(r, kThr);
   const uint32_t cadd = (0x8000u - kth) * 0x10001u;  // bf16: a half of k + cadd reaches 0x8000 iff k >= kth
   const int64_t R = a.srows, C = a.scols;
   int32_t* qb = nullptr;  // codes of this operand, if they were asked for
@@ -650,7 +647,13 @@ __global__ __launch_bounds__(kCountThreads) void round_count_kernel(QuantJobs J,
     for (int j = 0; j < 8; ++j) {
       if (j >= nin) continue;
       const float y = __uint_as_float(w[j]) * r;
-      const int32_t q = __builtin_fabsf(y) < 2147483648.0f ? (int32_t)__builtin_rintf(y) : 0;
+      int32_t q;
+      if (a.clip) {  // rne(min(|y|, beta)) = min(rne(|y|), beta); rne is odd-symmetric
+        const int32_t m = (int32_t)__builtin_rintf(__builtin_fminf(__builtin_fabsf(y), (float)a.beta));
+        q = y < 0.f ? -m : m;
+      } else {
+        q = __builtin_fabsf(y) < 2147483648.0f ? (int32_t)__builtin_rintf(y) : 0;
+      }
       const int64_t c = c0 + j;
       if (!a.transposed) qb[sr * C + c] = q;
       else qb[c * R + sr] = q;
@@ -678,7 +681,7 @@ __global__ __launch_bounds__(kCountThreads) void round_count_kernel(QuantJobs J,
       const uint32_t c_ = IMU_PICK(cnt_, lane);                                                         \
       const float f_ = KO::value(IMU_PICK(key_, lane)) * r;                                             \
       if (c_) atomicAdd(&srow_oob[(sb_) + lane], (int)c_);                                         \
-      atomicMax(&srow_max[(sb_) + lane], f_ < 2147483648.0f ? digits_of_max<BITS>(f_) : 1);       \
+      atomicMax(&srow_max[(sb_) + lane], line_digits<BITS>(f_, a.clip, a.beta));       \
     }                                                                                              \
   }
   // two groups alternate: one group's loads fly while the other is reduced
@@ -717,12 +720,12 @@ __global__ __launch_bounds__(kCountThreads) void round_count_kernel(QuantJobs J,
     if (c < a.scols && m) {
       const float f = KO::value(m - 1u) * r;
       if (lcnt[i]) atomicAdd(&scol_oob[c], lcnt[i]);
-      atomicMax(&scol_max[c], f < 2147483648.0f ? digits_of_max<BITS>(f) : 1);
+      atomicMax(&scol_max[c], line_digits<BITS>(f, a.clip, a.beta));
     }
   }
   if (threadIdx.x == 0) {
     if (ltot) atomicAdd(&hd->total, ltot);
-    if (KO::value(lamax) * r >= 2147483648.0f) atomicOr(&hd->status, kStatusRange);
+    if (!a.clip && KO::value(lamax) * r >= 2147483648.0f) atomicOr(&hd->status, kStatusRange);
   }
 }
 
@@ -829,7 +832,7 @@ __global__ __launch_bounds__(kResidualThreads) void residual_kernel(QuantJobs J)
       const Row4 key_ = wave_max_keys4<DT>(rm_);                                                   \
       if (lane < kRowsInFlight && (sb_) + lane < r1) {                                             \
         const float f_ = KO::value(IMU_PICK(key_, lane)) * r;                                           \
-        atomicMax(&srow_res[(sb_) + lane], f_ < 2147483648.0f ? digits_of_max<BITS>(f_) : 1);      \
+        atomicMax(&srow_res[(sb_) + lane], line_digits<BITS>(f_, a.clip, a.beta));      \
       }                                                                                            \
     }                                                                                              \
   }
@@ -859,7 +862,7 @@ __global__ __launch_bounds__(kResidualThreads) void residual_kernel(QuantJobs J)
     const uint32_t m = lmax[i];
     if (c < a.scols && m) {
       const float f = KO::value(m - 1u) * r;
-      atomicMax(&scol_res[c], f < 2147483648.0f ? digits_of_max<BITS>(f) : 1);
+      atomicMax(&scol_res[c], line_digits<BITS>(f, a.clip, a.beta));
     }
   }
 }

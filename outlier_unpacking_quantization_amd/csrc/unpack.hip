@@ -78,8 +78,14 @@ __device__ inline void load8_vec(const typename Elem<DT>::T* p, float v[8]) {
 
 __device__ inline int slot(int kk) { return kk + (kk >> 5); }
 
-// Sign-magnitude word of the RTN code of x (|q| < 2^31, so |q| << 1 fits).
-__device__ inline uint32_t code_word(float x, float r) {
+// Sign-magnitude word of the RTN code of x (|q| < 2^31, so |q| << 1 fits);
+// with clipping the magnitude is min(rne(|x r|), beta).
+__device__ inline uint32_t code_word(float x, float r, int clip, int beta) {
+  if (clip) {
+    const float y = x * r;
+    const uint32_t m = (uint32_t)__builtin_rintf(__builtin_fminf(__builtin_fabsf(y), (float)beta));
+    return (m << 1) | (uint32_t)(y < 0.f && m != 0);
+  }
   bool bad = false;
   const int32_t q = rtn_code(x, r, &bad);
   const uint32_t m = q < 0 ? 0u - (uint32_t)q : (uint32_t)q;
@@ -89,14 +95,15 @@ __device__ inline uint32_t code_word(float x, float r) {
 // The four low digits of the RTN code of x as two's-complement bytes (digit t
 // in byte t), for codes with at most four digits (|q| < 2^(4 (BITS-1))).
 template <int BITS>
-__device__ inline uint32_t digit_word(float x, float r) {
-  const float y = x * r;  // the RTN product; q = rne(y)
+__device__ inline uint32_t digit_word(float x, float r, int clip, int beta) {
+  const float y = x * r;  // the RTN product; q = rne(y) (clamped to beta when clipping)
+  const float ya = clip ? __builtin_fminf(__builtin_fabsf(y), (float)beta) : __builtin_fabsf(y);
   uint32_t m;             // |q|
   if constexpr (4 * (BITS - 1) <= 22) {
     // |y| < 2^22: adding 1.5 * 2^23 leaves rne(|y|) in the low mantissa bits
-    m = __float_as_uint(__builtin_fabsf(y) + 12582912.0f) - 0x4B400000u;
+    m = __float_as_uint(ya + 12582912.0f) - 0x4B400000u;
   } else {
-    m = (uint32_t)__builtin_rintf(__builtin_fabsf(y));
+    m = (uint32_t)__builtin_rintf(ya);
   }
   uint32_t w;
   if constexpr (BITS == 5) {  // nibbles -> bytes
@@ -215,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
   // digits per byte.  (Inner-contiguous shape only: the 64-line shape keeps
   // one form, which holds its per-thread table entries in registers.)
   const float fmax = __uint_as_float(sth->maxkey) * r;
-  const bool fast = !OC && fmax < 2147483648.0f && digit_count<BITS>((uint32_t)__builtin_rintf(fmax)) <= 4;
+  const bool fast = !OC && (a.clip || fmax < 2147483648.0f) && line_digits<BITS>(fmax, a.clip, a.beta) <= 4;
   const PlanLayout& P = a.pl;
   const uint8_t* pe = a.plan + P.headers_bytes + b * P.entry_stride;
   const PlanHeader* ph = reinterpret_cast<const PlanHeader*>(a.plan + b * kPlanHeaderStride);
@@ -315,8 +322,9 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
         }
       }
     };
-    if (fast) stage([&](float x) { return digit_word<BITS>(x, r); });
-    else stage([&](float x) { return code_word(x, r); });
+    const int clip = a.clip, beta = a.beta;
+    if (fast) stage([&](float x) { return digit_word<BITS>(x, r, clip, beta); });
+    else stage([&](float x) { return code_word(x, r, clip, beta); });
     // this window's K' positions: per segment the range [P0, P1), as groups of
     // 4 positions flattened over the segments (s_pre: first flat group of each
     // segment), so that all segments' groups are spread over all threads

@@ -75,6 +75,7 @@ class Problem:
     strat_b: str = "mix"
     gamma: int = 2
     extra: dict = field(default_factory=dict)
+    clip: bool = False  # the clipping quantizer of the ablation rows
 
     @property
     def mnk(self):
@@ -82,7 +83,7 @@ class Problem:
 
     def with_strategies(self, sa: str, sb: str) -> "Problem":
         return Problem(f"{self.name}[{sa}/{sb}]", self.a, self.b, self.beta, self.bits,
-                       self.p_num, self.p_den, sa, sb, self.gamma, dict(self.extra))
+                       self.p_num, self.p_den, sa, sb, self.gamma, dict(self.extra), self.clip)
 
 
 # ----------------------------------------------------------------------------
@@ -250,7 +251,7 @@ def config(idx: int, **shape) -> List[Problem]:
 def random_problem(seed: int, m: int, k: int, n: int, *, dtype: str = "bf16",
                    layout_a: str = "normal", layout_b: str = "normal", batch: int = 1,
                    beta: int = 15, bits: int = 5, strat_a: str = "mix", strat_b: str = "mix",
-                   kind: str = "linear") -> Problem:
+                   kind: str = "linear", p=(95, 100), clip: bool = False) -> Problem:
     """A small problem of any shape with one of the recipe value models.
 
     kind "linear": activations x weights (config-1 models); "grad": Student-t
@@ -284,5 +285,5 @@ def random_problem(seed: int, m: int, k: int, n: int, *, dtype: str = "bf16",
             raise ValueError(kind)
     a = _store("A", logical_to_stored(av, layout_a), dtype, layout_a)
     b = _store("B", logical_to_stored(bv, layout_b), dtype, layout_b)
-    return Problem(f"rand{seed}_{m}x{k}x{n}", a, b, beta=beta, bits=bits,
-                   strat_a=strat_a, strat_b=strat_b)
+    return Problem(f"rand{seed}_{m}x{k}x{n}", a, b, beta=beta, bits=bits, p_num=p[0], p_den=p[1],
+                   strat_a=strat_a, strat_b=strat_b, clip=clip)

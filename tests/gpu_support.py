@@ -34,7 +34,7 @@ def logical_f32(op: W.Operand, b: int) -> np.ndarray:
 
 def params_of(pr: W.Problem) -> B.ImuParams:
     return B.params(beta=pr.beta, bits=pr.bits, p=(pr.p_num, pr.p_den), strat_a=pr.strat_a,
-                    strat_b=pr.strat_b, gamma=pr.gamma)
+                    strat_b=pr.strat_b, gamma=pr.gamma, clip=pr.clip)
 
 
 def oracle_entries(pr: W.Problem, unpacked: bool = True):
@@ -42,7 +42,7 @@ def oracle_entries(pr: W.Problem, unpacked: bool = True):
     for b in range(pr.a.batch):
         out.append(O.imunpack_matmul(logical_f32(pr.a, b), logical_f32(pr.b, b), pr.beta, pr.bits,
                                      pr.p_num, pr.p_den, pr.strat_a, pr.strat_b, pr.gamma,
-                                     unpacked=unpacked))
+                                     unpacked=unpacked, clip=pr.clip))
     return out
 
 

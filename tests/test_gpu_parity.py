@@ -44,6 +44,13 @@ SMALL = [
          layout_b="transposed"),
     dict(seed=11, m=129, k=200, n=131, kind="linear", bits=6, beta=31, dtype="f32"),
     dict(seed=12, m=70, k=500, n=90, kind="grad", bits=8, beta=255),
+    # quantizer variants of the page's ablation rows: clipping at the
+    # 99.5-percentile (beta = 15 at b = 5 leaves every code in range; beta = 7
+    # at b = 3 still unpacks the clipped codes) and p = 100% with beta = 255
+    dict(seed=16, m=200, k=300, n=150, kind="linear", p=(995, 1000), clip=True, layout_b="transposed"),
+    dict(seed=17, m=150, k=260, n=140, kind="gauss", beta=7, bits=3, p=(995, 1000), clip=True, dtype="f32"),
+    dict(seed=18, m=180, k=260, n=140, kind="linear", beta=255, bits=5, p=(100, 100)),
+    dict(seed=19, m=140, k=200, n=130, kind="grad", beta=255, bits=8, p=(100, 100), layout_a="transposed"),
 ]
 
 
