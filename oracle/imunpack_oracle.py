@@ -48,8 +48,8 @@ import numpy as np
 # status codes, same meaning as the C ABI's (values are part of the contract)
 OK, ERR_INVALID_ARG, ERR_NONFINITE, ERR_RANGE = 0, 1, 2, 3
 
-CANDIDATE_ORDER = ("row", "col", "cr", "rc")  # tie order of the joint choice (R-7)
-ALLOWED = {"row": ("row",), "col": ("col",), "mix": CANDIDATE_ORDER}
+CANDIDATE_ORDER = ("row", "col", "cr", "rc", "greedy")  # tie order of the joint choice (R-7)
+ALLOWED = {"row": ("row",), "col": ("col",), "mix": ("row", "col", "cr", "rc"), "greedy": ("greedy",)}
 
 
 class OracleError(Exception):
@@ -207,6 +207,7 @@ def candidates(n: np.ndarray, st: LineStats, strategy: str, gamma: int = 2
          digit count; every row then takes the largest digit count over the
          columns outside H_c (at least 1).
     rc : the mirror of cr with heavy rows H_r = {i : row_oob[i] * R > gamma * T}.
+    greedy: the line-at-a-time depths of greedy_depths (strategy "greedy" only).
     Every candidate covers every code: d_r[i] + d_c[k] - 1 >= n[i, k].
     """
     R, C = n.shape
@@ -226,10 +227,45 @@ def candidates(n: np.ndarray, st: LineStats, strategy: str, gamma: int = 2
             d_r = np.where(heavy, st.row_maxdig, 1)
             rest = n[~heavy, :]
             d_c = np.maximum(1, rest.max(axis=0)) if rest.shape[0] else np.ones(C, np.int64)
+        elif name == "greedy":
+            d_r, d_c = greedy_depths(n)
         else:
             raise OracleError(ERR_INVALID_ARG, name)
         out[name] = (d_r.astype(np.int64), d_c.astype(np.int64))
     return out
+
+
+def greedy_depths(n: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Line-at-a-time unpacking (the page's Mix, "chosen per matrix via outlier
+    counts", read as a greedy): all depths start at 1; while some code is not
+    covered (n[i, k] > d_r[i] + d_c[k] - 1), the line holding the most
+    uncovered codes gets one more level, rows before columns and lower indices
+    first on equal counts.  Raising row i to depth d covers exactly the codes
+    with n[i, k] = d + d_c[k] - 1 (they needed one more level than the row
+    had), so the counts are updated along that line only."""
+    R, C = n.shape
+    d_r = np.ones(R, np.int64)
+    d_c = np.ones(C, np.int64)
+    unc = n > 1
+    cnt_r = unc.sum(axis=1).astype(np.int64)
+    cnt_c = unc.sum(axis=0).astype(np.int64)
+    while True:
+        mr = int(cnt_r.max()) if R else 0
+        mc = int(cnt_c.max()) if C else 0
+        if max(mr, mc) == 0:
+            return d_r, d_c
+        if mr >= mc:
+            i = int(np.argmax(cnt_r))  # first line with the largest count
+            d_r[i] += 1
+            newly = n[i, :] == d_r[i] + d_c - 1
+            cnt_c -= newly
+            cnt_r[i] -= int(newly.sum())
+        else:
+            k = int(np.argmax(cnt_c))
+            d_c[k] += 1
+            newly = n[:, k] == d_r + d_c[k] - 1
+            cnt_r -= newly
+            cnt_c[k] -= int(newly.sum())
 
 
 @dataclass

@@ -31,6 +31,8 @@ PINS = [
     P.test_hand_worked_examples,
     P.test_clipping_quantizer_is_rounding_then_clamp,
     P.test_clipped_path_is_in_range_when_beta_fits,
+    P.test_greedy_closed_forms,
+    P.test_greedy_matches_recount_from_scratch_and_covers,
 ]
 PARAMS = {
     "test_percentile_matches_sorted_bruteforce": {"p": (95, 100)},
@@ -153,7 +155,41 @@ def _clip_dropped(x32, r, beta):
     return np.rint(np.nan_to_num(y, posinf=2.0 ** 31 - 1, neginf=-(2.0 ** 31 - 1))).astype(np.int64)
 
 
+def _greedy_columns_first(n):
+    d_r, d_c = _orig_greedy(n.T)
+    return d_c, d_r
+
+
+def _greedy_stale_update(n):
+    # covers the codes the line needed before its new level (off by one)
+    R, C = n.shape
+    d_r, d_c = np.ones(R, np.int64), np.ones(C, np.int64)
+    unc = n > 1
+    cr, cc = unc.sum(1), unc.sum(0)
+    for _ in range(R * C * 40):
+        if max(cr.max(initial=0), cc.max(initial=0)) == 0:
+            break
+        if cr.max(initial=0) >= cc.max(initial=0):
+            i = int(np.argmax(cr))
+            newly = n[i, :] == d_r[i] + d_c - 1
+            d_r[i] += 1
+            cc -= newly
+            cr[i] -= int(newly.sum())
+        else:
+            k = int(np.argmax(cc))
+            newly = n[:, k] == d_r + d_c[k] - 1
+            d_c[k] += 1
+            cr -= newly
+            cc[k] -= int(newly.sum())
+    return d_r, d_c
+
+
+_orig_greedy = O.greedy_depths
+
+
 MUTATIONS = {
+    "greedy_columns_first": ("greedy_depths", _greedy_columns_first),
+    "greedy_stale_update": ("greedy_depths", _greedy_stale_update),
     "clip_dropped": ("rtn_clipped", _clip_dropped),
     "widen_shift_15": ("widen", _widen_shift_15),
     "widen_reads_binary16": ("widen", _widen_through_f16),

@@ -317,7 +317,7 @@ def test_candidates_bruteforce_and_coverage():
 
 def test_joint_choice_bruteforce_min_and_tie_order():
     rng = np.random.default_rng(6)
-    order = O.CANDIDATE_ORDER
+    order = O.ALLOWED["mix"]  # the Mix candidates, in tie order
     for _ in range(40):
         M, K, N = (int(v) for v in rng.integers(1, 7, 3))
         bits = int(rng.integers(2, 7))
@@ -385,6 +385,8 @@ def test_unpacked_operands_reconstruct_codes(bits):
         na, nb = O.digit_count(qa, bits), O.digit_count(qb, bits)
         ca = O.candidates(na, O.line_stats(na), "mix")
         cb = O.candidates(nb, O.line_stats(nb), "mix")
+        ca.update(O.candidates(na, O.line_stats(na), "greedy"))  # every candidate map, greedy included
+        cb.update(O.candidates(nb, O.line_stats(nb), "greedy"))
         for xa, xb in itertools.product(O.CANDIDATE_ORDER, repeat=2):
             da_r, da_c = ca[xa]
             db_r, db_c = cb[xb]
@@ -614,3 +616,68 @@ def test_p100_beta255_maps_the_largest_magnitude_to_beta():
         assert res.C.tolist() == brute_matmul(res.qa.q, res.qb.q)
         S = 2 ** (bits - 1)
         assert res.qa.n.max() == (2 if 255 >= S else 1)
+
+
+# ---------------------------------------------------------------------------
+# greedy line-at-a-time Mix (strategy "greedy")
+# ---------------------------------------------------------------------------
+
+def greedy_from_scratch(n):
+    """The greedy rule with every count recounted from the whole matrix at
+    every step (no incremental bookkeeping)."""
+    n = np.asarray(n)
+    R, C = n.shape
+    d_r, d_c = [1] * R, [1] * C
+    while True:
+        unc = [[n[i][k] > d_r[i] + d_c[k] - 1 for k in range(C)] for i in range(R)]
+        rows = [sum(unc[i]) for i in range(R)]
+        cols = [sum(unc[i][k] for i in range(R)) for k in range(C)]
+        best = max(rows + cols)
+        if best == 0:
+            return d_r, d_c
+        lines = [("r", i) for i in range(R)] + [("c", k) for k in range(C)]
+        counts = rows + cols
+        kind, idx = lines[counts.index(best)]  # rows first, then the lowest index
+        if kind == "r":
+            d_r[idx] += 1
+        else:
+            d_c[idx] += 1
+
+
+def test_greedy_closed_forms():
+    n = np.ones((6, 7), np.int64)
+    n[2, 5] = 4  # one code of four digits: its row takes all three extra levels (rows first)
+    d_r, d_c = O.greedy_depths(n)
+    assert d_r.tolist() == [1, 1, 4, 1, 1, 1] and d_c.tolist() == [1] * 7
+    n = np.ones((6, 7), np.int64)
+    n[:, 3] = 2  # a whole column of two-digit codes: one column level covers them
+    d_r, d_c = O.greedy_depths(n)
+    assert d_r.tolist() == [1] * 6 and d_c.tolist() == [1, 1, 1, 2, 1, 1, 1]
+    assert [v.tolist() for v in O.greedy_depths(np.ones((3, 4), np.int64))] == [[1] * 3, [1] * 4]
+
+
+def test_greedy_matches_recount_from_scratch_and_covers():
+    rng = np.random.default_rng(81)
+    for trial in range(60):
+        R, C = int(rng.integers(1, 7)), int(rng.integers(1, 7))
+        bits = int(rng.choice([2, 3, 5]))
+        q = rand_codes(rng, (R, C), bits, oob_frac=float(rng.choice([0.1, 0.4])), big=600)
+        n = O.digit_count(q, bits)
+        d_r, d_c = O.greedy_depths(n)
+        ref_r, ref_c = greedy_from_scratch(n)
+        assert d_r.tolist() == ref_r and d_c.tolist() == ref_c, (trial, n.tolist())
+        assert np.all(d_r[:, None] + d_c[None, :] - 1 >= n)
+
+
+def test_greedy_strategy_path_is_exact():
+    rng = np.random.default_rng(82)
+    for trial in range(12):
+        M, K, N = (int(v) for v in rng.integers(2, 9, size=3))
+        bits = int(rng.choice([3, 5]))
+        a = rng.standard_normal((M, K)).astype(np.float32)
+        b = rng.standard_normal((K, N)).astype(np.float32)
+        a[rng.random(a.shape) < 0.15] *= 40
+        res = O.imunpack_matmul(a, b, 15 if bits == 5 else 3, bits, 90, 100, "greedy", "mix")
+        assert res.plan.choice.cand_a == "greedy"
+        assert set(k[0] for k in res.plan.choice.table) == {"greedy"}
+        assert res.C.tolist() == brute_matmul(res.qa.q, res.qb.q)
