@@ -432,6 +432,18 @@ def main():
         torch.cuda.synchronize()
         pair_ms[key] = round((time.perf_counter() - t1) / max(1, args.pair_steps) * 1e3, 4)
 
+    # the greedy line-at-a-time planner on both operands (plan quality against Mix)
+    pg = prm("greedy", "greedy")
+    for _ in range(2):
+        _, _, ginfo = step(pg)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(max(1, args.pair_steps)):
+        step(pg)
+    torch.cuda.synchronize()
+    ratios["greedy/greedy"] = round(ginfo[0]["unpack_ratio"], 4)
+    pair_ms["greedy/greedy"] = round((time.perf_counter() - t1) / max(1, args.pair_steps) * 1e3, 4)
+
     # quantizer variants of the page's ablation rows on the same operands: p =
     # 100% with beta = 255, and clipping at the 99.5-percentile
     variants = {}

@@ -71,13 +71,20 @@ typedef enum { IMU_F32 = 0, IMU_BF16 = 1 } imu_dtype;
  * (a weight W of shape N x K used as B = W^T with layout TRANSPOSED). */
 typedef enum { IMU_NORMAL = 0, IMU_TRANSPOSED = 1 } imu_layout;
 
-/* Unpacking strategy of one operand ("Approach"; Mix in the unpack-ratio rows). */
-typedef enum { IMU_ROW = 0, IMU_COL = 1, IMU_MIX = 2 } imu_strategy;
+/* Unpacking strategy of one operand ("Approach"; Mix in the unpack-ratio rows).
+ * IMU_GREEDY: line-at-a-time unpacking (all depths start at 1; while a code is
+ * not covered, the row or column holding the most uncovered codes gets one more
+ * level, rows first and lower indices first on ties), for comparing plan
+ * quality with Mix; the operand may have at most 28672 rows + columns. */
+typedef enum { IMU_ROW = 0, IMU_COL = 1, IMU_MIX = 2, IMU_GREEDY = 3 } imu_strategy;
 
-/* Candidate depth maps the planner chooses from (Mix allows all four):
+/* Candidate depth maps the planner chooses from (Mix allows the first four):
  * ROW: each row gets its largest digit count; COL: each column does;
- * CR: heavy columns first, then rows; RC: heavy rows first, then columns. */
-typedef enum { IMU_CAND_ROW = 0, IMU_CAND_COL = 1, IMU_CAND_CR = 2, IMU_CAND_RC = 3 } imu_candidate;
+ * CR: heavy columns first, then rows; RC: heavy rows first, then columns;
+ * GREEDY: the line-at-a-time depths (strategy IMU_GREEDY only). */
+typedef enum {
+  IMU_CAND_ROW = 0, IMU_CAND_COL = 1, IMU_CAND_CR = 2, IMU_CAND_RC = 3, IMU_CAND_GREEDY = 4
+} imu_candidate;
 
 /* One operand as it enters C = A.B.  `rows` x `cols` is the LOGICAL shape
  * (A: M x K, B: K x N).  `ld` >= stored row length; `batch` >= 1 entries spaced
@@ -130,7 +137,7 @@ typedef struct {
   int32_t choice_a, choice_b;/* imu_candidate chosen for A and B */
   int32_t pad_;
   double unpack_ratio;       /* M'K'N' / (MKN) */
-  int64_t pair_sizes[16][3]; /* (M',K',N') of every candidate pair, A-major; -1 if not allowed */
+  int64_t pair_sizes[25][3]; /* (M',K',N') of every candidate pair, A-major (5 x 5); -1 if not allowed */
 } imu_plan_info;
 
 /* Byte offsets inside one batch entry of a statistics buffer (see imu_stats_layout).

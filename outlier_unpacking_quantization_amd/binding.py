@@ -26,8 +26,8 @@ LIB_PATH = os.path.join(HERE, "libimunpack.so")
 OK, ERR_INVALID_ARG, ERR_NONFINITE, ERR_RANGE, ERR_WORKSPACE, ERR_HIP, ERR_UNSUPPORTED = range(7)
 F32, BF16 = 0, 1
 NORMAL, TRANSPOSED = 0, 1
-STRATEGY = {"row": 0, "col": 1, "mix": 2}
-CANDIDATES = ("row", "col", "cr", "rc")
+STRATEGY = {"row": 0, "col": 1, "mix": 2, "greedy": 3}
+CANDIDATES = ("row", "col", "cr", "rc", "greedy")
 
 
 class ImunpackError(RuntimeError):
@@ -60,7 +60,7 @@ class ImuPlanInfo(ctypes.Structure):
                 ("a_offset", ctypes.c_int64), ("b_offset", ctypes.c_int64),
                 ("n_seg", ctypes.c_int32), ("choice_a", ctypes.c_int32), ("choice_b", ctypes.c_int32),
                 ("pad_", ctypes.c_int32), ("unpack_ratio", ctypes.c_double),
-                ("pair_sizes", (ctypes.c_int64 * 3) * 16)]
+                ("pair_sizes", (ctypes.c_int64 * 3) * 25)]
 
     def as_dict(self) -> dict:
         d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("pair_sizes", "pad_")}
@@ -68,7 +68,7 @@ class ImuPlanInfo(ctypes.Structure):
         pairs = {}
         for ia, ca in enumerate(CANDIDATES):
             for ib, cb in enumerate(CANDIDATES):
-                s = tuple(int(v) for v in self.pair_sizes[ia * 4 + ib])
+                s = tuple(int(v) for v in self.pair_sizes[ia * len(CANDIDATES) + ib])
                 if s[0] >= 0:
                     pairs[(ca, cb)] = s
         d["pairs"] = pairs
@@ -319,8 +319,8 @@ class Plan:
         """(padded offsets, lengths) of the exponent segments of K'."""
         h = self.header_raw(b).cpu()
         n_seg = int(h[12:16].view(torch.int32)[0])
-        # PlanHeader: 4 ints, 3 + 4 + 1 int64, 4 ints, 16*3 int64, then seg_off[65] int64, seg_len[64] int32
-        off0 = 16 + 8 * 8 + 16 + 16 * 3 * 8
+        # PlanHeader: 4 ints, 3 + 4 + 1 int64, 4 ints, 25*3 int64, then seg_off[65] int64, seg_len[64] int32
+        off0 = 16 + 8 * 8 + 16 + 25 * 3 * 8
         seg_off = h[off0:off0 + 8 * 65].view(torch.int64)[:n_seg + 1].tolist()
         seg_len = h[off0 + 8 * 65:off0 + 8 * 65 + 4 * 64].view(torch.int32)[:n_seg].tolist()
         return seg_off, seg_len

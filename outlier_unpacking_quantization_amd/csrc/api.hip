@@ -94,8 +94,8 @@ imu_status check_params(const imu_params* p) {
   if (p->gamma < 0 || p->gamma > 1000000) return fail(IMU_ERR_INVALID_ARG, "gamma must be in [0, 1e6]");
   if (p->clip != 0 && p->clip != 1) return fail(IMU_ERR_INVALID_ARG, "clip must be 0 or 1");
   for (int s : {p->strat_a, p->strat_b})
-    if (s != IMU_ROW && s != IMU_COL && s != IMU_MIX)
-      return fail(IMU_ERR_INVALID_ARG, "strategy must be IMU_ROW, IMU_COL or IMU_MIX");
+    if (s != IMU_ROW && s != IMU_COL && s != IMU_MIX && s != IMU_GREEDY)
+      return fail(IMU_ERR_INVALID_ARG, "strategy must be IMU_ROW, IMU_COL, IMU_MIX or IMU_GREEDY");
   return IMU_OK;
 }
 
@@ -107,6 +107,10 @@ imu_status check_pair(const imu_matrix* a, const imu_matrix* b, const imu_params
   if (a->cols != b->rows) return fail(IMU_ERR_INVALID_ARG, "a.cols must equal b.rows (K)");
   if (a->cols > kMaxK) return fail(IMU_ERR_UNSUPPORTED, "K must be below 2^20 - 1");
   if (a->batch != b->batch) return fail(IMU_ERR_INVALID_ARG, "a.batch must equal b.batch");
+  if ((p->strat_a == IMU_GREEDY && a->rows + a->cols > kGreedyMaxLines) ||
+      (p->strat_b == IMU_GREEDY && b->rows + b->cols > kGreedyMaxLines))
+    return fail(IMU_ERR_UNSUPPORTED, "the greedy planner holds at most %d rows + columns of an operand",
+                kGreedyMaxLines);
   return IMU_OK;
 }
 
@@ -208,6 +212,35 @@ imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p
   uint8_t* stats_a = ra.stats;
   uint8_t* stats_b = rb.stats;
   const StatsLayout &la = ra.L, &lb = rb.L;
+  const PlanLayout pl = plan_layout(oa.R, oa.C, ob.C, batch, p->bits);
+  if (p->strat_a == IMU_GREEDY || p->strat_b == IMU_GREEDY) {
+    GreedyArgs g{};
+    g.plan = plan;
+    g.pl = pl;
+    g.bits = p->bits;
+    g.clip = p->clip;
+    g.beta = p->beta;
+    auto add = [&](const Operand& op, const StatsRef& r, int64_t rows_off, int64_t cols_off) {
+      GreedyOp& o = g.op[g.nops++];
+      o.x = op.m->data;
+      o.dtype = op.dtype;
+      o.transposed = op.tr ? 1 : 0;
+      o.ld = op.m->ld;
+      o.bstride = op.m->batch_stride;
+      o.R = op.R;
+      o.C = op.C;
+      o.stats = r.stats;
+      o.stats_stride = r.L.stride;
+      o.row_oob = r.L.row_oob;
+      o.col_oob = r.L.col_oob;
+      o.rows_off = rows_off;
+      o.cols_off = cols_off;
+    };
+    // greedy area: A rows [M], A cols [K], B rows [K], B cols [N]
+    if (p->strat_a == IMU_GREEDY) add(oa, ra, 0, oa.R);
+    if (p->strat_b == IMU_GREEDY) add(ob, rb, oa.R + oa.C, oa.R + 2 * oa.C);
+    IMU_HIP(launch_greedy(g, batch, s));
+  }
   PlanArgs pa{};
   pa.stats_a = stats_a;
   pa.stats_b = stats_b;
@@ -216,7 +249,7 @@ imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p
   pa.sla = la;
   pa.slb = lb;
   pa.plan = plan;
-  pa.pl = plan_layout(oa.R, oa.C, ob.C, batch, p->bits);
+  pa.pl = pl;
   pa.gamma = p->gamma;
   pa.strat_a = p->strat_a;
   pa.strat_b = p->strat_b;
@@ -355,6 +388,7 @@ imu_status finish_plan(const Operand& oa, const Operand& ob, const uint8_t* hdrs
   if (b_total) *b_total = boff;
   if (status & kStatusNonfinite) return fail(IMU_ERR_NONFINITE, "an input element is NaN or Inf");
   if (status & kStatusRange) return fail(IMU_ERR_RANGE, "|x * r| >= 2^31 for some element");
+  if (status & kStatusGreedy) return fail(IMU_ERR_HIP, "the greedy planner did not finish");
   return IMU_OK;
 }
 

@@ -18,6 +18,10 @@ constexpr int kKPad = 128;          // every exponent segment of K' is padded to
 constexpr int kMaxSeg = 64;         // room for 2*max_digits(2)-1 = 61 segments
 constexpr int kStatusNonfinite = 1; // device status bits
 constexpr int kStatusRange = 2;
+constexpr int kStatusGreedy = 4;    // the greedy planner did not finish (cannot happen for consistent counts)
+constexpr int kNumCand = 5;         // candidate depth maps: row, col, cr, rc, greedy
+constexpr int kNumPairs = kNumCand * kNumCand;
+constexpr int kGreedyMaxLines = 28672;  // rows + columns of an operand the greedy planner holds in LDS
 
 __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 __host__ __device__ inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -79,7 +83,7 @@ struct PlanHeader {
   int64_t m_base, n_base, m_alloc, n_alloc;
   int64_t k_pad;
   int32_t lev_a, lev_b, emax, pad0;
-  int64_t pair[16][3];
+  int64_t pair[kNumPairs][3];
   int64_t seg_off[kMaxSeg + 1];
   int32_t seg_len[kMaxSeg];
   int64_t reserved[8];  // [0]: tag closing the host copy; [1]: the planner's arrival counter
@@ -96,15 +100,16 @@ static_assert(sizeof(PlanHeader) <= kPlanHeaderStride, "plan header");
 // byte offsets read by the Python binding
 static_assert(offsetof(PlanHeader, n_seg) == 12, "plan header layout");
 static_assert(offsetof(PlanHeader, pair) == 96, "plan header layout");
-static_assert(offsetof(PlanHeader, seg_off) == 480, "plan header layout");
-static_assert(offsetof(PlanHeader, seg_len) == 1000, "plan header layout");
+static_assert(offsetof(PlanHeader, seg_off) == 696, "plan header layout");
+static_assert(offsetof(PlanHeader, seg_len) == 1216, "plan header layout");
 
 // The planner splits the lines (rows of A, columns of B, then k) into chunks
 // of kPlanLines, one workgroup each; every workgroup keeps a record.
 constexpr int kPlanLines = 512;
 constexpr int kPlanTasks = 64;  // >= max levels and >= max segments
+constexpr int kPlanSums = 2 * kNumCand + kNumPairs;  // M'[5], N'[5], K'[5][5]
 struct PlanWgRecord {
-  long long sum[24];       // candidate sizes: M'[4], N'[4], K'[4][4] of this chunk
+  long long sum[kPlanSums + 1];  // candidate sizes of this chunk: M'[5], N'[5], K'[5][5] (+1: 16-byte size)
   int32_t cnt[kPlanTasks]; // per task (level or segment): entries of this chunk
   int32_t off[kPlanTasks]; // per task: entries of earlier chunks of the same kind
   int32_t mx[4];           // chunk maxima: depth (rows/cols) or dA, dB, dA + dB - 2 (k)
@@ -120,6 +125,7 @@ struct PlanLayout {
   int64_t kmap = 0, kmap_max = 0;
   int64_t wg_a = 0, wg_b = 0, wg_k = 0;  // planner workgroups over A's rows, B's columns, k
   int64_t cand = 0, rec = 0;             // packed candidate depths; workgroup records
+  int64_t gdep = 0;                      // greedy depths: A rows [M], A cols [K], B rows [K], B cols [N]
   int64_t total = 0;
 };
 
@@ -193,6 +199,7 @@ inline PlanLayout plan_layout(int64_t M, int64_t K, int64_t N, int64_t batch, in
   L.wg_b = ceil_div(N, kPlanLines);
   L.wg_k = ceil_div(K, kPlanLines);
   L.cand = take(4 * (M + N + 2 * K));
+  L.gdep = take(4 * (M + N + 2 * K));
   L.rec = take((int64_t)sizeof(PlanWgRecord) * (L.wg_a + L.wg_b + L.wg_k));
   L.entry_stride = o;
   L.total = L.headers_bytes + batch * L.entry_stride;

@@ -32,6 +32,26 @@ struct PlanArgs {  // the plan headers must be zero when the planner starts (arr
 };
 hipError_t launch_plan(const PlanArgs& a, hipEvent_t done, hipStream_t s);  // done: completes with the last launch, or null
 
+// Greedy depths of the operands whose strategy is IMU_GREEDY (before the plan
+// launches, after the headers are cleared).
+struct GreedyOp {
+  const void* x;
+  int dtype, transposed;        // element (i, k) of the logical operand at transposed ? k*ld+i : i*ld+k
+  int64_t ld, bstride;          // elements
+  int64_t R, C;                 // logical shape (rows + cols <= kGreedyMaxLines)
+  const uint8_t* stats;
+  int64_t stats_stride, row_oob, col_oob;  // out-of-range counts of the logical rows / columns
+  int64_t rows_off, cols_off;   // int32 offsets of its row / column depths in the plan's greedy area
+};
+struct GreedyArgs {
+  GreedyOp op[2];
+  int nops;
+  uint8_t* plan;
+  PlanLayout pl;
+  int bits, clip, beta;
+};
+hipError_t launch_greedy(const GreedyArgs& g, int batch, hipStream_t s);
+
 // unpack.hip
 struct UnpackArgs {
   const void* x;

@@ -144,8 +144,11 @@ __device__ inline uint32_t col_depths(const Src& s, int64_t k, int gamma) {
 __device__ inline int pick(uint32_t packed, int c) { return (packed >> (8 * c)) & 0xFF; }
 
 __device__ inline bool allowed(int strat, int c) {
-  return strat == IMU_MIX || (strat == IMU_ROW && c == 0) || (strat == IMU_COL && c == 1);
+  return (strat == IMU_MIX && c < 4) || (strat == IMU_ROW && c == 0) || (strat == IMU_COL && c == 1) ||
+         (strat == IMU_GREEDY && c == 4);
 }
+// Depth of candidate c of a line: packed bytes for row..rc, the greedy depth g for c = 4.
+__device__ inline int dep(uint32_t packed, int g, int c) { return c == 4 ? g : pick(packed, c); }
 
 // number of triples (k, v, v') with v + v' = e, v < dA, v' < dB
 __device__ inline int seg_count(int dA, int dB, int e) {
@@ -182,6 +185,7 @@ struct Entry {  // one batch entry's plan buffers
   PlanHeader* ph;
   int32_t *da_r, *da_c, *db_r, *db_c, *lvl_a, *lvl_b, *amap, *bmap, *kpre;
   uint32_t *kmap, *cand;
+  int32_t* gdep;  // greedy depths: A rows [M], A cols [K], B rows [K], B cols [N]
   PlanWgRecord* rec;
 };
 __device__ inline Entry entry_of(const PlanArgs& a, int b) {
@@ -201,6 +205,7 @@ __device__ inline Entry entry_of(const PlanArgs& a, int b) {
   x.kmap = reinterpret_cast<uint32_t*>(e + L.kmap);
   x.cand = reinterpret_cast<uint32_t*>(e + L.cand);  // [M] A rows, [N] B cols, [K] A cols, [K] B rows
   x.rec = reinterpret_cast<PlanWgRecord*>(e + L.rec);
+  x.gdep = reinterpret_cast<int32_t*>(e + L.gdep);
   return x;
 }
 
@@ -213,9 +218,9 @@ __device__ inline uint32_t* arrive_counter(const PlanArgs& a, int b) {
 
 // Shared memory of a planner workgroup, all phases.
 struct PlanShared {
-  long long red[kThreads / 24][24];
-  int red32[kWaves][16];
-  long long tot[24];
+  long long red[kThreads / kPlanSums][kPlanSums];
+  int red32[kWaves][kNumPairs];
+  long long tot[kPlanSums];
   int choice[2];
   int flag;
   int hist[(kMaxD + 1) * (kMaxD + 1)];  // depth histogram (rows/cols) or (dA, dB) pairs (k)
@@ -239,23 +244,33 @@ __device__ void phase_sums(const PlanArgs& a, int b, int64_t w, PlanShared& S) {
   const Src B = src_of(a.stats_b + b * a.stats_stride_b, a.slb);
   const Chunk c = chunk_of(L, w);
   const int gamma = a.gamma;
-  if (w == 0 && t == 0)  // status of this plan; later failures are OR-ed in
+  if (w == 0 && t == 0)  // status of this plan (and of the greedy planner); later failures are OR-ed in
     E.ph->status = (int32_t)(reinterpret_cast<const StatsHeader*>(a.stats_a + b * a.stats_stride_a)->status |
-                             reinterpret_cast<const StatsHeader*>(a.stats_b + b * a.stats_stride_b)->status);
+                             reinterpret_cast<const StatsHeader*>(a.stats_b + b * a.stats_stride_b)->status |
+                             (int32_t)E.ph->reserved[2]);
   // a chunk's shares fit 32 bits (kPlanLines lines, depths <= 32); only its kind's
-  // 4 (rows, columns) or 16 (k) sums are non-zero
-  int acc[16];
+  // 5 (rows, columns) or 25 (k) sums are non-zero
+  int acc[kNumPairs];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0;
+  for (int j = 0; j < kNumPairs; ++j) acc[j] = 0;
   uint32_t dx[kPer], dy[kPer];
+  int gx[kPer], gy[kPer];  // greedy depths (1 when that operand's strategy is not greedy)
+  const bool ga = a.strat_a == IMU_GREEDY, gb = a.strat_b == IMU_GREEDY;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {  // clamped indices: all loads issued before use
     const int64_t i = min64(c.first + t + (int64_t)j * kThreads, c.n - 1);
-    if (c.kind == 0) dx[j] = row_depths(A, i, gamma);
-    else if (c.kind == 1) dx[j] = col_depths(B, i, gamma);
-    else {
+    gx[j] = gy[j] = 1;
+    if (c.kind == 0) {
+      dx[j] = row_depths(A, i, gamma);
+      if (ga) gx[j] = E.gdep[i];
+    } else if (c.kind == 1) {
+      dx[j] = col_depths(B, i, gamma);
+      if (gb) gx[j] = E.gdep[L.M + 2 * L.K + i];
+    } else {
       dx[j] = col_depths(A, i, gamma);
       dy[j] = row_depths(B, i, gamma);
+      if (ga) gx[j] = E.gdep[L.M + i];
+      if (gb) gy[j] = E.gdep[L.M + L.K + i];
     }
   }
 #pragma unroll
@@ -265,31 +280,32 @@ __device__ void phase_sums(const PlanArgs& a, int b, int64_t w, PlanShared& S) {
     if (c.kind == 0) {
       E.cand[i] = dx[j];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += pick(dx[j], q);
+      for (int q = 0; q < kNumCand; ++q) acc[q] += dep(dx[j], gx[j], q);
     } else if (c.kind == 1) {
       E.cand[L.M + i] = dx[j];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += pick(dx[j], q);
+      for (int q = 0; q < kNumCand; ++q) acc[q] += dep(dx[j], gx[j], q);
     } else {
       E.cand[L.M + L.N + i] = dx[j];
       E.cand[L.M + L.N + L.K + i] = dy[j];
 #pragma unroll
-      for (int ca = 0; ca < 4; ++ca)
+      for (int ca = 0; ca < kNumCand; ++ca)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[ca * 4 + cb] += pick(dx[j], ca) * pick(dy[j], cb);
+        for (int cb = 0; cb < kNumCand; ++cb)
+          acc[ca * kNumCand + cb] += dep(dx[j], gx[j], ca) * dep(dy[j], gy[j], cb);
     }
   }
-  const int nsum = c.kind == 2 ? 16 : 4;  // uniform over the workgroup
+  const int nsum = c.kind == 2 ? kNumPairs : kNumCand;  // uniform over the workgroup
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < kNumPairs; ++j) {
     if (j < nsum) {
       const int v = wave_sum_i32(acc[j]);
       if (lane == 0) S.red32[wave][j] = v;
     }
   }
   __syncthreads();
-  if (t < 24) {  // record slots: [0,4) A rows, [4,8) B columns, [8,24) k pairs
-    const int first = c.kind == 0 ? 0 : c.kind == 1 ? 4 : 8;
+  if (t < kPlanSums) {  // record slots: [0,5) A rows, [5,10) B columns, [10,35) k pairs
+    const int first = c.kind == 0 ? 0 : c.kind == 1 ? kNumCand : 2 * kNumCand;
     long long v = 0;
     if (t >= first && t < first + nsum)
       for (int q = 0; q < kWaves; ++q) v += S.red32[q][t - first];
@@ -306,9 +322,9 @@ __device__ void choose(const PlanArgs& a, int b, int64_t G, bool write_header, P
   // acquire at device scope (drops stale cached lines) plain loads see them
   // and can all be in flight at once
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  constexpr int kGroups = kThreads / 24;  // thread t adds value t % 24 of records t / 24 (mod kGroups)
-  if (t < kGroups * 24) {  // loads of 4 records in flight at a time
-    const int j = t % 24, g = t / 24;
+  constexpr int kGroups = kThreads / kPlanSums;  // thread t adds value t % 35 of records t / 35 (mod kGroups)
+  if (t < kGroups * kPlanSums) {  // loads of 4 records in flight at a time
+    const int j = t % kPlanSums, g = t / kPlanSums;
     long long v = 0;
     for (int64_t q0 = g; q0 < G; q0 += 4 * kGroups) {
       long long w[4];
@@ -319,7 +335,7 @@ __device__ void choose(const PlanArgs& a, int b, int64_t G, bool write_header, P
     S.red[g][j] = v;
   }
   __syncthreads();
-  if (t < 24) {
+  if (t < kPlanSums) {
     long long v = 0;
     for (int g = 0; g < kGroups; ++g) v += S.red[g][t];
     S.tot[t] = v;
@@ -328,26 +344,26 @@ __device__ void choose(const PlanArgs& a, int b, int64_t G, bool write_header, P
   // cost of pair (ca, cb) = M'[ca] K'[ca][cb] N'[cb] < 2^88: M'K' < 2^59 is
   // exact in 64 bits (M' < 2^29, K' < 2^30), its product with N' < 2^29 is
   // kept as (high, low) 64-bit words
-  if (t < 64) {  // wave 0: lane q < 16 is pair (q >> 2, q & 3)
-    const int q = t, ca = q >> 2, cb = q & 3;
-    const bool ok = q < 16 && allowed(a.strat_a, ca) && allowed(a.strat_b, cb);
+  if (t < 64) {  // wave 0: lane q < 25 is pair (q / 5, q % 5)
+    const int q = t, ca = q / kNumCand, cb = q % kNumCand;
+    const bool ok = q < kNumPairs && allowed(a.strat_a, ca) && allowed(a.strat_b, cb);
     unsigned long long hi = ~0ull, lo = ~0ull;
     if (ok) {
-      const unsigned long long mk = (unsigned long long)S.tot[ca] * (unsigned long long)S.tot[8 + q];
-      const unsigned long long nu = (unsigned long long)S.tot[4 + cb];
+      const unsigned long long mk = (unsigned long long)S.tot[ca] * (unsigned long long)S.tot[2 * kNumCand + q];
+      const unsigned long long nu = (unsigned long long)S.tot[kNumCand + cb];
       hi = __umul64hi(mk, nu);
       lo = mk * nu;
     }
-    if (write_header && q < 16) {
+    if (write_header && q < kNumPairs) {
       E.ph->pair[q][0] = ok ? S.tot[ca] : -1;
-      E.ph->pair[q][1] = ok ? S.tot[8 + q] : -1;
-      E.ph->pair[q][2] = ok ? S.tot[4 + cb] : -1;
+      E.ph->pair[q][1] = ok ? S.tot[2 * kNumCand + q] : -1;
+      E.ph->pair[q][2] = ok ? S.tot[kNumCand + cb] : -1;
     }
-    // smallest cost over the 16 lanes, ties to the first pair in A-major
-    // order: butterflies on (not allowed, high, low, index)
+    // smallest cost over lanes 0..31 (the 25 pairs), ties to the first pair in
+    // A-major order: butterflies on (not allowed, high, low, index)
     int best = ok ? q : 64 + q;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
+    for (int o = 1; o < 32; o <<= 1) {
       const unsigned long long ohi = __shfl_xor(hi, o, 64), olo = __shfl_xor(lo, o, 64);
       const int obest = __shfl_xor(best, o, 64);
       const bool take = ohi < hi || (ohi == hi && (olo < lo || (olo == lo && obest < best)));
@@ -358,7 +374,7 @@ __device__ void choose(const PlanArgs& a, int b, int64_t G, bool write_header, P
       }
     }
     if (q == 0) {
-      const int best_a = (best & 15) >> 2, best_b = best & 3;
+      const int best_a = (best & 63) / kNumCand, best_b = (best & 63) % kNumCand;
       S.choice[0] = best_a;
       S.choice[1] = best_b;
       if (write_header) {
@@ -366,8 +382,8 @@ __device__ void choose(const PlanArgs& a, int b, int64_t G, bool write_header, P
         ph->choice_a = best_a;
         ph->choice_b = best_b;
         ph->m_u = S.tot[best_a];
-        ph->k_u = S.tot[8 + (best & 15)];
-        ph->n_u = S.tot[4 + best_b];
+        ph->k_u = S.tot[2 * kNumCand + (best & 63)];
+        ph->n_u = S.tot[kNumCand + best_b];
       }
     }
   }
@@ -383,14 +399,22 @@ __device__ void phase_counts(const PlanArgs& a, int b, int64_t w, int ca, int cb
   for (int i = t; i < (kMaxD + 1) * (kMaxD + 1); i += kThreads) S.hist[i] = 0;
   __syncthreads();
   uint32_t dx[kPer], dy[kPer];
+  int gx[kPer], gy[kPer];  // greedy depths when the chosen candidate is the greedy one
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int64_t i = min64(c.first + t + (int64_t)j * kThreads, c.n - 1);
-    if (c.kind == 0) dx[j] = E.cand[i];
-    else if (c.kind == 1) dx[j] = E.cand[L.M + i];
-    else {
+    gx[j] = gy[j] = 1;
+    if (c.kind == 0) {
+      dx[j] = E.cand[i];
+      if (ca == 4) gx[j] = E.gdep[i];
+    } else if (c.kind == 1) {
+      dx[j] = E.cand[L.M + i];
+      if (cb == 4) gx[j] = E.gdep[L.M + 2 * L.K + i];
+    } else {
       dx[j] = E.cand[L.M + L.N + i];
       dy[j] = E.cand[L.M + L.N + L.K + i];
+      if (ca == 4) gx[j] = E.gdep[L.M + i];
+      if (cb == 4) gy[j] = E.gdep[L.M + L.K + i];
     }
   }
   int m0 = 1, m1 = 1, m2 = 0;
@@ -399,12 +423,12 @@ __device__ void phase_counts(const PlanArgs& a, int b, int64_t w, int ca, int cb
     const int64_t i = c.first + t + (int64_t)j * kThreads;
     if (i >= c.n) continue;
     if (c.kind < 2) {
-      const int d = pick(dx[j], c.kind == 0 ? ca : cb);
+      const int d = dep(dx[j], gx[j], c.kind == 0 ? ca : cb);
       (c.kind == 0 ? E.da_r : E.db_c)[i] = d;
       m0 = max(m0, d);
       atomicAdd(&S.hist[d], 1);
     } else {
-      const int x = pick(dx[j], ca), y = pick(dy[j], cb);
+      const int x = dep(dx[j], gx[j], ca), y = dep(dy[j], gy[j], cb);
       E.da_c[i] = x;
       E.db_r[i] = y;
       m0 = max(m0, x);
@@ -563,7 +587,7 @@ __device__ void layout(const PlanArgs& a, int b, int64_t w, bool write_header, P
         const PlanHeader* ph = E.ph;
         int64_t pr[3] = {0, 0, 0}, mu = 0, ku = 0, nu = 0;
         int32_t ca = 0, cb = 0, stt = 0;
-        if (lane < 16) {
+        if (lane < kNumPairs) {
           pr[0] = ph->pair[lane][0];
           pr[1] = ph->pair[lane][1];
           pr[2] = ph->pair[lane][2];
@@ -580,7 +604,7 @@ __device__ void layout(const PlanArgs& a, int b, int64_t w, bool write_header, P
           __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         };
         put(hh, sys);
-        if (lane < 16) {
+        if (lane < kNumPairs) {
           sys(&hh->pair[lane][0], pr[0]);
           sys(&hh->pair[lane][1], pr[1]);
           sys(&hh->pair[lane][2], pr[2]);
@@ -709,6 +733,102 @@ __device__ void phase_write(const PlanArgs& a, int b, int64_t w, PlanShared& S) 
   }
 }
 
+// --- greedy line-at-a-time depths (strategy IMU_GREEDY) ---------------------
+// One workgroup per (operand, batch entry).  All depths start at 1, so the
+// uncovered codes of each line start as its out-of-range count.  Each step
+// raises the line with the most uncovered codes (rows first, then the lowest
+// index, on equal counts: the largest key count << 32 | ~line) by one level;
+// a row raised to depth d covers exactly its codes with n = d + d_c[k] - 1,
+// whose digit counts are recomputed from the operand (the RTN code of x r), so
+// only the crossing columns' counts change.  A line stops being chosen once its
+// depth reaches its largest digit count, so at most (R + C) * 32 steps run.
+constexpr int kGreedyThreads = 1024;
+__global__ __launch_bounds__(kGreedyThreads) void greedy_kernel(GreedyArgs g) {
+  __shared__ int32_t s_cnt[kGreedyMaxLines];
+  __shared__ uint8_t s_dep[kGreedyMaxLines];
+  __shared__ unsigned long long s_key[kGreedyThreads / 64];
+  __shared__ int32_t s_sum[kGreedyThreads / 64];
+  __shared__ unsigned long long s_best;
+  const GreedyOp& o = g.op[blockIdx.x];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t R = o.R, C = o.C, NL = R + C;
+  const uint8_t* st = o.stats + b * o.stats_stride;
+  const float r = reinterpret_cast<const StatsHeader*>(st)->r;
+  const int32_t* row_oob = reinterpret_cast<const int32_t*>(st + o.row_oob);
+  const int32_t* col_oob = reinterpret_cast<const int32_t*>(st + o.col_oob);
+  const uint8_t* xb = static_cast<const uint8_t*>(o.x) + b * o.bstride * (o.dtype == IMU_F32 ? 4 : 2);
+  for (int64_t l = tid; l < NL; l += kGreedyThreads) {
+    s_dep[l] = 1;
+    s_cnt[l] = l < R ? row_oob[l] : col_oob[l - R];
+  }
+  // digit count of the code of logical element (i, k)
+  auto ndig = [&](int64_t i, int64_t k) __attribute__((always_inline)) {
+    const int64_t at = o.transposed ? k * o.ld + i : i * o.ld + k;
+    const float v = o.dtype == IMU_F32 ? reinterpret_cast<const float*>(xb)[at]
+                                       : bf16_to_f32(reinterpret_cast<const uint16_t*>(xb)[at]);
+    const float y = __builtin_fabsf(v * r);
+    const uint32_t m = g.clip ? (uint32_t)__builtin_rintf(__builtin_fminf(y, (float)g.beta))
+                              : (y < 2147483648.0f ? (uint32_t)__builtin_rintf(y) : 0x7FFFFFFFu);
+    const int bl = 32 - __clz((int)m);
+    return bl == 0 ? 1 : 1 + (bl - 1) / (g.bits - 1);
+  };
+  __syncthreads();
+  const int64_t cap = NL * 32 + 1;
+  int64_t step = 0;
+  for (;; ++step) {
+    unsigned long long key = 0;
+    for (int64_t l = tid; l < NL; l += kGreedyThreads)
+      key = max(key, (unsigned long long)(uint32_t)s_cnt[l] << 32 | (0xFFFFFFFFu - (uint32_t)l));
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) key = max(key, (unsigned long long)__shfl_xor(key, sh, 64));
+    if (lane == 0) s_key[wave] = key;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long k2 = 0;
+      for (int q = 0; q < kGreedyThreads / 64; ++q) k2 = max(k2, s_key[q]);
+      s_best = k2;
+      if ((k2 >> 32) != 0 && step < cap) ++s_dep[0xFFFFFFFFu - (uint32_t)k2];
+    }
+    __syncthreads();
+    const unsigned long long best = s_best;
+    if ((best >> 32) == 0 || step >= cap) break;
+    const int64_t line = 0xFFFFFFFFu - (uint32_t)best;
+    const int d = s_dep[line];
+    int local = 0;
+    if (line < R) {
+      for (int64_t k = tid; k < C; k += kGreedyThreads)
+        if (ndig(line, k) == d + s_dep[R + k] - 1) {
+          --s_cnt[R + k];
+          ++local;
+        }
+    } else {
+      const int64_t k = line - R;
+      for (int64_t i = tid; i < R; i += kGreedyThreads)
+        if (ndig(i, k) == s_dep[i] + d - 1) {
+          --s_cnt[i];
+          ++local;
+        }
+    }
+    local = wave_sum_i32(local);
+    if (lane == 0) s_sum[wave] = local;
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int q = 0; q < kGreedyThreads / 64; ++q) tot += s_sum[q];
+      s_cnt[line] -= tot;
+    }
+    __syncthreads();
+  }
+  int32_t* gd = reinterpret_cast<int32_t*>(g.plan + g.pl.headers_bytes + b * g.pl.entry_stride + g.pl.gdep);
+  for (int64_t l = tid; l < NL; l += kGreedyThreads)
+    gd[l < R ? o.rows_off + l : o.cols_off + (l - R)] = s_dep[l];
+  if (step >= cap && tid == 0)  // cannot happen for consistent counts; reported by the planner
+    atomicOr(reinterpret_cast<unsigned long long*>(
+                 &reinterpret_cast<PlanHeader*>(g.plan + b * kPlanHeaderStride)->reserved[2]),
+             (unsigned long long)kStatusGreedy);
+}
+
 // The three launches.  Records a kernel's own workgroups exchange travel as
 // device-scope atomics; records of an earlier launch are read with plain loads.
 __global__ __launch_bounds__(kThreads) void plan_sums_kernel(PlanArgs a) {
@@ -743,6 +863,14 @@ __global__ __launch_bounds__(kThreads) void plan_write_kernel(PlanArgs a) {
 }
 
 }  // namespace
+
+hipError_t launch_greedy(const GreedyArgs& g, int batch, hipStream_t s) {
+  if (g.nops < 1 || g.nops > 2 || batch < 1 || batch > 65535) return hipErrorInvalidValue;
+  for (int i = 0; i < g.nops; ++i)
+    if (g.op[i].R + g.op[i].C > kGreedyMaxLines) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)g.nops, (unsigned)batch), dim3(kGreedyThreads), 0, s, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const PlanArgs& a, hipEvent_t done, hipStream_t s) {
   const PlanLayout& L = a.pl;

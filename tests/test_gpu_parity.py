@@ -51,6 +51,11 @@ SMALL = [
     dict(seed=17, m=150, k=260, n=140, kind="gauss", beta=7, bits=3, p=(995, 1000), clip=True, dtype="f32"),
     dict(seed=18, m=180, k=260, n=140, kind="linear", beta=255, bits=5, p=(100, 100)),
     dict(seed=19, m=140, k=200, n=130, kind="grad", beta=255, bits=8, p=(100, 100), layout_a="transposed"),
+    # the greedy line-at-a-time planner (strategy "greedy"), alone and against Mix
+    dict(seed=20, m=200, k=300, n=150, kind="linear", strat_a="greedy", strat_b="greedy", layout_b="transposed"),
+    dict(seed=21, m=130, k=257, n=129, kind="gauss", dtype="f32", strat_a="greedy", strat_b="mix"),
+    dict(seed=22, m=150, k=200, n=140, kind="grad", bits=4, beta=31, strat_a="mix", strat_b="greedy",
+         layout_a="transposed", batch=2),
 ]
 
 
@@ -341,3 +346,19 @@ def test_entry_points_need_init_and_release_frees():
     assert st == B.ERR_INVALID_ARG and b"imu_init" in B.lib().imu_last_error()
     out2, c2, _ = B.imunpack_matmul(a, b, p)  # the binding sets the device up again
     assert torch.equal(c1, c2) and torch.equal(out1, out2)
+
+
+def test_full_size_greedy_plan():
+    """The greedy planner on the LLaMA-shaped linear layer at full size (2681
+    and 4405 greedy steps): plan sizes and C against the oracle."""
+    pr = W.config(1)[0].with_strategies("greedy", "greedy")
+    print(f"\n[full] {pr.name} greedy/greedy", flush=True)
+    a, b = G.to_device(pr.a), G.to_device(pr.b)
+    out, c, infos = B.imunpack_matmul(a, b, G.params_of(pr), ws=B.Workspace("cuda"))
+    torch.cuda.synchronize()
+    ref = G.oracle_entries(pr, unpacked=False)[0]
+    ch = ref.plan.choice
+    assert infos[0]["choice"] == ("greedy", "greedy")
+    assert (infos[0]["m_u"], infos[0]["k_u"], infos[0]["n_u"]) == (ch.m_u, ch.k_u, ch.n_u)
+    assert np.array_equal(c[0].cpu().numpy(), ref.C32)
+    assert G.ulp_diff(out[0].cpu().numpy(), ref.out) <= 1
