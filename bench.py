@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective int-TOPS (orig M·N·K) + unpack ratio + % int8 MFMA peak, 1×MI355X"
 INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
+FP6_PEAK_TFLOPS = 10100.0  # MI355X dense fp6 / fp4 MFMA, 10.1 PFLOP/s
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20  # written between cold steps: more than the 256 MB MALL and the 8 x 4 MB L2
 
@@ -64,6 +65,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2,
                     help="workload recipe index (default 2: MLP up-projection; 1: LLaMA-shaped linear)")
     ap.add_argument("--cold-steps", type=int, default=20, help="steps timed after a cache flush each")
+    ap.add_argument("--digits", choices=("auto", "int8", "fp6"), default="auto",
+                    help="digit format of the unpacked operands (auto: fp6 where it applies)")
     ap.add_argument("--pair-steps", type=int, default=5, help="timed steps of each fixed row/column pairing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-steps", action="store_true",
@@ -331,9 +334,9 @@ def main():
     a = device_matrix(pr.a, torch, B)
     b = device_matrix(pr.b, torch, B)
 
-    def prm(sa, sb):
+    def prm(sa, sb, digits=args.digits):
         return B.params(beta=pr.beta, bits=pr.bits, p=(pr.p_num, pr.p_den), strat_a=sa, strat_b=sb,
-                        gamma=pr.gamma)
+                        gamma=pr.gamma, digits=digits)
 
     p = prm(pr.strat_a, pr.strat_b)
     ws = B.Workspace("cuda")
@@ -360,8 +363,10 @@ def main():
     hev.close()
     info = infos[0]
 
+    fp6 = info["digits"] == B.DIGITS["fp6"]
     if args.only_steps:
         print(json.dumps({"workload": pr.name, "steps": args.steps, "warmup": args.warmup,
+                          "digits": "fp6" if fp6 else "int8",
                           "ms_per_step": round(t_step * 1e3, 4), "gemm_us": round(t_gemm * 1e6, 2)}))
         return
 
@@ -449,7 +454,7 @@ def main():
     variants = {}
     for key, vb, vp, vclip in (("p100_beta255", 255, (100, 100), False), ("clip_p995", pr.beta, (995, 1000), True)):
         pv = B.params(beta=vb, bits=pr.bits, p=vp, strat_a=pr.strat_a, strat_b=pr.strat_b, gamma=pr.gamma,
-                      clip=vclip)
+                      clip=vclip, digits=args.digits)
         for _ in range(2):
             _, _, vinfo = step(pv)
         torch.cuda.synchronize()
@@ -462,9 +467,35 @@ def main():
                          "unpack_ratio": round(vinfo[0]["unpack_ratio"], 4),
                          "ms_per_step": round(tv * 1e3, 4), "tops": round(2.0 * M * N * K * nb / tv / 1e12, 3)}
 
-    # dominant kernel: the unpacked int8 GEMM of the warm steps (events above)
+    # the other digit format on the same plan (where fp6 applies): whole step and GEMM
+    formats = {}
+    if fp6 or pr.bits <= 4:
+        for dg in ("int8", "fp6"):
+            pd = prm(pr.strat_a, pr.strat_b, dg)
+            try:
+                for _ in range(2):
+                    step(pd)
+            except B.ImunpackError:
+                continue
+            dev = HipEvents(2 * max(1, args.pair_steps))
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for i in range(max(1, args.pair_steps)):
+                B.set_gemm_events(dev.ev[2 * i], dev.ev[2 * i + 1])
+                step(pd)
+            torch.cuda.synchronize()
+            B.set_gemm_events(None, None)
+            td = (time.perf_counter() - t1) / max(1, args.pair_steps)
+            gd = sum(dev.elapsed_ms(2 * i, 2 * i + 1) for i in range(max(1, args.pair_steps))) / max(1, args.pair_steps)
+            dev.close()
+            formats[dg] = {"ms_per_step": round(td * 1e3, 4), "tops": round(2.0 * M * N * K * nb / td / 1e12, 3),
+                           "gemm_us": round(gd * 1e3, 2)}
+
+    # dominant kernel: the unpacked digit GEMM of the warm steps (events above),
+    # against the dense MFMA peak of its operand type
     gemm_ops = sum(2.0 * f["m_u"] * f["k_u"] * f["n_u"] for f in infos)  # every batch entry
     gemm_tops = gemm_ops / t_gemm / 1e12
+    peak = FP6_PEAK_TFLOPS if fp6 else INT8_PEAK_TOPS
     tr = GEMM_TRAFFIC.get(pr.name)
     traffic = tr["bytes_per_launch"] if tr and tr["source_sha256"] == gemm_source_sha() else None
 
@@ -480,11 +511,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": "fp6" if fp6 else "i8",
         "data": "synthetic",
         "config": {"workload": f"{pr.name}: A {M}x{K} {pr.a.dtype} ({pr.a.layout}) @ B {K}x{N} {pr.b.dtype} "
                                f"({pr.b.layout}), beta={pr.beta} b={pr.bits} p={pr.p_num}/{pr.p_den} "
-                               f"{pr.strat_a}/{pr.strat_b}",
+                               f"{pr.strat_a}/{pr.strat_b}, digits {'fp6 (e2m3)' if fp6 else 'int8'}",
                    "M": M, "K": K, "N": N, "batch": nb},
         "warm": {"ms_per_step": round(t_step * 1e3, 4), "tops": round(eff(t_step), 3),
                  "gemm_us": round(t_gemm * 1e6, 2)},
@@ -500,10 +531,11 @@ def main():
         "plan": {"choice": list(info["choice"]), "m_u": info["m_u"], "k_u": info["k_u"], "n_u": info["n_u"],
                  "k_pad": info["k_pad"], "segments": info["n_seg"]},
         "gemm_pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
+        "digit_formats": formats,
         "stages_us": stages_us,
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (imu_unpacked_gemm)",
-                     "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+        "roofline": {"bound": "mfma", "kernel": f"gemm_kernel ({'fp6' if fp6 else 'int8'} digits, imu_unpacked_gemm)",
+                     "achieved": round(gemm_tops, 2), "peak": peak, "unit": "TFLOP/s" if fp6 else "TOP/s",
+                     "frac": round(gemm_tops / peak, 4), "traffic": traffic,
                      "launch_us": round(t_gemm * 1e6, 2), "ops_per_launch": gemm_ops},
     }
     if nb == 1 and pr.b.layout == "transposed":

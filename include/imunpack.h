@@ -33,8 +33,9 @@
  *   latched in the operand's statistics and returned at the next wait.
  * - The integer result C is defined modulo 2^32 (two's complement int32),
  *   which equals the exact product whenever it fits in int32.  There is no
- *   overflow status: the int8 x int8 -> int32 MFMA products and the int32
- *   shift-and-add fold never form the product in wider integers, so an exact
+ *   overflow status: the digit products (int8 -> int32 MFMA, or fp6 -> fp32
+ *   MFMA with exact integer partial sums below 2^24 moved into int32) and
+ *   the int32 shift-and-add fold never form the product in wider integers, so an exact
  *   overflow test would need a second, wider product.  A caller can bound
  *   |C| <= K * max|q_A| * max|q_B| from the statistics headers (maxkey and r).
  * - Batched operands (batch > 1) are independent problems: each batch entry
@@ -97,6 +98,16 @@ typedef struct {
   int64_t batch, batch_stride;
 } imu_matrix;
 
+/* Digit format of the unpacked operands.  INT8: one signed byte per digit,
+ * products on the int8 MFMA.  FP6: each digit as its e2m3 code (every integer
+ * |d| <= 7 is exact in e2m3: sign bit 5, magnitudes 0..7 as 0, 8, 16, 20, 24,
+ * 26, 28, 30), six bits per position, products on the f8f6f4 MFMA with fp32
+ * accumulation; every partial sum is an integer below 2^24 in magnitude, so
+ * the result is the same integer product.  FP6 needs bits <= 4 and both
+ * operands K-contiguous (A IMU_NORMAL, B IMU_TRANSPOSED).  AUTO: FP6 where it
+ * applies, else INT8. */
+typedef enum { IMU_DIGITS_AUTO = 0, IMU_DIGITS_INT8 = 1, IMU_DIGITS_FP6 = 2 } imu_digits;
+
 /* beta >= 1: the integer the p-percentile magnitude maps to.
  * p = p_num / p_den in (0, 1], held as a ratio of integers.
  * bits in [2, 8]: an in-range code satisfies |q| <= 2^(bits-1) - 1; unpacked
@@ -111,6 +122,8 @@ typedef struct {
                    quantizer of the page's ablation rows ("Measured effects":
                    clipping at the 99.5-percentile): q = clamp(rne(fl32(x r)),
                    -beta, beta), so no code exceeds beta and none is an error */
+  int32_t digits; /* imu_digits: format of the unpacked operands (IMU_DIGITS_FP6
+                     where it does not apply: IMU_ERR_UNSUPPORTED) */
 } imu_params;
 
 /* Statistics of one operand prepared ahead of a call by imu_prepare_operand
@@ -135,7 +148,7 @@ typedef struct {
   int64_t a_offset, b_offset;/* byte offsets of this entry in the unpacked buffers */
   int32_t n_seg;             /* number of exponent segments of K' */
   int32_t choice_a, choice_b;/* imu_candidate chosen for A and B */
-  int32_t pad_;
+  int32_t digits;            /* format of A' and B'^T: IMU_DIGITS_INT8 or IMU_DIGITS_FP6 */
   double unpack_ratio;       /* M'K'N' / (MKN) */
   int64_t pair_sizes[25][3]; /* (M',K',N') of every candidate pair, A-major (5 x 5); -1 if not allowed */
 } imu_plan_info;
@@ -220,30 +233,40 @@ imu_status imu_plan_unpack(const imu_matrix* a, const imu_matrix* b, const imu_p
                            void* stats_a, void* stats_b, void* plan,
                            imu_plan_info* info /* host, batch entries */, hipStream_t stream);
 
-/* Unpack one operand into int8 digits ("Approach": out-of-range integers
+/* Unpack one operand into its digits ("Approach": out-of-range integers
  * decomposed into several in-range low bit-width integers in extra rows or
- * columns; summary: "larger matrices").  operand 0 = A -> A' (m_alloc x k_pad per
- * entry), operand 1 = B -> B'^T (n_alloc x k_pad per entry), each entry at
- * info.a_offset / info.b_offset of x_u.  B'^T is row-major.  A' is stored in
+ * columns; summary: "larger matrices").  operand 0 = A -> A' (m_alloc x k_pad
+ * per entry), operand 1 = B -> B'^T (n_alloc x k_pad per entry), each entry at
+ * info.a_offset / info.b_offset of x_u, in the plan's digit format
+ * (info.digits; fp6 only for A IMU_NORMAL, B IMU_TRANSPOSED).
+ * int8 digits: one byte per position.  B'^T is row-major.  A' is stored in
  * MFMA fragment order: 1 KB blocks of 32 rows x 32 K' bytes, ordered by row
- * block then K' block, block (rb, c) at byte (rb * k_pad/32 + c) * 1024; inside
- * a block, bytes [16h, 16h + 16) of the block's row r are at 16 * (r + 32h)
- * (h = 0, 1).  Rows are level-major (original lines
+ * block then K' block, block (rb, c) at byte (rb * k_pad/32 + c) * 1024;
+ * inside a block, bytes [16h, 16h + 16) of the block's row r are at
+ * 16 * (r + 32h) (h = 0, 1).
+ * fp6 digits: the e2m3 code of each digit (imu_digits), six bits per position.
+ * A row of B'^T is a bit stream of 3/4 k_pad bytes, position p at bits
+ * [6p, 6p + 6) (little endian).  A' takes 1536-byte blocks of 32 rows x 64
+ * positions, block (rb, c) at byte (rb * k_pad/64 + c) * 1536; inside a block,
+ * the 24 bytes at 24 * (r + 32h) hold positions 32h .. 32h + 31 of the block's
+ * row r as such a stream.
+ * Rows are level-major (original lines
  * first, then level 1 lines, ...).  A's rows keep their index order inside a
  * level; B's columns (the rows of B'^T) are in depth order, descending depth
  * then index: row j < N of B'^T is the column at position j of that order, and
  * level w >= 1 of the column at position j is row n_base + (columns deeper than
  * 1, ..., w-1, summed) + j.  Columns are the exponent segments of K'
- * (e = v + v' ascending, then k, then v), each padded with zero bytes to a
- * multiple of 128.  Every byte of the valid rows is written. */
+ * (e = v + v' ascending, then k, then v), each padded with zero digits to a
+ * multiple of 128 positions.  Every byte of the valid rows is written. */
 imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p,
                       const void* stats, const void* plan, const imu_plan_info* info,
                       int8_t* x_u, hipStream_t stream);
 
 /* Low bit-width GEMMs on the unpacked operands with the shift-and-accumulate
  * fold and dequantization ("Approach": power-of-two scaling and summation
- * reproduce the integer GEMM exactly).  For each exponent segment e the int8
- * MFMA product P_e = A'[:,K'_e] . B'[K'_e,:] is accumulated as
+ * reproduce the integer GEMM exactly).  For each exponent segment e the digit
+ * product P_e = A'[:,K'_e] . B'[K'_e,:] (int8 MFMA, or fp6 MFMA into fp32
+ * partial sums of at most 2048 * 128 positions, moved into int32) is accumulated as
  * acc = acc * 2^(bits-1) + P_e (from the highest e down); each unpacked
  * element (i,u),(n,w) then adds acc << ((bits-1)(u+w)) into C[i,n] (mod 2^32).
  * c: int32 M x N row-major per entry (ldc elements per row, entries

@@ -28,6 +28,7 @@ F32, BF16 = 0, 1
 NORMAL, TRANSPOSED = 0, 1
 STRATEGY = {"row": 0, "col": 1, "mix": 2, "greedy": 3}
 CANDIDATES = ("row", "col", "cr", "rc", "greedy")
+DIGITS = {"auto": 0, "int8": 1, "fp6": 2}  # imu_digits
 
 
 class ImunpackError(RuntimeError):
@@ -45,7 +46,7 @@ class ImuMatrix(ctypes.Structure):
 class ImuParams(ctypes.Structure):
     _fields_ = [("beta", ctypes.c_int32), ("p_num", ctypes.c_int32), ("p_den", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("gamma", ctypes.c_int32), ("strat_a", ctypes.c_int32),
-                ("strat_b", ctypes.c_int32), ("clip", ctypes.c_int32)]
+                ("strat_b", ctypes.c_int32), ("clip", ctypes.c_int32), ("digits", ctypes.c_int32)]
 
 
 class ImuPrepared(ctypes.Structure):
@@ -59,11 +60,11 @@ class ImuPlanInfo(ctypes.Structure):
                 ("m_base", ctypes.c_int64), ("n_base", ctypes.c_int64),
                 ("a_offset", ctypes.c_int64), ("b_offset", ctypes.c_int64),
                 ("n_seg", ctypes.c_int32), ("choice_a", ctypes.c_int32), ("choice_b", ctypes.c_int32),
-                ("pad_", ctypes.c_int32), ("unpack_ratio", ctypes.c_double),
+                ("digits", ctypes.c_int32), ("unpack_ratio", ctypes.c_double),
                 ("pair_sizes", (ctypes.c_int64 * 3) * 25)]
 
     def as_dict(self) -> dict:
-        d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("pair_sizes", "pad_")}
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "pair_sizes"}
         d["choice"] = (CANDIDATES[self.choice_a], CANDIDATES[self.choice_b])
         pairs = {}
         for ia, ca in enumerate(CANDIDATES):
@@ -237,8 +238,9 @@ class Matrix:
 
 
 def params(beta: int = 15, bits: int = 5, p: Tuple[int, int] = (95, 100), strat_a: str = "mix",
-           strat_b: str = "mix", gamma: int = 2, clip: bool = False) -> ImuParams:
-    return ImuParams(beta, p[0], p[1], bits, gamma, STRATEGY[strat_a], STRATEGY[strat_b], 1 if clip else 0)
+           strat_b: str = "mix", gamma: int = 2, clip: bool = False, digits: str = "auto") -> ImuParams:
+    return ImuParams(beta, p[0], p[1], bits, gamma, STRATEGY[strat_a], STRATEGY[strat_b], 1 if clip else 0,
+                     DIGITS[digits])
 
 
 def _as_matrix(x) -> Matrix:
@@ -357,12 +359,14 @@ def unpacked_bytes(plan: Plan, operand: int) -> int:
     last = plan.info[plan.batch - 1]
     rows = last.m_alloc if operand == 0 else last.n_alloc
     off = last.a_offset if operand == 0 else last.b_offset
-    return int(off + (rows * last.k_pad + 255) // 256 * 256)
+    row_bytes = last.k_pad * 3 // 4 if last.digits == DIGITS["fp6"] else last.k_pad
+    return int(off + (rows * row_bytes + 255) // 256 * 256)
 
 
 def unpack(x, operand: int, p: ImuParams, stats: Stats, plan: Plan, stream=None) -> torch.Tensor:
-    """Digits of one operand as int8 (imu_unpack): A' (operand 0) or B'^T (operand 1),
-    all batch entries in one flat buffer at info[b].a_offset / b_offset."""
+    """Digits of one operand (imu_unpack): A' (operand 0) or B'^T (operand 1) as
+    int8 bytes or fp6 codes (the plan's format, info[b].digits), all batch
+    entries in one flat byte buffer at info[b].a_offset / b_offset."""
     x = _as_matrix(x)
     out = torch.empty(unpacked_bytes(plan, operand), dtype=torch.int8, device=x.stored.device)
     m = x.c()

@@ -93,10 +93,21 @@ imu_status check_params(const imu_params* p) {
   if (p->p_num < 1 || p->p_num > p->p_den) return fail(IMU_ERR_INVALID_ARG, "p = p_num/p_den must be in (0, 1]");
   if (p->gamma < 0 || p->gamma > 1000000) return fail(IMU_ERR_INVALID_ARG, "gamma must be in [0, 1e6]");
   if (p->clip != 0 && p->clip != 1) return fail(IMU_ERR_INVALID_ARG, "clip must be 0 or 1");
+  if (p->digits != IMU_DIGITS_AUTO && p->digits != IMU_DIGITS_INT8 && p->digits != IMU_DIGITS_FP6)
+    return fail(IMU_ERR_INVALID_ARG, "digits must be IMU_DIGITS_AUTO, IMU_DIGITS_INT8 or IMU_DIGITS_FP6");
   for (int s : {p->strat_a, p->strat_b})
     if (s != IMU_ROW && s != IMU_COL && s != IMU_MIX && s != IMU_GREEDY)
       return fail(IMU_ERR_INVALID_ARG, "strategy must be IMU_ROW, IMU_COL, IMU_MIX or IMU_GREEDY");
   return IMU_OK;
+}
+
+// fp6 digits apply when every digit is at most 7 in magnitude (bits <= 4) and
+// both operands are K-contiguous, the layout the fp6 unpack is written for.
+bool fp6_applies(const Operand& oa, const Operand& ob, const imu_params* p) {
+  return p->bits <= 4 && !oa.tr && ob.tr;
+}
+int digit_fmt(const Operand& oa, const Operand& ob, const imu_params* p) {
+  return p->digits != IMU_DIGITS_INT8 && fp6_applies(oa, ob, p) ? kDigitsFp6 : kDigitsInt8;
 }
 
 imu_status check_pair(const imu_matrix* a, const imu_matrix* b, const imu_params* p, Operand* oa,
@@ -111,6 +122,8 @@ imu_status check_pair(const imu_matrix* a, const imu_matrix* b, const imu_params
       (p->strat_b == IMU_GREEDY && b->rows + b->cols > kGreedyMaxLines))
     return fail(IMU_ERR_UNSUPPORTED, "the greedy planner holds at most %d rows + columns of an operand",
                 kGreedyMaxLines);
+  if (p->digits == IMU_DIGITS_FP6 && !fp6_applies(*oa, *ob, p))
+    return fail(IMU_ERR_UNSUPPORTED, "fp6 digits need bits <= 4, A IMU_NORMAL and B IMU_TRANSPOSED");
   return IMU_OK;
 }
 
@@ -254,6 +267,7 @@ imu_status plan_launch(const Operand& oa, const Operand& ob, const imu_params* p
   pa.strat_a = p->strat_a;
   pa.strat_b = p->strat_b;
   pa.bits = p->bits;
+  pa.fmt = digit_fmt(oa, ob, p);
   pa.host_hdr = host_hdr;
   pa.host_tag = host_tag;
   IMU_HIP(launch_plan(pa, done, s));
@@ -377,6 +391,7 @@ imu_status finish_plan(const Operand& oa, const Operand& ob, const uint8_t* hdrs
       f.n_seg = h->n_seg;
       f.choice_a = h->choice_a;
       f.choice_b = h->choice_b;
+      f.digits = h->fmt == kDigitsFp6 ? IMU_DIGITS_FP6 : IMU_DIGITS_INT8;
       f.unpack_ratio = (double)h->m_u * (double)h->k_u * (double)h->n_u /
                        ((double)oa.R * (double)oa.C * (double)ob.C);
       std::memcpy(f.pair_sizes, h->pair, sizeof(f.pair_sizes));
@@ -410,7 +425,7 @@ imu_status plan_impl(const Operand& oa, const Operand& ob, const imu_params* p, 
 // after all A' entries of x_u; cap: bytes available at x_u.
 UnpackArgs unpack_args(const Operand& op, int operand, const imu_params* p, const uint8_t* stats,
                        const uint8_t* plan, int64_t M, int64_t K, int64_t N, int8_t* x_u, bool after_a,
-                       int64_t cap) {
+                       int64_t cap, int fmt) {
   const StatsLayout L = stats_layout(op.R, op.C);
   const imu_matrix* x = op.m;
   UnpackArgs u{};
@@ -441,13 +456,14 @@ UnpackArgs unpack_args(const Operand& op, int operand, const imu_params* p, cons
   u.cap = cap;
   u.beta = p->beta;
   u.clip = p->clip;
+  u.fmt = fmt;
   return u;
 }
 
 imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, const uint8_t* stats,
                        const uint8_t* plan, int64_t M, int64_t K, int64_t N, int8_t* x_u, bool after_a,
-                       int64_t cap, hipStream_t s) {
-  const UnpackArgs u = unpack_args(op, operand, p, stats, plan, M, K, N, x_u, after_a, cap);
+                       int64_t cap, int fmt, hipStream_t s) {
+  const UnpackArgs u = unpack_args(op, operand, p, stats, plan, M, K, N, x_u, after_a, cap, fmt);
   IMU_HIP(launch_unpack(op.dtype, p->bits, &u, 1, (int)op.m->batch, s));
   return IMU_OK;
 }
@@ -455,6 +471,7 @@ imu_status unpack_impl(const Operand& op, int operand, const imu_params* p, cons
 // Tile-relevant sizes of one batch entry's plan.
 struct EntrySizes {
   int64_t m_base, n_base, m_alloc, n_alloc;
+  int fmt;
 };
 
 // GEMM launches for `batch` entries whose sizes come from get(b) (the staged
@@ -478,6 +495,8 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
     const EntrySizes f = get(b);
     if (f.m_base % 256 || f.n_base % 128 || f.m_alloc % 256 || f.n_alloc % 128)
       return fail(IMU_ERR_INVALID_ARG, "plan sizes are not tile multiples");
+    if (f.fmt != get(0).fmt || (f.fmt != kDigitsInt8 && f.fmt != kDigitsFp6))
+      return fail(IMU_ERR_INVALID_ARG, "the entries' digit formats differ or are unknown");
     base_tiles = std::max(base_tiles, (f.m_base / 256) * (f.n_base / 128));
     base_total += (f.m_base / 256) * (f.n_base / 128);
   }
@@ -522,6 +541,7 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   g.N = N;
   g.bits = p->bits;
   g.fold_cols = fold_cols ? 1 : 0;
+  g.fmt = get(0).fmt;
   // Tile order: each XCD takes a run of tiles covering G tile rows; its L2
   // then fills G row panels of A' and about T / (8 G) column panels of B'^T,
   // which is least near G = sqrt(T BN / (8 BM)) (rounded to a power of two).
@@ -560,7 +580,8 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
 imu_status check_info(const imu_plan_info* info, int64_t batch, int64_t M, int64_t K, int64_t N) {
   if (!info) return fail(IMU_ERR_INVALID_ARG, "info is NULL");
   for (int64_t b = 0; b < batch; ++b)
-    if (info[b].m != M || info[b].k != K || info[b].n != N || info[b].k_pad <= 0)
+    if (info[b].m != M || info[b].k != K || info[b].n != N || info[b].k_pad <= 0 ||
+        (info[b].digits != IMU_DIGITS_INT8 && info[b].digits != IMU_DIGITS_FP6) || info[b].digits != info[0].digits)
       return fail(IMU_ERR_INVALID_ARG, "info does not describe this problem");
   return IMU_OK;
 }
@@ -618,14 +639,15 @@ imu_status matmul_impl(const Operand& oa, const Operand& ob, const imu_params* p
   const uint8_t* hdrs = nullptr;
   IMU_TRY(plan_staged(*st, oa, ob, p, ra, rb, plan, stream, &hdrs));
   int8_t* region = reinterpret_cast<int8_t*>(w + fixed);
+  const int fmt = digit_fmt(oa, ob, p);  // the format the plan was made for
   const int64_t cap = ws_bytes - fixed;
   if (oa.dtype == ob.dtype) {  // both operands in one launch
-    const UnpackArgs u[2] = {unpack_args(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap),
-                             unpack_args(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap)};
+    const UnpackArgs u[2] = {unpack_args(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap, fmt),
+                             unpack_args(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap, fmt)};
     IMU_HIP(launch_unpack(oa.dtype, p->bits, u, 2, (int)batch, stream));
   } else {
-    IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap, stream));
-    IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap, stream));
+    IMU_TRY(unpack_impl(oa, 0, p, stats_a, plan, oa.R, oa.C, ob.C, region, false, cap, fmt, stream));
+    IMU_TRY(unpack_impl(ob, 1, p, stats_b, plan, oa.R, oa.C, ob.C, region, true, cap, fmt, stream));
   }
   IMU_TRY(wait_headers(*st, (int)batch, stream));
   int64_t a_bytes = 0, b_bytes = 0;
@@ -639,7 +661,7 @@ imu_status matmul_impl(const Operand& oa, const Operand& ob, const imu_params* p
   int8_t* b_u = region + a_bytes;
   auto sizes = [hdrs](int64_t b) {
     const PlanHeader* h = reinterpret_cast<const PlanHeader*>(hdrs + (size_t)b * kPlanHeaderStride);
-    return EntrySizes{h->m_base, h->n_base, h->m_alloc, h->n_alloc};
+    return EntrySizes{h->m_base, h->n_base, h->m_alloc, h->n_alloc, h->fmt};
   };
   return gemm_impl(a_u, b_u, p, stats_a, stats_b, plan, oa.R, oa.C, ob.C, batch, sizes, c, ob.C, oa.R * ob.C, out,
                    stream);
@@ -797,8 +819,12 @@ imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p,
   const int64_t M = operand == 0 ? op.R : info[0].m, K = operand == 0 ? op.C : op.R,
                 N = operand == 0 ? info[0].n : op.C;
   IMU_TRY(check_info(info, x->batch, M, K, N));
+  const int fmt = info[0].digits == IMU_DIGITS_FP6 ? kDigitsFp6 : kDigitsInt8;
+  // the fp6 unpack reads K-contiguous operands: A IMU_NORMAL, B IMU_TRANSPOSED
+  if (fmt == kDigitsFp6 && (p->bits > 4 || op.tr != (operand == 1)))
+    return fail(IMU_ERR_INVALID_ARG, "info holds fp6 digits, which this operand's layout or bits cannot give");
   return unpack_impl(op, operand, p, static_cast<const uint8_t*>(stats), static_cast<const uint8_t*>(plan), M, K,
-                     N, x_u, false, INT64_MAX, stream);
+                     N, x_u, false, INT64_MAX, fmt, stream);
 }
 
 imu_status imu_unpacked_gemm(const int8_t* a_u, const int8_t* b_u, const imu_params* p, const void* stats_a,
@@ -814,7 +840,8 @@ imu_status imu_unpacked_gemm(const int8_t* a_u, const int8_t* b_u, const imu_par
   if (batch > 1 && c_batch_stride < (info[0].m - 1) * ldc + info[0].n)
     return fail(IMU_ERR_INVALID_ARG, "c_batch_stride overlaps batch entries");
   auto sizes = [info](int64_t b) {
-    return EntrySizes{info[b].m_base, info[b].n_base, info[b].m_alloc, info[b].n_alloc};
+    return EntrySizes{info[b].m_base, info[b].n_base, info[b].m_alloc, info[b].n_alloc,
+                      info[b].digits == IMU_DIGITS_FP6 ? kDigitsFp6 : kDigitsInt8};
   };
   return gemm_impl(a_u, b_u, p, static_cast<const uint8_t*>(stats_a), static_cast<const uint8_t*>(stats_b),
                    static_cast<const uint8_t*>(plan), info[0].m, info[0].k, info[0].n, batch, sizes, c, ldc,

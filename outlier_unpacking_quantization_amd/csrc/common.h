@@ -14,7 +14,7 @@ namespace imu {
 // ---------------------------------------------------------------------------
 constexpr int kHistBins = 32768;    // 15-bit magnitude key of bf16 (and the top of fp32)
 constexpr int kHistCoarse = 256;    // coarse counts (128 keys each) kept after the key bins
-constexpr int kKPad = 128;          // every exponent segment of K' is padded to this many bytes
+constexpr int kKPad = 128;          // every exponent segment of K' is padded to this many positions
 constexpr int kMaxSeg = 64;         // room for 2*max_digits(2)-1 = 61 segments
 constexpr int kStatusNonfinite = 1; // device status bits
 constexpr int kStatusRange = 2;
@@ -82,7 +82,7 @@ struct PlanHeader {
   int64_t m_u, k_u, n_u;
   int64_t m_base, n_base, m_alloc, n_alloc;
   int64_t k_pad;
-  int32_t lev_a, lev_b, emax, pad0;
+  int32_t lev_a, lev_b, emax, fmt;  // fmt: digit format of A' and B'^T (kDigitsInt8 / kDigitsFp6)
   int64_t pair[kNumPairs][3];
   int64_t seg_off[kMaxSeg + 1];
   int32_t seg_len[kMaxSeg];
@@ -150,6 +150,28 @@ __host__ __device__ inline int64_t frag_row_offset(int64_t row, int64_t k_pad) {
 }
 __host__ __device__ inline int64_t frag_pos_offset(int64_t p) {
   return (p >> 5) * 1024 + ((p >> 4) & 1) * 512 + (p & 15);
+}
+
+// Digit formats of the unpacked operands.  int8: one byte per position.  fp6:
+// the e2m3 code of each digit (|d| <= 7 is exact; sign in bit 5, magnitudes
+// 0..7 as 0, 8, 16, 20, 24, 26, 28, 30), six bits per position, for bits <= 4.
+// B'^T rows are then bit streams (position p at bits [6p, 6p + 6) of the
+// row, 3/4 k_pad bytes); A' keeps the MFMA fragment order of the 32 x 64
+// operand of v_mfma_f32_32x32x64_f8f6f4: 1536-byte blocks of 32 rows x 64
+// positions, ordered by row block then position block, where lane
+// l = row % 32 + 32 ((p % 64) / 32) holds 24 bytes with position p % 32 at bits
+// [6 (p % 32), 6 (p % 32) + 6).
+constexpr int kDigitsInt8 = 0, kDigitsFp6 = 1;
+constexpr uint64_t kFp6Mag = 0x1E1C1A1814100800ull;  // byte m: e2m3 magnitude code of m
+__host__ __device__ inline int64_t unpacked_row_bytes(int64_t k_pad, int fmt) {
+  return fmt == kDigitsFp6 ? k_pad / 4 * 3 : k_pad;
+}
+__host__ __device__ inline int64_t frag6_row_offset(int64_t row, int64_t k_pad) {
+  return (row >> 5) * (k_pad >> 6) * 1536 + (row & 31) * 24;
+}
+// position p a multiple of 16: the 12 bytes of positions p .. p + 15 in a lane
+__host__ __device__ inline int64_t frag6_pos_offset(int64_t p) {
+  return (p >> 6) * 1536 + ((p >> 5) & 1) * 768 + ((p >> 4) & 1) * 12;
 }
 
 // GEMM macro tile (rows of A' x rows of B'^T) used for a problem of this shape;

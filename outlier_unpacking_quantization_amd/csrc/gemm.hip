@@ -48,14 +48,19 @@ namespace imu {
 
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int FR = 2;  // 32-row A fragments per wave
 constexpr int BM = 128 * FR, BN = 128, BK = 128;
 constexpr int kThreads = 256;
 constexpr int BSTR = BK + 16;  // LDS bytes per staged B row
+constexpr int BSTR6 = BK / 4 * 3 + 8;  // fp6: 96 bytes of a step plus 8 (row r starts at bank 26 r mod 32)
+constexpr int kF32Steps = 2048;        // fp6: steps an fp32 partial sum may take (2048 * 128 * 49 < 2^24)
 constexpr int kXcds = 8;
 static_assert(BK == kKPad, "a K step must not straddle exponent segments");
 
@@ -112,6 +117,19 @@ __device__ inline void quad_transpose(int (&x)[4]) {
   x[1] = odd ? x[1] : s[0];
   x[2] = odd ? s[3] : x[2];
   x[3] = odd ? x[3] : s[2];
+}
+
+// fp6: the exact integer partial sums of the fp32 accumulators move into
+// the int32 ones (at the same exponent), which leaves the fp32 ones zero.
+__device__ inline void flush_f32(v16i (&acc)[FR][4], v16f (&accf)[FR][4]) {
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = (int)((uint32_t)acc[i][j][r] + (uint32_t)(int)accf[i][j][r]);
+      accf[i][j] = v16f{0.f};
+    }
 }
 
 __device__ inline void shift_acc(v16i (&acc)[FR][4], int sh) {
@@ -206,15 +224,24 @@ constexpr int kMaxLevels = 32;  // digits of an int32 code in base 2^(bits-1), b
 // FOLD: the base pass also folds the extra columns of entries whose plan has
 // extra columns only (their levels w > 0 land on the tile's own columns), so
 // those entries need no atomic pass.
-template <bool FOLD>
+// F6: fp6 digits (e2m3 codes) on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+// scales): a K step is two substeps of 64 positions; the fp32 accumulators
+// hold one exponent's partial sums (integers below 2^24 in magnitude, so
+// exact), which move into the int32 Horner accumulators at every exponent
+// change and every kF32Steps steps.
+template <bool FOLD, bool F6>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * BSTR];
+  constexpr int SB = F6 ? BSTR6 : BSTR;  // LDS bytes per staged B row
+  constexpr int NQ = F6 ? 2 : 4;         // MFMA substeps per K step
+  __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * SB];
   // this workgroup's batch entry: sizes from its plan header (scalar loads)
   const int entry = blockIdx.y;
   const uint8_t* hdr = g.plan + (int64_t)entry * kPlanHeaderStride;
   const HdrC ph = (HdrC)hdr;
   const int64_t m_alloc = ph->m_alloc, n_alloc = ph->n_alloc, m_base = ph->m_base, n_base = ph->n_base;
   const int64_t kp = ph->k_pad;
+  if (ph->fmt != (F6 ? kDigitsFp6 : kDigitsInt8)) return;  // the host launches the plan's format
+  const int64_t rowb = F6 ? kp / 4 * 3 : kp;                // bytes per B'^T row
   const bool rowx = m_alloc > m_base, colx = n_alloc > n_base;
   // the atomic pass serves entries with extra rows (and their extra columns),
   // and entries with extra columns only unless those are folded in the base
@@ -234,8 +261,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   int64_t a_off = 0, b_off = 0;
   for (int e = 0; e < entry; ++e) {
     const HdrC h = (HdrC)(g.plan + (int64_t)e * kPlanHeaderStride);
-    a_off += round_up(h->m_alloc * h->k_pad, 256);
-    b_off += round_up(h->n_alloc * h->k_pad, 256);
+    const int64_t rb = h->fmt == kDigitsFp6 ? h->k_pad / 4 * 3 : h->k_pad;
+    a_off += round_up(h->m_alloc * rb, 256);
+    b_off += round_up(h->n_alloc * rb, 256);
   }
   const uint8_t* pe = g.plan + g.headers_bytes + entry * g.entry_stride;
   const int32_t* amap = reinterpret_cast<const int32_t*>(pe + g.amap_off);
@@ -250,31 +278,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int shift = g.bits - 1;
 
   // A' fragment f (rows row0 + 32f ..) of K substep q at step offset k is the
-  // contiguous 1 KB at block (row0/32 + f, k/32 + q); lane l holds bytes
-  // [16l, 16l + 16) of it.
-  const int8_t* ga = g.a_u + a_off + frag_row_offset(row0, kp) + lane * 16;
-  const int64_t ga_f = (kp >> 5) * 1024;
-  // B staging: thread copies rows br + 32j (j < 4), bytes [bc, bc + 16) of the step
-  const int br = tid >> 3, bc = (tid & 7) * 16;
-  const int8_t* gb = g.b_u + b_off + (col0 + br) * kp + bc;
-  const int64_t gb_j = 32 * kp;
+  // contiguous block (row0/32 + f, k/32 + q) of 1 KB (int8: lane l holds bytes
+  // [16l, 16l + 16)) or (row0/32 + f, k/64 + q) of 1536 bytes (fp6: lane l
+  // holds bytes [24l, 24l + 24)).
+  const int8_t* ga = g.a_u + a_off + (F6 ? frag6_row_offset(row0, kp) + lane * 24 : frag_row_offset(row0, kp) + lane * 16);
+  const int64_t ga_f = F6 ? (kp >> 6) * 1536 : (kp >> 5) * 1024;
+  // B staging.  int8: thread copies rows br + 32j (j < 4), bytes [bc, bc + 16)
+  // of the step.  fp6: row br, bytes [bc, bc + 48) of the step's 96.
+  constexpr int NB = F6 ? 1 : 4;  // B rows a thread stages
+  const int br = F6 ? tid >> 1 : tid >> 3, bc = F6 ? (tid & 1) * 48 : (tid & 7) * 16;
+  const int8_t* gb = g.b_u + b_off + (col0 + br) * rowb + bc;
+  const int64_t gb_j = 32 * rowb;
   const int8_t* gbase = g.b_u + b_off + bc;
-  const int sb_w = br * BSTR + bc;
+  const int sb_w = br * SB + bc;
   // B fragment j (columns col0 + 32j + lane%32) of substep q
-  const int sb_r = (lane & 31) * BSTR + 16 * (lane >> 5);
+  const int sb_r = (lane & 31) * SB + (F6 ? 24 : 16) * (lane >> 5);
   const int64_t k_last = kp - BK;  // loads past the walk re-read the last step (never used)
 
   v16i acc[FR][4];
+  v16f accf[FR][4];  // fp6: the current exponent's partial sums
 #pragma unroll
   for (int i = 0; i < FR; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{0}, accf[i][j] = v16f{0.f};
 
   const SegTable off = (SegTable)ph->seg_off;
   const int nseg = ph->n_seg;
   // levels of the tile's columns (1 unless this entry folds extra columns)
   int nlev = 1;
-  int64_t gbo[4];    // byte offsets of the B staging rows at lb's level (FOLD)
+  int64_t gbo[NB];   // byte offsets of the B staging rows at lb's level (FOLD)
   uint32_t bvm = 0xF, bvl = 0xF;  // rows present at lb's level / in the last load (FOLD)
   if constexpr (FOLD) {
     // levels present in the tile: B's columns are in depth order, so level w
@@ -291,10 +323,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     const int64_t cnt = w == 0 ? n_alloc : (int64_t)ph->lvcnt_b[w];
     const int64_t base = w == 0 ? 0 : ph->lvbase_b[w];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int c = br + 32 * j;
       const bool live = col0 + c < cnt;
-      gbo[j] = (base + col0 + (live ? c : 0)) * kp;
+      gbo[j] = (base + col0 + (live ? c : 0)) * rowb;
       bvm |= (uint32_t)live << j;
     }
   };
@@ -318,28 +350,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   Cur la = cc, lb = cc;  // A loads (one step ahead), B loads (two ahead)
   int lbw = 0;           // level of lb's rows (FOLD)
 
-  v4i ar[4][FR];  // A fragments of the current step, refilled substep by substep
-  v4i bs[4];      // B staging registers
-  v4i bf[2][4];   // B fragments, double-buffered by substep
+  using Frag = std::conditional_t<F6, v8i, v4i>;  // MFMA operand (fp6: 6 of the 8 dwords)
+  Frag ar[NQ][FR];  // A fragments of the current step, refilled substep by substep
+  v4i bs[F6 ? 3 : 4];  // B staging registers
+  Frag bf[2][4];    // B fragments, double-buffered by substep
+  int f32_steps = 0;  // fp6: steps in the fp32 accumulators
 #define IMU_LOAD_A(q, k)                                                                       \
   {                                                                                            \
     const int64_t k_ = min64((k), k_last);                                                     \
-    _Pragma("unroll") for (int f = 0; f < FR; ++f) ar[q][f] =                                  \
-        *reinterpret_cast<const v4i*>(ga + f * ga_f + k_ * 32 + 1024 * (q));                   \
+    if constexpr (F6) {                                                                        \
+      _Pragma("unroll") for (int f = 0; f < FR; ++f) {                                         \
+        const int8_t* pa_ = ga + f * ga_f + k_ * 24 + 1536 * (q);                              \
+        const v2i x0 = *reinterpret_cast<const v2i*>(pa_), x1 = *reinterpret_cast<const v2i*>(pa_ + 8), \
+                  x2 = *reinterpret_cast<const v2i*>(pa_ + 16);                                \
+        ar[q][f] = Frag{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, 0, 0};                             \
+      }                                                                                        \
+    } else {                                                                                   \
+      _Pragma("unroll") for (int f = 0; f < FR; ++f) ar[q][f] =                                \
+          *reinterpret_cast<const Frag*>(ga + f * ga_f + k_ * 32 + 1024 * (q));                \
+    }                                                                                          \
   }
 #define IMU_LOAD_B(k)                                                                          \
   {                                                                                            \
-    const int64_t k_ = min64((k), k_last);                                                     \
-    if constexpr (FOLD) {                                                                      \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gbase + gbo[j] + k_); \
+    const int64_t kb_ = min64((k), k_last) / 4 * (F6 ? 3 : 4);  /* byte offset of the step */ \
+    if constexpr (F6) {                                                                        \
+      const int8_t* pb_ = (FOLD ? gbase + gbo[0] : gb) + kb_;                                  \
+      _Pragma("unroll") for (int j = 0; j < 3; ++j) bs[j] = *reinterpret_cast<const v4i*>(pb_ + 16 * j); \
+      if constexpr (FOLD) bvl = bvm;                                                           \
+    } else if constexpr (FOLD) {                                                               \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gbase + gbo[j] + kb_); \
       bvl = bvm;                                                                               \
     } else {                                                                                   \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gb + j * gb_j + k_); \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gb + j * gb_j + kb_); \
     }                                                                                          \
   }
 #define IMU_STORE_B(buf)                                                                       \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(&sB[buf][sb_w + j * 32 * BSTR]) = \
-      (!FOLD || ((bvl >> j) & 1u)) ? bs[j] : v4i{0, 0, 0, 0};
+  if constexpr (F6) {                                                                          \
+    const bool live_ = !FOLD || (bvl & 1u);                                                    \
+    _Pragma("unroll") for (int j = 0; j < 3; ++j) {                                            \
+      const v4i x_ = live_ ? bs[j] : v4i{0, 0, 0, 0};                                          \
+      *reinterpret_cast<v2i*>(&sB[buf][sb_w + 16 * j]) = v2i{x_.x, x_.y};                      \
+      *reinterpret_cast<v2i*>(&sB[buf][sb_w + 16 * j + 8]) = v2i{x_.z, x_.w};                  \
+    }                                                                                          \
+  } else {                                                                                     \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(&sB[buf][sb_w + j * 32 * SB]) = \
+        (!FOLD || ((bvl >> j) & 1u)) ? bs[j] : v4i{0, 0, 0, 0};                                \
+  }
 #define IMU_ADV_B()                                                                            \
   {                                                                                            \
     adv(lb);                                                                                   \
@@ -350,33 +406,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
       }                                                                                        \
     }                                                                                          \
   }
-#define IMU_READ_B(d, sbuf, q) \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) bf[d][j] = *reinterpret_cast<const v4i*>((sbuf) + sb_r + j * 32 * BSTR + 32 * (q));
+#define IMU_READ_B(d, sbuf, q)                                                                 \
+  if constexpr (F6) {                                                                          \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                            \
+      const int8_t* pr_ = (sbuf) + sb_r + j * 32 * SB + 48 * (q);                              \
+      const v2i x0 = *reinterpret_cast<const v2i*>(pr_), x1 = *reinterpret_cast<const v2i*>(pr_ + 8), \
+                x2 = *reinterpret_cast<const v2i*>(pr_ + 16);                                  \
+      bf[d][j] = Frag{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, 0, 0};                               \
+    }                                                                                          \
+  } else {                                                                                     \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) bf[d][j] = *reinterpret_cast<const Frag*>((sbuf) + sb_r + j * 32 * SB + 32 * (q)); \
+  }
 #define IMU_MFMA(d, q)                                                                             \
   _Pragma("unroll") for (int f = 0; f < FR; ++f)                                                   \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                    \
-    acc[f][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[q][f], bf[d][j], acc[f][j], 0, 0, 0);
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                  \
+    if constexpr (F6)                                                                              \
+      accf[f][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ar[q][f], bf[d][j], accf[f][j], 2, 2, 0, 0, 0, 0); \
+    else                                                                                           \
+      acc[f][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[q][f], bf[d][j], acc[f][j], 0, 0, 0);   \
+  }
 
+  // The prologue issues its loads in the loop's order (the last substep's A
+  // fragments after the second B load), so the loads in flight at the loop
+  // head are the same on entry and on the back edge: the wait before the B
+  // store then covers the B loads only, not the A fragments issued after them.
 #pragma unroll
-  for (int q = 0; q < 4; ++q) IMU_LOAD_A(q, la.k);
-  adv(la);
+  for (int q = 0; q < NQ - 1; ++q) IMU_LOAD_A(q, la.k);
   if constexpr (FOLD) set_level(lb.w), lbw = lb.w;
   IMU_LOAD_B(lb.k);
   IMU_ADV_B();
   IMU_STORE_B(0);
   IMU_LOAD_B(lb.k);
   IMU_ADV_B();
+  IMU_LOAD_A(NQ - 1, la.k);
+  adv(la);
   __syncthreads();
   IMU_READ_B(0, sB[0], 0);
   int prev_s = expo(cc);
   for (int64_t i = 0; i < steps; ++i) {
     if (expo(cc) != prev_s) {  // Horner: the exponents between the two steps
+      if constexpr (F6) flush_f32(acc, accf), f32_steps = 0;
       shift_acc(acc, shift * (prev_s - expo(cc)));
       prev_s = expo(cc);
     }
+    if constexpr (F6) {
+      if (f32_steps == kF32Steps) flush_f32(acc, accf), f32_steps = 0;
+      ++f32_steps;
+    }
     const int8_t* sbuf = sB[i & 1];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
+    for (int q = 0; q < NQ - 1; ++q) {
       IMU_READ_B((q + 1) & 1, sbuf, q + 1);
       __builtin_amdgcn_sched_barrier(0);
       IMU_MFMA(q & 1, q);
@@ -389,8 +468,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     __syncthreads();
     IMU_READ_B(0, sB[(i + 1) & 1], 0);
     __builtin_amdgcn_sched_barrier(0);
-    IMU_MFMA(1, 3);
-    IMU_LOAD_A(3, la.k);
+    IMU_MFMA(1, NQ - 1);
+    IMU_LOAD_A(NQ - 1, la.k);
     __builtin_amdgcn_sched_barrier(0);
     adv(la);
     adv(cc);
@@ -401,6 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 #undef IMU_READ_B
 #undef IMU_MFMA
 #undef IMU_ADV_B
+  if constexpr (F6) flush_f32(acc, accf);
   if (prev_s > 0) shift_acc(acc, shift * prev_s);  // exponents below the last non-empty segment
 
   // epilogue: accumulator register r of lane l holds element
@@ -506,12 +586,18 @@ hipError_t launch_gemm(const GemmArgs& g, int64_t tiles_x, int batch, bool fold,
     return hipGetLastError();
   }
   const dim3 grid((unsigned)tiles_x, (unsigned)batch);
-  if (fold) {
-    if (start || stop) hipExtLaunchKernelGGL(gemm_kernel<true>, grid, dim3(kThreads), 0, s, start, stop, 0, g);
-    else hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(kThreads), 0, s, g);
+  auto go = [&](auto kernel) {
+    if (start || stop) hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, start, stop, 0, g);
+    else hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, g);
+  };
+  if (g.fmt == kDigitsFp6) {
+    if (fold) go(gemm_kernel<true, true>);
+    else go(gemm_kernel<false, true>);
+  } else if (g.fmt == kDigitsInt8) {
+    if (fold) go(gemm_kernel<true, false>);
+    else go(gemm_kernel<false, false>);
   } else {
-    if (start || stop) hipExtLaunchKernelGGL(gemm_kernel<false>, grid, dim3(kThreads), 0, s, start, stop, 0, g);
-    else hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(kThreads), 0, s, g);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -8,7 +8,7 @@ namespace imu {
 // Byte offset of batch entry b inside the unpacked buffer of an operand: the
 // entries before it, each (rows x k_pad) rounded up to 256 bytes.
 __host__ __device__ inline int64_t unpacked_entry_bytes(const PlanHeader* h, int operand) {
-  return round_up((operand == 0 ? h->m_alloc : h->n_alloc) * h->k_pad, 256);
+  return round_up((operand == 0 ? h->m_alloc : h->n_alloc) * unpacked_row_bytes(h->k_pad, h->fmt), 256);
 }
 
 // quantize.hip
@@ -27,6 +27,7 @@ struct PlanArgs {  // the plan headers must be zero when the planner starts (arr
   uint8_t* plan;
   PlanLayout pl;
   int gamma, strat_a, strat_b, bits;
+  int fmt;                 // digit format the unpack and the GEMM will use (kDigitsInt8 / kDigitsFp6)
   uint8_t* host_hdr;       // pinned host copy of the headers (kPlanHeaderStride per entry), or null
   int64_t host_tag;        // written last into reserved[0] of each host copy
 };
@@ -67,6 +68,7 @@ struct UnpackArgs {
   int8_t* out;                  // start of the unpacked buffer (all batch entries)
   int after_a;                  // 1: B' entries follow all A' entries of the buffer
   int beta, clip;               // clipping quantizer: codes clamped to [-beta, beta]
+  int fmt;                      // digit format (kDigitsInt8 / kDigitsFp6): must match the plan's
   int64_t cap;                  // bytes available at out; entries that would not fit are skipped
 };
 // Operands of one dtype share a launch: launch_unpack takes one or two
@@ -95,6 +97,7 @@ struct GemmArgs {
                               // entry: add to C after that pass, or store C, folding extra columns)
   int fold_cols;              // entries with extra columns only fold them in the base pass
   int group_m;                // tile rows per group of the workgroup -> tile order (power of two)
+  int fmt;                    // digit format of every entry (kDigitsInt8 / kDigitsFp6)
 };
 // tiles_x: the largest tile count of an entry for this mode; batch entries on
 // blockIdx.y.  start / stop: events recorded as the launch starts / ends

@@ -566,6 +566,7 @@ __device__ void layout(const PlanArgs& a, int b, int64_t w, bool write_header, P
           st(&h->lev_a, (int32_t)S.lev[0]);
           st(&h->lev_b, (int32_t)S.lev[1]);
           st(&h->emax, (int32_t)(S.nseg - 1));
+          st(&h->fmt, (int32_t)a.fmt);
         }
       };
       put(E.ph, [](auto* p, auto v) __attribute__((always_inline)) { *p = v; });

@@ -119,6 +119,46 @@ __device__ inline uint32_t digit_word(float x, float r, int clip, int beta) {
   return (w & ~neg) | (((0x80808080u - w) ^ 0x80808080u) & neg);
 }
 
+// e2m3 codes of the magnitudes 0..7 held in the bytes of m4 (byte-wise lookup)
+__device__ inline uint32_t fp6_mag4(uint32_t m4) { return __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, m4); }
+
+// The fp6 digit format's staging word: the e2m3 codes of the four low digits
+// of the RTN code of x (digit t in byte t), for codes with at most four digits.
+template <int BITS>
+__device__ inline uint32_t digit_word6(float x, float r, int clip, int beta) {
+  static_assert(BITS <= 4, "e2m3 holds digits up to 7");
+  const float y = x * r;
+  const float ya = clip ? __builtin_fminf(__builtin_fabsf(y), (float)beta) : __builtin_fabsf(y);
+  const uint32_t m = __float_as_uint(ya + 12582912.0f) - 0x4B400000u;  // rne(|y|), |y| < 2^22
+  constexpr uint32_t kD = BITS - 1, kMask = (1u << kD) - 1u;
+  const uint32_t mags = (m & kMask) | ((m >> kD) & kMask) << 8 | ((m >> (2 * kD)) & kMask) << 16 |
+                        ((m >> (3 * kD)) & kMask) << 24;
+  const uint32_t c = fp6_mag4(mags);
+  // sign bit 5 on the nonzero codes of a negative x (nonzero codes have bit 3 or 4)
+  const uint32_t nz = ((c >> 3) | (c >> 4)) & 0x01010101u;
+  const uint32_t neg = (uint32_t)((int32_t)__float_as_uint(y) >> 31);
+  return c | ((nz << 5) & neg);
+}
+
+// e2m3 code (low byte) of the signed digit whose magnitude starts at bit sh1
+// of the sign-magnitude word w; zero digits get code 0.
+template <int BITS>
+__device__ inline uint32_t fp6_digit(uint32_t w, uint32_t sh1) {
+  const uint32_t d = (w >> sh1) & ((1u << (BITS - 1)) - 1u);
+  const uint32_t c = fp6_mag4(d) & 0xFFu;
+  return c | (c != 0u ? (w & 1u) << 5 : 0u);
+}
+
+// Four e2m3 codes (bytes of x, each < 64) -> 24 bits, code j at bits [6j, 6j + 6).
+__device__ inline uint32_t pack6x4(uint32_t x) {
+  return (x & 0x3Fu) | ((x >> 2) & 0xFC0u) | ((x >> 4) & 0x3F000u) | ((x >> 6) & 0xFC0000u);
+}
+typedef uint32_t v3u32 __attribute__((ext_vector_type(3)));
+// Sixteen codes as four 24-bit runs -> the 12 bytes of the bit stream.
+__device__ inline v3u32 pack6x16(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3) {
+  return v3u32{p0 | p1 << 24, p1 >> 8 | p2 << 16, p2 >> 16 | p3 << 8};
+}
+
 // Two's-complement byte of the signed digit whose magnitude starts at bit sh1
 // of the sign-magnitude word w (sh1 = 1 + t (BITS-1) <= 31).
 // digit_signed leaves garbage above the low byte (callers that pack bytes with
@@ -185,8 +225,14 @@ struct UnpackJobs {
   int nblk[2], wgs[2], wpg[2];
 };
 
-template <int DT, int BITS, bool OC>
+// F6: the fp6 digit format (inner-contiguous shape, bits <= 4): groups of 16
+// positions (12 bytes), each written by the window that holds its first
+// position; the group that runs past a window's last position (one per
+// segment at most) reads the elements of its remaining positions from global
+// memory.
+template <int DT, int BITS, bool OC, bool F6>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
+  static_assert(!F6 || (!OC && BITS <= 4), "fp6 digits: inner-contiguous operands, bits <= 4");
   int bid = blockIdx.x, jo = 0;
   if (J.nops > 1 && bid >= J.wgs[0]) {
     bid -= J.wgs[0];
@@ -235,6 +281,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
   // failed or which would not fit in the buffer (the host reports both)
   const int64_t start = entry_offset(a.plan, (int)gridDim.z, b, a.operand, a.after_a != 0);
   if (start < 0 || start + unpacked_entry_bytes(ph, a.operand) > a.cap) return;
+  if (ph->fmt != (F6 ? kDigitsFp6 : kDigitsInt8)) return;  // the host launches the plan's format
   int8_t* out = a.out + start;
   // this entry's bytes as a buffer when 32-bit offsets reach all of it
   const int64_t entry_bytes = unpacked_entry_bytes(ph, a.operand);
@@ -245,6 +292,13 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
   const int nseg = ph->n_seg;
   const int tid = threadIdx.x;
   const int kap_sh = is_a ? 20 : 25, last_sh = is_a ? 30 : 31;
+  const int64_t rowb = unpacked_row_bytes(kp, F6 ? kDigitsFp6 : kDigitsInt8);
+  // byte offset of unpacked row `row` (the part that does not depend on the position)
+  auto row_offset = [&](int64_t row) __attribute__((always_inline)) -> int64_t {
+    if (row < 0) return -1;
+    if constexpr (F6) return is_a ? frag6_row_offset(row, kp) : row * rowb;
+    else return is_a ? frag_row_offset(row, kp) : row * kp;
+  };
 
   for (int s = tid; s <= nseg; s += kThreads) s_off[s] = ph->seg_off[s];
   if (tid < L) {
@@ -323,17 +377,24 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
       }
     };
     const int clip = a.clip, beta = a.beta;
-    if (fast) stage([&](float x) { return digit_word<BITS>(x, r, clip, beta); });
-    else stage([&](float x) { return code_word(x, r, clip, beta); });
+    if constexpr (F6) {
+      if (fast) stage([&](float x) { return digit_word6<BITS>(x, r, clip, beta); });
+      else stage([&](float x) { return code_word(x, r, clip, beta); });
+    } else {
+      if (fast) stage([&](float x) { return digit_word<BITS>(x, r, clip, beta); });
+      else stage([&](float x) { return code_word(x, r, clip, beta); });
+    }
     // this window's K' positions: per segment the range [P0, P1), as groups of
-    // 4 positions flattened over the segments (s_pre: first flat group of each
-    // segment), so that all segments' groups are spread over all threads
+    // 4 positions (16 fully inside the range for F6) flattened over the
+    // segments (s_pre: first flat group of each segment), so that all
+    // segments' groups are spread over all threads
     if (tid <= nseg) {
       s_p0[tid] = P0;
       s_p1[tid] = P1;
-      s_ng[tid] = P1 > P0 ? (int)(((P1 + 3) >> 2) - (P0 >> 2)) : 0;
+      if constexpr (F6) s_ng[tid] = (int)max64(0, (P1 >> 4) - ((P0 + 15) >> 4));
+      else s_ng[tid] = P1 > P0 ? (int)(((P1 + 3) >> 2) - (P0 >> 2)) : 0;
     }
-    if (tid < L) rowoff[tid] = row_u0 < 0 ? (int64_t)-1 : is_a ? frag_row_offset(row_u0, kp) : row_u0 * kp;
+    if (tid < L) rowoff[tid] = row_offset(row_u0);
     __syncthreads();
     if (tid <= nseg) {
       int run = 0;
@@ -346,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
         __syncthreads();  // readers of the previous level's rowoff are done
         if (tid < L) {
           const int64_t row = s_dout[tid] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + s_line[tid]] : (int64_t)-1;
-          rowoff[tid] = row < 0 ? (int64_t)-1 : is_a ? frag_row_offset(row, kp) : row * kp;
+          rowoff[tid] = row_offset(row);
         }
         __syncthreads();
       }
@@ -360,113 +421,232 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
       for (int i = 0; i < LR; ++i) rb_s[i] = buf_row(uniform64(rowoff[i]));
 #define IMU_RB(i) (L <= 16 ? rb_s[(i) % LR] : buf_row(uniform64(rowoff[i])))
 #define IMU_RO(i) uniform64(rowoff[i])
-      const int gtot = s_pre[nseg];
-      for (int gb = 0; gb < gtot; gb += kThreads * kInFlight) {
-        // table entries of up to kInFlight groups per thread, loads first
-        uint4 e4[kInFlight];
-        int64_t gq[kInFlight];
-        int sq[kInFlight];
-#pragma unroll
-        for (int j = 0; j < kInFlight; ++j) {
-          const int gi = min(gb + tid + j * kThreads, gtot - 1);
+      if constexpr (F6) {
+        // work items: (group, part of the lines), NS parts of LP lines each, so
+        // that a window's few 16-position groups still spread over all threads
+        constexpr int NS = 4, LP = L / NS;
+        const int gtot = s_pre[nseg];
+        for (int it = tid; it < gtot * NS; it += kThreads) {
+          const int gi = it / NS, part = it % NS;
           int lo = 0, hi = nseg - 1;  // segment of flat group gi: last s with s_pre[s] <= gi
           while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (s_pre[mid] <= gi) lo = mid;
             else hi = mid - 1;
           }
-          sq[j] = lo;
-          gq[j] = (s_p0[lo] >> 2) + (gi - s_pre[lo]);
-          e4[j] = *reinterpret_cast<const uint4*>(kmap + 4 * gq[j]);
-        }
+          const int64_t g = ((s_p0[lo] + 15) >> 4) + (gi - s_pre[lo]);  // group of positions 16g .. 16g + 15
+          uint32_t ent[16];
 #pragma unroll
-        for (int j = 0; j < kInFlight; ++j) {
-          if (gb + tid + j * kThreads >= gtot) continue;
-          const int64_t g = gq[j], P0 = s_p0[sq[j]], P1 = s_p1[sq[j]];
-          const uint32_t ent[4] = {e4[j].x, e4[j].y, e4[j].z, e4[j].w};
-          // per position: word of the element and shift of digit t (codes),
-          // or byte t of the element's word (digit bytes, t < 4)
-          uint32_t adr[4], sh[4];
-          bool inr[4];
+          for (int q = 0; q < 4; ++q) {
+            const uint4 e4 = *reinterpret_cast<const uint4*>(kmap + 16 * g + 4 * q);
+            ent[4 * q] = e4.x, ent[4 * q + 1] = e4.y, ent[4 * q + 2] = e4.z, ent[4 * q + 3] = e4.w;
+          }
+          // per position: LDS byte of the code of digit t (digit words) or
+          // word of the element and shift of digit t (sign-magnitude codes)
+          uint32_t adr[16], sh[16];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int64_t p = 4 * g + c;
-            inr[c] = p >= P0 && p < P1;
+          for (int c = 0; c < 16; ++c) {
             const uint32_t e = ent[c];
             const int kap = (int)((e >> kap_sh) & 31u);
             const bool last = (e >> last_sh) & 1u;
             const int t = u == 0 ? kap : (last ? kap + u : D);
             const int kk = (int)((int64_t)(e & 0xFFFFFu) - kw0);
-            const bool ok = inr[c] && e != kKmapPad && t < (fast ? 4 : D) && kk >= 0 && kk < W;
+            const bool ok = e != kKmapPad && t < (fast ? 4 : D) && kk >= 0 && kk < W;
             adr[c] = fast ? (ok ? 4u * (uint32_t)slot(kk) + (uint32_t)t : 4u * kZero) : (ok ? (uint32_t)slot(kk) : kZero);
             sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
           }
-          const uint32_t pos = (uint32_t)(is_a ? frag_pos_offset(4 * g) : 4 * g);
-          const bool full = inr[0] && inr[3];  // the whole dword lies in the range
-          // rows of the group: digit (low byte, two's complement) of position c
-          // in line cl from the digit bytes or from the sign-magnitude code
-#define IMU_EMIT_ROWS()                                                                                                           \
-          if (use_buf) {                                                                                                          \
-            /* Buffer stores at 32-bit offsets into this entry; absent rows and */                                                \
-            /* bytes outside the range get an offset past the end, which the */                                                   \
-            /* hardware drops, so the lines form one branch-free block in which */                                                \
-            /* the LDS reads of later lines overlap the work on earlier ones. */                                                  \
-            if (full) {                                                                                                           \
-_Pragma("unroll(L <= 16 ? L : 8)")                                                                                                \
-              for (int i = 0; i < L; ++i) {                                                                                       \
-                const uint32_t o = IMU_RB(i) + pos;                                                                               \
-                const uint32_t* cl = codes + i * LS;                                                                              \
-                __builtin_amdgcn_raw_buffer_store_b32(IMU_DWORD(cl), rs, (int)o, 0, 0);                                           \
-              }                                                                                                                   \
-            } else {                                                                                                              \
-_Pragma("unroll 4")                                                                                                               \
-              for (int i = 0; i < L; ++i) {                                                                                       \
-                const uint32_t rb = IMU_RB(i);                                                                                    \
-                const uint32_t* cl = codes + i * LS;                                                                              \
-_Pragma("unroll")                                                                                                                 \
-                for (int c = 0; c < 4; ++c) {                                                                                     \
-                  const uint32_t o = inr[c] ? rb + pos + c : kDrop;                                                               \
-                  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)IMU_DIG(cl, c), rs, (int)o, 0, 0);                                \
-                }                                                                                                                 \
-              }                                                                                                                   \
-            }                                                                                                                     \
-          } else if (full) { /* entries of 2 GB and more: pointer stores, one line at a time */                                   \
-_Pragma("unroll")                                                                                                                 \
-            for (int i = 0; i < L; ++i) {                                                                                         \
-              const int64_t ro = IMU_RO(i);                                                                                       \
-              if (ro < 0) continue; /* uniform: row offsets are scalar */                                                         \
-              const uint32_t* cl = codes + i * LS;                                                                                \
-              uint32_t dw = 0;                                                                                                    \
-_Pragma("unroll")                                                                                                                 \
-              for (int c = 0; c < 4; ++c) dw |= (IMU_DIG(cl, c) & 0xFFu) << (8 * c);                                              \
-              *reinterpret_cast<uint32_t*>(out + ro + pos) = dw;                                                                  \
-            }                                                                                                                     \
-          } else {                                                                                                                \
-_Pragma("unroll 4")                                                                                                               \
-            for (int i = 0; i < L; ++i) {                                                                                         \
-              const int64_t ro = IMU_RO(i);                                                                                       \
-              if (ro < 0) continue;                                                                                               \
-              const uint32_t* cl = codes + i * LS;                                                                                \
-              int8_t* dst = out + ro + pos;                                                                                       \
-_Pragma("unroll")                                                                                                                 \
-              for (int c = 0; c < 4; ++c)                                                                                         \
-                if (inr[c]) dst[c] = (int8_t)(uint8_t)(IMU_DIG(cl, c) & 0xFFu);                                                   \
-            }                                                                                                                     \
+          const uint32_t pos = (uint32_t)(is_a ? frag6_pos_offset(16 * g) : 12 * g);
+          auto group_bits = [&](const uint32_t* cl) __attribute__((always_inline)) -> v3u32 {
+            uint32_t pk[4];
+            if (fast) {
+              const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cl);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const uint32_t ad[4] = {adr[4 * q], adr[4 * q + 1], adr[4 * q + 2], adr[4 * q + 3]};
+                pk[q] = pack6x4(dword_of_bytes(c8, ad));
+              }
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v |= fp6_digit<BITS>(cl[adr[4 * q + j]], sh[4 * q + j]) << (6 * j);
+                pk[q] = v;
+              }
+            }
+            return pack6x16(pk[0], pk[1], pk[2], pk[3]);
+          };
+#pragma unroll
+          for (int ii = 0; ii < LP; ++ii) {
+            const int i = part * LP + ii;
+            const int64_t ro = rowoff[i];
+            if (use_buf) {
+              __builtin_amdgcn_raw_buffer_store_b96(group_bits(codes + i * LS), rs, (int)(buf_row(ro) + pos), 0, 0);
+            } else if (ro >= 0) {
+              const v3u32 v = group_bits(codes + i * LS);
+              uint32_t* dst = reinterpret_cast<uint32_t*>(out + ro + pos);
+              dst[0] = v.x, dst[1] = v.y, dst[2] = v.z;
+            }
           }
-          if (fast) {
-#define IMU_DIG(cl, c) ((uint32_t)reinterpret_cast<const uint8_t*>(cl)[adr[c]])
-#define IMU_DWORD(cl) dword_of_bytes(reinterpret_cast<const uint8_t*>(cl), adr)
-            IMU_EMIT_ROWS();
-#undef IMU_DWORD
-#undef IMU_DIG
+        }
+        // Tail groups: per segment, the group holding the range's last
+        // position when it runs past the range (and starts inside it).  One
+        // thread per (segment, line); positions past the range read their
+        // element from global memory.
+        for (int item = tid; item < nseg * L; item += kThreads) {
+          const int s = item / L, i = item - s * L;
+          const int64_t P0 = s_p0[s], P1 = s_p1[s], G = P1 & ~(int64_t)15;
+          if ((P1 & 15) == 0 || G < P0) continue;
+          const int64_t ro = rowoff[i];
+          if (ro < 0) continue;
+          const T* xl = xb + (int64_t)s_line[i] * a.so;
+          uint32_t ent[16];
+#pragma unroll
+          for (int c = 0; c < 16; ++c) ent[c] = kmap[G + c];
+          float xv[16];
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const bool glob = G + c >= P1 && ent[c] != kKmapPad;
+            xv[c] = glob ? load_elem<DT>(xl + (int64_t)(ent[c] & 0xFFFFFu) * a.sk) : 0.f;
+          }
+          uint32_t pk[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const uint32_t e = ent[c];
+            const int kap = (int)((e >> kap_sh) & 31u);
+            const bool last = (e >> last_sh) & 1u;
+            const int t = u == 0 ? kap : (last ? kap + u : D);
+            uint32_t cd = 0;
+            if (e != kKmapPad && t < D) {
+              const uint32_t sh1 = (uint32_t)(1 + t * (BITS - 1));
+              if (G + c < P1) {
+                const int kk = (int)((int64_t)(e & 0xFFFFFu) - kw0);  // in [0, W): the position is in range
+                const uint32_t w = codes[i * LS + (kk >= 0 && kk < W ? slot(kk) : (int)kZero)];
+                cd = fast ? (t < 4 ? (w >> (8 * t)) & 0xFFu : 0u) : fp6_digit<BITS>(w, sh1);
+              } else {
+                cd = fp6_digit<BITS>(code_word(xv[c], r, clip, beta), sh1);
+              }
+            }
+            pk[c >> 2] |= cd << (6 * (c & 3));
+          }
+          const v3u32 v = pack6x16(pk[0], pk[1], pk[2], pk[3]);
+          const int64_t at = ro + (is_a ? frag6_pos_offset(G) : G / 16 * 12);
+          if (use_buf) {
+            __builtin_amdgcn_raw_buffer_store_b96(v, rs, (int)at, 0, 0);
           } else {
-#define IMU_DIG(cl, c) digit_signed<BITS>((cl)[adr[c]], sh[c])
-#define IMU_DWORD(cl) dword_of_digits<BITS>(cl, adr, sh)
-            IMU_EMIT_ROWS();
-#undef IMU_DWORD
-#undef IMU_DIG
+            uint32_t* dst = reinterpret_cast<uint32_t*>(out + at);
+            dst[0] = v.x, dst[1] = v.y, dst[2] = v.z;
           }
-#undef IMU_EMIT_ROWS
+        }
+      } else {
+        const int gtot = s_pre[nseg];
+        for (int gb = 0; gb < gtot; gb += kThreads * kInFlight) {
+          // table entries of up to kInFlight groups per thread, loads first
+          uint4 e4[kInFlight];
+          int64_t gq[kInFlight];
+          int sq[kInFlight];
+  #pragma unroll
+          for (int j = 0; j < kInFlight; ++j) {
+            const int gi = min(gb + tid + j * kThreads, gtot - 1);
+            int lo = 0, hi = nseg - 1;  // segment of flat group gi: last s with s_pre[s] <= gi
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (s_pre[mid] <= gi) lo = mid;
+              else hi = mid - 1;
+            }
+            sq[j] = lo;
+            gq[j] = (s_p0[lo] >> 2) + (gi - s_pre[lo]);
+            e4[j] = *reinterpret_cast<const uint4*>(kmap + 4 * gq[j]);
+          }
+  #pragma unroll
+          for (int j = 0; j < kInFlight; ++j) {
+            if (gb + tid + j * kThreads >= gtot) continue;
+            const int64_t g = gq[j], P0 = s_p0[sq[j]], P1 = s_p1[sq[j]];
+            const uint32_t ent[4] = {e4[j].x, e4[j].y, e4[j].z, e4[j].w};
+            // per position: word of the element and shift of digit t (codes),
+            // or byte t of the element's word (digit bytes, t < 4)
+            uint32_t adr[4], sh[4];
+            bool inr[4];
+  #pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int64_t p = 4 * g + c;
+              inr[c] = p >= P0 && p < P1;
+              const uint32_t e = ent[c];
+              const int kap = (int)((e >> kap_sh) & 31u);
+              const bool last = (e >> last_sh) & 1u;
+              const int t = u == 0 ? kap : (last ? kap + u : D);
+              const int kk = (int)((int64_t)(e & 0xFFFFFu) - kw0);
+              const bool ok = inr[c] && e != kKmapPad && t < (fast ? 4 : D) && kk >= 0 && kk < W;
+              adr[c] = fast ? (ok ? 4u * (uint32_t)slot(kk) + (uint32_t)t : 4u * kZero) : (ok ? (uint32_t)slot(kk) : kZero);
+              sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
+            }
+            const uint32_t pos = (uint32_t)(is_a ? frag_pos_offset(4 * g) : 4 * g);
+            const bool full = inr[0] && inr[3];  // the whole dword lies in the range
+            // rows of the group: digit (low byte, two's complement) of position c
+            // in line cl from the digit bytes or from the sign-magnitude code
+  #define IMU_EMIT_ROWS()                                                                                                           \
+            if (use_buf) {                                                                                                          \
+              /* Buffer stores at 32-bit offsets into this entry; absent rows and */                                                \
+              /* bytes outside the range get an offset past the end, which the */                                                   \
+              /* hardware drops, so the lines form one branch-free block in which */                                                \
+              /* the LDS reads of later lines overlap the work on earlier ones. */                                                  \
+              if (full) {                                                                                                           \
+  _Pragma("unroll(L <= 16 ? L : 8)")                                                                                                \
+                for (int i = 0; i < L; ++i) {                                                                                       \
+                  const uint32_t o = IMU_RB(i) + pos;                                                                               \
+                  const uint32_t* cl = codes + i * LS;                                                                              \
+                  __builtin_amdgcn_raw_buffer_store_b32(IMU_DWORD(cl), rs, (int)o, 0, 0);                                           \
+                }                                                                                                                   \
+              } else {                                                                                                              \
+  _Pragma("unroll 4")                                                                                                               \
+                for (int i = 0; i < L; ++i) {                                                                                       \
+                  const uint32_t rb = IMU_RB(i);                                                                                    \
+                  const uint32_t* cl = codes + i * LS;                                                                              \
+  _Pragma("unroll")                                                                                                                 \
+                  for (int c = 0; c < 4; ++c) {                                                                                     \
+                    const uint32_t o = inr[c] ? rb + pos + c : kDrop;                                                               \
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)IMU_DIG(cl, c), rs, (int)o, 0, 0);                                \
+                  }                                                                                                                 \
+                }                                                                                                                   \
+              }                                                                                                                     \
+            } else if (full) { /* entries of 2 GB and more: pointer stores, one line at a time */                                   \
+  _Pragma("unroll")                                                                                                                 \
+              for (int i = 0; i < L; ++i) {                                                                                         \
+                const int64_t ro = IMU_RO(i);                                                                                       \
+                if (ro < 0) continue; /* uniform: row offsets are scalar */                                                         \
+                const uint32_t* cl = codes + i * LS;                                                                                \
+                uint32_t dw = 0;                                                                                                    \
+  _Pragma("unroll")                                                                                                                 \
+                for (int c = 0; c < 4; ++c) dw |= (IMU_DIG(cl, c) & 0xFFu) << (8 * c);                                              \
+                *reinterpret_cast<uint32_t*>(out + ro + pos) = dw;                                                                  \
+              }                                                                                                                     \
+            } else {                                                                                                                \
+  _Pragma("unroll 4")                                                                                                               \
+              for (int i = 0; i < L; ++i) {                                                                                         \
+                const int64_t ro = IMU_RO(i);                                                                                       \
+                if (ro < 0) continue;                                                                                               \
+                const uint32_t* cl = codes + i * LS;                                                                                \
+                int8_t* dst = out + ro + pos;                                                                                       \
+  _Pragma("unroll")                                                                                                                 \
+                for (int c = 0; c < 4; ++c)                                                                                         \
+                  if (inr[c]) dst[c] = (int8_t)(uint8_t)(IMU_DIG(cl, c) & 0xFFu);                                                   \
+              }                                                                                                                     \
+            }
+            if (fast) {
+  #define IMU_DIG(cl, c) ((uint32_t)reinterpret_cast<const uint8_t*>(cl)[adr[c]])
+  #define IMU_DWORD(cl) dword_of_bytes(reinterpret_cast<const uint8_t*>(cl), adr)
+              IMU_EMIT_ROWS();
+  #undef IMU_DWORD
+  #undef IMU_DIG
+            } else {
+  #define IMU_DIG(cl, c) digit_signed<BITS>((cl)[adr[c]], sh[c])
+  #define IMU_DWORD(cl) dword_of_digits<BITS>(cl, adr, sh)
+              IMU_EMIT_ROWS();
+  #undef IMU_DWORD
+  #undef IMU_DIG
+            }
+  #undef IMU_EMIT_ROWS
+          }
         }
       }
 #undef IMU_RO
@@ -477,7 +657,7 @@ _Pragma("unroll")                                                               
 }
 
 template <int DT, bool OC>
-hipError_t unpack_launch(int bits, const UnpackArgs* ops, int nops, int batch, hipStream_t s) {
+hipError_t unpack_launch(int bits, bool f6, const UnpackArgs* ops, int nops, int batch, hipStream_t s) {
   constexpr int L = Shape<OC>::L, W = Shape<OC>::W;
   UnpackJobs J{};
   J.nops = nops;
@@ -498,10 +678,27 @@ hipError_t unpack_launch(int bits, const UnpackArgs* ops, int nops, int batch, h
   if (total == 0) return hipSuccess;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid((unsigned)total, 1, (unsigned)batch);
+  if (f6) {
+    if constexpr (OC) {
+      return hipErrorInvalidValue;
+    } else {
+      switch (bits) {
+#define IMU_UP(B)                                                                                     \
+  case B:                                                                                             \
+    hipLaunchKernelGGL((unpack_kernel<DT, B, false, true>), grid, dim3(kThreads), 0, s, J);           \
+    break;
+        IMU_UP(2) IMU_UP(3) IMU_UP(4)
+#undef IMU_UP
+        default:
+          return hipErrorInvalidValue;
+      }
+    }
+    return hipGetLastError();
+  }
   switch (bits) {
 #define IMU_UP(B)                                                                                     \
   case B:                                                                                             \
-    hipLaunchKernelGGL((unpack_kernel<DT, B, OC>), grid, dim3(kThreads), 0, s, J);                    \
+    hipLaunchKernelGGL((unpack_kernel<DT, B, OC, false>), grid, dim3(kThreads), 0, s, J);             \
     break;
     IMU_UP(2) IMU_UP(3) IMU_UP(4) IMU_UP(5) IMU_UP(6) IMU_UP(7) IMU_UP(8)
 #undef IMU_UP
@@ -518,8 +715,11 @@ hipError_t unpack_dt(int bits, const UnpackArgs* ops, int nops, int batch, hipSt
     hipError_t e = unpack_dt<DT>(bits, ops, 1, batch, s);
     return e != hipSuccess ? e : unpack_dt<DT>(bits, ops + 1, 1, batch, s);
   }
-  return ops[0].sk == 1 ? unpack_launch<DT, false>(bits, ops, nops, batch, s)
-                        : unpack_launch<DT, true>(bits, ops, nops, batch, s);
+  const bool f6 = ops[0].fmt == kDigitsFp6;
+  for (int o = 0; o < nops; ++o)
+    if (ops[o].fmt != ops[0].fmt || (f6 && (ops[o].sk != 1 || bits > 4))) return hipErrorInvalidValue;
+  return ops[0].sk == 1 ? unpack_launch<DT, false>(bits, f6, ops, nops, batch, s)
+                        : unpack_launch<DT, true>(bits, f6, ops, nops, batch, s);
 }
 
 }  // namespace

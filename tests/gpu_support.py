@@ -32,9 +32,9 @@ def logical_f32(op: W.Operand, b: int) -> np.ndarray:
     return O.widen(op.logical_bits(b), op.dtype)
 
 
-def params_of(pr: W.Problem) -> B.ImuParams:
+def params_of(pr: W.Problem, digits: str = "auto") -> B.ImuParams:
     return B.params(beta=pr.beta, bits=pr.bits, p=(pr.p_num, pr.p_den), strat_a=pr.strat_a,
-                    strat_b=pr.strat_b, gamma=pr.gamma, clip=pr.clip)
+                    strat_b=pr.strat_b, gamma=pr.gamma, clip=pr.clip, digits=digits)
 
 
 def oracle_entries(pr: W.Problem, unpacked: bool = True):
@@ -93,6 +93,62 @@ def untile_a(flat: np.ndarray, m_alloc: int, kp: int) -> np.ndarray:
     it, 16-byte half h of row r of the block is lane r + 32 h."""
     t = np.asarray(flat).reshape(m_alloc // 32, kp // 32, 2, 32, 16)  # rb, c, h, r, byte
     return t.transpose(0, 3, 1, 2, 4).reshape(m_alloc, kp)
+
+
+# e2m3 (fp6) codes of the integers 0..7: 1 sign, 2 exponent (bias 1) and 3
+# mantissa bits, value 2^(e-1) (1 + m/8) for e > 0 and m/8 for e = 0.  The
+# table is derived from that definition here, so it pins the HIP side's table.
+def _e2m3_value(code: int) -> float:
+    e, m = (code >> 3) & 3, code & 7
+    v = m / 8.0 if e == 0 else 2.0 ** (e - 1) * (1 + m / 8.0)
+    return -v if code & 0x20 else v
+
+
+E2M3_DIGIT = np.full(64, 99, np.int64)  # 99: a code that is no integer digit, or a signed zero
+for _c in range(64):
+    _v = _e2m3_value(_c)
+    if _v == int(_v) and (_v != 0 or _c == 0):
+        E2M3_DIGIT[_c] = int(_v)
+
+
+def fp6_digits(codes: np.ndarray) -> np.ndarray:
+    """e2m3 codes -> integer digits, 99 for a code that is no integer digit
+    (or a negative zero: zero digits are stored as code 0), which no oracle
+    digit equals.  Rows past the valid ones are never written and may hold
+    anything."""
+    return E2M3_DIGIT[np.asarray(codes, np.int64)]
+
+
+def unpack_6bit(rows: np.ndarray, n: int) -> np.ndarray:
+    """Byte rows holding 6-bit fields (field j at bits [6j, 6j + 6), little
+    endian) -> the first n fields of each row."""
+    bits = np.unpackbits(np.ascontiguousarray(rows, np.uint8), axis=-1, bitorder="little")
+    f = bits[..., :6 * n].reshape(*rows.shape[:-1], n, 6).astype(np.int64)
+    return (f << np.arange(6)).sum(-1)
+
+
+def b_rows(b_u: np.ndarray, info: dict) -> np.ndarray:
+    """B'^T as stored -> n_alloc x k_pad integer digits (int8 bytes, or fp6
+    bit-stream rows of 3/4 k_pad bytes)."""
+    n, kp = info["n_alloc"], info["k_pad"]
+    if info["digits"] == B.DIGITS["fp6"]:
+        raw = np.asarray(b_u)[:n * kp * 3 // 4].view(np.uint8).reshape(n, kp * 3 // 4)
+        return fp6_digits(unpack_6bit(raw, kp))
+    return np.asarray(b_u)[:n * kp].view(np.int8).reshape(n, kp).astype(np.int64)
+
+
+def a_rows(a_u: np.ndarray, info: dict) -> np.ndarray:
+    """A' as stored (MFMA fragment order) -> m_alloc x k_pad integer digits.
+
+    int8: untile_a.  fp6: blocks of 32 rows x 64 positions, 1536 bytes, at
+    (rb * k_pad/64 + c) * 1536; inside, lane r + 32 h holds 24 bytes: the 6-bit
+    codes of positions 32 h .. 32 h + 31 of the block's row r."""
+    m, kp = info["m_alloc"], info["k_pad"]
+    if info["digits"] == B.DIGITS["fp6"]:
+        raw = np.asarray(a_u)[:m * kp * 3 // 4].view(np.uint8).reshape(m // 32, kp // 64, 2, 32, 24)
+        codes = unpack_6bit(raw, 32)  # rb, c, h, r, j
+        return fp6_digits(codes.transpose(0, 3, 1, 2, 4).reshape(m, kp))
+    return untile_a(np.asarray(a_u)[:m * kp].view(np.int8), m, kp).astype(np.int64)
 
 
 def ulp_diff(a: np.ndarray, b: np.ndarray) -> int:

@@ -96,6 +96,34 @@ def test_invalid_params_rejected_before_any_device_work(lib, bad):
     assert lib.imu_last_error()
 
 
+def test_fp6_digits_need_bits_4_and_k_contiguous_operands(lib):
+    """fp6 digits (e2m3 holds integers up to 7) need bits <= 4 and the
+    K-contiguous layouts; asked for elsewhere they are refused before any
+    device work, and an unknown format is an argument error."""
+    a = cpu_matrix(64, 128).c()
+    bt = cpu_matrix(128, 64, layout="transposed").c()
+    bn = cpu_matrix(128, 64).c()
+    at = cpu_matrix(64, 128, layout="transposed").c()
+    size = lambda x, y, p: lib.imu_plan_bytes(ctypes.byref(x), ctypes.byref(y), ctypes.byref(p))
+    for bits in (2, 3, 4):
+        assert size(a, bt, B.params(bits=bits, digits="fp6")) > 0
+    assert size(a, bt, B.params(bits=5, digits="fp6")) == 0
+    assert b"fp6" in lib.imu_last_error()
+    assert size(a, bn, B.params(bits=4, digits="fp6")) == 0
+    assert size(at, bt, B.params(bits=4, digits="fp6")) == 0
+    for digits in ("auto", "int8"):  # fall back / ask for int8: always valid
+        assert size(a, bn, B.params(bits=4, digits=digits)) > 0
+        assert size(a, bt, B.params(bits=5, digits=digits)) > 0
+    bad = B.params(bits=4)
+    bad.digits = 3
+    assert size(a, bt, bad) == 0 and b"digits" in lib.imu_last_error()
+    need = ctypes.c_size_t(0)
+    p = B.params(bits=5, digits="fp6")
+    st = lib.imu_imunpack_matmul(ctypes.byref(a), ctypes.byref(bt), ctypes.byref(p), ctypes.c_void_p(1), None,
+                                 None, 0, ctypes.byref(need), None, None)
+    assert st == B.ERR_UNSUPPORTED
+
+
 def test_invalid_shapes_rejected(lib):
     p = B.params()
     a, b = cpu_matrix(8, 9).c(), cpu_matrix(10, 4).c()  # K mismatch

@@ -59,6 +59,25 @@ SMALL = [
 ]
 
 
+# fp6 digits (bits <= 4, A row-major, B stored N x K): several 128-wide tiles,
+# ragged tails, K over several 512-wide unpack windows (so segments end inside
+# 16-position groups at window ends), each digit base, Mix / fixed / greedy
+# plans, clipping, batches
+FP6 = [
+    dict(seed=31, m=300, k=1100, n=260, kind="linear", dtype="bf16", layout_b="transposed", beta=31, bits=4),
+    dict(seed=32, m=130, k=257, n=129, kind="gauss", dtype="f32", layout_b="transposed", beta=15, bits=4),
+    dict(seed=33, m=200, k=1333, n=150, kind="grad", dtype="bf16", layout_b="transposed", beta=7, bits=3, batch=2),
+    dict(seed=34, m=100, k=90, n=70, kind="gauss", layout_b="transposed", beta=1, bits=2),
+    dict(seed=35, m=150, k=700, n=140, kind="gauss", dtype="f32", layout_b="transposed", beta=7, bits=3,
+         p=(995, 1000), clip=True),
+    dict(seed=36, m=200, k=600, n=150, kind="linear", layout_b="transposed", beta=31, bits=4,
+         strat_a="greedy", strat_b="mix"),
+    dict(seed=37, m=260, k=640, n=200, kind="linear", layout_b="transposed", beta=15, bits=4,
+         strat_a="row", strat_b="col"),
+    dict(seed=38, m=160, k=520, n=64, kind="attn", dtype="bf16", layout_b="transposed", beta=15, bits=4, batch=3),
+]
+
+
 def _id(c):
     return f"s{c['seed']}_{c['m']}x{c['k']}x{c['n']}_{c['kind']}"
 
@@ -81,6 +100,45 @@ def check_stats(st: B.Stats, q_entries, b: int, tag: str):
 @pytest.mark.parametrize("cfg", SMALL, ids=[_id(c) for c in SMALL])
 def test_staged_path_matches_oracle(cfg):
     _staged(cfg)
+
+
+@pytest.mark.parametrize("cfg", FP6, ids=[_id(c) for c in FP6])
+def test_fp6_digits_match_oracle(cfg):
+    """The fp6 digit format (e2m3 codes on the f8f6f4 MFMA, fp32 partial sums
+    moved into the int32 Horner accumulators): the same plan, the digits
+    decoded from the fp6 buffers equal the oracle's A' and B', and C is the
+    same integer product."""
+    _staged_problem(W.random_problem(**cfg), digits="fp6")
+
+
+def test_fp6_wide_codes_and_levels():
+    """fp6 with codes of five and more base-8 digits (|q| >= 2^12 at b = 4):
+    the unpack stages sign-magnitude codes and writes levels u > 0."""
+    pr = W.random_problem(seed=39, m=96, k=700, n=80, kind="gauss", dtype="f32", layout_b="transposed",
+                          beta=15, bits=4)
+    rng = np.random.Generator(np.random.PCG64(39))
+    for op, scale in ((pr.a, 3e3), (pr.b, 1e3)):
+        flat = op.stored.reshape(-1)
+        idx = rng.choice(flat.size, 7, replace=False)
+        flat[idx] *= np.float32(scale)
+    _staged_problem(pr, digits="fp6")
+
+
+@pytest.mark.parametrize("fold", ["1", "0"], ids=["fold_columns", "atomic_columns"])
+def test_fp6_and_int8_give_the_same_bytes(fold, monkeypatch):
+    """The two digit formats of one problem: same plan, same C and output."""
+    monkeypatch.setenv("IMU_FOLD_COLUMNS", fold)
+    pr = W.random_problem(seed=40, m=300, k=900, n=260, kind="linear", dtype="bf16", layout_b="transposed",
+                          beta=31, bits=4, strat_a="row", strat_b="col")
+    a, b = G.to_device(pr.a), G.to_device(pr.b)
+    out8, c8, i8 = B.imunpack_matmul(a, b, G.params_of(pr, "int8"))
+    out6, c6, i6 = B.imunpack_matmul(a, b, G.params_of(pr, "fp6"))
+    outa, ca, ia = B.imunpack_matmul(a, b, G.params_of(pr, "auto"))
+    assert i8[0]["digits"] == B.DIGITS["int8"] and i6[0]["digits"] == B.DIGITS["fp6"]
+    assert ia[0]["digits"] == B.DIGITS["fp6"]
+    assert torch.equal(c8, c6) and torch.equal(out8, out6) and torch.equal(ca, c6)
+    ref = G.oracle_entries(pr, unpacked=False)[0]
+    assert np.array_equal(c6[0].cpu().numpy(), ref.C32)
 
 
 def test_wide_codes_match_oracle():
@@ -132,12 +190,12 @@ def _staged(cfg):
     _staged_problem(W.random_problem(**cfg))
 
 
-def _staged_problem(pr):
+def _staged_problem(pr, digits="auto"):
     print(f"\n[case] {pr.name} a={pr.a.dtype}/{pr.a.layout} b={pr.b.layout} bits={pr.bits} beta={pr.beta} "
-          f"strat={pr.strat_a}/{pr.strat_b} batch={pr.a.batch}", flush=True)
+          f"strat={pr.strat_a}/{pr.strat_b} batch={pr.a.batch} digits={digits}", flush=True)
     refs = G.oracle_entries(pr)
     a, b = G.to_device(pr.a), G.to_device(pr.b)
-    p = G.params_of(pr)
+    p = G.params_of(pr, digits)
     sa = B.quantize_rtn(a, p, want_q=True)
     sb = B.quantize_rtn(b, p, want_q=True)
     plan = B.plan_unpack(a, b, p, sa, sb)
@@ -171,9 +229,9 @@ def _staged_problem(pr):
         assert info["k_pad"] == seg_off[-1]
         # unpacked operands, padding stripped through the documented layout
         kp = info["k_pad"]
-        A_g = G.untile_a(a_u[info["a_offset"]:info["a_offset"] + info["m_alloc"] * kp].cpu().numpy(),
-                         info["m_alloc"], kp)
-        B_g = b_u[info["b_offset"]:info["b_offset"] + info["n_alloc"] * kp].view(info["n_alloc"], kp).cpu().numpy()
+        assert info["digits"] == B.DIGITS[digits if digits != "auto" else "int8"], tag
+        A_g = G.a_rows(a_u[info["a_offset"]:].cpu().numpy(), info)
+        B_g = G.b_rows(b_u[info["b_offset"]:].cpu().numpy(), info)
         rows = G.padded_line_index(pl.rows_a, M, info["m_base"])
         cols = G.depth_order_col_index(pl.cols_b, pl.db_c, info["n_base"])
         bmap = plan.array("bmap", e).cpu().numpy()
@@ -275,16 +333,20 @@ def test_workspace_grows_and_results_repeat():
 # full workload sizes, bench launch configuration
 # ---------------------------------------------------------------------------
 
-FULL = [(0, 0), (1, 0), (2, 0), (3, 0), (4, 0), (4, 1), (4, 2)]
+# (config, sub-problem, digit format): "auto" takes fp6 where it applies (the
+# MLP up-projection and the training forward GEMM, b = 4), which also run with
+# int8 digits
+FULL = [(0, 0, "auto"), (1, 0, "auto"), (2, 0, "auto"), (2, 0, "int8"), (3, 0, "auto"), (4, 0, "auto"),
+        (4, 0, "int8"), (4, 1, "auto"), (4, 2, "auto")]
 
 
-@pytest.mark.parametrize("idx,sub", FULL, ids=[f"config{i}_{j}" for i, j in FULL])
-def test_full_size_workload(idx, sub):
+@pytest.mark.parametrize("idx,sub,digits", FULL, ids=[f"config{i}_{j}_{d}" for i, j, d in FULL])
+def test_full_size_workload(idx, sub, digits):
     pr = W.config(idx)[sub]
     M, K, N = pr.mnk
-    print(f"\n[full] {pr.name} M={M} K={K} N={N} batch={pr.a.batch}", flush=True)
+    print(f"\n[full] {pr.name} M={M} K={K} N={N} batch={pr.a.batch} digits={digits}", flush=True)
     a, b = G.to_device(pr.a), G.to_device(pr.b)
-    p = G.params_of(pr)
+    p = G.params_of(pr, digits)
     ws = B.Workspace("cuda")
     out, c, infos = B.imunpack_matmul(a, b, p, ws=ws)
     torch.cuda.synchronize()
@@ -297,7 +359,8 @@ def test_full_size_workload(idx, sub):
         assert info["pairs"] == ch.table
         assert np.array_equal(c[e].cpu().numpy(), ref.C32), (pr.name, e)
         assert G.ulp_diff(out[e].cpu().numpy(), ref.out) <= 1, (pr.name, e)
-    print(f"[full] {pr.name} ok ratio={infos[0]['unpack_ratio']:.3f} choice={infos[0]['choice']}", flush=True)
+    print(f"[full] {pr.name} ok ratio={infos[0]['unpack_ratio']:.3f} choice={infos[0]['choice']} "
+          f"digits={infos[0]['digits']}", flush=True)
 
 
 def test_full_size_fp32_gradient_operand():
