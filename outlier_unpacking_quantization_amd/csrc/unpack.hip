@@ -231,7 +231,7 @@ struct UnpackJobs {
 // segment at most) reads the elements of its remaining positions from global
 // memory.
 template <int DT, int BITS, bool OC, bool F6>
-__global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
+__global__ __launch_bounds__(kThreads, 4) void unpack_kernel(UnpackJobs J) {
   static_assert(!F6 || (!OC && BITS <= 4), "fp6 digits: inner-contiguous operands, bits <= 4");
   int bid = blockIdx.x, jo = 0;
   if (J.nops > 1 && bid >= J.wgs[0]) {
@@ -247,6 +247,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
   constexpr uint32_t kZero = LS - 1;  // zero word of each line
   __shared__ uint32_t codes[L * LS];
   __shared__ int64_t rowoff[L];  // row part of the byte offset of row (line, level u), -1 if absent
+  __shared__ int64_t rowoffs[F6 ? D : 1][L];  // F6: the same for every level at once
   __shared__ int s_dout[L];
   __shared__ int32_t s_line[L];  // operand line staged in slot i
   __shared__ int64_t s_off[kMaxSeg + 1];
@@ -315,6 +316,15 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
   __syncthreads();
   int umax = 0;
   for (int i = 0; i < L; ++i) umax = max(umax, s_dout[i]);
+  if constexpr (F6) {
+    // the rows of every level of the workgroup's lines, once (the window
+    // loop's first barrier publishes them)
+    for (int x = tid; x < umax * L; x += kThreads) {
+      const int u = x / L, i = x - u * L;
+      const int64_t row = s_dout[i] > u ? (int64_t)lvl[(int64_t)u * a.n_outer + s_line[i]] : (int64_t)-1;
+      rowoffs[u][i] = row_offset(row);
+    }
+  }
 
   for (int64_t w = w_begin; w < w_end; ++w) {
     const int64_t kw0 = w * W, kw1 = min64(kw0 + W, K);
@@ -402,7 +412,8 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
       s_pre[tid] = run;
     }
     __syncthreads();
-    for (int u = 0; u < umax; ++u) {
+    // F6 walks the levels inside each work item (one pass here)
+    for (int u = 0; u < (F6 ? min(umax, 1) : umax); ++u) {
       if (u > 0) {  // rows of the unpacked levels (rare): one more round trip each
         __syncthreads();  // readers of the previous level's rowoff are done
         if (tid < L) {
@@ -441,6 +452,8 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
             const uint4 e4 = *reinterpret_cast<const uint4*>(kmap + 16 * g + 4 * q);
             ent[4 * q] = e4.x, ent[4 * q + 1] = e4.y, ent[4 * q + 2] = e4.z, ent[4 * q + 3] = e4.w;
           }
+          const uint32_t pos = (uint32_t)(is_a ? frag6_pos_offset(16 * g) : 12 * g);
+          for (int uu = 0; uu < umax; ++uu) {
           // per position: LDS byte of the code of digit t (digit words) or
           // word of the element and shift of digit t (sign-magnitude codes)
           uint32_t adr[16], sh[16];
@@ -449,13 +462,12 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
             const uint32_t e = ent[c];
             const int kap = (int)((e >> kap_sh) & 31u);
             const bool last = (e >> last_sh) & 1u;
-            const int t = u == 0 ? kap : (last ? kap + u : D);
+            const int t = uu == 0 ? kap : (last ? kap + uu : D);
             const int kk = (int)((int64_t)(e & 0xFFFFFu) - kw0);
             const bool ok = e != kKmapPad && t < (fast ? 4 : D) && kk >= 0 && kk < W;
             adr[c] = fast ? (ok ? 4u * (uint32_t)slot(kk) + (uint32_t)t : 4u * kZero) : (ok ? (uint32_t)slot(kk) : kZero);
             sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
           }
-          const uint32_t pos = (uint32_t)(is_a ? frag6_pos_offset(16 * g) : 12 * g);
           auto group_bits = [&](const uint32_t* cl) __attribute__((always_inline)) -> v3u32 {
             uint32_t pk[4];
             if (fast) {
@@ -479,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
 #pragma unroll
           for (int ii = 0; ii < LP; ++ii) {
             const int i = part * LP + ii;
-            const int64_t ro = rowoff[i];
+            const int64_t ro = rowoffs[uu][i];
             if (use_buf) {
               __builtin_amdgcn_raw_buffer_store_b96(group_bits(codes + i * LS), rs, (int)(buf_row(ro) + pos), 0, 0);
             } else if (ro >= 0) {
@@ -487,6 +499,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
               uint32_t* dst = reinterpret_cast<uint32_t*>(out + ro + pos);
               dst[0] = v.x, dst[1] = v.y, dst[2] = v.z;
             }
+          }
           }
         }
         // Tail groups: per segment, the group holding the range's last
@@ -496,9 +509,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
         for (int item = tid; item < nseg * L; item += kThreads) {
           const int s = item / L, i = item - s * L;
           const int64_t P0 = s_p0[s], P1 = s_p1[s], G = P1 & ~(int64_t)15;
-          if ((P1 & 15) == 0 || G < P0) continue;
-          const int64_t ro = rowoff[i];
-          if (ro < 0) continue;
+          if ((P1 & 15) == 0 || G < P0 || s_dout[i] == 0) continue;
           const T* xl = xb + (int64_t)s_line[i] * a.so;
           uint32_t ent[16];
 #pragma unroll
@@ -509,33 +520,42 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackJobs J) {
             const bool glob = G + c >= P1 && ent[c] != kKmapPad;
             xv[c] = glob ? load_elem<DT>(xl + (int64_t)(ent[c] & 0xFFFFFu) * a.sk) : 0.f;
           }
+          // the code words of the 16 positions (staged or read above), then
+          // each level of the line
+          uint32_t cw[16];
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const int kk = (int)((int64_t)(ent[c] & 0xFFFFFu) - kw0);  // in [0, W) for staged positions
+            cw[c] = G + c < P1 ? codes[i * LS + (kk >= 0 && kk < W ? slot(kk) : (int)kZero)]
+                               : code_word(xv[c], r, clip, beta);
+          }
+          for (int uu = 0; uu < s_dout[i]; ++uu) {
+          const int64_t ro = rowoffs[uu][i];
           uint32_t pk[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
           for (int c = 0; c < 16; ++c) {
             const uint32_t e = ent[c];
             const int kap = (int)((e >> kap_sh) & 31u);
             const bool last = (e >> last_sh) & 1u;
-            const int t = u == 0 ? kap : (last ? kap + u : D);
+            const int t = uu == 0 ? kap : (last ? kap + uu : D);
             uint32_t cd = 0;
             if (e != kKmapPad && t < D) {
               const uint32_t sh1 = (uint32_t)(1 + t * (BITS - 1));
-              if (G + c < P1) {
-                const int kk = (int)((int64_t)(e & 0xFFFFFu) - kw0);  // in [0, W): the position is in range
-                const uint32_t w = codes[i * LS + (kk >= 0 && kk < W ? slot(kk) : (int)kZero)];
-                cd = fast ? (t < 4 ? (w >> (8 * t)) & 0xFFu : 0u) : fp6_digit<BITS>(w, sh1);
-              } else {
-                cd = fp6_digit<BITS>(code_word(xv[c], r, clip, beta), sh1);
-              }
+              // staged digit words hold the codes of digits 0..3; the others
+              // are sign-magnitude code words
+              cd = fast && G + c < P1 ? (t < 4 ? (cw[c] >> (8 * t)) & 0xFFu : 0u) : fp6_digit<BITS>(cw[c], sh1);
             }
             pk[c >> 2] |= cd << (6 * (c & 3));
           }
           const v3u32 v = pack6x16(pk[0], pk[1], pk[2], pk[3]);
+          if (ro < 0) continue;
           const int64_t at = ro + (is_a ? frag6_pos_offset(G) : G / 16 * 12);
           if (use_buf) {
             __builtin_amdgcn_raw_buffer_store_b96(v, rs, (int)at, 0, 0);
           } else {
             uint32_t* dst = reinterpret_cast<uint32_t*>(out + at);
             dst[0] = v.x, dst[1] = v.y, dst[2] = v.z;
+          }
           }
         }
       } else {
