@@ -294,8 +294,7 @@ def static_weight(pr, a, b, p_mix, prm, steps: int, warmup: int):
     out = torch.empty((1, M, N), dtype=torch.float32, device="cuda")
 
     def run(fn, n):
-        for _ in range(warmup):
-            fn()
+        warm_up(fn, warmup, torch)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(n):
