@@ -149,10 +149,6 @@ __device__ inline uint32_t fp6_digit(uint32_t w, uint32_t sh1) {
   return c | (c != 0u ? (w & 1u) << 5 : 0u);
 }
 
-// Four e2m3 codes (bytes of x, each < 64) -> 24 bits, code j at bits [6j, 6j + 6).
-__device__ inline uint32_t pack6x4(uint32_t x) {
-  return (x & 0x3Fu) | ((x >> 2) & 0xFC0u) | ((x >> 4) & 0x3F000u) | ((x >> 6) & 0xFC0000u);
-}
 typedef uint32_t v3u32 __attribute__((ext_vector_type(3)));
 // Sixteen codes as four 24-bit runs -> the 12 bytes of the bit stream.
 __device__ inline v3u32 pack6x16(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3) {
@@ -453,54 +449,64 @@ __global__ __launch_bounds__(kThreads, 4) void unpack_kernel(UnpackJobs J) {
             ent[4 * q] = e4.x, ent[4 * q + 1] = e4.y, ent[4 * q + 2] = e4.z, ent[4 * q + 3] = e4.w;
           }
           const uint32_t pos = (uint32_t)(is_a ? frag6_pos_offset(16 * g) : 12 * g);
-          for (int uu = 0; uu < umax; ++uu) {
-          // per position: LDS byte of the code of digit t (digit words) or
-          // word of the element and shift of digit t (sign-magnitude codes)
-          uint32_t adr[16], sh[16];
+          // per position, once for all levels: LDS word of the element (the
+          // zero word for a padding entry or an element outside the window)
+          // in bits 0..15, its inner index in bits 16..20 and the last-index
+          // flag in bit 21
+          uint32_t pi[16];
 #pragma unroll
           for (int c = 0; c < 16; ++c) {
             const uint32_t e = ent[c];
-            const int kap = (int)((e >> kap_sh) & 31u);
-            const bool last = (e >> last_sh) & 1u;
-            const int t = uu == 0 ? kap : (last ? kap + uu : D);
             const int kk = (int)((int64_t)(e & 0xFFFFFu) - kw0);
-            const bool ok = e != kKmapPad && t < (fast ? 4 : D) && kk >= 0 && kk < W;
-            adr[c] = fast ? (ok ? 4u * (uint32_t)slot(kk) + (uint32_t)t : 4u * kZero) : (ok ? (uint32_t)slot(kk) : kZero);
-            sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
+            const uint32_t w = e != kKmapPad && kk >= 0 && kk < W ? (uint32_t)slot(kk) : kZero;
+            pi[c] = w | ((e >> kap_sh) & 31u) << 16 | ((e >> last_sh) & 1u) << 21;
           }
-          auto group_bits = [&](const uint32_t* cl) __attribute__((always_inline)) -> v3u32 {
-            uint32_t pk[4];
-            if (fast) {
-              const uint8_t* c8 = reinterpret_cast<const uint8_t*>(cl);
+          const uint32_t* cpart = codes + part * LP * LS;  // the part's first line
+          // digit words (FAST) or sign-magnitude code words, one instance each
+          auto emit = [&](auto FAST) __attribute__((always_inline)) {
+            constexpr bool kFast = decltype(FAST)::value;
+            for (int uu = 0; uu < umax; ++uu) {
+              // per position: LDS byte of the code of digit t (digit words),
+              // or word of the element and shift of digit t (code words)
+              uint32_t adr[16], sh[kFast ? 1 : 16];
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const uint32_t ad[4] = {adr[4 * q], adr[4 * q + 1], adr[4 * q + 2], adr[4 * q + 3]};
-                pk[q] = pack6x4(dword_of_bytes(c8, ad));
+              for (int c = 0; c < 16; ++c) {
+                const uint32_t w = pi[c] & 0xFFFFu;
+                const int kap = (int)((pi[c] >> 16) & 31u);
+                const int t = uu == 0 ? kap : ((pi[c] >> 21) & 1u ? kap + uu : D);
+                const bool ok = w != kZero && t < (kFast ? 4 : D);
+                if constexpr (kFast) {
+                  adr[c] = ok ? 4u * w + (uint32_t)t : 4u * kZero;
+                } else {
+                  adr[c] = ok ? w : kZero;
+                  sh[c] = ok ? (uint32_t)(1 + t * (BITS - 1)) : 1u;
+                }
               }
-            } else {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                uint32_t v = 0;
+              for (int ii = 0; ii < LP; ++ii) {
+                const uint32_t* cl = cpart + ii * LS;
+                uint32_t cd[16];  // the 16 codes, each below 64
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v |= fp6_digit<BITS>(cl[adr[4 * q + j]], sh[4 * q + j]) << (6 * j);
-                pk[q] = v;
+                for (int c = 0; c < 16; ++c) {
+                  if constexpr (kFast) cd[c] = reinterpret_cast<const uint8_t*>(cl)[adr[c]];
+                  else cd[c] = fp6_digit<BITS>(cl[adr[c]], sh[c]);
+                }
+                // code c at bits [6c, 6c + 6) of the 96-bit group
+                const v3u32 v = {cd[0] | cd[1] << 6 | cd[2] << 12 | cd[3] << 18 | cd[4] << 24 | cd[5] << 30,
+                                 cd[5] >> 2 | cd[6] << 4 | cd[7] << 10 | cd[8] << 16 | cd[9] << 22 | cd[10] << 28,
+                                 cd[10] >> 4 | cd[11] << 2 | cd[12] << 8 | cd[13] << 14 | cd[14] << 20 | cd[15] << 26};
+                const int64_t ro = rowoffs[uu][part * LP + ii];
+                if (use_buf) {
+                  __builtin_amdgcn_raw_buffer_store_b96(v, rs, (int)(buf_row(ro) + pos), 0, 0);
+                } else if (ro >= 0) {
+                  uint32_t* dst = reinterpret_cast<uint32_t*>(out + ro + pos);
+                  dst[0] = v.x, dst[1] = v.y, dst[2] = v.z;
+                }
               }
             }
-            return pack6x16(pk[0], pk[1], pk[2], pk[3]);
           };
-#pragma unroll
-          for (int ii = 0; ii < LP; ++ii) {
-            const int i = part * LP + ii;
-            const int64_t ro = rowoffs[uu][i];
-            if (use_buf) {
-              __builtin_amdgcn_raw_buffer_store_b96(group_bits(codes + i * LS), rs, (int)(buf_row(ro) + pos), 0, 0);
-            } else if (ro >= 0) {
-              const v3u32 v = group_bits(codes + i * LS);
-              uint32_t* dst = reinterpret_cast<uint32_t*>(out + ro + pos);
-              dst[0] = v.x, dst[1] = v.y, dst[2] = v.z;
-            }
-          }
-          }
+          if (fast) emit(std::true_type{});
+          else emit(std::false_type{});
         }
         // Tail groups: per segment, the group holding the range's last
         // position when it runs past the range (and starts inside it).  One
