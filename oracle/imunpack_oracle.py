@@ -22,7 +22,7 @@ Low Precision Integers" (atlas.scime.ai).  The page fixes what is computed:
 
 The page gives no formula for the percentile, the in-range interval, the digit
 base, the Mix rule or the layout of the unpacked matrices.  This oracle takes
-one reading of each (numbered R-1 ... R-12 in the docstrings below, the same
+one reading of each (numbered R-1 ... R-15 in the docstrings below, the same
 numbering the design notes use) and implements it plainly:
 
 * integer arithmetic is int64 (Python integers where int64 could overflow);
@@ -131,11 +131,11 @@ def rtn(x32: np.ndarray, r: np.float32) -> np.ndarray:
 
 
 def rtn_clipped(x32: np.ndarray, r: np.float32, beta: int) -> np.ndarray:
-    """The clipping quantizer of the page's ablation rows ("Measured effects":
-    clipping at the 99.5-percentile costs accuracy; p = 100% with beta = 255
-    restricts every value to the range): the RTN code of fl32(x * r), rounded
-    half to even, then clamped to [-beta, beta].  A product that overflows
-    binary32 is clamped like any other code beyond beta."""
+    """R-13: the clipping quantizer of the page's ablation rows ("Measured
+    effects" table, the 99.5-percentile clipping row, set against p = 100% with
+    beta = 255, R-14): the RTN code of fl32(x * r), rounded half to even, then
+    clamped to [-beta, beta].  A product that overflows binary32 is clamped like
+    any other code beyond beta."""
     with np.errstate(over="ignore"):
         y = np.asarray(x32, dtype=np.float32) * np.float32(r)
     return np.clip(np.rint(y), -beta, beta).astype(np.int64)
@@ -236,8 +236,8 @@ def candidates(n: np.ndarray, st: LineStats, strategy: str, gamma: int = 2
 
 
 def greedy_depths(n: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Line-at-a-time unpacking (the page's Mix, "chosen per matrix via outlier
-    counts", read as a greedy): all depths start at 1; while some code is not
+    """R-15: line-at-a-time unpacking (the page's per-matrix choice from
+    outlier counts, "Approach", read as a greedy): all depths start at 1; while some code is not
     covered (n[i, k] > d_r[i] + d_c[k] - 1), the line holding the most
     uncovered codes gets one more level, rows before columns and lower indices
     first on equal counts.  Raising row i to depth d covers exactly the codes

@@ -1,44 +1,50 @@
-// Low bit-width GEMM on the unpacked operands with the shift-and-accumulate
-// fold and the dequantization epilogue (gfx950, int8 MFMA); one launch serves
-// every batch entry (blockIdx.y).
+// Digit GEMM on the unpacked operands, with the shift-and-accumulate fold and
+// the dequantization epilogue (gfx950); one launch serves every batch entry
+// (blockIdx.y).
 //
 // Method: summary page "IM-Unpack: Training and Inference with Arbitrarily Low
-// Precision Integers", "Approach": products of the narrow-integer unpacked
-// matrices, multiplied by powers of two and summed, give the integer product of
-// the original operands with no error.  Here every digit is int8 and the products run on
-// v_mfma_i32_32x32x32_i8.  K' is split into exponent segments; walking them from
-// the highest exponent down, acc = acc * 2^(bits-1) + P_e (Horner), so one set
-// of int32 accumulators holds sum_e 2^((bits-1)e) P_e.  The unpacked row (i, u)
-// and column (n, w) fold into C[i, n] with a further shift of (bits-1)(u+w);
-// all int32 arithmetic wraps modulo 2^32.  Extra columns (w > 0) of a plan
-// without extra rows are folded inside the base tile of their original
-// columns: the shift is one more exponent, so the tile walks (level, segment)
-// pairs by combined exponent under the same Horner accumulator, with the B'^T
-// rows of level w staged into the LDS slots of their own columns.  The plan
-// puts B's columns in depth order (descending, then by index), so a tile's
-// 128 columns share their depth except at the few tiles where the depth
-// changes, the tile runs only the levels its columns have, and level w's rows
-// of the tile are contiguous in B'^T; the epilogue stores each column through
-// the order's map.  Extra rows fold in a separate pass of extra tiles with
-// atomic adds.
+// Precision Integers", "Approach".  Each unpacked matrix holds small signed
+// digits; a digit of weight 2^((bits-1)t) contributes its product scaled by
+// that power, so the scaled sum of the narrow products is the original integer
+// product.  The digits are int8 bytes (v_mfma_i32_32x32x32_i8, int32
+// accumulators) or, for bits <= 4, e2m3 codes (v_mfma_f32_32x32x64_f8f6f4:
+// every product is an integer of magnitude at most 49, the fp32 accumulators
+// hold one exponent's partial sums, exact below 2^24, and move into int32
+// accumulators at each exponent change and every kF32Steps steps).  K' is split
+// into exponent segments; walking them from the highest exponent down,
+// acc = acc * 2^(bits-1) + P_e (Horner), so one set of int32 accumulators holds
+// sum_e 2^((bits-1)e) P_e.  The unpacked row (i, u) and column (n, w) fold
+// into C[i, n] with a further shift of (bits-1)(u+w); all int32 arithmetic
+// wraps modulo 2^32.  Extra columns (w > 0) of a plan without extra rows are
+// folded inside the base tile of their original columns: the shift is one
+// more exponent, so the tile walks (level, segment) pairs by combined exponent
+// under the same Horner accumulator, with the B'^T rows of level w staged into
+// the LDS slots of their own columns.  The plan puts B's columns in depth
+// order (descending, then by index), so a tile's 128 columns share their depth
+// except at the few tiles where the depth changes, the tile runs only the
+// levels its columns have, and level w's rows of the tile are contiguous in
+// B'^T; the epilogue stores each column through the order's map.  Extra rows
+// fold in a separate pass of extra tiles with atomic adds.
 //
 // Operands: A' (m_alloc x k_pad) in MFMA fragment order and B'^T (n_alloc x
 // k_pad), both K-contiguous.  Workgroup tile 256 x 128, four waves stacked along
 // M, each owning 64 rows x 128 columns (2 x 4 blocks of 32 x 32, 128
-// accumulator registers).  A wave's A rows belong to it alone, so its A
-// fragments are contiguous 1 KB loads straight into registers, refilled one K
-// substep at a time one step ahead; the B tile (128 x 128 bytes per K step) is
-// shared by the four waves through LDS, double-buffered, rows 144 bytes apart
-// (16-byte reads of 8 consecutive rows touch disjoint banks), its global loads
-// two steps ahead.  B fragments are double-buffered by substep: the reads of
-// substep q+1 are issued before the MFMAs of substep q, and substep 0 of the
-// next step is read right after the barrier, under the MFMAs of substep 3.
-// Segments are padded to the K step, so a step never straddles two exponents.
-// Tiles are dealt to the 8 XCDs (hardware order w % 8) in contiguous runs of a
-// grouped order (groups of G tile rows, G chosen by the host to minimise the
-// L2 fills), so the workgroups sharing an XCD's L2 share A and B panels; inside
-// a group the tile columns are taken in residue classes mod 8, which spreads
-// the deep (costly) columns over all runs.
+// accumulator registers).  A K step is 128 positions: 4 substeps of 32 (int8)
+// or 2 of 64 (fp6).  A wave's A rows belong to it alone, so its A fragments
+// are contiguous loads straight into registers, refilled one K substep at a
+// time one step ahead, one load after each MFMA of the substep; the B tile is
+// shared by the four waves through LDS, double-buffered (int8 rows 144 bytes
+// apart: 16-byte reads of 8 consecutive rows touch disjoint banks; fp6 rows 104
+// bytes apart), its global loads two steps ahead.  B fragments are
+// double-buffered by substep: the reads of substep q+1 are issued before the
+// MFMAs of substep q, and substep 0 of the next step is read right after the
+// barrier, under the MFMAs of the last substep.  Segments are padded to the K
+// step, so a step never straddles two exponents.  Tiles are dealt to the 8
+// XCDs (hardware order w % 8) in contiguous runs of a grouped order (groups of
+// G tile rows, G chosen by the host to minimise the L2 fills), so the
+// workgroups sharing an XCD's L2 share A and B panels; inside a group the tile
+// columns are taken in residue classes mod 8, which spreads the deep (costly)
+// columns over all runs.
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -430,6 +436,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // fragments after the second B load), so the loads in flight at the loop
   // head are the same on entry and on the back edge: the wait before the B
   // store then covers the B loads only, not the A fragments issued after them.
+  // the A loads of a substep go out one after each of its 8 MFMAs
+#define IMU_INTERLEAVE()                                                                       \
+  _Pragma("unroll") for (int k_ = 0; k_ < 8; ++k_) {                                          \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* one MFMA */                          \
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* one vector-memory read */            \
+  }
 #pragma unroll
   for (int q = 0; q < NQ - 1; ++q) IMU_LOAD_A(q, la.k);
   if constexpr (FOLD) set_level(lb.w), lbw = lb.w;
@@ -460,6 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       IMU_MFMA(q & 1, q);
       IMU_LOAD_A(q, la.k);
+      IMU_INTERLEAVE();
       __builtin_amdgcn_sched_barrier(0);
     }
     IMU_STORE_B((i + 1) & 1);  // B of step i+1 (loaded during step i-1)
@@ -470,10 +483,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);
     IMU_MFMA(1, NQ - 1);
     IMU_LOAD_A(NQ - 1, la.k);
+    IMU_INTERLEAVE();
     __builtin_amdgcn_sched_barrier(0);
     adv(la);
     adv(cc);
   }
+#undef IMU_INTERLEAVE
 #undef IMU_LOAD_A
 #undef IMU_LOAD_B
 #undef IMU_STORE_B
