@@ -48,12 +48,12 @@ PAGE_RATIOS = {"mix": 1.06, "row/row": 2.02, "row/col": 5.36, "col/row": 1.64, "
 # the GEMM source: when gemm.hip no longer hashes to `source_sha256` the
 # traffic is reported as null.
 GEMM_TRAFFIC = {
-    ("mlp_up", "fp6"): {"source_sha256": "e6f817ae7cd58384b9f02d0c976cd2cacd448039b254100522fa1a81e14ac138",
-                        "fetch_kib": 1511760.4, "write_kib": 385078.6, "fetch_factor": 1.9998, "write_factor": 1.0000,
-                        "bytes_per_launch": 3490096177},
-    ("llama_linear", "int8"): {"source_sha256": "e6f817ae7cd58384b9f02d0c976cd2cacd448039b254100522fa1a81e14ac138",
-                               "fetch_kib": 151229.6, "write_kib": 65536.0, "fetch_factor": 1.9998,
-                               "write_factor": 1.0000, "bytes_per_launch": 376796113},
+    ("mlp_up", "fp6"): {"source_sha256": "79f07262db18e6a6ac657097dbee831c7293dbbfe6901a08b1f51924493bc061",
+                        "fetch_kib": 1494980.6, "write_kib": 385293.3, "fetch_factor": 1.9998, "write_factor": 1.0000,
+                        "bytes_per_launch": 3455954436},
+    ("llama_linear", "int8"): {"source_sha256": "79f07262db18e6a6ac657097dbee831c7293dbbfe6901a08b1f51924493bc061",
+                               "fetch_kib": 151227.5, "write_kib": 65536.0, "fetch_factor": 1.9998,
+                               "write_factor": 1.0000, "bytes_per_launch": 376791813},
 }
 
 

@@ -211,8 +211,11 @@ class Matrix:
             bstride, ld = t.stride(0), t.stride(1)
         else:
             raise ImunpackError(ERR_INVALID_ARG, "operand must be 2-D or 3-D")
-        if t.stride(-1) != 1:
+        # strides of size-1 dimensions address nothing: numpy and torch leave them arbitrary
+        if t.stride(-1) != 1 and sc > 1:
             raise ImunpackError(ERR_INVALID_ARG, "operand must have unit stride in its last dimension")
+        if sr == 1:
+            ld = sc
         if t.dtype == torch.float32:
             dt = F32
         elif t.dtype == torch.bfloat16:

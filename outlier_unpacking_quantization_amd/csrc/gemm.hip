@@ -147,83 +147,80 @@ __device__ inline void shift_acc(v16i (&acc)[FR][4], int sh) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = sh >= 32 ? 0 : (int)((uint32_t)acc[i][j][r] << sh);
 }
 
-// Position in the walk over K' steps: segment s (walked from the highest
-// exponent down, empty segments skipped), K' offset k of the step and the end
-// of its segment.  The segment table is read through the constant address
-// space: the GEMM never writes it, so the loads are scalar and the cursors stay
-// in SGPRs (vector loads here would make the compiler wait for the operand
-// prefetches as well).
-struct Cursor {
-  int s;
-  int64_t k, end;
+// Position in a walk over K' steps.  Without column folding the walk takes
+// the segments s from the highest exponent down (empty segments skipped), the
+// exponent being e = s.  With it, the walk takes the pairs (level w, segment s)
+// in decreasing order of the combined exponent e = w + s, so one Horner
+// accumulator holds sum 2^((bits-1)(s+w)) P_(w,s).  k is the K' offset of the
+// step; `left` counts the steps up to the end of the segment, so the common
+// step is an add and a count, and the segment table (read through the
+// constant address space: the GEMM never writes it, so the loads are scalar
+// and the cursors stay in SGPRs) is looked at only when a segment ends.  Once
+// the walk is over, k keeps growing (loads clamp it) and `left` is too large
+// to run out.  K' < 2^31 (K < 2^20 and at most 31 x 31 digit pairs per
+// position), so offsets in positions fit 32 bits.
+struct Walk {
+  int k, left, s, w, e;
 };
 typedef __attribute__((address_space(4))) const int64_t* SegTable;
-__device__ inline void cursor_advance(Cursor& c, SegTable off) {
-  c.k += BK;
-  if (c.k >= c.end && c.s > 0) {
-    --c.s;
-    while (c.s > 0 && off[c.s] == off[c.s + 1]) --c.s;
-    c.k = off[c.s];
-    c.end = off[c.s + 1];
-    // finish the scalar loads here: left pending, they would make the loop
-    // wait on lgkmcnt(0) every step, which also drains the LDS reads in flight
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
-  }
-}
-__device__ inline Cursor cursor_top(int nseg, SegTable off) {
-  Cursor c;
-  c.s = nseg - 1;
-  while (c.s > 0 && off[c.s] == off[c.s + 1]) --c.s;
-  c.k = off[c.s];
-  c.end = off[c.s + 1];
-  return c;
-}
+constexpr int kWalkOver = 1 << 30;
 
-// The walk of a tile that also folds extra columns (levels w > 0 of its own
-// columns): pairs (level w, segment s) in decreasing order of the combined
-// exponent w + s, each over its segment's K' steps, so one Horner accumulator
-// holds sum 2^((bits-1)(s+w)) P_(w,s).  Empty segments are skipped; once the
-// walk is over, k keeps growing (loads clamp it).
-struct FoldCursor {
-  int s, w, sum;
-  int64_t k, end;
-};
-typedef __attribute__((address_space(4))) const PlanHeader* HdrC;
-__device__ inline bool fold_next_pair(FoldCursor& c, int nseg, int nlev, SegTable off) {
-  int s = c.s, w = c.w, sum = c.sum;
-  for (;;) {
-    if (w + 1 <= min(nlev - 1, sum)) {
-      ++w;
-    } else {
-      if (sum == 0) return false;
-      --sum;
-      w = max(0, sum - (nseg - 1));
+__device__ inline void walk_enter(Walk& c, SegTable off) {
+  c.k = (int)off[c.s];
+  c.left = (int)((off[c.s + 1] - off[c.s]) / BK);
+}
+// Next non-empty segment (pair) after the current one; false when the walk is over.
+template <bool FOLD>
+__device__ inline bool walk_next(Walk& c, int nseg, int nlev, SegTable off) {
+  if constexpr (FOLD) {
+    int w = c.w, e = c.e, s;
+    for (;;) {
+      if (w + 1 <= min(nlev - 1, e)) {
+        ++w;
+      } else {
+        if (e == 0) return false;
+        --e;
+        w = max(0, e - (nseg - 1));
+      }
+      s = e - w;
+      if (off[s] != off[s + 1]) break;
     }
-    s = sum - w;
-    if (off[s] != off[s + 1]) break;
+    c.s = s, c.w = w, c.e = e;
+  } else {
+    int s = c.s;
+    do {
+      if (s == 0) return false;
+      --s;
+    } while (off[s] == off[s + 1]);
+    c.s = s, c.e = s;
   }
-  c.s = s;
-  c.w = w;
-  c.sum = sum;
-  c.k = off[s];
-  c.end = off[s + 1];
+  walk_enter(c, off);
   return true;
 }
-__device__ inline void fold_advance(FoldCursor& c, int nseg, int nlev, SegTable off) {
-  c.k += BK;
-  if (c.k >= c.end && fold_next_pair(c, nseg, nlev, off))
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only (see cursor_advance)
-}
-__device__ inline FoldCursor fold_top(int nseg, int nlev, SegTable off) {
-  FoldCursor c;
-  c.w = nlev - 1;
-  c.sum = (nseg - 1) + (nlev - 1);
+template <bool FOLD>
+__device__ inline Walk walk_top(int nseg, int nlev, SegTable off) {
+  Walk c;
   c.s = nseg - 1;
-  c.k = off[c.s];
-  c.end = off[c.s + 1];
-  if (c.k == c.end) fold_next_pair(c, nseg, nlev, off);
+  c.w = FOLD ? nlev - 1 : 0;
+  c.e = c.s + c.w;
+  walk_enter(c, off);
+  if (c.left == 0 && !walk_next<FOLD>(c, nseg, nlev, off)) c.left = kWalkOver;
   return c;
 }
+// One step along the walk; true when it entered a new segment.
+template <bool FOLD>
+__device__ inline bool walk_step(Walk& c, int nseg, int nlev, SegTable off) {
+  c.k += BK;
+  if (--c.left != 0) return false;
+  const bool moved = walk_next<FOLD>(c, nseg, nlev, off);
+  if (!moved) c.left = kWalkOver;
+  // finish the scalar loads here: left pending, they would make the loop
+  // wait on lgkmcnt(0) every step, which also drains the LDS reads in flight
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+  return moved;
+}
+
+typedef __attribute__((address_space(4))) const PlanHeader* HdrC;
 
 constexpr int kMaxLevels = 32;  // digits of an int32 code in base 2^(bits-1), bits >= 2: at most 31
 
@@ -299,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int sb_w = br * SB + bc;
   // B fragment j (columns col0 + 32j + lane%32) of substep q
   const int sb_r = (lane & 31) * SB + (F6 ? 24 : 16) * (lane >> 5);
-  const int64_t k_last = kp - BK;  // loads past the walk re-read the last step (never used)
+  const int k_last = (int)(kp - BK);  // loads past the walk re-read the last step (never used)
 
   v16i acc[FR][4];
   v16f accf[FR][4];  // fp6: the current exponent's partial sums
@@ -338,32 +335,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   };
   if constexpr (FOLD) set_level(0);
   const int64_t steps = kp / BK * nlev;
-  using Cur = std::conditional_t<FOLD, FoldCursor, Cursor>;
-  auto top = [&]() __attribute__((always_inline)) {
-    if constexpr (FOLD) return fold_top(nseg, nlev, off);
-    else return cursor_top(nseg, off);
-  };
-  auto adv = [&](Cur& c) __attribute__((always_inline)) {
-    if constexpr (FOLD) fold_advance(c, nseg, nlev, off);
-    else cursor_advance(c, off);
-  };
-  auto expo = [](const Cur& c) __attribute__((always_inline)) {
-    if constexpr (FOLD) return c.sum;
-    else return c.s;
-  };
 
-  Cur cc = top();        // compute
-  Cur la = cc, lb = cc;  // A loads (one step ahead), B loads (two ahead)
-  int lbw = 0;           // level of lb's rows (FOLD)
+  Walk cc = walk_top<FOLD>(nseg, nlev, off);  // compute
+  Walk la = cc, lb = cc;  // A loads (one step ahead), B loads (two ahead)
+  int lbw = 0;            // level of lb's rows (FOLD)
+  int prev_e = cc.e;   // exponent of the accumulators' contents
+  int f32_steps = 0;   // fp6: steps in the fp32 accumulators
 
   using Frag = std::conditional_t<F6, v8i, v4i>;  // MFMA operand (fp6: 6 of the 8 dwords)
   Frag ar[NQ][FR];  // A fragments of the current step, refilled substep by substep
   v4i bs[F6 ? 3 : 4];  // B staging registers
   Frag bf[2][4];    // B fragments, double-buffered by substep
-  int f32_steps = 0;  // fp6: steps in the fp32 accumulators
 #define IMU_LOAD_A(q, k)                                                                       \
   {                                                                                            \
-    const int64_t k_ = min64((k), k_last);                                                     \
+    const int64_t k_ = min((k), k_last);                                                       \
     if constexpr (F6) {                                                                        \
       _Pragma("unroll") for (int f = 0; f < FR; ++f) {                                         \
         const int8_t* pa_ = ga + f * ga_f + k_ * 24 + 1536 * (q);                              \
@@ -378,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   }
 #define IMU_LOAD_B(k)                                                                          \
   {                                                                                            \
-    const int64_t kb_ = min64((k), k_last) / 4 * (F6 ? 3 : 4);  /* byte offset of the step */ \
+    const int64_t kb_ = (int64_t)(min((k), k_last) / 4) * (F6 ? 3 : 4);  /* byte offset of the step */ \
     if constexpr (F6) {                                                                        \
       const int8_t* pb_ = (FOLD ? gbase + gbo[0] : gb) + kb_;                                  \
       _Pragma("unroll") for (int j = 0; j < 3; ++j) bs[j] = *reinterpret_cast<const v4i*>(pb_ + 16 * j); \
@@ -403,8 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
         (!FOLD || ((bvl >> j) & 1u)) ? bs[j] : v4i{0, 0, 0, 0};                                \
   }
 #define IMU_ADV_B()                                                                            \
-  {                                                                                            \
-    adv(lb);                                                                                   \
+  if (walk_step<FOLD>(lb, nseg, nlev, off)) {                                                  \
     if constexpr (FOLD) {                                                                      \
       if (lb.w != lbw) {                                                                       \
         lbw = lb.w;                                                                            \
@@ -451,15 +435,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   IMU_LOAD_B(lb.k);
   IMU_ADV_B();
   IMU_LOAD_A(NQ - 1, la.k);
-  adv(la);
+  walk_step<FOLD>(la, nseg, nlev, off);
   __syncthreads();
   IMU_READ_B(0, sB[0], 0);
-  int prev_s = expo(cc);
   for (int64_t i = 0; i < steps; ++i) {
-    if (expo(cc) != prev_s) {  // Horner: the exponents between the two steps
+    if (cc.e != prev_e) {  // Horner: the exponents between the two steps
       if constexpr (F6) flush_f32(acc, accf), f32_steps = 0;
-      shift_acc(acc, shift * (prev_s - expo(cc)));
-      prev_s = expo(cc);
+      shift_acc(acc, shift * (prev_e - cc.e));
+      prev_e = cc.e;
     }
     if constexpr (F6) {
       if (f32_steps == kF32Steps) flush_f32(acc, accf), f32_steps = 0;
@@ -485,8 +468,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     IMU_LOAD_A(NQ - 1, la.k);
     IMU_INTERLEAVE();
     __builtin_amdgcn_sched_barrier(0);
-    adv(la);
-    adv(cc);
+    walk_step<FOLD>(la, nseg, nlev, off);
+    walk_step<FOLD>(cc, nseg, nlev, off);
   }
 #undef IMU_INTERLEAVE
 #undef IMU_LOAD_A
@@ -496,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 #undef IMU_MFMA
 #undef IMU_ADV_B
   if constexpr (F6) flush_f32(acc, accf);
-  if (prev_s > 0) shift_acc(acc, shift * prev_s);  // exponents below the last non-empty segment
+  if (prev_e > 0) shift_acc(acc, shift * prev_e);  // exponents below the last non-empty segment
 
   // epilogue: accumulator register r of lane l holds element
   // (8*(r/4) + 4*(l/32) + r%4, l%32) of each 32x32 block.  Rows are visited one

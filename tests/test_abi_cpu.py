@@ -164,6 +164,13 @@ def test_binding_matrix_marshalling():
         B.Matrix(torch.zeros((4, 4), dtype=torch.float64)).c()
     with pytest.raises(B.ImunpackError):
         B.Matrix(torch.zeros((4, 4)).t()).c()  # non-unit last stride
+    # size-1 dimensions may carry any stride (numpy's contiguous (17, 1) transpose of a (1, 17) row)
+    col = torch.zeros((1, 17)).t()
+    assert col.stride() == (1, 17)
+    m = B.Matrix(col, "transposed").c()
+    assert (m.rows, m.cols, m.ld) == (1, 17, 1)
+    m = B.Matrix(torch.zeros(17).as_strided((1, 17), (1, 1))).c()  # one stored row, torch row stride 1
+    assert (m.rows, m.cols, m.ld) == (1, 17, 17)
 
 
 def test_training_wrapper_rejects_bad_shapes():

@@ -285,6 +285,23 @@ def test_edge_cases(name):
                                                         ref.plan.choice.n_u)
 
 
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_cases_fp6(name):
+    """The same degenerate shapes through the 6-bit digit path (b = 4, B given as its
+    transpose so that every digit row is K-contiguous)."""
+    a_np, b_np = (np.asarray(x, np.float32) for x in EDGE[name])
+    print(f"\n[edge fp6] {name} {a_np.shape}x{b_np.shape}", flush=True)
+    ref = O.imunpack_matmul(a_np, b_np, 7, 4)
+    a = B.Matrix(torch.from_numpy(np.ascontiguousarray(a_np)).to("cuda"))
+    b = B.Matrix(torch.from_numpy(np.ascontiguousarray(b_np.T)).to("cuda"), "transposed")
+    out, c, info = B.imunpack_matmul(a, b, B.params(beta=7, bits=4, digits="fp6"))
+    assert info[0]["digits"] == B.DIGITS["fp6"]
+    assert np.array_equal(c[0].cpu().numpy(), ref.C32)
+    assert G.ulp_diff(out[0].cpu().numpy(), ref.out) <= 1
+    assert (info[0]["m_u"], info[0]["k_u"], info[0]["n_u"]) == (ref.plan.choice.m_u, ref.plan.choice.k_u,
+                                                              ref.plan.choice.n_u)
+
+
 @pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
 def test_nonfinite_input_is_reported(bad):
     a = np.ones((20, 30), np.float32)
