@@ -22,7 +22,7 @@ Low Precision Integers" (atlas.scime.ai).  The page fixes what is computed:
 
 The page gives no formula for the percentile, the in-range interval, the digit
 base, the Mix rule or the layout of the unpacked matrices.  This oracle takes
-one reading of each (numbered R-1 ... R-15 in the docstrings below, the same
+one reading of each (numbered R-1 ... R-17 in the docstrings below, the same
 numbering the design notes use) and implements it plainly:
 
 * integer arithmetic is int64 (Python integers where int64 could overflow);
@@ -565,3 +565,107 @@ def imunpack_matmul(a32: np.ndarray, b32: np.ndarray, beta: int, bits: int, p_nu
             raise AssertionError("unpacked GEMM + fold differs from the direct product")
         res.Ap, res.Bp, res.C_unpacked = Ap, Bp, Cu
     return res
+
+
+# ----------------------------------------------------------------------------
+# row softmax of attention logits (the P of the attention-output GEMM P.V)
+# ----------------------------------------------------------------------------
+# The page's attention-output GEMMs ("Key results", third bullet; the
+# "Measured effects" row that quantizes all GEMMs) multiply the softmax
+# probabilities P by V.  The page fixes no softmax arithmetic.  R-17: P is the
+# binary32 softmax of each row of logits, rounded to bf16, with every step
+# fixed so that one result is defined:
+#
+#   m   = the largest logit of the row (NaNs ignored, as IEEE maxNum);
+#   t   = x - m, y = t * L with L = binary32(log2 e), both rounded;
+#   e   = 0 when y < -100, else 2^n * poly(f) with n = y rounded to the nearest
+#         integer (ties to even) and f = y - n (exact): poly is the Taylor
+#         polynomial of 2^f = exp(f ln 2) to degree 7, coefficients
+#         binary32((ln 2)^k / k!), evaluated by Horner with a rounded product
+#         and a rounded sum per step (no fused multiply-add);
+#   S   = the sum of the row's e: the row is taken in chunks of 256 positions;
+#         "lane" l (0..63) adds, in order, positions 256 j + 4 l + c for
+#         j = 0, 1, ... and c = 0..3 (those inside the row) to a binary32 sum
+#         that starts at 0; the 64 lane sums are then halved pairwise
+#         (lanes l and l + 32, then l and l + 16, ... down to 1);
+#   P   = e / S rounded to binary32, then to bf16 (nearest, ties to even; any
+#         NaN becomes the quiet NaN 0x7FC0).
+#
+# A row holding a NaN or +Inf gives a NaN row (the statistics then report a
+# non-finite operand); -Inf logits give P = 0 (masked positions).
+# Pins: tests/test_oracle_softmax.py.
+
+SOFTMAX_LOG2E = np.float32(1.4426950408889634)
+SOFTMAX_EXP_CUT = -100.0
+SOFTMAX_LANES, SOFTMAX_CHUNK = 64, 4
+
+
+def exp2_coefficients() -> List[np.float32]:
+    """binary32((ln 2)^k / k!) for k = 0..7 (R-17)."""
+    import math
+    return [np.float32(math.log(2.0) ** k / math.factorial(k)) for k in range(8)]
+
+
+def softmax_exp(t: np.ndarray) -> np.ndarray:
+    """e = exp(t) for binary32 t <= 0 (or NaN) by the steps of R-17."""
+    t = np.asarray(t, dtype=np.float32)
+    y = (t * SOFTMAX_LOG2E).astype(np.float32)
+    e = np.zeros_like(y)
+    nan = np.isnan(y)
+    e[nan] = np.float32(np.nan)
+    live = ~nan & ~(y < np.float32(SOFTMAX_EXP_CUT))
+    yl = y[live]
+    n = np.rint(yl).astype(np.float32)
+    f = (yl - n).astype(np.float32)
+    c = exp2_coefficients()
+    p = np.full_like(f, c[7])
+    for k in range(6, -1, -1):
+        p = ((p * f).astype(np.float32) + c[k]).astype(np.float32)
+    e[live] = np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+    return e
+
+
+def softmax_row_sum(e: np.ndarray) -> np.float32:
+    """S of R-17: per-lane sums in chunk order, then the pairwise halving over the 64 lanes."""
+    e = np.asarray(e, dtype=np.float32)
+    n = e.shape[0]
+    span = SOFTMAX_LANES * SOFTMAX_CHUNK
+    J = max(1, -(-n // span))
+    padded = np.zeros(J * span, dtype=np.float32)  # +0 leaves a sum of non-negative terms unchanged
+    padded[:n] = e
+    lanes = padded.reshape(J, SOFTMAX_LANES, SOFTMAX_CHUNK).transpose(1, 0, 2).reshape(SOFTMAX_LANES, -1)
+    v = np.add.accumulate(lanes, axis=1, dtype=np.float32)[:, -1]  # left to right, binary32
+    s = SOFTMAX_LANES // 2
+    while s >= 1:
+        v = (v[:s] + v[s:2 * s]).astype(np.float32)
+        s //= 2
+    return np.float32(v[0])
+
+
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """binary32 -> bf16 bits, nearest with ties to even; NaN -> 0x7FC0."""
+    x = np.atleast_1d(np.asarray(x, dtype=np.float32))
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r[np.isnan(x)] = np.uint16(0x7FC0)
+    return r
+
+
+def softmax_f32(row: np.ndarray) -> np.ndarray:
+    """e / S of R-17 for one row of binary32 logits, before the bf16 rounding."""
+    row = np.asarray(row, dtype=np.float32)
+    m = np.fmax.reduce(row) if row.size else np.float32(0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        t = (row - np.float32(m)).astype(np.float32)
+        e = softmax_exp(t)
+        S = softmax_row_sum(e)
+        return (e / S).astype(np.float32)
+
+
+def softmax_bf16(logits: np.ndarray) -> np.ndarray:
+    """P of R-17 for every row of ``logits`` (rows x cols, binary32): bf16 bits."""
+    z = np.asarray(logits, dtype=np.float32)
+    out = np.empty(z.shape, dtype=np.uint16)
+    for i in range(z.shape[0]):
+        out[i] = f32_to_bf16_rne(softmax_f32(z[i]))
+    return out

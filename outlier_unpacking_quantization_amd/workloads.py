@@ -137,13 +137,18 @@ def gradients(rng: np.random.Generator, rows: int, cols: int, nu: float = 3.0,
     return (rng.standard_t(nu, size=(rows, cols)) * scale).astype(np.float32)
 
 
+def attention_logits(rng: np.random.Generator, seq: int, kv: int, logit_std: float = 3.0) -> np.ndarray:
+    """One head's N(0, logit_std^2) attention logits, float32 (seq x kv)."""
+    return rng.standard_normal((seq, kv), dtype=np.float32) * np.float32(logit_std)
+
+
 def attention_probs(rng: np.random.Generator, heads: int, seq: int, kv: Optional[int] = None,
                     logit_std: float = 3.0) -> np.ndarray:
     """Row softmax of N(0, logit_std^2) logits, computed in float32; (heads, seq, kv)."""
     kv = seq if kv is None else kv
     out = np.empty((heads, seq, kv), dtype=np.float32)
     for h in range(heads):
-        z = rng.standard_normal((seq, kv), dtype=np.float32) * np.float32(logit_std)
+        z = attention_logits(rng, seq, kv, logit_std)
         z -= z.max(axis=1, keepdims=True)
         np.exp(z, out=z)
         z /= z.sum(axis=1, keepdims=True)
