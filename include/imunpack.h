@@ -332,6 +332,29 @@ imu_status imu_imunpack_matmul_prepared(const imu_matrix* a, const imu_matrix* b
                                         float* out, void* ws, size_t ws_bytes, size_t* ws_needed,
                                         imu_plan_info* info, hipStream_t stream);
 
+/* Attention probabilities P = row softmax of `logits`, quantized as the A
+ * operand of the attention-output GEMM P.V ("Key results", third bullet: the
+ * attention-output GEMMs; "Measured effects": RTN for all GEMMs).  Writes P
+ * (bf16, into `p`) and P's statistics (as imu_prepare_operand(p) would, into
+ * `stats`, imu_stats_bytes(p) bytes, contents replaced) for
+ * imu_imunpack_matmul_prepared; P's percentile histogram is counted while P
+ * is written, so P is not read for it.
+ * The page fixes no softmax arithmetic; P is the binary32 softmax fixed step
+ * by step: m = maxNum of the row, t = x - m, y = t * fl(log2 e); e = 0 when
+ * y < -100, else 2^n * poly(f) with n = rint(y), f = y - n and poly the
+ * degree-7 Taylor polynomial of 2^f (coefficients fl((ln 2)^k / k!), Horner,
+ * no fused multiply-add); S = the row's e summed by 64 lanes, lane l adding
+ * positions 256 j + 4 l + c (j = 0, 1, ..., c = 0..3) in order, then the 64
+ * lane sums halved pairwise (l and l + 32, then l + 16, ... l + 1); P =
+ * bf16 nearest-even of fl(e / S).  -Inf logits give P = 0; a row with a NaN
+ * or +Inf gives NaN probabilities, reported as IMU_ERR_NONFINITE by the call
+ * that uses the statistics.
+ * logits: IMU_F32 or IMU_BF16, IMU_NORMAL (the softmax runs along stored
+ * rows), rows x cols per batch entry.  p: IMU_BF16, IMU_NORMAL, the same rows,
+ * cols and batch, sharing no bytes with the logits.  Asynchronous. */
+imu_status imu_softmax_prepare(const imu_matrix* logits, const imu_matrix* p_out, const imu_params* p, void* stats,
+                               hipStream_t stream);
+
 /* Fixed part of the imu_imunpack_matmul workspace (statistics and plan); the
  * unpacked operands need sum over entries of (m_alloc + n_alloc) * k_pad more. */
 size_t imu_workspace_fixed_bytes(const imu_matrix* a, const imu_matrix* b, const imu_params* p);

@@ -122,6 +122,7 @@ def lib() -> ctypes.CDLL:
                                               P(ImuPlanInfo), V]),
         "imu_noalloc_scratch_bytes": (S, []),
         "imu_prepare_operand": (I32, [P(ImuMatrix), P(ImuParams), V, V]),
+        "imu_softmax_prepare": (I32, [P(ImuMatrix), P(ImuMatrix), P(ImuParams), V, V]),
         "imu_imunpack_matmul_prepared": (I32, [P(ImuMatrix), P(ImuMatrix), P(ImuParams), P(ImuPrepared),
                                                P(ImuPrepared), V, V, V, S, P(S), P(ImuPlanInfo), V]),
         "imu_init": (I32, [I64]),
@@ -139,7 +140,7 @@ EXPORTED = ("imu_init", "imu_release", "imu_stats_bytes", "imu_stats_layout", "i
             "imu_plan_layout", "imu_workspace_fixed_bytes", "imu_quantize_rtn", "imu_plan_unpack",
             "imu_unpack", "imu_unpacked_gemm", "imu_imunpack_matmul", "imu_status_string", "imu_last_error",
             "imu_version", "imu_set_gemm_events", "imu_imunpack_matmul_noalloc", "imu_noalloc_scratch_bytes",
-            "imu_prepare_operand", "imu_imunpack_matmul_prepared")
+            "imu_prepare_operand", "imu_imunpack_matmul_prepared", "imu_softmax_prepare")
 
 
 def _check(status: int):
@@ -467,6 +468,22 @@ def prepare_operand(x, p: ImuParams, stream=None) -> Stats:
     _check(lib().imu_prepare_operand(ctypes.byref(x.c()), ctypes.byref(p), _ptr(st.buf),
                                      ctypes.c_void_p(_stream(stream))))
     return st
+
+
+def softmax_prepare(logits, p: ImuParams, p_out: Optional[torch.Tensor] = None, stream=None):
+    """imu_softmax_prepare: P = row softmax of `logits` (2-D or 3-D, float32 or
+    bfloat16, row-major) as bfloat16 and P's statistics.  Returns (P, Stats)."""
+    z = _as_matrix(logits)
+    if z.layout != "normal":
+        raise ImunpackError(ERR_INVALID_ARG, "logits must be row-major (layout normal)")
+    t = z.stored
+    if p_out is None:
+        p_out = torch.empty(t.shape, dtype=torch.bfloat16, device=t.device)
+    pm = Matrix(p_out)
+    st = Stats(pm)
+    _check(lib().imu_softmax_prepare(ctypes.byref(z.c()), ctypes.byref(pm.c()), ctypes.byref(p), _ptr(st.buf),
+                                     ctypes.c_void_p(_stream(stream))))
+    return p_out, st
 
 
 def _prepared(pre) -> Optional[ImuPrepared]:

@@ -3,6 +3,7 @@
 // plan-header readback.  Contains no kernels; the device work lives in
 // quantize.hip, plan.hip, unpack.hip and gemm.hip.
 #include <algorithm>
+#include <utility>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -879,6 +880,49 @@ imu_status imu_prepare_operand(const imu_matrix* x, const imu_params* p, void* s
   J.op[0].batch = (int)x->batch;
   J.nops = 1;
   IMU_HIP(launch_residual(op.dtype, p->bits, J, stream));
+  return IMU_OK;
+}
+
+imu_status imu_softmax_prepare(const imu_matrix* logits, const imu_matrix* p_out, const imu_params* p,
+                               void* stats, hipStream_t stream) {
+  Operand oz, op;
+  IMU_TRY(check_matrix(logits, "logits", &oz));
+  IMU_TRY(check_matrix(p_out, "p", &op));
+  IMU_TRY(check_params(p));
+  if (!stats) return fail(IMU_ERR_INVALID_ARG, "stats is NULL");
+  if (logits->layout != IMU_NORMAL || p_out->layout != IMU_NORMAL)
+    return fail(IMU_ERR_UNSUPPORTED, "the softmax runs along stored rows: logits and p must be IMU_NORMAL");
+  if (p_out->dtype != IMU_BF16) return fail(IMU_ERR_INVALID_ARG, "p.dtype must be IMU_BF16");
+  if (logits->rows != p_out->rows || logits->cols != p_out->cols || logits->batch != p_out->batch)
+    return fail(IMU_ERR_INVALID_ARG, "logits and p must have the same rows, cols and batch");
+  // P must not share bytes with the logits (rows longer than 2048 are read again after P is written)
+  auto span = [](const imu_matrix* x, int elem) {
+    const int64_t n = (x->batch - 1) * (x->batch > 1 ? x->batch_stride : 0) + (x->rows - 1) * x->ld + x->cols;
+    const uintptr_t b = reinterpret_cast<uintptr_t>(x->data);
+    return std::make_pair(b, b + (uintptr_t)(n * elem));
+  };
+  const auto zs = span(logits, oz.elem), ps = span(p_out, 2);
+  if (zs.first < ps.second && ps.first < zs.second) return fail(IMU_ERR_INVALID_ARG, "p overlaps the logits");
+  uint8_t* st = static_cast<uint8_t*>(stats);
+  const StatsLayout L = stats_layout(op.R, op.C);
+  const int batch = (int)p_out->batch;
+  IMU_HIP(launch_fill_u32(st, 0u, L.stride * batch / 4, stream));
+  QuantJobs J{};
+  J.op[0].s = stream_args(op, st, L, p);
+  J.op[0].batch = batch;
+  J.nops = 1;
+  SoftmaxIn in{};
+  in.z = logits->data;
+  in.ld = logits->ld;
+  in.bstride = batch > 1 ? logits->batch_stride : 0;
+  const uintptr_t za = reinterpret_cast<uintptr_t>(logits->data), pa = reinterpret_cast<uintptr_t>(p_out->data);
+  const int zal = oz.elem * 4;  // bytes of 4 logits
+  in.vec_ok = za % zal == 0 && logits->ld % 4 == 0 && (batch == 1 || logits->batch_stride % 4 == 0) && pa % 8 == 0 &&
+              p_out->ld % 4 == 0 && (batch == 1 || p_out->batch_stride % 4 == 0);
+  J.op[0].s.bstride = batch > 1 ? p_out->batch_stride : 0;
+  IMU_HIP(launch_softmax_hist(oz.dtype, in, J, stream));
+  IMU_HIP(launch_round_count(IMU_BF16, p->bits, J, nullptr, nullptr, stream));
+  IMU_HIP(launch_residual(IMU_BF16, p->bits, J, stream));
   return IMU_OK;
 }
 

@@ -17,6 +17,14 @@ hipError_t launch_fill_2d(int32_t* p, int64_t rows, int64_t cols, int64_t ld, in
 hipError_t launch_hist(int dtype, QuantJobs J, int pass, int final_pass, hipStream_t s);
 hipError_t launch_round_count(int dtype, int bits, QuantJobs J, int32_t* q0, int32_t* q1, hipStream_t s);
 hipError_t launch_residual(int dtype, int bits, QuantJobs J, hipStream_t s);
+// Row softmax of logits into the bf16 operand of J.op[0] (its first
+// histogram pass included); the other passes follow as for any operand.
+struct SoftmaxIn {
+  const void* z;        // logits, rows x cols per batch entry (row-major)
+  int64_t ld, bstride;  // elements
+  int vec_ok;           // groups of 4 logits and of 4 outputs are aligned loads and stores
+};
+hipError_t launch_softmax_hist(int zdtype, const SoftmaxIn& in, QuantJobs J, hipStream_t s);
 
 // plan.hip
 struct PlanArgs {  // the plan headers must be zero when the planner starts (arrival counter)

@@ -387,6 +387,62 @@ __device__ __forceinline__ void select_two_level(StatsHeader* hd, const uint32_t
   if (lane == 0) apply_selection(hd, 0, final_pass, fhits ? bin : 0xFFFFFFFFu, blw, k, beta, hd->maxkey, hd->status);
 }
 
+// End of a first pass over 15-bit keys (kHistBins bins in LDS, counted by
+// every thread of the workgroup; smax and sbad hold the workgroup's largest
+// key and its non-finite flag): the bins and the coarse counts go to the
+// entry's global histogram, and the last workgroup of the entry selects the
+// percentile key.  Every flush is a device-scope atomic; each thread waits
+// until its own have completed before the arrival counter moves (a
+// device-scope release fence would also write back this XCD's whole L2,
+// which costs tens of us across the grid).  The last workgroup then acquires
+// at device scope, which drops stale cached lines before it reads the
+// histogram.  Ends with the bins zeroed for a next pass unless final_pass.
+__device__ __forceinline__ void finish_first_pass(const uint32_t* h, uint32_t smax, int sbad, uint32_t& slast,
+                                                  StatsHeader* hd, uint32_t* gh, int count, int64_t nelem,
+                                                  int final_pass, int beta, int p_num, int p_den) {
+  constexpr int NB = kHistBins;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // key bins: lane-consecutive bins, so that a wave's atomics fall on two
+  // 128-byte lines
+  for (int i = threadIdx.x; i < NB; i += blockDim.x) {
+    const uint32_t c = h[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+  // coarse counts: thread t sums bins [32t, 32t + 32) (16-byte reads, the
+  // chunk order rotated by lane so that 8 lanes read 8 different banks);
+  // four threads make one coarse bin, stored after the key bins
+  static_assert(NB == 32 * 1024, "one run of 32 bins per thread");
+  {
+    const int t = threadIdx.x;
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&h[32 * t + 4 * ((j + lane) & 7)]);
+      c += v.x + v.y + v.z + v.w;
+    }
+    c += __shfl_xor(c, 1, 64);
+    c += __shfl_xor(c, 2, 64);
+    if ((t & 3) == 0 && c) atomicAdd(&gh[NB + (t >> 2)], c);
+  }
+  if (threadIdx.x == 0) {
+    atomicMax(&hd->maxkey, smax);
+    if (sbad) atomicOr(&hd->status, kStatusNonfinite);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) slast = atomicAdd(&hd->arrive, 1u) == (uint32_t)(count - 1);
+  __syncthreads();
+  if (!slast) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (threadIdx.x == 0) hd->arrive = 0;  // ready for the next pass (stream ordered)
+  if (wave == 0) select_two_level(hd, gh, gh + NB, nelem, final_pass, beta, p_num, p_den);
+  if (!final_pass) {  // the next pass uses the first 256 bins
+    __syncthreads();
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) gh[i] = 0;
+  }
+}
+
 template <int DT, int NB, int PASS, bool VEC>
 __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass) {
   using T = typename Elem<DT>::T;
@@ -487,38 +543,16 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
     }
   }
   __syncthreads();
-  // key bins: lane-consecutive bins, so that a wave's atomics fall on two
-  // 128-byte lines
+  if constexpr (PASS == 0) {
+    finish_first_pass(h, smax, sbad, slast, hd, gh, jp.count, a.srows * a.scols, final_pass, a.beta, a.p_num,
+                      a.p_den);
+    return;
+  }
   for (int i = threadIdx.x; i < NB; i += blockDim.x) {
     const uint32_t c = h[i];
     if (c) atomicAdd(&gh[i], c);
   }
-  if constexpr (PASS == 0) {
-    // coarse counts: thread t sums bins [32t, 32t + 32) (16-byte reads, the
-    // chunk order rotated by lane so that 8 lanes read 8 different banks);
-    // four threads make one coarse bin, stored after the key bins
-    static_assert(NB == 32 * 1024, "one run of 32 bins per thread");
-    const int t = threadIdx.x;
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&h[32 * t + 4 * ((j + lane) & 7)]);
-      c += v.x + v.y + v.z + v.w;
-    }
-    c += __shfl_xor(c, 1, 64);
-    c += __shfl_xor(c, 2, 64);
-    if ((t & 3) == 0 && c) atomicAdd(&gh[NB + (t >> 2)], c);
-  }
-  if (PASS == 0 && threadIdx.x == 0) {
-    atomicMax(&hd->maxkey, smax);
-    if (sbad) atomicOr(&hd->status, kStatusNonfinite);
-  }
-  // The last workgroup of this entry selects.  Every flush above is a
-  // device-scope atomic; each thread waits until its own have completed before
-  // the arrival counter moves (a device-scope release fence would also write
-  // back this XCD's whole L2, which costs tens of us across the grid).  The
-  // last workgroup then acquires at device scope, which drops stale cached
-  // lines before it reads the histogram.
+  // The last workgroup of this entry selects (see finish_first_pass).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) slast = atomicAdd(&hd->arrive, 1u) == (uint32_t)(jp.count - 1);
@@ -526,15 +560,180 @@ __global__ __launch_bounds__(1024) void hist_kernel(QuantJobs J, int final_pass)
   if (!slast) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x == 0) hd->arrive = 0;  // ready for the next pass (stream ordered)
-  if constexpr (PASS == 0) {
-    if (wave == 0) select_two_level(hd, gh, gh + NB, a.srows * a.scols, final_pass, a.beta, a.p_num, a.p_den);
-    if (!final_pass) {  // the next pass uses the first 256 bins
-      __syncthreads();
-      for (int i = threadIdx.x; i < 256; i += blockDim.x) gh[i] = 0;
+  select_from_hist(st, a.hist, a.srows * a.scols, PASS, final_pass, a.beta, a.p_num, a.p_den, part, found, h);
+}
+
+// --- row softmax of attention logits + first histogram pass -----------------
+// The P operand of the attention-output GEMM P.V ("Key results", third
+// bullet) is the row softmax of the logits.  This kernel computes P, stores it
+// as bf16 and counts its 15-bit keys in the same pass, so P's percentile
+// needs no read of P.  The arithmetic is the binary32 softmax fixed step by
+// step (no contraction of a product and a sum into an fma):
+//   m = maxNum over the row; t = x - m; y = t * fl(log2 e);
+//   e = 0 when y < -100, else 2^n * poly(f), n = rint(y), f = y - n, poly the
+//       degree-7 Taylor polynomial of 2^f (coefficients fl((ln 2)^k / k!))
+//       by Horner;
+//   S = sum of e: lane l adds the row's positions 256 j + 4 l + c in order
+//       (j = 0, 1, ..., c = 0..3), then the 64 lane sums are halved pairwise
+//       (xor 32, 16, ..., 1);
+//   P = bf16 nearest-even of fl(e / S); a NaN becomes 0x7FC0.
+// One wave owns a row.  Rows of at most kSmRegChunks * 256 logits are held in
+// registers (one read); longer rows are read three times (max, sum, write),
+// recomputing the same e.
+constexpr int kSmRegChunks = 8;  // 2048 logits per row in registers
+constexpr float kSmLog2e = 0x1.715476p+0f;                    // fl(log2 e)
+constexpr float kSmC[8] = {0x1p+0f,        0x1.62e430p-1f,  0x1.ebfbe0p-3f,  0x1.c6b08ep-5f,
+                           0x1.3b2ab6p-7f, 0x1.5d87fep-10f, 0x1.430912p-13f, 0x1.ffcbfcp-17f};
+
+__device__ inline float sm_exp(float t) {
+#pragma clang fp contract(off)
+  const float y = t * kSmLog2e;
+  if (y != y) return y;
+  if (y < -100.0f) return 0.0f;
+  const float n = __builtin_rintf(y);  // in [-100, 0]
+  const float f = y - n;
+  float p = kSmC[7];
+#pragma unroll
+  for (int k = 6; k >= 0; --k) p = p * f + kSmC[k];
+  return p * __int_as_float(((int)n + 127) << 23);  // exact: 2^n and the product are normal
+}
+__device__ inline uint32_t sm_bf16(float p) {
+  const uint32_t u = __float_as_uint(p);
+  return p != p ? 0x7FC0u : (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+template <int DT>
+__device__ inline void sm_load4(const typename Elem<DT>::T* row, int64_t i, int64_t n, bool vec, float fill,
+                                float (&v)[4]) {
+  if (vec && i + 3 < n) {
+    if constexpr (DT == IMU_F32) {
+      const float4 x = *reinterpret_cast<const float4*>(row + i);
+      v[0] = x.x, v[1] = x.y, v[2] = x.z, v[3] = x.w;
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(row + i);
+      v[0] = __uint_as_float(x.x << 16), v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(x.y << 16), v[3] = __uint_as_float(x.y & 0xFFFF0000u);
     }
   } else {
-    select_from_hist(st, a.hist, a.srows * a.scols, PASS, final_pass, a.beta, a.p_num, a.p_den, part, found, h);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (DT == IMU_F32) v[c] = i + c < n ? row[i + c] : fill;
+      else v[c] = i + c < n ? __uint_as_float((uint32_t)row[i + c] << 16) : fill;
+    }
   }
+}
+
+template <int DT>
+__global__ __launch_bounds__(1024) void softmax_hist_kernel(QuantJobs J, SoftmaxIn in) {
+#pragma clang fp contract(off)
+  using T = typename Elem<DT>::T;
+  __shared__ __attribute__((aligned(16))) uint32_t h[kHistBins];
+  __shared__ uint32_t smax;
+  __shared__ int sbad;
+  __shared__ uint32_t slast;
+  const JobPos jp = find_job(J, blockIdx.x);
+  if (jp.count == 0) return;
+  const StreamArgs& a = J.op[0].s;  // P: bf16, rows x cols, the statistics' operand
+  uint16_t* pb = static_cast<uint16_t*>(const_cast<void*>(a.x)) + jp.entry * a.bstride;
+  const T* zb = static_cast<const T*>(in.z) + jp.entry * in.bstride;
+  uint8_t* st = a.stats + jp.entry * a.stats_stride;
+  StatsHeader* hd = reinterpret_cast<StatsHeader*>(st);
+  uint32_t* gh = reinterpret_cast<uint32_t*>(st + a.hist);
+  const int lane = threadIdx.x & 63, nwave = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t R = a.srows, N = a.scols;
+  const int64_t r0 = R * jp.local / jp.count, r1 = R * (jp.local + 1) / jp.count;
+  const bool vec = in.vec_ok != 0;
+  static_assert(kHistBins % 4 == 0, "16-byte clears");
+  for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x) reinterpret_cast<uint4*>(h)[i] = uint4{0, 0, 0, 0};
+  if (threadIdx.x == 0) smax = 0, sbad = 0;
+  __syncthreads();
+  uint32_t mx = 0;  // largest key, as a binary32 magnitude pattern
+  auto emit = [&](uint16_t* prow, int64_t i, const float (&e)[4], float S) __attribute__((always_inline)) {
+    uint32_t b[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      b[c] = sm_bf16(e[c] / S);
+      if (i + c < N) {
+        atomicAdd(&h[b[c] & 0x7FFFu], 1u);
+        mx = max(mx, (b[c] & 0x7FFFu) << 16);
+      }
+    }
+    if (vec && i + 3 < N) {
+      *reinterpret_cast<uint2*>(prow + i) = uint2{b[0] | b[1] << 16, b[2] | b[3] << 16};
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (i + c < N) prow[i + c] = (uint16_t)b[c];
+    }
+  };
+  for (int64_t r = r0 + wave; r < r1; r += nwave) {
+    const T* zrow = zb + r * in.ld;
+    uint16_t* prow = pb + r * a.ld;
+    if (N <= 256 * kSmRegChunks) {
+      float v[kSmRegChunks][4];
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < kSmRegChunks; ++j) {
+        if (256 * j < N) {
+          sm_load4<DT>(zrow, 256 * j + 4 * lane, N, vec, -__builtin_inff(), v[j]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) m = fmaxf(m, v[j][c]);
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kSmRegChunks; ++j) {
+        if (256 * j < N) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            v[j][c] = sm_exp(v[j][c] - m);
+            if (256 * j + 4 * lane + c < N) acc = acc + v[j][c];
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, 64);
+#pragma unroll
+      for (int j = 0; j < kSmRegChunks; ++j)
+        if (256 * j < N) emit(prow, 256 * j + 4 * lane, v[j], acc);
+    } else {
+      float m = -__builtin_inff();
+      for (int64_t j0 = 0; j0 < N; j0 += 256) {
+        float v[4];
+        sm_load4<DT>(zrow, j0 + 4 * lane, N, vec, -__builtin_inff(), v);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m = fmaxf(m, v[c]);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float acc = 0.0f;
+      for (int64_t j0 = 0; j0 < N; j0 += 256) {
+        float v[4];
+        sm_load4<DT>(zrow, j0 + 4 * lane, N, vec, -__builtin_inff(), v);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (j0 + 4 * lane + c < N) acc = acc + sm_exp(v[c] - m);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o, 64);
+      for (int64_t j0 = 0; j0 < N; j0 += 256) {
+        float v[4];
+        sm_load4<DT>(zrow, j0 + 4 * lane, N, vec, -__builtin_inff(), v);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = sm_exp(v[c] - m);
+        emit(prow, j0 + 4 * lane, v, acc);
+      }
+    }
+  }
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    atomicMax(&smax, mx);
+    if (mx >= 0x7F800000u) atomicOr(&sbad, 1);  // a NaN row
+  }
+  __syncthreads();
+  finish_first_pass(h, smax, sbad, slast, hd, gh, jp.count, R * N, 1, a.beta, a.p_num, a.p_den);
 }
 
 // --- fused RTN + outlier statistics -------------------------------------------
@@ -934,6 +1133,20 @@ static hipError_t hist_vec(int dtype, QuantJobs& J, int pass, int final_pass, hi
 
 hipError_t launch_hist(int dtype, QuantJobs J, int pass, int final_pass, hipStream_t s) {
   return all_vec(J) ? hist_vec<true>(dtype, J, pass, final_pass, s) : hist_vec<false>(dtype, J, pass, final_pass, s);
+}
+
+hipError_t launch_softmax_hist(int zdtype, const SoftmaxIn& in, QuantJobs J, hipStream_t s) {
+  // about one 1024-thread workgroup per CU (the 128 KB histogram allows one),
+  // split over the batch entries by rows
+  QuantOp& q = J.op[0];
+  constexpr int kWgs = 256;
+  q.wgs_per_entry = (int)min64(max64(ceil_div(kWgs, q.batch), 1), max64(q.s.srows, 1));
+  q.wg_begin = 0;
+  J.nops = 1;
+  const int grid = q.wgs_per_entry * q.batch;
+  if (zdtype == IMU_F32) hipLaunchKernelGGL((softmax_hist_kernel<IMU_F32>), dim3(grid), dim3(1024), 0, s, J, in);
+  else hipLaunchKernelGGL((softmax_hist_kernel<IMU_BF16>), dim3(grid), dim3(1024), 0, s, J, in);
+  return hipGetLastError();
 }
 
 // Count kernels: tiles of 512 columns x rows_per_wg rows, about kCountWgs workgroups

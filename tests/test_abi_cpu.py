@@ -181,3 +181,26 @@ def test_training_wrapper_rejects_bad_shapes():
         T.imunpack_linear(torch.zeros(4, 3), torch.zeros(5, 2), p)
     with pytest.raises(B.ImunpackError):
         T.imunpack_linear(torch.zeros(4, 3, 2), torch.zeros(5, 3), p)
+
+
+def test_softmax_prepare_validates_before_any_device_work(lib):
+    """imu_softmax_prepare: P must be bf16, row-major, the logits' shape, and
+    apart from the logits; each violation is refused synchronously."""
+    p = B.params()
+    st = ctypes.c_void_p(1)  # never written: every call below fails validation
+    call = lambda z, o, prm=p, s=st: lib.imu_softmax_prepare(ctypes.byref(z), ctypes.byref(o), ctypes.byref(prm),
+                                                             s, None)
+    z = B.Matrix(torch.zeros((16, 40), dtype=torch.float32)).c()
+    assert call(z, B.Matrix(torch.zeros((16, 40), dtype=torch.float32)).c()) == B.ERR_INVALID_ARG
+    assert b"bf16" in lib.imu_last_error().lower() or b"BF16" in lib.imu_last_error()
+    assert call(z, B.Matrix(torch.zeros((16, 41), dtype=torch.bfloat16)).c()) == B.ERR_INVALID_ARG
+    assert call(z, B.Matrix(torch.zeros((40, 16), dtype=torch.bfloat16), "transposed").c()) == B.ERR_UNSUPPORTED
+    zt = B.Matrix(torch.zeros((40, 16), dtype=torch.float32), "transposed").c()
+    assert call(zt, B.Matrix(torch.zeros((16, 40), dtype=torch.bfloat16)).c()) == B.ERR_UNSUPPORTED
+    buf = torch.zeros((16, 40), dtype=torch.bfloat16)
+    same = B.Matrix(buf).c()
+    assert call(same, same) == B.ERR_INVALID_ARG and b"overlap" in lib.imu_last_error()
+    assert call(z, B.Matrix(buf).c(), s=None) == B.ERR_INVALID_ARG
+    bad = B.params()
+    bad.bits = 9
+    assert call(z, B.Matrix(buf).c(), prm=bad) == B.ERR_INVALID_ARG
