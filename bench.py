@@ -331,6 +331,56 @@ def static_weight(pr, a, b, p_mix, prm, steps: int, warmup: int):
                                        "note": "A row-unpacked so that B'^T depends on W alone; staged entry points"}}
 
 
+def from_logits(v, p, M, N, K, nb, steps: int):
+    """The attention output from its logits (fused softmax -> quantize): the
+    logits of this workload's P (fp32, resident), imu_softmax_prepare against
+    torch's softmax + bf16 cast + imu_prepare_operand, and the whole step
+    logits -> P.V through the prepared product.  Algorithmic bytes of the
+    fused softmax: 4 (logit read) + 2 (P write) per element."""
+    import torch
+    from outlier_unpacking_quantization_amd import binding as B
+    from outlier_unpacking_quantization_amd import workloads as W
+    z = torch.from_numpy(W.attn_logits(1003, nb, M)).to("cuda")
+    P = torch.empty(z.shape, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((nb, M, N), dtype=torch.int32, device="cuda")
+    out = torch.empty((nb, M, N), dtype=torch.float32, device="cuda")
+    ws = B.Workspace("cuda")
+
+    def fused():
+        return B.softmax_prepare(z, p, p_out=P)[1]
+
+    def separate():
+        P.copy_(torch.softmax(z, dim=-1))
+        return B.prepare_operand(B.Matrix(P), p)
+
+    def whole():
+        st = fused()
+        return B.imunpack_matmul_prepared(B.Matrix(P), v, p, pre_a=st, out=out, c=c, ws=ws)
+
+    def timed(fn):
+        warm_up(fn, 2, torch)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+        for i in range(steps):
+            ev[2 * i].record()
+            fn()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        return float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)])) / 1000.0
+
+    t_fused, t_sep, t_whole = timed(fused), timed(separate), timed(whole)
+    elems = nb * M * K
+    # algorithmic bytes of the call: logits read (4) and P written (2) by the
+    # fused softmax + histogram, P read by the count (2) and residual (2) passes
+    call_bytes = 10 * elems
+    return {"logits": f"{nb} x {M} x {K} fp32 (the softmax inputs of this workload's P, resident)",
+            "softmax_prepare_us": round(t_fused * 1e6, 2),
+            "torch_softmax_then_prepare_us": round(t_sep * 1e6, 2),
+            "step_ms": round(t_whole * 1e3, 4), "tops": round(2.0 * M * N * K * nb / t_whole / 1e12, 3),
+            "softmax_prepare_hbm": {"bytes": call_bytes, "gbs": round(call_bytes / t_fused / 1e9, 1),
+                                    "frac_of_8tbs": round(call_bytes / t_fused / 8e12, 4),
+                                    "note": "whole call; 10 B per element (4 + 2 softmax, 2 count, 2 residual)"}}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -562,6 +612,8 @@ def main():
     }
     if nb == 1 and pr.b.layout == "transposed":
         rec["static_weight"] = static_weight(pr, a, b, p, prm, max(3, args.pair_steps), 2)
+    if pr.name == "attn_out":
+        rec["from_logits"] = from_logits(b, p, M, N, K, nb, max(5, args.pair_steps))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pr)
     print(json.dumps(rec))

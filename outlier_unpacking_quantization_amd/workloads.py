@@ -219,6 +219,13 @@ def attn_out(seed: int = 1003, heads: int = 32, seq: int = 2048, dim: int = 128)
                    _store("V", v, "bf16", "normal"), beta=15, bits=5)
 
 
+def attn_logits(seed: int = 1003, heads: int = 32, seq: int = 2048) -> np.ndarray:
+    """The logits the attention-output problem's P is the softmax of (the same
+    draws as ``attn_out`` with the same seed): (heads, seq, seq) float32."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.stack([attention_logits(rng, seq, seq) for _ in range(heads)])
+
+
 def training(seed: int = 1004, tokens: int = 8192, d_in: int = 768, d_out: int = 3072) -> List[Problem]:
     """Forward, dgrad and wgrad GEMMs of a d_in -> d_out linear layer; beta=31, b=4, Mix.
 
