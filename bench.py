@@ -48,12 +48,12 @@ PAGE_RATIOS = {"mix": 1.06, "row/row": 2.02, "row/col": 5.36, "col/row": 1.64, "
 # the GEMM source: when gemm.hip no longer hashes to `source_sha256` the
 # traffic is reported as null.
 GEMM_TRAFFIC = {
-    ("mlp_up", "fp6"): {"source_sha256": "79f07262db18e6a6ac657097dbee831c7293dbbfe6901a08b1f51924493bc061",
-                        "fetch_kib": 1494980.6, "write_kib": 385293.3, "fetch_factor": 1.9998, "write_factor": 1.0000,
-                        "bytes_per_launch": 3455954436},
-    ("llama_linear", "int8"): {"source_sha256": "79f07262db18e6a6ac657097dbee831c7293dbbfe6901a08b1f51924493bc061",
-                               "fetch_kib": 151227.5, "write_kib": 65536.0, "fetch_factor": 1.9998,
-                               "write_factor": 1.0000, "bytes_per_launch": 376791813},
+    ("mlp_up", "fp6"): {"source_sha256": "4ac18924ace4f1418e62a0f320e35befe56895c86288846135d44db868ec13df",
+                        "fetch_kib": 1500406.8, "write_kib": 385203.8, "fetch_factor": 1.9998, "write_factor": 1.0000,
+                        "bytes_per_launch": 3466974534},
+    ("llama_linear", "int8"): {"source_sha256": "4ac18924ace4f1418e62a0f320e35befe56895c86288846135d44db868ec13df",
+                               "fetch_kib": 151225.5, "write_kib": 65536.0, "fetch_factor": 1.9998,
+                               "write_factor": 1.0000, "bytes_per_launch": 376787717},
 }
 
 
@@ -88,6 +88,8 @@ def parse():
                     help="digit format of the unpacked operands (auto: fp6 where it applies)")
     ap.add_argument("--pair-steps", type=int, default=5, help="timed steps of each fixed row/column pairing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-logits", action="store_true",
+                    help="attention workload: time imu_softmax_prepare on its logits only (for profiler runs)")
     ap.add_argument("--only-steps", action="store_true",
                     help="run the warm steps only (no cold, per-stage, fixed-pair or CPU legs): for profiler runs")
     ap.add_argument("--training-step", action="store_true",
@@ -331,6 +333,30 @@ def static_weight(pr, a, b, p_mix, prm, steps: int, warmup: int):
                                        "note": "A row-unpacked so that B'^T depends on W alone; staged entry points"}}
 
 
+def only_logits(args):
+    """imu_softmax_prepare on the attention workload's logits, warm steps only."""
+    import torch
+    from outlier_unpacking_quantization_amd import binding as B
+    from outlier_unpacking_quantization_amd import workloads as W
+    pr = W.config(3)[0]
+    z = torch.from_numpy(W.attn_logits(1003, pr.a.batch, pr.a.rows)).to("cuda")
+    P = torch.empty(z.shape, dtype=torch.bfloat16, device="cuda")
+    p = B.params(beta=pr.beta, bits=pr.bits, p=(pr.p_num, pr.p_den))
+
+    def call():
+        return B.softmax_prepare(z, p, p_out=P)
+
+    n_warm = warm_up(call, args.warmup, torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"workload": "attn_out logits", "shape": list(z.shape), "steps": args.steps,
+                      "warmup_steps_run": n_warm, "softmax_prepare_us": round(t * 1e6, 2)}))
+
+
 def from_logits(v, p, M, N, K, nb, steps: int):
     """The attention output from its logits (fused softmax -> quantize): the
     logits of this workload's P (fp32, resident), imu_softmax_prepare against
@@ -394,6 +420,9 @@ def main():
         return
     if args.training_step:
         training_step(args)
+        return
+    if args.only_logits:
+        only_logits(args)
         return
 
     import torch
