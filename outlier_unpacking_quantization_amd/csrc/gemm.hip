@@ -222,7 +222,12 @@ __device__ inline bool walk_step(Walk& c, int nseg, int nlev, SegTable off) {
 
 typedef __attribute__((address_space(4))) const PlanHeader* HdrC;
 
-constexpr int kMaxLevels = 32;  // digits of an int32 code in base 2^(bits-1), bits >= 2: at most 31
+constexpr int kMaxLevels = 32;
+
+// 64 zero bytes in global memory: a B staging load for a slot that is absent
+// at a level (its column has fewer levels) reads here, at the same bytes every
+// step, so the staged tile needs no per-step selection.
+__device__ __attribute__((aligned(64))) const int8_t kZeroBlock[64] = {};  // digits of an int32 code in base 2^(bits-1), bits >= 2: at most 31
 
 // FOLD: the base pass also folds the extra columns of entries whose plan has
 // extra columns only (their levels w > 0 land on the tile's own columns), so
@@ -309,8 +314,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int nseg = ph->n_seg;
   // levels of the tile's columns (1 unless this entry folds extra columns)
   int nlev = 1;
-  int64_t gbo[NB];   // byte offsets of the B staging rows at lb's level (FOLD)
-  uint32_t bvm = 0xF, bvl = 0xF;  // rows present at lb's level / in the last load (FOLD)
+  // B staging rows at lb's level (FOLD): source of row j = gbase + gbo[j] +
+  // (step byte offset & kmsk[j]); absent rows point at kZeroBlock with mask 0
+  int64_t gbo[NB];
+  uint32_t kmsk[NB];
   if constexpr (FOLD) {
     // levels present in the tile: B's columns are in depth order, so level w
     // is present iff some slot of the tile lies below lvcnt_b[w]
@@ -319,18 +326,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   }
   // B staging rows of level w for this thread (FOLD): slot col0 + c of level
   // w > 0 is B'^T row lvbase_b[w] + col0 + c; slots past lvcnt_b[w] are absent
-  // (their column has fewer levels): they re-read the tile's first row of that
-  // level, which is present, and are zeroed when stored
+  // (their column has fewer levels) and stage zeros from kZeroBlock
+  const int64_t zoff = (int64_t)((intptr_t)kZeroBlock - (intptr_t)gbase);
   auto set_level = [&](int w) __attribute__((always_inline)) {
-    bvm = 0;
     const int64_t cnt = w == 0 ? n_alloc : (int64_t)ph->lvcnt_b[w];
     const int64_t base = w == 0 ? 0 : ph->lvbase_b[w];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int c = br + 32 * j;
       const bool live = col0 + c < cnt;
-      gbo[j] = (base + col0 + (live ? c : 0)) * rowb;
-      bvm |= (uint32_t)live << j;
+      gbo[j] = live ? (base + col0 + c) * rowb : zoff;
+      kmsk[j] = live ? 0xFFFFFFFFu : 0u;
     }
   };
   if constexpr (FOLD) set_level(0);
@@ -363,29 +369,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   }
 #define IMU_LOAD_B(k)                                                                          \
   {                                                                                            \
-    const int64_t kb_ = (int64_t)(min((k), k_last) / 4) * (F6 ? 3 : 4);  /* byte offset of the step */ \
+    const uint32_t kb_ = (uint32_t)(min((k), k_last) / 4) * (F6 ? 3u : 4u);  /* byte offset of the step */ \
     if constexpr (F6) {                                                                        \
-      const int8_t* pb_ = (FOLD ? gbase + gbo[0] : gb) + kb_;                                  \
+      const int8_t* pb_ = FOLD ? gbase + gbo[0] + (kb_ & kmsk[0]) : gb + kb_;                  \
       _Pragma("unroll") for (int j = 0; j < 3; ++j) bs[j] = *reinterpret_cast<const v4i*>(pb_ + 16 * j); \
-      if constexpr (FOLD) bvl = bvm;                                                           \
     } else if constexpr (FOLD) {                                                               \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gbase + gbo[j] + kb_); \
-      bvl = bvm;                                                                               \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                            \
+        bs[j] = *reinterpret_cast<const v4i*>(gbase + gbo[j] + (kb_ & kmsk[j]));              \
     } else {                                                                                   \
       _Pragma("unroll") for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const v4i*>(gb + j * gb_j + kb_); \
     }                                                                                          \
   }
 #define IMU_STORE_B(buf)                                                                       \
   if constexpr (F6) {                                                                          \
-    const bool live_ = !FOLD || (bvl & 1u);                                                    \
     _Pragma("unroll") for (int j = 0; j < 3; ++j) {                                            \
-      const v4i x_ = live_ ? bs[j] : v4i{0, 0, 0, 0};                                          \
-      *reinterpret_cast<v2i*>(&sB[buf][sb_w + 16 * j]) = v2i{x_.x, x_.y};                      \
-      *reinterpret_cast<v2i*>(&sB[buf][sb_w + 16 * j + 8]) = v2i{x_.z, x_.w};                  \
+      *reinterpret_cast<v2i*>(&sB[buf][sb_w + 16 * j]) = v2i{bs[j].x, bs[j].y};                \
+      *reinterpret_cast<v2i*>(&sB[buf][sb_w + 16 * j + 8]) = v2i{bs[j].z, bs[j].w};            \
     }                                                                                          \
   } else {                                                                                     \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(&sB[buf][sb_w + j * 32 * SB]) = \
-        (!FOLD || ((bvl >> j) & 1u)) ? bs[j] : v4i{0, 0, 0, 0};                                \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(&sB[buf][sb_w + j * 32 * SB]) = bs[j]; \
   }
 #define IMU_ADV_B()                                                                            \
   if (walk_step<FOLD>(lb, nseg, nlev, off)) {                                                  \
@@ -438,7 +440,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   walk_step<FOLD>(la, nseg, nlev, off);
   __syncthreads();
   IMU_READ_B(0, sB[0], 0);
-  for (int64_t i = 0; i < steps; ++i) {
+  const int nsteps = (int)steps;  // kp / BK * nlev < 2^29
+  for (int i = 0; i < nsteps; ++i) {
     if (cc.e != prev_e) {  // Horner: the exponents between the two steps
       if constexpr (F6) flush_f32(acc, accf), f32_steps = 0;
       shift_acc(acc, shift * (prev_e - cc.e));
