@@ -8,12 +8,15 @@
 // that power, so the scaled sum of the narrow products is the original integer
 // product.  The digits are int8 bytes (v_mfma_i32_32x32x32_i8, int32
 // accumulators) or, for bits <= 4, e2m3 codes (v_mfma_f32_32x32x64_f8f6f4:
-// every product is an integer of magnitude at most 49, the fp32 accumulators
-// hold one exponent's partial sums, exact below 2^24, and move into int32
-// accumulators at each exponent change and every kF32Steps steps).  K' is split
-// into exponent segments; walking them from the highest exponent down,
-// acc = acc * 2^(bits-1) + P_e (Horner), so one set of int32 accumulators holds
-// sum_e 2^((bits-1)e) P_e.  The unpacked row (i, u) and column (n, w) fold
+// every product is an integer of magnitude at most 49, and the fp32
+// accumulators hold integers, exact while their magnitude stays at most 2^24).
+// K' is split into exponent segments; walking them from the highest exponent
+// down, acc = acc * 2^(bits-1) + P_e (Horner), so one set of accumulators holds
+// sum_e 2^((bits-1)e) P_e.  With fp6 digits each wave keeps an upper bound on
+// its |acc| (a K step adds at most 128 (2^(bits-1)-1)^2); when the next step
+// or Horner shift could pass 2^24 it takes the true maximum, and if that is
+// still too large it adds its exact partial sum, shifted to its exponent, into
+// C (int32 arithmetic modulo 2^32) and restarts from zero.  The unpacked row (i, u) and column (n, w) fold
 // into C[i, n] with a further shift of (bits-1)(u+w); all int32 arithmetic
 // wraps modulo 2^32.  Extra columns (w > 0) of a plan without extra rows are
 // folded inside the base tile of their original columns: the shift is one
@@ -66,7 +69,7 @@ constexpr int BM = 128 * FR, BN = 128, BK = 128;
 constexpr int kThreads = 256;
 constexpr int BSTR = BK + 16;  // LDS bytes per staged B row
 constexpr int BSTR6 = BK / 4 * 3 + 8;  // fp6: 96 bytes of a step plus 8 (row r starts at bank 26 r mod 32)
-constexpr int kF32Steps = 2048;        // fp6: steps an fp32 partial sum may take (2048 * 128 * 49 < 2^24)
+constexpr uint32_t kF32Exact = 1u << 24;  // integers up to 2^24 in magnitude are exact in binary32
 constexpr int kXcds = 8;
 static_assert(BK == kKPad, "a K step must not straddle exponent segments");
 
@@ -125,19 +128,6 @@ __device__ inline void quad_transpose(int (&x)[4]) {
   x[3] = odd ? x[3] : s[2];
 }
 
-// fp6: the exact integer partial sums of the fp32 accumulators move into
-// the int32 ones (at the same exponent), which leaves the fp32 ones zero.
-__device__ inline void flush_f32(v16i (&acc)[FR][4], v16f (&accf)[FR][4]) {
-#pragma unroll
-  for (int i = 0; i < FR; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = (int)((uint32_t)acc[i][j][r] + (uint32_t)(int)accf[i][j][r]);
-      accf[i][j] = v16f{0.f};
-    }
-}
-
 __device__ inline void shift_acc(v16i (&acc)[FR][4], int sh) {
 #pragma unroll
   for (int i = 0; i < FR; ++i)
@@ -146,6 +136,32 @@ __device__ inline void shift_acc(v16i (&acc)[FR][4], int sh) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = sh >= 32 ? 0 : (int)((uint32_t)acc[i][j][r] << sh);
 }
+// fp6: multiply the accumulators by 2^sh, 0 <= sh <= 24 (exact: a power of
+// two, and the products stay finite)
+__device__ inline void shift_acc(v16f (&acc)[FR][4], int sh) {
+  const float f = __int_as_float((127 + sh) << 23);
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] *= f;
+}
+// fp6: largest |acc| of the wave (an integer at most 2^24), wave-uniform
+__device__ inline uint32_t wave_absmax(const v16f (&acc)[FR][4]) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = __builtin_fmaxf(m, __builtin_fabsf(acc[i][j][r]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)m);
+}
+// an accumulator as the int32 it stands for, times 2^sh, modulo 2^32 (fp6
+// accumulators hold integers of magnitude at most 2^24)
+__device__ inline int32_t acc_int(int32_t v, int sh) { return sh >= 32 ? 0 : (int32_t)((uint32_t)v << sh); }
+__device__ inline int32_t acc_int(float v, int sh) { return sh >= 32 ? 0 : (int32_t)((uint32_t)(int32_t)v << sh); }
 
 // Position in a walk over K' steps.  Without column folding the walk takes
 // the segments s from the highest exponent down (empty segments skipped), the
@@ -234,11 +250,11 @@ __device__ __attribute__((aligned(64))) const int8_t kZeroBlock[64] = {};  // di
 // those entries need no atomic pass.
 // F6: fp6 digits (e2m3 codes) on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
 // scales): a K step is two substeps of 64 positions; the fp32 accumulators
-// hold one exponent's partial sums (integers below 2^24 in magnitude, so
-// exact), which move into the int32 Horner accumulators at every exponent
-// change and every kF32Steps steps.
+// run the Horner sum themselves, kept at most 2^24 in magnitude (so exact) by
+// the wave's bound and its flushes into C.  With a single set of
+// accumulators the kernel fits two workgroups per CU.
 template <bool FOLD, bool F6>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads, F6 ? 2 : 1) void gemm_kernel(GemmArgs g) {
   constexpr int SB = F6 ? BSTR6 : BSTR;  // LDS bytes per staged B row
   constexpr int NQ = F6 ? 2 : 4;         // MFMA substeps per K step
   __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * SB];
@@ -303,12 +319,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int sb_r = (lane & 31) * SB + (F6 ? 24 : 16) * (lane >> 5);
   const int k_last = (int)(kp - BK);  // loads past the walk re-read the last step (never used)
 
-  v16i acc[FR][4];
-  v16f accf[FR][4];  // fp6: the current exponent's partial sums
+  using Acc = std::conditional_t<F6, v16f, v16i>;
+  Acc acc[FR][4];
 #pragma unroll
   for (int i = 0; i < FR; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16i{0}, accf[i][j] = v16f{0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{0};
 
   const SegTable off = (SegTable)ph->seg_off;
   const int nseg = ph->n_seg;
@@ -346,7 +362,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   Walk la = cc, lb = cc;  // A loads (one step ahead), B loads (two ahead)
   int lbw = 0;            // level of lb's rows (FOLD)
   int prev_e = cc.e;   // exponent of the accumulators' contents
-  int f32_steps = 0;   // fp6: steps in the fp32 accumulators
+  // fp6: upper bound on the wave's |acc| (wave-uniform), what one K step can
+  // add to it, and whether the wave has already added a partial sum into C
+  uint32_t ub = 0;
+  const uint32_t step_add = (uint32_t)(((1 << shift) - 1) * ((1 << shift) - 1) * BK);
+  bool flushed = false;
 
   using Frag = std::conditional_t<F6, v8i, v4i>;  // MFMA operand (fp6: 6 of the 8 dwords)
   Frag ar[NQ][FR];  // A fragments of the current step, refilled substep by substep
@@ -413,10 +433,112 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   _Pragma("unroll") for (int f = 0; f < FR; ++f)                                                   \
   _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                  \
     if constexpr (F6)                                                                              \
-      accf[f][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ar[q][f], bf[d][j], accf[f][j], 2, 2, 0, 0, 0, 0); \
+      acc[f][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ar[q][f], bf[d][j], acc[f][j], 2, 2, 0, 0, 0, 0); \
     else                                                                                           \
       acc[f][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ar[q][f], bf[d][j], acc[f][j], 0, 0, 0);   \
   }
+
+  // C stores of the wave's accumulators, each taken as the integer it holds
+  // times 2^esh (modulo 2^32).  add: add to C (entries whose extra rows were
+  // folded first, or after an earlier flush of this wave); last: also write the
+  // dequantized output.
+  auto store_c = [&](int esh, bool add, bool last) __attribute__((always_inline)) {
+    // accumulator register r of lane l holds element
+    // (8*(r/4) + 4*(l/32) + r%4, l%32) of each 32x32 block.  Rows are visited one
+    // at a time (f, r/4, r%4) with the four column blocks j of the row, so only a
+    // row's pointers are live.
+    const float sab = sa->s * sb->s;
+    const int64_t ldc = g.ldc;
+    int64_t r_lane = row0 + 4 * (lane >> 5), c_lane = col0 + (lane & 31);
+    // a flush sits in the K loop: its addresses are made opaque there, so the
+    // compiler cannot hoist (and spill) them ahead of the loop
+    if (!last) asm volatile("" : "+v"(r_lane), "+v"(c_lane));
+    if (mode == 2) {  // extra tiles: every element lands on some C[i, n] with its shift
+#pragma unroll
+      for (int f = 0; f < FR; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t gr = r_lane + f * 32 + 8 * (r >> 2) + (r & 3);
+            const int64_t gc = c_lane + j * 32;
+            const int32_t am = amap[gr], bm = bmap[gc];
+            if (am < 0 || bm < 0) continue;
+            const int sh = esh + shift * ((am >> 24) + (bm >> 24));
+            if (sh >= 32) continue;
+            atomicAdd(&c_e[(int64_t)(am & 0xFFFFFF) * ldc + (bm & 0xFFFFFF)], acc_int(acc[f][j][r], sh));
+          }
+      return;
+    }
+    // Base tiles.  A 4 x 4 transpose inside each quad of lanes turns the four
+    // rows r4 * 8 + 4 * (l / 32) + 0..3 held at column l % 32 into four
+    // consecutive columns of row ... + l % 4, so each lane stores 16 bytes and a
+    // store instruction covers eight full 128-byte row segments.  Needs 16-byte
+    // aligned rows and the whole tile inside N; otherwise one element per store.
+    // With B's columns in depth order (b_perm) the tile's slots map to scattered
+    // columns of C: element stores through the column map.  A flush (not
+    // last) also takes element stores, which need fewer registers.
+    const bool bperm = ph->b_perm != 0;
+    const bool vec = last && !bperm && (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c_e) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(out_e) & 15) == 0 && col0 + BN <= g.N;
+    if (vec) {
+      const int64_t r_v = row0 + 4 * (lane >> 5) + (lane & 3), c_v = col0 + 4 * ((lane & 31) >> 2);
+#pragma unroll
+      for (int f = 0; f < FR; ++f)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t gr = r_v + f * 32 + 8 * r4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            int x[4] = {acc_int(acc[f][j][4 * r4], esh), acc_int(acc[f][j][4 * r4 + 1], esh),
+                        acc_int(acc[f][j][4 * r4 + 2], esh), acc_int(acc[f][j][4 * r4 + 3], esh)};
+            quad_transpose(x);
+            if (gr < g.M) {
+              v4u v = {(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
+              v4u* cp = reinterpret_cast<v4u*>(c_e + gr * ldc + c_v + 32 * j);
+              if (add) v += *cp;
+              *cp = v;
+              if (last && out_e) {
+                const float4 o = {(float)(int32_t)v.x * sab, (float)(int32_t)v.y * sab, (float)(int32_t)v.z * sab,
+                                  (float)(int32_t)v.w * sab};
+                *reinterpret_cast<float4*>(out_e + gr * ldc + c_v + 32 * j) = o;
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      return;
+    }
+    // column of C held by this lane in block j (slot c_lane + 32 j), -1 past N
+    int64_t cmapx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t slot = c_lane + 32 * j;
+      cmapx[j] = slot >= g.N ? -1 : bperm ? (int64_t)(bmap[slot] & 0xFFFFFF) : slot;
+    }
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+#pragma unroll
+        for (int r3 = 0; r3 < 4; ++r3) {
+          const int r = 4 * r4 + r3;
+          const int64_t gr = r_lane + f * 32 + 8 * r4 + r3;
+          if (gr >= g.M) continue;
+          int32_t* crow = c_e + gr * ldc;
+          float* orow = out_e ? out_e + gr * ldc : nullptr;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (cmapx[j] < 0) continue;
+            const int32_t v = acc_int(acc[f][j][r], esh);
+            const int32_t cv = add ? (int32_t)((uint32_t)crow[cmapx[j]] + (uint32_t)v) : v;
+            crow[cmapx[j]] = cv;
+            if (last && orow) orow[cmapx[j]] = (float)cv * sab;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
 
   // The prologue issues its loads in the loop's order (the last substep's A
   // fragments after the second B load), so the loads in flight at the loop
@@ -442,14 +564,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   IMU_READ_B(0, sB[0], 0);
   const int nsteps = (int)steps;  // kp / BK * nlev < 2^29
   for (int i = 0; i < nsteps; ++i) {
-    if (cc.e != prev_e) {  // Horner: the exponents between the two steps
-      if constexpr (F6) flush_f32(acc, accf), f32_steps = 0;
+    if constexpr (F6) {
+      // Horner shift to this step's exponent, then the step: the accumulators
+      // must stay at most 2^24 in magnitude.  If the bound does not allow it,
+      // take the true maximum; if that does not allow it either, add the
+      // partial sums (at the exponent they hold) into C and restart from zero.
+      if (__builtin_expect(cc.e != prev_e || ub > kF32Exact - step_add, 0)) {
+        const int sh = shift * (prev_e - cc.e);
+        auto fits = [&](uint32_t u) __attribute__((always_inline)) {
+          return u == 0 || (sh <= 24 && ((uint64_t)u << sh) + step_add <= kF32Exact);
+        };
+        if (!fits(ub)) {
+          ub = wave_absmax(acc);
+          if (!fits(ub)) {
+            store_c(shift * prev_e, mode == 1 || flushed, false);
+            flushed = true;
+#pragma unroll
+            for (int f = 0; f < FR; ++f)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[f][j] = Acc{0};
+            ub = 0;
+          }
+        }
+        if (sh != 0) {
+          shift_acc(acc, min(sh, 24));  // with sh > 24 the accumulators are zero here
+          ub <<= min(sh, 24);
+        }
+        prev_e = cc.e;
+      }
+      ub += step_add;
+    } else if (cc.e != prev_e) {  // Horner: the exponents between the two steps
       shift_acc(acc, shift * (prev_e - cc.e));
       prev_e = cc.e;
-    }
-    if constexpr (F6) {
-      if (f32_steps == kF32Steps) flush_f32(acc, accf), f32_steps = 0;
-      ++f32_steps;
     }
     const int8_t* sbuf = sB[i & 1];
 #pragma unroll
@@ -481,99 +627,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 #undef IMU_READ_B
 #undef IMU_MFMA
 #undef IMU_ADV_B
-  if constexpr (F6) flush_f32(acc, accf);
-  if (prev_e > 0) shift_acc(acc, shift * prev_e);  // exponents below the last non-empty segment
-
-  // epilogue: accumulator register r of lane l holds element
-  // (8*(r/4) + 4*(l/32) + r%4, l%32) of each 32x32 block.  Rows are visited one
-  // at a time (f, r/4, r%4) with the four column blocks j of the row, so only a
-  // row's pointers are live.
-  const float sab = sa->s * sb->s;
-  const int64_t ldc = g.ldc;
-  const int64_t r_lane = row0 + 4 * (lane >> 5), c_lane = col0 + (lane & 31);
-  if (mode == 2) {  // extra tiles: every element lands on some C[i, n] with its shift
-#pragma unroll
-    for (int f = 0; f < FR; ++f)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t gr = r_lane + f * 32 + 8 * (r >> 2) + (r & 3);
-          const int64_t gc = c_lane + j * 32;
-          const int32_t am = amap[gr], bm = bmap[gc];
-          if (am < 0 || bm < 0) continue;
-          const int sh = shift * ((am >> 24) + (bm >> 24));
-          if (sh >= 32) continue;
-          atomicAdd(&c_e[(int64_t)(am & 0xFFFFFF) * ldc + (bm & 0xFFFFFF)], (int)((uint32_t)acc[f][j][r] << sh));
-        }
-    return;
-  }
-  // Base tiles.  A 4 x 4 transpose inside each quad of lanes turns the four
-  // rows r4 * 8 + 4 * (l / 32) + 0..3 held at column l % 32 into four
-  // consecutive columns of row ... + l % 4, so each lane stores 16 bytes and a
-  // store instruction covers eight full 128-byte row segments.  Needs 16-byte
-  // aligned rows and the whole tile inside N; otherwise one element per store.
-  // With B's columns in depth order (b_perm) the tile's slots map to scattered
-  // columns of C: element stores through the column map.
-  const bool bperm = ph->b_perm != 0;
-  const bool vec = !bperm && (ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(c_e) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(out_e) & 15) == 0 && col0 + BN <= g.N;
-  if (vec) {
-    const int64_t r_v = row0 + 4 * (lane >> 5) + (lane & 3), c_v = col0 + 4 * ((lane & 31) >> 2);
-#pragma unroll
-    for (int f = 0; f < FR; ++f)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int64_t gr = r_v + f * 32 + 8 * r4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int x[4] = {acc[f][j][4 * r4], acc[f][j][4 * r4 + 1], acc[f][j][4 * r4 + 2], acc[f][j][4 * r4 + 3]};
-          quad_transpose(x);
-          if (gr < g.M) {
-            v4u v = {(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
-            v4u* cp = reinterpret_cast<v4u*>(c_e + gr * ldc + c_v + 32 * j);
-            if (mode == 1) v += *cp;
-            *cp = v;
-            if (out_e) {
-              const float4 o = {(float)(int32_t)v.x * sab, (float)(int32_t)v.y * sab, (float)(int32_t)v.z * sab,
-                                (float)(int32_t)v.w * sab};
-              *reinterpret_cast<float4*>(out_e + gr * ldc + c_v + 32 * j) = o;
-            }
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    return;
-  }
-  // column of C held by this lane in block j (slot c_lane + 32 j), -1 past N
-  int64_t cmapx[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t slot = c_lane + 32 * j;
-    cmapx[j] = slot >= g.N ? -1 : bperm ? (int64_t)(bmap[slot] & 0xFFFFFF) : slot;
-  }
-#pragma unroll
-  for (int f = 0; f < FR; ++f)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-#pragma unroll
-      for (int r3 = 0; r3 < 4; ++r3) {
-        const int r = 4 * r4 + r3;
-        const int64_t gr = r_lane + f * 32 + 8 * r4 + r3;
-        if (gr >= g.M) continue;
-        int32_t* crow = c_e + gr * ldc;
-        float* orow = out_e ? out_e + gr * ldc : nullptr;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (cmapx[j] < 0) continue;
-          const int32_t v = acc[f][j][r];
-          const int32_t cv = mode == 1 ? (int32_t)((uint32_t)crow[cmapx[j]] + (uint32_t)v) : v;
-          crow[cmapx[j]] = cv;
-          if (orow) orow[cmapx[j]] = (float)cv * sab;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  // the exponent of the last non-empty segment is the shift still to apply
+  store_c(shift * prev_e, mode == 1 || flushed, true);
 }
 
 }  // namespace

@@ -104,8 +104,8 @@ def test_staged_path_matches_oracle(cfg):
 
 @pytest.mark.parametrize("cfg", FP6, ids=[_id(c) for c in FP6])
 def test_fp6_digits_match_oracle(cfg):
-    """The fp6 digit format (e2m3 codes on the f8f6f4 MFMA, fp32 partial sums
-    moved into the int32 Horner accumulators): the same plan, the digits
+    """The fp6 digit format (e2m3 codes on the f8f6f4 MFMA, the Horner sum in
+    the fp32 accumulators): the same plan, the digits
     decoded from the fp6 buffers equal the oracle's A' and B', and C is the
     same integer product."""
     _staged_problem(W.random_problem(**cfg), digits="fp6")
@@ -122,6 +122,33 @@ def test_fp6_wide_codes_and_levels():
         idx = rng.choice(flat.size, 7, replace=False)
         flat[idx] *= np.float32(scale)
     _staged_problem(pr, digits="fp6")
+
+
+@pytest.mark.parametrize("strats", [("mix", "mix"), ("row", "col"), ("col", "col"), ("col", "row")], ids="/".join)
+@pytest.mark.parametrize("fold", ["1", "0"], ids=["fold_columns", "atomic_columns"])
+def test_fp6_partial_sums_flushed_into_c(fold, strats, monkeypatch):
+    """fp6 products far beyond 2^24 (and beyond int32): the fp32 accumulators
+    cannot hold them, so waves add their exact partial sums into C on the way
+    (base tiles that store, base tiles that add after the extra-row pass, and
+    extra tiles) and C still equals the oracle's product modulo 2^32."""
+    monkeypatch.setenv("IMU_FOLD_COLUMNS", fold)
+    rng = np.random.Generator(np.random.PCG64(41))
+    a = rng.standard_normal((300, 1000)).astype(np.float32)
+    b = rng.standard_normal((1000, 260)).astype(np.float32)
+    a[5, 17], a[40, 3], a[280, 900] = 3e5, -2e5, 1e5
+    b[17, 9], b[3, 250], b[900, 140] = 4e5, 3e5, -2e5
+    ref = O.imunpack_matmul(a, b, 7, 4, strat_a=strats[0], strat_b=strats[1])
+    big = np.abs(np.asarray(ref.C, np.float64))
+    assert big.max() > 2 ** 31 and (big > 2 ** 24).sum() >= 3
+    print(f"\n[fp6 flush] fold={fold} {strats} plan {ref.plan.choice.m_u}x{ref.plan.choice.k_u}x"
+          f"{ref.plan.choice.n_u}", flush=True)
+    da = B.Matrix(torch.from_numpy(a).to("cuda"))
+    db = B.Matrix(torch.from_numpy(np.ascontiguousarray(b.T)).to("cuda"), "transposed")
+    out, c, info = B.imunpack_matmul(da, db, B.params(beta=7, bits=4, strat_a=strats[0], strat_b=strats[1],
+                                                       digits="fp6"))
+    assert info[0]["digits"] == B.DIGITS["fp6"]
+    assert np.array_equal(c[0].cpu().numpy(), ref.C32)
+    assert G.ulp_diff(out[0].cpu().numpy(), ref.out) <= 1
 
 
 @pytest.mark.parametrize("fold", ["1", "0"], ids=["fold_columns", "atomic_columns"])
