@@ -226,8 +226,10 @@ struct UnpackJobs {
 // position; the group that runs past a window's last position (one per
 // segment at most) reads the elements of its remaining positions from global
 // memory.
+// (fp6: three workgroups per CU leave room for the 16-position groups of
+// eight lines without spills)
 template <int DT, int BITS, bool OC, bool F6>
-__global__ __launch_bounds__(kThreads, 4) void unpack_kernel(UnpackJobs J) {
+__global__ __launch_bounds__(kThreads, F6 ? 3 : 4) void unpack_kernel(UnpackJobs J) {
   static_assert(!F6 || (!OC && BITS <= 4), "fp6 digits: inner-contiguous operands, bits <= 4");
   int bid = blockIdx.x, jo = 0;
   if (J.nops > 1 && bid >= J.wgs[0]) {
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 4) void unpack_kernel(UnpackJobs J) {
       if constexpr (F6) {
         // work items: (group, part of the lines), NS parts of LP lines each, so
         // that a window's few 16-position groups still spread over all threads
-        constexpr int NS = 4, LP = L / NS;
+        constexpr int NS = 2, LP = L / NS;
         const int gtot = s_pre[nseg];
         for (int it = tid; it < gtot * NS; it += kThreads) {
           const int gi = it / NS, part = it % NS;
