@@ -49,11 +49,11 @@ PAGE_RATIOS = {"mix": 1.06, "row/row": 2.02, "row/col": 5.36, "col/row": 1.64, "
 # traffic is reported as null.
 GEMM_TRAFFIC = {
     ("mlp_up", "fp6"): {"source_sha256": "75ee940b59fd7fa9c4df8209c17ad76ac5ef899d8c47478722c675d14f4044ec",
-                        "fetch_kib": 1573495.8, "write_kib": 384921.3, "fetch_factor": 1.9998, "write_factor": 1.0000,
-                        "bytes_per_launch": 3616356558},
-    ("llama_linear", "int8"): {"source_sha256": "4ac18924ace4f1418e62a0f320e35befe56895c86288846135d44db868ec13df",
-                               "fetch_kib": 151225.5, "write_kib": 65536.0, "fetch_factor": 1.9998,
-                               "write_factor": 1.0000, "bytes_per_launch": 376787717},
+                        "fetch_kib": 1583157.9, "write_kib": 384870.0, "fetch_factor": 1.9998, "write_factor": 1.0000,
+                        "bytes_per_launch": 3636090028},
+    ("llama_linear", "int8"): {"source_sha256": "75ee940b59fd7fa9c4df8209c17ad76ac5ef899d8c47478722c675d14f4044ec",
+                               "fetch_kib": 151235.0, "write_kib": 65536.0, "fetch_factor": 1.9998,
+                               "write_factor": 1.0000, "bytes_per_launch": 376807171},
 }
 
 
