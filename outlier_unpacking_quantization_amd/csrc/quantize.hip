@@ -1151,16 +1151,21 @@ hipError_t launch_softmax_hist(int zdtype, const SoftmaxIn& in, QuantJobs J, hip
 
 // Count kernels: tiles of 512 columns x rows_per_wg rows, about kCountWgs workgroups
 // in total (fewer workgroups: fewer column atomics; more: more loads in flight).
+// An operand's share is in proportion to the tile lanes it occupies (a row
+// narrower than a tile still takes the tile's width), so a narrow operand
+// beside a wide one gets short workgroups instead of a few long ones.
 static int plan_tiles(QuantJobs& J, int kCountWgs) {
+  auto lanes = [](const QuantOp& q) {
+    return (double)q.s.srows * (double)(ceil_div(q.s.scols, kColsPerTile) * kColsPerTile) * q.batch;
+  };
   double total = 0;
-  for (int o = 0; o < J.nops; ++o) total += (double)J.op[o].s.srows * J.op[o].s.scols * J.op[o].batch;
+  for (int o = 0; o < J.nops; ++o) total += lanes(J.op[o]);
   int begin = 0;
   for (int o = 0; o < J.nops; ++o) {
     QuantOp& q = J.op[o];
     const int64_t ctiles = ceil_div(q.s.scols, kColsPerTile);
-    const double el = (double)q.s.srows * q.s.scols * q.batch;
-    const int64_t want = max64((int64_t)(kCountWgs * el / total + 0.5), 1);  // workgroups for this operand
-    int64_t rblocks = max64(want / (ctiles * q.batch), 1);
+    const int64_t want = max64((int64_t)(kCountWgs * lanes(q) / total + 0.5), 1);  // workgroups for this operand
+    int64_t rblocks = max64(ceil_div(want, ctiles * q.batch), 1);
     int64_t rpw = ceil_div(q.s.srows, rblocks);
     rpw = min64(max64(rpw, 4), 32768);  // column counts of the bf16 path are 16-bit
     rblocks = ceil_div(q.s.srows, rpw);
