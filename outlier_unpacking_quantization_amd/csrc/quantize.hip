@@ -1090,8 +1090,9 @@ hipError_t launch_fill_2d(int32_t* p, int64_t rows, int64_t cols, int64_t ld, in
   return hipGetLastError();
 }
 
-// Histogram: about `target` workgroups in total, shared in proportion to size
-// (at least one per batch entry).
+// Histogram: at most about `target` workgroups in total (one per CU: the
+// 128 KB histogram allows one), shared in proportion to size and rounded
+// down, so that the launch is one round (at least one per batch entry).
 static int plan_hist(QuantJobs& J, int target) {
   double total = 0;
   for (int o = 0; o < J.nops; ++o) total += (double)J.op[o].s.srows * J.op[o].s.scols * J.op[o].batch;
@@ -1100,7 +1101,7 @@ static int plan_hist(QuantJobs& J, int target) {
     QuantOp& q = J.op[o];
     const double el = (double)q.s.srows * q.s.scols;
     const int64_t units = q.s.srows * ceil_div(q.s.scols, kColsPerTile);
-    int64_t per = (int64_t)(target * el / total + 0.5);
+    int64_t per = (int64_t)(target * el / total);
     per = min64(max64(per, 1), max64(units, 1));
     q.wgs_per_entry = (int)per;
     q.wg_begin = begin;
