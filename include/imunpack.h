@@ -34,8 +34,9 @@
  * - The integer result C is defined modulo 2^32 (two's complement int32),
  *   which equals the exact product whenever it fits in int32.  There is no
  *   overflow status: the digit products (int8 -> int32 MFMA, or fp6 -> fp32
- *   MFMA with exact integer partial sums below 2^24 moved into int32) and
- *   the int32 shift-and-add fold never form the product in wider integers, so an exact
+ *   MFMA whose integer sums stay within 2^24 and are added into C as int32
+ *   when they could pass it) and the int32 shift-and-add fold never form the
+ *   product in wider integers, so an exact
  *   overflow test would need a second, wider product.  A caller can bound
  *   |C| <= K * max|q_A| * max|q_B| from the statistics headers (maxkey and r).
  * - Batched operands (batch > 1) are independent problems: each batch entry
@@ -266,7 +267,9 @@ imu_status imu_unpack(const imu_matrix* x, int32_t operand, const imu_params* p,
  * fold and dequantization ("Approach": power-of-two scaling and summation
  * reproduce the integer GEMM exactly).  For each exponent segment e the digit
  * product P_e = A'[:,K'_e] . B'[K'_e,:] (int8 MFMA, or fp6 MFMA into fp32
- * partial sums of at most 2048 * 128 positions, moved into int32) is accumulated as
+ * sums that stay integers within 2^24: each wave bounds its sums and, before
+ * they could pass 2^24, adds them into C as int32 shifted to their exponent
+ * and starts again from zero) is accumulated as
  * acc = acc * 2^(bits-1) + P_e (from the highest e down); each unpacked
  * element (i,u),(n,w) then adds acc << ((bits-1)(u+w)) into C[i,n] (mod 2^32).
  * c: int32 M x N row-major per entry (ldc elements per row, entries
