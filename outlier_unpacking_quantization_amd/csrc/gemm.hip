@@ -545,6 +545,13 @@ __global__ __launch_bounds__(kThreads, F6 ? 2 : 1) void gemm_kernel(GemmArgs g) 
   // head are the same on entry and on the back edge: the wait before the B
   // store then covers the B loads only, not the A fragments issued after them.
   // the A loads of a substep go out one after each of its 8 MFMAs
+// fp6 (two workgroups per CU): a wave raises its priority while it issues a
+// substep's MFMAs, so the two waves of a SIMD take turns at the MFMA pipe
+#define IMU_PRIO(p)                                                                            \
+  if constexpr (F6) {                                                                          \
+    __builtin_amdgcn_s_setprio(p);                                                             \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+  }
 #define IMU_INTERLEAVE()                                                                       \
   _Pragma("unroll") for (int k_ = 0; k_ < 8; ++k_) {                                          \
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* one MFMA */                          \
@@ -602,10 +609,12 @@ __global__ __launch_bounds__(kThreads, F6 ? 2 : 1) void gemm_kernel(GemmArgs g) 
     for (int q = 0; q < NQ - 1; ++q) {
       IMU_READ_B((q + 1) & 1, sbuf, q + 1);
       __builtin_amdgcn_sched_barrier(0);
+      IMU_PRIO(1);
       IMU_MFMA(q & 1, q);
       IMU_LOAD_A(q, la.k);
       IMU_INTERLEAVE();
       __builtin_amdgcn_sched_barrier(0);
+      IMU_PRIO(0);
     }
     IMU_STORE_B((i + 1) & 1);  // B of step i+1 (loaded during step i-1)
     IMU_LOAD_B(lb.k);          // B of step i+2
@@ -613,14 +622,17 @@ __global__ __launch_bounds__(kThreads, F6 ? 2 : 1) void gemm_kernel(GemmArgs g) 
     __syncthreads();
     IMU_READ_B(0, sB[(i + 1) & 1], 0);
     __builtin_amdgcn_sched_barrier(0);
+    IMU_PRIO(1);
     IMU_MFMA(1, NQ - 1);
     IMU_LOAD_A(NQ - 1, la.k);
     IMU_INTERLEAVE();
     __builtin_amdgcn_sched_barrier(0);
+    IMU_PRIO(0);
     walk_step<FOLD>(la, nseg, nlev, off);
     walk_step<FOLD>(cc, nseg, nlev, off);
   }
 #undef IMU_INTERLEAVE
+#undef IMU_PRIO
 #undef IMU_LOAD_A
 #undef IMU_LOAD_B
 #undef IMU_STORE_B
