@@ -48,12 +48,12 @@ PAGE_RATIOS = {"mix": 1.06, "row/row": 2.02, "row/col": 5.36, "col/row": 1.64, "
 # the GEMM source: when gemm.hip no longer hashes to `source_sha256` the
 # traffic is reported as null.
 GEMM_TRAFFIC = {
-    ("mlp_up", "fp6"): {"source_sha256": "75ee940b59fd7fa9c4df8209c17ad76ac5ef899d8c47478722c675d14f4044ec",
-                        "fetch_kib": 1583157.9, "write_kib": 384870.0, "fetch_factor": 1.9998, "write_factor": 1.0000,
-                        "bytes_per_launch": 3636090028},
-    ("llama_linear", "int8"): {"source_sha256": "75ee940b59fd7fa9c4df8209c17ad76ac5ef899d8c47478722c675d14f4044ec",
-                               "fetch_kib": 151235.0, "write_kib": 65536.0, "fetch_factor": 1.9998,
-                               "write_factor": 1.0000, "bytes_per_launch": 376807171},
+    ("mlp_up", "fp6"): {"source_sha256": "12ba33480fb65dcb01da2106562874d38a2404b7005609f43d25e54375f9bbfb",
+                        "fetch_kib": 1677433.2, "write_kib": 384845.3, "fetch_factor": 1.9998, "write_factor": 1.0000,
+                        "bytes_per_launch": 3829121242},
+    ("llama_linear", "int8"): {"source_sha256": "12ba33480fb65dcb01da2106562874d38a2404b7005609f43d25e54375f9bbfb",
+                               "fetch_kib": 151231.6, "write_kib": 65536.0, "fetch_factor": 1.9998,
+                               "write_factor": 1.0000, "bytes_per_launch": 376800209},
 }
 
 
