@@ -28,6 +28,10 @@
  *   read the plan header (the unpacked sizes are data dependent).  Calls on one
  *   device from several host threads take turns between the planner launch and
  *   that read (they share the device's header buffer).
+ * - IMU_LOG=1 in the environment prints, at that read, one line per batch
+ *   entry on stderr: the chosen candidates, M' K' N', the unpack ratio, k_pad
+ *   and the exponent segments' lengths, the row and column bases and
+ *   allocations, the digit format and the plan status.
  * - Argument errors are returned synchronously and nothing is enqueued.
  *   Conditions found on the device (non-finite input, |x.r| >= 2^31) are
  *   latched in the operand's statistics and returned at the next wait.

@@ -372,13 +372,37 @@ imu_status plan_staged(DeviceCtx& st, const Operand& oa, const Operand& ob, cons
 
 // Fill info from the staged headers (B' entries follow all A' entries) and
 // report a failed plan.  *a_total / *b_total: bytes of all A' / B' entries.
+// IMU_LOG=1: one line per batch entry on stderr with the plan a call made
+// (candidates chosen, unpacked sizes, exponent segments, layout, digit format).
+void log_plan(const Operand& oa, const Operand& ob, const PlanHeader* h, int b) {
+  static const char* const kCand[] = {"row", "col", "cr", "rc", "greedy"};
+  auto cand = [](int c) { return c >= 0 && c < 5 ? kCand[c] : "?"; };
+  char segs[kMaxSeg * 12 + 1];
+  int at = 0;
+  for (int q = 0; q < h->n_seg && q < kMaxSeg && at < (int)sizeof(segs) - 12; ++q)
+    at += std::snprintf(segs + at, sizeof(segs) - at, q ? ",%d" : "%d", h->seg_len[q]);
+  segs[at] = 0;
+  std::fprintf(stderr,
+               "imu plan: entry %d: %lldx%lldx%lld choice %s/%s M'=%lld K'=%lld N'=%lld unpack ratio %.4f; "
+               "k_pad %lld, segments [%s]; rows base %lld alloc %lld, columns base %lld alloc %lld; digits %s; "
+               "status %d\n",
+               b, (long long)oa.R, (long long)oa.C, (long long)ob.C, cand(h->choice_a), cand(h->choice_b),
+               (long long)h->m_u, (long long)h->k_u, (long long)h->n_u,
+               (double)h->m_u * (double)h->k_u * (double)h->n_u / ((double)oa.R * (double)oa.C * (double)ob.C),
+               (long long)h->k_pad, segs, (long long)h->m_base, (long long)h->m_alloc, (long long)h->n_base,
+               (long long)h->n_alloc, h->fmt == kDigitsFp6 ? "fp6" : "int8", h->status);
+}
+
 imu_status finish_plan(const Operand& oa, const Operand& ob, const uint8_t* hdrs, int batch, imu_plan_info* info,
                        int64_t* a_total, int64_t* b_total) {
   int status = 0;
   int64_t aoff = 0, boff = 0;
+  const char* lg = std::getenv("IMU_LOG");
+  const bool log = lg && lg[0] == '1';
   for (int b = 0; b < batch; ++b) {
     const PlanHeader* h = reinterpret_cast<const PlanHeader*>(hdrs + (size_t)b * kPlanHeaderStride);
     status |= h->status;
+    if (log) log_plan(oa, ob, h, b);
     if (info) {
       imu_plan_info& f = info[b];
       std::memset(&f, 0, sizeof(f));

@@ -361,6 +361,22 @@ def test_int32_wraparound_matches_modular_oracle():
     assert G.ulp_diff(out, ref.out) <= 1
 
 
+def test_plan_log_lines(monkeypatch, capfd):
+    """IMU_LOG=1: one stderr line per batch entry naming the plan the call
+    made, which is the oracle's (candidates and unpacked sizes)."""
+    monkeypatch.setenv("IMU_LOG", "1")
+    pr = W.random_problem(seed=60, m=130, k=257, n=129, kind="linear", batch=2)
+    a, b = G.to_device(pr.a), G.to_device(pr.b)
+    _, _, info = B.imunpack_matmul(a, b, G.params_of(pr))
+    torch.cuda.synchronize()
+    lines = [ln for ln in capfd.readouterr().err.splitlines() if ln.startswith("imu plan: entry")]
+    assert len(lines) == 2
+    for e, (ln, ref) in enumerate(zip(lines, G.oracle_entries(pr, unpacked=False))):
+        ch = ref.plan.choice
+        assert ln.startswith(f"imu plan: entry {e}: 130x257x129 choice {info[e]['choice'][0]}/{info[e]['choice'][1]} ")
+        assert f"M'={ch.m_u} K'={ch.k_u} N'={ch.n_u} " in ln and "status 0" in ln
+
+
 def test_workspace_grows_and_results_repeat():
     pr = W.random_problem(21, 150, 300, 140, kind="linear")
     a, b = G.to_device(pr.a), G.to_device(pr.b)
