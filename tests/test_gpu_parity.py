@@ -364,10 +364,14 @@ def test_int32_wraparound_matches_modular_oracle():
 def test_plan_log_lines(monkeypatch, capfd):
     """IMU_LOG=1: one stderr line per batch entry naming the plan the call
     made, which is the oracle's (candidates and unpacked sizes)."""
-    monkeypatch.setenv("IMU_LOG", "1")
     pr = W.random_problem(seed=60, m=130, k=257, n=129, kind="linear", batch=2)
     a, b = G.to_device(pr.a), G.to_device(pr.b)
-    _, _, info = B.imunpack_matmul(a, b, G.params_of(pr))
+    ws = B.Workspace("cuda")
+    B.imunpack_matmul(a, b, G.params_of(pr), ws=ws)  # sizes the workspace (a call that reports
+    torch.cuda.synchronize()                        # IMU_ERR_WORKSPACE also logs its plan)
+    monkeypatch.setenv("IMU_LOG", "1")
+    capfd.readouterr()
+    _, _, info = B.imunpack_matmul(a, b, G.params_of(pr), ws=ws)
     torch.cuda.synchronize()
     lines = [ln for ln in capfd.readouterr().err.splitlines() if ln.startswith("imu plan: entry")]
     assert len(lines) == 2
