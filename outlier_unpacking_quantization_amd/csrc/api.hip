@@ -528,7 +528,6 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
       return fail(IMU_ERR_INVALID_ARG, "plan sizes are not tile multiples");
     if (f.fmt != get(0).fmt || (f.fmt != kDigitsInt8 && f.fmt != kDigitsFp6))
       return fail(IMU_ERR_INVALID_ARG, "the entries' digit formats differ or are unknown");
-    base_tiles = std::max(base_tiles, (f.m_base / 256) * (f.n_base / 128));
     base_total += (f.m_base / 256) * (f.n_base / 128);
   }
   int cus = 0;
@@ -536,6 +535,17 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
     DeviceCtx* ctx = nullptr;
     IMU_TRY(current_ctx(0, &ctx));
     cus = ctx->cus;
+  }
+  // Tile rows: 256, or for int8 digits 128 when the 256-row base tiles would
+  // be fewer than the CUs (a launch that would leave CUs idle gets twice the
+  // tiles, and its smaller tiles fit more workgroups per CU).  m_base and
+  // m_alloc are multiples of 256, so of either.
+  const int64_t tr = get(0).fmt == kDigitsInt8 && base_total < cus ? 128 : 256;
+  base_total = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    const EntrySizes f = get(b);
+    base_tiles = std::max(base_tiles, (f.m_base / tr) * (f.n_base / 128));
+    base_total += (f.m_base / tr) * (f.n_base / 128);
   }
   // IMU_FOLD_COLUMNS=1 / 0 forces the choice (both give the same result)
   const char* fe = std::getenv("IMU_FOLD_COLUMNS");
@@ -547,7 +557,7 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
     const bool rowx = f.m_alloc > f.m_base, colx = f.n_alloc > f.n_base;
     if (rowx || (colx && !fold_cols)) {
       any_atomic = true;
-      extra_tiles = std::max(extra_tiles, (f.m_alloc / 256) * (f.n_alloc / 128));
+      extra_tiles = std::max(extra_tiles, (f.m_alloc / tr) * (f.n_alloc / 128));
     } else if (colx) {
       any_fold = true;
     }
@@ -573,6 +583,7 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   g.bits = p->bits;
   g.fold_cols = fold_cols ? 1 : 0;
   g.fmt = get(0).fmt;
+  g.tile_rows = (int)tr;
   // Tile order: each XCD takes a run of tiles covering G tile rows; its L2
   // then fills G row panels of A' and about T / (8 G) column panels of B'^T,
   // which is least near G = sqrt(T BN / (8 BM)) (rounded to a power of two).
@@ -580,12 +591,12 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
     int64_t tm = 1, tn = 1;
     for (int64_t b = 0; b < batch; ++b) {
       const EntrySizes f = get(b);
-      if ((f.m_base / 256) * (f.n_base / 128) >= tm * tn) {
-        tm = f.m_base / 256;
+      if ((f.m_base / tr) * (f.n_base / 128) >= tm * tn) {
+        tm = f.m_base / tr;
         tn = f.n_base / 128;
       }
     }
-    const double ideal = std::sqrt((double)(tm * tn) * 128.0 / (8.0 * 256.0));
+    const double ideal = std::sqrt((double)(tm * tn) * 128.0 / (8.0 * (double)tr));
     int gsz = 1;
     while (gsz * 2 <= tm && std::log2(gsz * 2.0) <= std::log2(std::max(ideal, 1.0)) + 0.5) gsz *= 2;
     g.group_m = gsz;

@@ -64,8 +64,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-constexpr int FR = 2;  // 32-row A fragments per wave
-constexpr int BM = 128 * FR, BN = 128, BK = 128;
+constexpr int BN = 128, BK = 128;
 constexpr int kThreads = 256;
 constexpr int BSTR = BK + 16;  // LDS bytes per staged B row
 constexpr int BSTR6 = BK / 4 * 3 + 8;  // fp6: 96 bytes of a step plus 8 (row r starts at bank 26 r mod 32)
@@ -128,6 +127,7 @@ __device__ inline void quad_transpose(int (&x)[4]) {
   x[3] = odd ? x[3] : s[2];
 }
 
+template <int FR>
 __device__ inline void shift_acc(v16i (&acc)[FR][4], int sh) {
 #pragma unroll
   for (int i = 0; i < FR; ++i)
@@ -138,6 +138,7 @@ __device__ inline void shift_acc(v16i (&acc)[FR][4], int sh) {
 }
 // fp6: multiply the accumulators by 2^sh, 0 <= sh <= 24 (exact: a power of
 // two, and the products stay finite)
+template <int FR>
 __device__ inline void shift_acc(v16f (&acc)[FR][4], int sh) {
   const float f = __int_as_float((127 + sh) << 23);
 #pragma unroll
@@ -146,6 +147,7 @@ __device__ inline void shift_acc(v16f (&acc)[FR][4], int sh) {
     for (int j = 0; j < 4; ++j) acc[i][j] *= f;
 }
 // fp6: largest |acc| of the wave (an integer at most 2^24), wave-uniform
+template <int FR>
 __device__ inline uint32_t wave_absmax(const v16f (&acc)[FR][4]) {
   float m = 0.f;
 #pragma unroll
@@ -253,8 +255,12 @@ __device__ __attribute__((aligned(64))) const int8_t kZeroBlock[64] = {};  // di
 // run the Horner sum themselves, kept at most 2^24 in magnitude (so exact) by
 // the wave's bound and its flushes into C.  With a single set of
 // accumulators the kernel fits two workgroups per CU.
-template <bool FOLD, bool F6>
-__global__ __launch_bounds__(kThreads, F6 ? 2 : 1) void gemm_kernel(GemmArgs g) {
+// FR: 32-row A fragments per wave, 2 (tile 256 x 128) or, for int8 digits,
+// 1 (tile 128 x 128: more, smaller tiles for launches that would leave CUs
+// idle, and a third of the registers for more workgroups per CU).
+template <bool FOLD, bool F6, int FR>
+__global__ __launch_bounds__(kThreads, F6 || FR == 1 ? 2 : 1) void gemm_kernel(GemmArgs g) {
+  constexpr int BM = 128 * FR;
   constexpr int SB = F6 ? BSTR6 : BSTR;  // LDS bytes per staged B row
   constexpr int NQ = F6 ? 2 : 4;         // MFMA substeps per K step
   __shared__ __attribute__((aligned(16))) int8_t sB[2][BN * SB];
@@ -658,12 +664,15 @@ hipError_t launch_gemm(const GemmArgs& g, int64_t tiles_x, int batch, bool fold,
     if (start || stop) hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, start, stop, 0, g);
     else hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, g);
   };
-  if (g.fmt == kDigitsFp6) {
-    if (fold) go(gemm_kernel<true, true>);
-    else go(gemm_kernel<false, true>);
-  } else if (g.fmt == kDigitsInt8) {
-    if (fold) go(gemm_kernel<true, false>);
-    else go(gemm_kernel<false, false>);
+  if (g.fmt == kDigitsFp6 && g.tile_rows == 256) {
+    if (fold) go(gemm_kernel<true, true, 2>);
+    else go(gemm_kernel<false, true, 2>);
+  } else if (g.fmt == kDigitsInt8 && g.tile_rows == 256) {
+    if (fold) go(gemm_kernel<true, false, 2>);
+    else go(gemm_kernel<false, false, 2>);
+  } else if (g.fmt == kDigitsInt8 && g.tile_rows == 128) {
+    if (fold) go(gemm_kernel<true, false, 1>);
+    else go(gemm_kernel<false, false, 1>);
   } else {
     return hipErrorInvalidValue;
   }

@@ -106,6 +106,7 @@ struct GemmArgs {
   int fold_cols;              // entries with extra columns only fold them in the base pass
   int group_m;                // tile rows per group of the workgroup -> tile order (power of two)
   int fmt;                    // digit format of every entry (kDigitsInt8 / kDigitsFp6)
+  int tile_rows;              // rows of a tile (columns: 128): 256, or 128 for int8 digits
 };
 // tiles_x: the largest tile count of an entry for this mode; batch entries on
 // blockIdx.y.  start / stop: events recorded as the launch starts / ends
