@@ -48,12 +48,12 @@ PAGE_RATIOS = {"mix": 1.06, "row/row": 2.02, "row/col": 5.36, "col/row": 1.64, "
 # the GEMM source: when gemm.hip no longer hashes to `source_sha256` the
 # traffic is reported as null.
 GEMM_TRAFFIC = {
-    ("mlp_up", "fp6"): {"source_sha256": "12ba33480fb65dcb01da2106562874d38a2404b7005609f43d25e54375f9bbfb",
-                        "fetch_kib": 1677433.2, "write_kib": 384845.3, "fetch_factor": 1.9998, "write_factor": 1.0000,
-                        "bytes_per_launch": 3829121242},
-    ("llama_linear", "int8"): {"source_sha256": "12ba33480fb65dcb01da2106562874d38a2404b7005609f43d25e54375f9bbfb",
-                               "fetch_kib": 151231.6, "write_kib": 65536.0, "fetch_factor": 1.9998,
-                               "write_factor": 1.0000, "bytes_per_launch": 376800209},
+    ("mlp_up", "fp6"): {"source_sha256": "f12a4fb5a112327b4d7dd453fd11369b1645b15aece5d5cf52fb55a3cbf4fbee",
+                        "fetch_kib": 1675866.7, "write_kib": 384852.2, "fetch_factor": 1.9998, "write_factor": 1.0000,
+                        "bytes_per_launch": 3825920437},
+    ("llama_linear", "int8"): {"source_sha256": "f12a4fb5a112327b4d7dd453fd11369b1645b15aece5d5cf52fb55a3cbf4fbee",
+                               "fetch_kib": 151217.5, "write_kib": 65536.0, "fetch_factor": 1.9998,
+                               "write_factor": 1.0000, "bytes_per_launch": 376771335},
 }
 
 
