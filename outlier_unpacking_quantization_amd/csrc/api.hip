@@ -538,9 +538,17 @@ imu_status gemm_impl(const int8_t* a_u, const int8_t* b_u, const imu_params* p, 
   }
   // Tile rows: 256, or for int8 digits 128 when the 256-row base tiles would
   // be fewer than the CUs (a launch that would leave CUs idle gets twice the
-  // tiles, and its smaller tiles fit more workgroups per CU).  m_base and
-  // m_alloc are multiples of 256, so of either.
-  const int64_t tr = get(0).fmt == kDigitsInt8 && base_total < cus ? 128 : 256;
+  // tiles, and its smaller tiles fit more workgroups per CU), or as many as
+  // the CUs with some entry folding extra columns (tiles of unequal depth:
+  // smaller ones even out the CUs' work).  m_base and m_alloc are multiples
+  // of 256, so of either.
+  bool folds = false;
+  for (int64_t b = 0; b < batch; ++b) {
+    const EntrySizes f = get(b);
+    folds = folds || (f.n_alloc > f.n_base && f.m_alloc == f.m_base);
+  }
+  const int64_t tr =
+      get(0).fmt == kDigitsInt8 && (base_total < cus || (base_total == cus && folds)) ? 128 : 256;
   base_total = 0;
   for (int64_t b = 0; b < batch; ++b) {
     const EntrySizes f = get(b);
