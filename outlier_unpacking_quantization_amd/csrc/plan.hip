@@ -323,14 +323,16 @@ __device__ void choose(const PlanArgs& a, int b, int64_t G, bool write_header, P
   // and can all be in flight at once
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   constexpr int kGroups = kThreads / kPlanSums;  // thread t adds value t % 35 of records t / 35 (mod kGroups)
-  if (t < kGroups * kPlanSums) {  // loads of 4 records in flight at a time
+  constexpr int kLoads = 8;                      // loads in flight per thread: 56 records a round
+  if (t < kGroups * kPlanSums) {
     const int j = t % kPlanSums, g = t / kPlanSums;
     long long v = 0;
-    for (int64_t q0 = g; q0 < G; q0 += 4 * kGroups) {
-      long long w[4];
+    for (int64_t q0 = g; q0 < G; q0 += kLoads * kGroups) {
+      long long w[kLoads];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = q0 + i * kGroups < G ? E.rec[q0 + i * kGroups].sum[j] : 0;
-      v += w[0] + w[1] + w[2] + w[3];
+      for (int i = 0; i < kLoads; ++i) w[i] = E.rec[min64(q0 + i * kGroups, G - 1)].sum[j];  // unconditional
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) v += q0 + i * kGroups < G ? w[i] : 0;
     }
     S.red[g][j] = v;
   }
@@ -479,36 +481,40 @@ __device__ void layout(const PlanArgs& a, int b, int64_t w, bool write_header, P
   const PlanLayout& L = a.pl;
   const Entry E = entry_of(a, b);
   const Chunk me = chunk_of(L, w);
-  const int64_t wk0[3] = {0, L.wg_a, L.wg_a + L.wg_b};
-  const int64_t wkn[3] = {L.wg_a, L.wg_b, L.wg_k};
+  // first record and number of records of a kind (selects, not an indexed
+  // array, which would live in scratch memory)
+  auto wk0 = [&](int kind) { return kind == 0 ? (int64_t)0 : kind == 1 ? L.wg_a : L.wg_a + L.wg_b; };
+  auto wkn = [&](int kind) { return kind == 0 ? L.wg_a : kind == 1 ? L.wg_b : L.wg_k; };
   // records written by the previous launch, read kBatch chunks at a time with
-  // all loads in flight (a plain loop would wait for each in turn)
-  constexpr int kBatch = 8;
+  // all loads in flight (a plain loop would wait for each in turn; the loads
+  // are unconditional, at clamped indices, so that none waits behind a branch)
+  constexpr int kBatch = 16;
   for (int job = t; job < 3 * kPlanTasks; job += kThreads) {
     const int kind = job / kPlanTasks, task = job % kPlanTasks;
+    const int64_t n0 = wk0(kind), nk = wkn(kind);
     long long run = 0;
-    for (int64_t r0 = 0; r0 < wkn[kind]; r0 += kBatch) {
+    for (int64_t r0 = 0; r0 < nk; r0 += kBatch) {
       int v[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        v[j] = r0 + j < wkn[kind] ? E.rec[wk0[kind] + r0 + j].cnt[task] : 0;
+      for (int j = 0; j < kBatch; ++j) v[j] = E.rec[n0 + min64(r0 + j, nk - 1)].cnt[task];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         if (kind == me.kind && r0 + j == me.rank) S.off[task] = (int)run;
-        run += v[j];
+        run += r0 + j < nk ? v[j] : 0;
       }
     }
     S.task_tot[kind][task] = run;
   }
   if (t < 3) {  // lev_a (A rows), lev_b (B columns), emax (k)
     const int kind = t, field = t == 2 ? 2 : 0;
+    const int64_t n0 = wk0(kind), nk = wkn(kind);
     int m = t == 2 ? 0 : 1;
-    for (int64_t r0 = 0; r0 < wkn[kind]; r0 += kBatch) {
+    for (int64_t r0 = 0; r0 < nk; r0 += kBatch) {
       int v[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) v[j] = r0 + j < wkn[kind] ? E.rec[wk0[kind] + r0 + j].mx[field] : m;
+      for (int j = 0; j < kBatch; ++j) v[j] = E.rec[n0 + min64(r0 + j, nk - 1)].mx[field];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) m = max(m, v[j]);
+      for (int j = 0; j < kBatch; ++j) m = max(m, v[j]);  // a clamped index repeats a record
     }
     if (t < 2) S.lev[t] = min(m, (int)L.levels);
     else S.nseg = min(m, (int)L.segments - 1) + 1;
