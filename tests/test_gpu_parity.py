@@ -329,6 +329,28 @@ def test_edge_cases_fp6(name):
                                                               ref.plan.choice.n_u)
 
 
+def test_plan_with_many_chunks():
+    """A plan over 57 chunks of 512 lines (28000 rows of A, one chunk each of k
+    and of B's columns): more than one round of the planner's record reads
+    (56 records a round in the choice, 16 in the layout), with heavy rows and
+    columns so that A takes extra rows."""
+    rng = np.random.default_rng(2024)
+    a_np = rng.standard_normal((28000, 64)).astype(np.float32)
+    a_np[rng.choice(28000, 40, replace=False)] *= 30
+    a_np[:, [3, 17]] *= 25
+    b_np = rng.standard_normal((64, 128)).astype(np.float32)
+    b_np[:, 5] *= 40
+    print(f"\n[chunks] {a_np.shape}x{b_np.shape}", flush=True)
+    ref = O.imunpack_matmul(a_np, b_np, 15, 5)
+    out, c, info = _single(a_np, b_np)
+    ch = ref.plan.choice
+    assert info["choice"] == (ch.cand_a, ch.cand_b)
+    assert (info["m_u"], info["k_u"], info["n_u"]) == (ch.m_u, ch.k_u, ch.n_u)
+    assert info["pairs"] == ch.table
+    assert np.array_equal(c, ref.C32)
+    assert G.ulp_diff(out, ref.out) <= 1
+
+
 @pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
 def test_nonfinite_input_is_reported(bad):
     a = np.ones((20, 30), np.float32)
