@@ -404,10 +404,18 @@ __device__ __forceinline__ void finish_first_pass(const uint32_t* h, uint32_t sm
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // key bins: lane-consecutive bins, so that a wave's atomics fall on two
-  // 128-byte lines
-  for (int i = threadIdx.x; i < NB; i += blockDim.x) {
-    const uint32_t c = h[i];
-    if (c) atomicAdd(&gh[i], c);
+  // 128-byte lines; 8 LDS reads in flight before their atomics (a loop of
+  // read, wait, atomic would pay the LDS latency 32 times).  The workgroup
+  // has 1024 threads.
+  static_assert(NB % (8 * 1024) == 0, "bins per thread in groups of 8");
+#pragma unroll
+  for (int j0 = 0; j0 < NB / 1024; j0 += 8) {
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = h[threadIdx.x + 1024 * (j0 + j)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c[j]) atomicAdd(&gh[threadIdx.x + 1024 * (j0 + j)], c[j]);
   }
   // coarse counts: thread t sums bins [32t, 32t + 32) (16-byte reads, the
   // chunk order rotated by lane so that 8 lanes read 8 different banks);
